@@ -1,0 +1,344 @@
+/*
+ * oracle.c -- plain, slow, f64 CPU oracle for block-quantized GEMV in LLM decode.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg may load this library.  It shares no code, header, table or
+ * helper with the HIP library; it reads the GGUF-native block bytes that the
+ * seeded generators write, never the packed device layout.
+ *
+ * Every value is carried in double precision.  Each function names the page
+ * and item its arithmetic follows:
+ *   [ILayer]  "Crate inferencelayer" (docs.rs, inferencelayer 0.2.4), items
+ *             under "Functions".
+ *   [Gpu]     "Module gpu" (cherenkov qwen4_exp::gpu docs), items under
+ *             "Structs", "Modules" and "Type Aliases".
+ *   [Honey]   "honeycrisp mod.rs" (Apple-Silicon Metal backend source), items
+ *             named by the Rust function or match arm they sit in.
+ *
+ * The pages never print a worked numeric example, so the tests pin this file
+ * with hand-built blocks, closed forms and invariants instead.  Two things
+ * stay "parity unpinned": agreement with a real GGUF artifact, and the exact
+ * GGUF bit order of Q4_0 nibbles and Q4_K (scale, min) pairs, which the pages
+ * leave open (readings listed in the design notes).
+ *
+ * Parallelism: output rows are independent, so an OpenMP loop runs over them.
+ * The order of the K-sum inside one output is the plain ascending k order.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_Q4_0 2
+#define ORC_Q8_0 8
+#define ORC_Q4_K 12
+
+/* ---------------------------------------------------------------------------
+ * IEEE 754 binary16 -> double, exact for every bit pattern (little-endian
+ * storage is a reading: the pages say the blocks are read "as-is" from GGUF,
+ * [ILayer] gemv_q8_0n_k_lcpp_src, and GGUF is little-endian).
+ * ------------------------------------------------------------------------- */
+double orc_f16(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 31;
+    int mant = h & 1023;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)mant, -24);                 /* zero / subnormal */
+    else if (expo == 31)
+        v = mant ? NAN : INFINITY;
+    else
+        v = ldexp((double)(mant + 1024), expo - 25);  /* 1.m * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+static uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* Bytes of one block and weights per block, per format. */
+int64_t orc_block_bytes(int fmt)
+{
+    switch (fmt) {
+    case ORC_Q4_0: return 18;   /* [ILayer] gemv_q1_k_lcpp_src: Q4_0 is 18 B per 32 weights */
+    case ORC_Q8_0: return 34;   /* [ILayer] gemv_q8_0n_k_lcpp_src: f16 d + 32 x i8 */
+    case ORC_Q4_K: return 144;  /* f16 d, f16 dmin, 12 B packed 6-bit pairs, 128 B nibbles */
+    default: return -1;
+    }
+}
+
+int64_t orc_block_weights(int fmt)
+{
+    switch (fmt) {
+    case ORC_Q4_0: return 32;
+    case ORC_Q8_0: return 32;
+    case ORC_Q4_K: return 256;  /* [Honey] quant_matmul: Q4_K when k % 256 == 0 */
+    default: return -1;
+    }
+}
+
+/* Q4_0: w = (q - 8) * d.  [ILayer] q4_0_to_q8_0n states the exact upcast
+ * d8 = d4, q8 = nib - 8, i.e. each weight is d times the nibble less 8.
+ * Nibble order (a reading): the low nibble of byte j is element j, the high
+ * nibble is element j + 16. */
+static void dq_q4_0(const uint8_t *b, double *w)
+{
+    double d = orc_f16(rd16(b));
+    const uint8_t *qs = b + 2;
+    for (int j = 0; j < 16; ++j) {
+        int lo = qs[j] & 15;
+        int hi = qs[j] >> 4;
+        w[j] = (double)(lo - 8) * d;
+        w[j + 16] = (double)(hi - 8) * d;
+    }
+}
+
+/* Q8_0: w = d * q with q a signed byte.  [ILayer] gemv_q8_0n_k_lcpp_src. */
+static void dq_q8_0(const uint8_t *b, double *w)
+{
+    double d = orc_f16(rd16(b));
+    const int8_t *qs = (const int8_t *)(b + 2);
+    for (int j = 0; j < 32; ++j)
+        w[j] = d * (double)qs[j];
+}
+
+/* The 6-bit (scale, min) pair of sub-block j from the 12 packed bytes.
+ * [ILayer] gemv_q5k_k_lcpp_src says Q5_K uses "the same 6-bit pack as Q4_K";
+ * the bit positions below are the GGUF K-quant reading of that pack:
+ * pairs 0..3 sit in the low 6 bits of bytes j and j+4; pairs 4..7 take their
+ * low 4 bits from byte j+4 (scale: low half, min: high half) and their top
+ * 2 bits from the spare top bits of bytes j-4 (scale) and j (min). */
+void orc_q4k_scale_min(const uint8_t *s, int j, int *sc, int *m)
+{
+    if (j < 4) {
+        *sc = s[j] & 63;
+        *m = s[j + 4] & 63;
+    } else {
+        *sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+        *m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+    }
+}
+
+/* Q4_K super-block of 256 weights: w = d * sc_j * q - dmin * m_j
+ * (form given for the 5-bit sibling in [ILayer] gemv_q5k_k_lcpp_src, minus
+ * the fifth bit).  Element order (a reading): chunk c = 0..3 covers 64
+ * elements; byte qs[32c + l] holds element 64c + l in its low nibble
+ * (sub-block 2c) and element 64c + 32 + l in its high nibble (sub-block
+ * 2c + 1). */
+static void dq_q4_k(const uint8_t *b, double *w)
+{
+    double d = orc_f16(rd16(b));
+    double dmin = orc_f16(rd16(b + 2));
+    const uint8_t *s = b + 4;
+    const uint8_t *qs = b + 16;
+    for (int c = 0; c < 4; ++c) {
+        int sc0, m0, sc1, m1;
+        orc_q4k_scale_min(s, 2 * c, &sc0, &m0);
+        orc_q4k_scale_min(s, 2 * c + 1, &sc1, &m1);
+        for (int l = 0; l < 32; ++l) {
+            int lo = qs[32 * c + l] & 15;
+            int hi = qs[32 * c + l] >> 4;
+            w[64 * c + l] = d * (double)sc0 * (double)lo - dmin * (double)m0;
+            w[64 * c + 32 + l] = d * (double)sc1 * (double)hi - dmin * (double)m1;
+        }
+    }
+}
+
+/* Dequantize one row of K weights (K a multiple of the block size) from its
+ * GGUF-native bytes.  A row is K/bs consecutive blocks ([Honey]
+ * transpose_q8_blocks: [n_rows, n_blocks, block] is the native order). */
+int orc_dequant_row(int fmt, const uint8_t *row, int64_t K, double *w)
+{
+    int64_t bb = orc_block_bytes(fmt), bw = orc_block_weights(fmt);
+    if (bb < 0 || K % bw != 0)
+        return -1;
+    for (int64_t b = 0; b < K / bw; ++b) {
+        const uint8_t *blk = row + b * bb;
+        double *out = w + b * bw;
+        if (fmt == ORC_Q4_0) dq_q4_0(blk, out);
+        else if (fmt == ORC_Q8_0) dq_q8_0(blk, out);
+        else dq_q4_k(blk, out);
+    }
+    return 0;
+}
+
+int64_t orc_row_bytes(int fmt, int64_t K)
+{
+    int64_t bb = orc_block_bytes(fmt), bw = orc_block_weights(fmt);
+    if (bb < 0 || K % bw != 0)
+        return -1;
+    return K / bw * bb;
+}
+
+/* ---------------------------------------------------------------------------
+ * GEMV: y[r][i] = sum_k w[n_i][k] * v[r][k], and A[r][i] = sum_k |w v|,
+ * the scale of the tolerance.  v is [nb][K] row-major (the row batch of
+ * [Gpu] module docs: nb consecutive positions, activations [nb][...]).
+ * rows == NULL means all N rows (nrows == N); otherwise only the listed rows
+ * are computed, and y, A are [nb][nrows].
+ * ------------------------------------------------------------------------- */
+int orc_gemv(int fmt, const uint8_t *W, int64_t N, int64_t K, const double *v, int64_t nb,
+             const int64_t *rows, int64_t nrows, double *y, double *A)
+{
+    int64_t rb = orc_row_bytes(fmt, K);
+    if (rb < 0)
+        return -1;
+    if (!rows)
+        nrows = N;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < nrows; ++i) {
+            int64_t n = rows ? rows[i] : i;
+            if (n < 0 || n >= N || !w) {
+                err = -1;
+                continue;
+            }
+            orc_dequant_row(fmt, W + n * rb, K, w);
+            for (int64_t r = 0; r < nb; ++r) {
+                const double *vr = v + r * K;
+                double s = 0.0, a = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    double p = w[k] * vr[k];
+                    s += p;
+                    a += fabs(p);
+                }
+                y[r * nrows + i] = s;
+                if (A)
+                    A[r * nrows + i] = a;
+            }
+        }
+        free(w);
+    }
+    return err;
+}
+
+/* RMSNorm of each row: n_k = x_k * gamma_k / sqrt(mean_k x_k^2 + eps).
+ * [Honey] execute, arm Op::RmsNorm { eps }: gamma has shape [d] and the op
+ * runs over the flattened batch; eps inside the root and the plain gamma
+ * multiply are readings (the weights module of [ILayer] folds any (1 + w)
+ * convention into gamma at load, so kernels take gamma as is). */
+void orc_rmsnorm(const double *x, const double *gamma, int64_t nb, int64_t K, double eps,
+                 double *out)
+{
+    for (int64_t r = 0; r < nb; ++r) {
+        const double *xr = x + r * K;
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            ss += xr[k] * xr[k];
+        double inv = 1.0 / sqrt(ss / (double)K + eps);
+        for (int64_t k = 0; k < K; ++k)
+            out[r * K + k] = xr[k] * inv * gamma[k];
+    }
+}
+
+/* SiLU-gated product h = silu(g) * u, silu(g) = g / (1 + e^-g).
+ * [Honey] fused_norm_swiglu_down, step "mid = silu(gate) * up". */
+void orc_swiglu(const double *g, const double *u, int64_t n, double *h)
+{
+    for (int64_t i = 0; i < n; ++i)
+        h[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
+}
+
+/* y = W v + r.  [Honey] forward_decode_fused_layers, the fused matmul +
+ * residual: y[row] = matmul(x, w)[row] + residual[row]. */
+int orc_gemv_res(int fmt, const uint8_t *W, int64_t N, int64_t K, const double *v,
+                 const double *r, int64_t nb, const int64_t *rows, int64_t nrows, double *y,
+                 double *A)
+{
+    if (!rows)
+        nrows = N;
+    if (orc_gemv(fmt, W, N, K, v, nb, rows, nrows, y, A))
+        return -1;
+    for (int64_t b = 0; b < nb; ++b)
+        for (int64_t i = 0; i < nrows; ++i) {
+            int64_t n = rows ? rows[i] : i;
+            y[b * nrows + i] += r[b * N + n];
+        }
+    return 0;
+}
+
+/* Greedy argmax of each row of y[nb][N]: the lowest index of the maximum.
+ * [Gpu] module sampling: logits projection then greedy argmax. */
+void orc_argmax(const double *y, int64_t nb, int64_t N, int64_t *idx)
+{
+    for (int64_t r = 0; r < nb; ++r) {
+        const double *yr = y + r * N;
+        int64_t best = 0;
+        for (int64_t n = 1; n < N; ++n)
+            if (yr[n] > yr[best])
+                best = n;
+        idx[r] = best;
+    }
+}
+
+/* Routed experts: y[r] = sum_{t = 0..topk-1} p[r][t] * (W_{id[r][t]} x_r), the
+ * terms added in ascending t.  [Gpu] type alias RouteStep carries the
+ * tokens, expert ids and routing weights of one step; the weights are
+ * applied to each selected expert's output and summed per row.
+ * W holds n_exp matrices of N x K back to back.  Also writes A = sum_t p *
+ * (sum_k |w x|), the tolerance scale. */
+int orc_moe(int fmt, const uint8_t *W, int64_t n_exp, int64_t N, int64_t K, const double *x,
+            int64_t nb, const int32_t *ids, const double *p, int64_t topk, const int64_t *rows,
+            int64_t nrows, double *y, double *A)
+{
+    int64_t rb = orc_row_bytes(fmt, K);
+    if (rb < 0)
+        return -1;
+    if (!rows)
+        nrows = N;
+    double *ye = (double *)malloc((size_t)nrows * sizeof(double));
+    double *ae = (double *)malloc((size_t)nrows * sizeof(double));
+    if (!ye || !ae) {
+        free(ye);
+        free(ae);
+        return -1;
+    }
+    int err = 0;
+    for (int64_t r = 0; r < nb && !err; ++r) {
+        for (int64_t i = 0; i < nrows; ++i) {
+            y[r * nrows + i] = 0.0;
+            if (A)
+                A[r * nrows + i] = 0.0;
+        }
+        for (int64_t t = 0; t < topk; ++t) {
+            int32_t e = ids[r * topk + t];
+            if (e < 0 || e >= n_exp) {
+                err = -1;
+                break;
+            }
+            const uint8_t *We = W + (int64_t)e * N * rb;
+            if (orc_gemv(fmt, We, N, K, x + r * K, 1, rows, nrows, ye, ae)) {
+                err = -1;
+                break;
+            }
+            double pt = p[r * topk + t];
+            for (int64_t i = 0; i < nrows; ++i) {
+                y[r * nrows + i] += pt * ye[i];
+                if (A)
+                    A[r * nrows + i] += fabs(pt) * ae[i];
+            }
+        }
+    }
+    free(ye);
+    free(ae);
+    return err;
+}
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+int orc_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}

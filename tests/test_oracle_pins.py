@@ -1,0 +1,441 @@
+"""Pins of the f64 oracle against facts fixed by the pages and by mathematics.
+
+None of these checks re-calls the oracle against itself: each compares it with a hand-worked
+fixture (tests/golden/), an independent library (numpy's float16), a closed form or an
+invariant chosen so that a plausible slip (a dropped term, a wrong sign or index, swapped
+nibbles, a transposed operand) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from conftest import golden_bytes, read_golden
+
+Q4_0, Q8_0, Q4_K = oracle.Q4_0, oracle.Q8_0, oracle.Q4_K
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _build():
+    oracle.build(force=False)
+
+
+def f16_bytes(val: float) -> bytes:
+    return np.array([val], dtype="<f2").tobytes()
+
+
+# ----------------------------------------------------------------------------- f16
+
+def test_f16_golden_table():
+    for bits, val in read_golden("f16_bits.txt"):
+        got = oracle.f16(int(bits, 16))
+        want = float(val)
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), (bits, got, want)
+
+
+def test_f16_every_pattern_matches_numpy():
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    ref = bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+# ----------------------------------------------------------------------------- block decode
+
+def _golden_weights(name):
+    rows = read_golden(name)
+    blk = golden_bytes(rows, "bytes")
+    want = [float(r[-1]) for r in rows if r[0].isdigit()]
+    return np.frombuffer(blk, dtype=np.uint8), np.array(want)
+
+
+def test_q4_0_hand_block():
+    blk, want = _golden_weights("q4_0_hand_block.txt")
+    assert blk.size == 18 and want.size == 32
+    got = oracle.dequant(Q4_0, blk, 32)[0]
+    assert np.array_equal(got, want)
+
+
+def test_q8_0_hand_block():
+    blk, want = _golden_weights("q8_0_hand_block.txt")
+    assert blk.size == 34 and want.size == 32
+    got = oracle.dequant(Q8_0, blk, 32)[0]
+    assert np.array_equal(got, want)
+
+
+def _q4k_golden():
+    rows = read_golden("q4_k_hand_block.txt")
+    scales = golden_bytes(rows, "scales")
+    pairs = {int(r[1]): (int(r[2]), int(r[3])) for r in rows if r[0] == "pair"}
+    elems = {int(r[1]): (int(r[2]), float(r[3])) for r in rows if r[0] == "elem"}
+    return scales, pairs, elems
+
+
+def _q4k_hand_block(scales: bytes) -> np.ndarray:
+    qs = bytes(((i & 15) | ((15 - (i & 15)) << 4)) for i in range(128))
+    blk = f16_bytes(1.0) + f16_bytes(0.5) + scales + qs
+    return np.frombuffer(blk, dtype=np.uint8)
+
+
+def test_q4_k_hand_scale_pairs():
+    scales, pairs, _ = _q4k_golden()
+    assert len(scales) == 12 and len(pairs) == 8
+    for j, (sc, m) in pairs.items():
+        assert oracle.q4k_scale_min(scales, j) == (sc, m), j
+
+
+def test_q4_k_hand_elements():
+    scales, _, elems = _q4k_golden()
+    w = oracle.dequant(Q4_K, _q4k_hand_block(scales), 256)[0]
+    for e, (_nib, val) in elems.items():
+        assert w[e] == val, (e, w[e], val)
+
+
+def _q4_0_from_q4k_nibbles(qs128: bytes, d: float) -> np.ndarray:
+    """8 Q4_0 blocks holding the same 256 nibbles in Q4_K element order (block 2c takes the low
+    nibbles of qs[32c..32c+31], block 2c+1 the high ones)."""
+    out = bytearray()
+    for c in range(4):
+        chunk = qs128[32 * c:32 * c + 32]
+        for part in (0, 1):
+            nib = [(b >> (4 * part)) & 15 for b in chunk]       # 32 elements of this sub-block
+            out += f16_bytes(d)
+            out += bytes(nib[j] | (nib[j + 16] << 4) for j in range(16))
+    return np.frombuffer(bytes(out), dtype=np.uint8)
+
+
+def test_q4_k_reduces_to_q4_0():
+    """d = dmin = delta, all sc = 1, all m = 8  =>  w = delta * (q - 8), i.e. eight Q4_0 blocks."""
+    g = np.random.default_rng(11)
+    delta = 0.0078125
+    # every pair (1, 8): pairs 0..3 low 6 bits 1 / 8, pairs 4..7: low nibbles 1 / 8, top bits 0
+    scales = bytes([1, 1, 1, 1, 8, 8, 8, 8, 0x81, 0x81, 0x81, 0x81])
+    for j in range(8):
+        assert oracle.q4k_scale_min(scales, j) == (1, 8)
+    for _ in range(20):
+        qs = g.integers(0, 256, 128, dtype=np.uint8).tobytes()
+        blk = np.frombuffer(f16_bytes(delta) + f16_bytes(delta) + scales + qs, dtype=np.uint8)
+        wk = oracle.dequant(Q4_K, blk, 256)[0]
+        w0 = oracle.dequant(Q4_0, _q4_0_from_q4k_nibbles(qs, delta), 256)[0]
+        assert np.array_equal(wk, w0)
+
+
+def _pack_one_pair(j: int, sc: int, m: int) -> bytes:
+    """12 scale bytes holding (sc, m) at pair j and zeros elsewhere, from the bit positions of the
+    6-bit pack (pairs 0..3 in low 6 bits of s[j], s[j+4]; pairs 4..7 split into a nibble of s[j+4]
+    and the top 2 bits of s[j-4] / s[j])."""
+    s = [0] * 12
+    if j < 4:
+        s[j] |= sc
+        s[j + 4] |= m
+    else:
+        s[j + 4] |= (sc & 15) | ((m & 15) << 4)
+        s[j - 4] |= (sc >> 4) << 6
+        s[j] |= (m >> 4) << 6
+    return bytes(s)
+
+
+def test_q4_k_six_bit_sweep():
+    """Each pair and each 6-bit value: nibbles all 1, x = indicator of sub-block j  =>
+    y = 32 d sc_j  (with dmin = 0), and y = -32 dmin m_j (with d = 0)."""
+    qs = bytes([0x11] * 128)
+    for j in range(8):
+        ind = np.zeros((1, 256))
+        c, part = divmod(j, 2)
+        ind[0, 64 * c + 32 * part: 64 * c + 32 * part + 32] = 1.0
+        for v in range(64):
+            s_sc = _pack_one_pair(j, v, 0)
+            s_m = _pack_one_pair(j, 0, v)
+            b1 = np.frombuffer(f16_bytes(0.5) + f16_bytes(0.0) + s_sc + qs, dtype=np.uint8)
+            b2 = np.frombuffer(f16_bytes(0.0) + f16_bytes(0.25) + s_m + qs, dtype=np.uint8)
+            y1, _ = oracle.gemv(Q4_K, b1, 1, 256, ind)
+            y2, _ = oracle.gemv(Q4_K, b2, 1, 256, ind)
+            assert y1[0, 0] == 32 * 0.5 * v, (j, v, y1)
+            assert y2[0, 0] == -32 * 0.25 * v, (j, v, y2)
+            # and nothing leaks into the other sub-blocks
+            wk = oracle.dequant(Q4_K, b1, 256)[0]
+            assert np.count_nonzero(wk) == (32 if v else 0)
+
+
+def test_q4_0_upcast_to_q8_0_is_exact():
+    """'Crate inferencelayer' docs, q4_0_to_q8_0n: d8 = d4, q8 = nib - 8 is lossless."""
+    g = np.random.default_rng(5)
+    N, K = 7, 96
+    d = g.uniform(0.001, 0.02, size=(N, K // 32)).astype("<f2")
+    nib = g.integers(0, 16, size=(N, K // 32, 32))
+    q4 = bytearray()
+    q8 = bytearray()
+    for n in range(N):
+        for b in range(K // 32):
+            db = d[n, b].tobytes()
+            q4 += db + bytes(int(nib[n, b, j] | (nib[n, b, j + 16] << 4)) for j in range(16))
+            q8 += db + (nib[n, b] - 8).astype(np.int8).tobytes()
+    W4 = np.frombuffer(bytes(q4), dtype=np.uint8)
+    W8 = np.frombuffer(bytes(q8), dtype=np.uint8)
+    assert np.array_equal(oracle.dequant(Q4_0, W4, K), oracle.dequant(Q8_0, W8, K))
+    x = g.standard_normal((3, K))
+    y4, _ = oracle.gemv(Q4_0, W4, N, K, x)
+    y8, _ = oracle.gemv(Q8_0, W8, N, K, x)
+    assert np.array_equal(y4, y8)
+
+
+# ----------------------------------------------------------------------------- GEMV
+
+def _distinct_scale_matrix(fmt, N, K):
+    """Every block of the matrix gets its own scale d(n, b) = (n * nblk + b + 1) / 16 and weights
+    all equal to d (Q4_0 nibble 9, Q8_0 q = 1)."""
+    nblk = K // 32
+    out = bytearray()
+    for n in range(N):
+        for b in range(nblk):
+            d = (n * nblk + b + 1) / 16.0
+            if fmt == Q4_0:
+                out += f16_bytes(d) + bytes([0x99] * 16)
+            else:
+                out += f16_bytes(d) + bytes([1] * 32)
+    return np.frombuffer(bytes(out), dtype=np.uint8)
+
+
+@pytest.mark.parametrize("fmt", [Q4_0, Q8_0])
+def test_gemv_one_hot_picks_row_and_block(fmt):
+    """x = e_k selects column k: y[n] = w[n][k] = d(n, k // 32).  N != K catches a transposed
+    operand, distinct scales catch a wrong row or block stride."""
+    N, K = 5, 96
+    W = _distinct_scale_matrix(fmt, N, K)
+    nblk = K // 32
+    for k in range(K):
+        x = np.zeros((1, K))
+        x[0, k] = 1.0
+        y, A = oracle.gemv(fmt, W, N, K, x)
+        want = np.array([(n * nblk + k // 32 + 1) / 16.0 for n in range(N)])
+        assert np.array_equal(y[0], want), k
+        assert np.array_equal(A[0], np.abs(want))
+
+
+def test_gemv_hand_block_dot():
+    """The Q4_0 hand block dotted with x = (1, 2, ..., 32), worked by hand:
+    low half  sum_{j<16} (j+1) * 0.5 (j - 8):  0.5 * (-120 + 392)  =  136
+    high half sum_{j<16} (j+17) * 0.5 (7 - j): 0.5 * (532 - 1068)  = -268
+    y = -132;  A = sum |w x| = 0.5 * (120 + 392) + 0.5 * (532 + 1068) = 256 + 800 = 1056."""
+    rows = read_golden("q4_0_hand_block.txt")
+    blk = np.frombuffer(golden_bytes(rows, "bytes"), dtype=np.uint8)
+    x = np.arange(1, 33, dtype=np.float64)[None, :]
+    y, A = oracle.gemv(Q4_0, blk, 1, 32, x)
+    assert y[0, 0] == -132.0
+    assert A[0, 0] == 1056.0
+
+
+@pytest.mark.parametrize("fmt", [Q4_0, Q8_0, Q4_K])
+def test_gemv_zero_weights_give_exact_zero(fmt):
+    g = np.random.default_rng(3)
+    N, K = 6, 512
+    if fmt == Q4_0:
+        blk = f16_bytes(0.0173) + bytes([0x88] * 16)           # every nibble 8 -> w = 0
+        W = np.frombuffer(blk * (N * K // 32), dtype=np.uint8)
+    elif fmt == Q8_0:
+        W = np.frombuffer((f16_bytes(0.0173) + bytes(32)) * (N * K // 32), dtype=np.uint8)
+    else:
+        blk = f16_bytes(0.0173) + f16_bytes(0.002) + bytes(12) + g.integers(0, 256, 128, dtype=np.uint8).tobytes()
+        W = np.frombuffer(blk * (N * K // 256), dtype=np.uint8)
+    x = g.standard_normal((3, K))
+    y, A = oracle.gemv(fmt, W, N, K, x)
+    assert np.all(y == 0.0) and np.all(A == 0.0)
+
+
+@pytest.mark.parametrize("fmt", [Q4_0, Q8_0, Q4_K])
+def test_gemv_scale_doubling_is_exact(fmt):
+    """Adding 1 to every f16 exponent doubles each scale exactly, so y doubles exactly."""
+    import workloads as wl
+    g = np.random.default_rng(9)
+    N, K = 9, 512
+    W = wl.matrix(fmt, g, N, K)
+    x = g.standard_normal((2, K))
+    y1, _ = oracle.gemv(fmt, W, N, K, x)
+    W2 = W.copy().reshape(N, -1, wl.BLOCK_BYTES[fmt])
+    nscale = 2 if fmt == Q4_K else 1
+    for s in range(nscale):
+        h = W2[..., 2 * s:2 * s + 2].copy().view("<u2")
+        h += 1 << 10
+        W2[..., 2 * s:2 * s + 2] = h.view(np.uint8)
+    y2, _ = oracle.gemv(fmt, W2.reshape(N, -1), N, K, x)
+    assert np.array_equal(y2, 2 * y1)
+
+
+def test_gemv_linear_in_x():
+    import workloads as wl
+    g = np.random.default_rng(13)
+    N, K = 11, 256
+    W = wl.q4_0_matrix(g, N, K)
+    x1 = g.standard_normal((1, K))
+    x2 = g.standard_normal((1, K))
+    y1, A1 = oracle.gemv(Q4_0, W, N, K, x1)
+    y2, A2 = oracle.gemv(Q4_0, W, N, K, x2)
+    yd, _ = oracle.gemv(Q4_0, W, N, K, 2 * x1)
+    ys, _ = oracle.gemv(Q4_0, W, N, K, x1 + x2)
+    assert np.array_equal(yd, 2 * y1)
+    assert np.all(np.abs(ys - (y1 + y2)) <= 1e-12 * (A1 + A2))
+
+
+def test_gemv_row_subset_matches_full():
+    import workloads as wl
+    g = np.random.default_rng(17)
+    N, K = 40, 256
+    W = wl.q4_0_matrix(g, N, K)
+    x = g.standard_normal((3, K))
+    y, A = oracle.gemv(Q4_0, W, N, K, x)
+    rows = np.array([39, 0, 17, 17, 5])
+    ys, As = oracle.gemv(Q4_0, W, N, K, x, rows=rows)
+    assert np.array_equal(ys, y[:, rows]) and np.array_equal(As, A[:, rows])
+
+
+# ----------------------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_constant_row():
+    """x = c everywhere, gamma = 1: n = c / sqrt(c^2 + eps).  With c = 1e-3, eps = 1e-5 the value
+    (0.3015...) tells eps inside the root from eps outside it or a missing eps."""
+    K = 64
+    c, eps = 1e-3, 1e-5
+    n = oracle.rmsnorm(np.full((1, K), c), np.ones(K), eps)
+    want = c / math.sqrt(c * c + eps)
+    assert np.all(np.abs(n - want) <= 1e-15 * want)
+    assert abs(want - 0.30151134457776363) < 1e-15
+
+
+def test_rmsnorm_mean_not_sum_and_gamma():
+    """sum x^2 = K and eps = 0  =>  rms = 1 and n = x * gamma exactly up to rounding; a sum in
+    place of the mean would give n = x gamma / sqrt(K)."""
+    g = np.random.default_rng(2)
+    K = 128
+    x = g.standard_normal(K)
+    x *= math.sqrt(K / np.sum(x * x))
+    gamma = g.uniform(0.5, 1.5, K)
+    n = oracle.rmsnorm(x[None], gamma, 0.0)[0]
+    assert np.all(np.abs(n - x * gamma) <= 1e-14 * np.abs(x * gamma) + 1e-300)
+
+
+def test_rmsnorm_rows_independent_and_scale_invariant():
+    g = np.random.default_rng(4)
+    K = 96
+    base = g.standard_normal(K)
+    x = np.stack([base, 3.0 * base, 0.125 * base])
+    gamma = g.uniform(0.5, 1.5, K)
+    n = oracle.rmsnorm(x, gamma, 0.0)
+    assert np.allclose(n[1], n[0], rtol=1e-14, atol=0) and np.allclose(n[2], n[0], rtol=1e-14, atol=0)
+
+
+# ----------------------------------------------------------------------------- SwiGLU
+
+SIGMA_1 = 0.7310585786300049   # logistic(1) = e / (1 + e)
+SIGMA_2 = 0.8807970779778823   # logistic(2) = e^2 / (1 + e^2)
+
+
+def test_swiglu_closed_forms():
+    g = np.array([0.0, 1.0, 2.0, 40.0, -40.0, 0.0])
+    u = np.array([5.0, 2.0, 1.0, 1.0, 1.0, -3.0])
+    h = oracle.swiglu(g, u)
+    assert h[0] == 0.0 and h[5] == 0.0
+    assert abs(h[1] - 2 * SIGMA_1) < 1e-15          # silu on the gate: silu(1) * 2
+    assert abs(h[2] - 2 * SIGMA_2) < 1e-15          # swapping roles would give silu(1)*2 here
+    assert abs(h[3] - 40.0) < 1e-12                 # silu(g) -> g for large g
+    assert abs(h[4]) < 1e-15                        # silu(g) -> 0 for very negative g
+
+
+def test_swiglu_odd_part_identity():
+    """silu(g) - silu(-g) = g for every g (u = 1)."""
+    g = np.linspace(-6, 6, 101)
+    hp = oracle.swiglu(g, np.ones_like(g))
+    hm = oracle.swiglu(-g, np.ones_like(g))
+    assert np.all(np.abs((hp - hm) - g) <= 1e-14 * (1 + np.abs(g)))
+
+
+def test_gus_nrm_zero_gate_or_up_gives_zero():
+    import workloads as wl
+    g = np.random.default_rng(8)
+    N, K = 12, 256
+    Wz = np.frombuffer((f16_bytes(0.01) + bytes([0x88] * 16)) * (N * K // 32), dtype=np.uint8)
+    Wr = wl.q4_0_matrix(g, N, K)
+    x = g.standard_normal((2, K))
+    gamma = g.uniform(0.5, 1.5, K)
+    h1, *_ = oracle.qgemv_gus_nrm(Q4_0, Wz, Wr, N, K, x, gamma, 1e-5)
+    h2, *_ = oracle.qgemv_gus_nrm(Q4_0, Wr, Wz, N, K, x, gamma, 1e-5)
+    assert np.all(h1 == 0.0) and np.all(h2 == 0.0)
+
+
+# ----------------------------------------------------------------------------- residual, argmax
+
+def test_residual_with_zero_weights_is_identity():
+    g = np.random.default_rng(21)
+    N, K = 10, 64
+    W = np.frombuffer((f16_bytes(0.5) + bytes([0x88] * 16)) * (N * K // 32), dtype=np.uint8)
+    x = g.standard_normal((2, K))
+    r = g.standard_normal((2, N))
+    y, _ = oracle.qgemv_res(Q4_0, W, N, K, x, r)
+    assert np.array_equal(y, r)
+
+
+def test_residual_adds_the_product():
+    N, K = 5, 96
+    W = _distinct_scale_matrix(Q4_0, N, K)
+    x = np.zeros((1, K))
+    x[0, 40] = 1.0
+    r = np.arange(N, dtype=np.float64)[None] * 100.0
+    y, _ = oracle.qgemv_res(Q4_0, W, N, K, x, r)
+    want = np.array([(n * 3 + 1 + 1) / 16.0 + 100.0 * n for n in range(N)])
+    assert np.array_equal(y[0], want)
+
+
+def test_argmax_ties_go_to_lowest_index():
+    y = np.array([[1.0, 3.0, 2.0, 3.0], [-5.0, -5.0, -6.0, -7.0], [0.0, 0.0, 0.0, 0.0],
+                  [-1.0, 2.0, 9.0, -9.0]])
+    assert list(oracle.argmax(y)) == [1, 0, 0, 2]
+
+
+# ----------------------------------------------------------------------------- routed experts
+
+def test_moe_same_expert_everywhere_is_plain_gemv():
+    import workloads as wl
+    g = np.random.default_rng(31)
+    n_exp, N, K, nb, topk = 4, 16, 256, 3, 8
+    W = wl.q4_k_matrix(g, n_exp * N, K)
+    x = g.standard_normal((nb, K))
+    ids = np.full((nb, topk), 2, dtype=np.int32)
+    p = np.full((nb, topk), 0.125)
+    y, A = oracle.qgemv_moe(Q4_K, W, n_exp, N, K, x, ids, p)
+    y0, A0 = oracle.gemv(Q4_K, W.reshape(n_exp, -1)[2], N, K, x)
+    assert np.all(np.abs(y - y0) <= 1e-13 * A0)
+    # top-1 with weight 1 is bit-for-bit the plain GEMV
+    y1, _ = oracle.qgemv_moe(Q4_K, W, n_exp, N, K, x, ids[:, :1], np.ones((nb, 1)))
+    assert np.array_equal(y1, y0)
+
+
+def test_moe_weighted_sum_exact():
+    """Experts with one-hot-readable outputs: expert 0 row n gives d0(n, b), expert 1 gives
+    d1(n, b); with p = (0.25, 0.75) and x = e_k the result is exact."""
+    N, K = 4, 64
+    Wa = _distinct_scale_matrix(Q4_0, N, K)
+    Wb = _distinct_scale_matrix(Q4_0, N, K).copy().reshape(N, -1, 18)
+    h = Wb[..., 0:2].copy().view("<u2")
+    h += 1 << 10                                    # expert 1 = 2 x expert 0
+    Wb[..., 0:2] = h.view(np.uint8)
+    W = np.concatenate([Wa, Wb.reshape(-1)])
+    x = np.zeros((2, K))
+    x[0, 3] = 1.0
+    x[1, 50] = 1.0
+    ids = np.array([[0, 1], [1, 0]], dtype=np.int32)
+    p = np.array([[0.25, 0.75], [0.5, 0.5]])
+    y, _ = oracle.qgemv_moe(Q4_0, W, 2, N, K, x, ids, p)
+    want0 = [(0.25 * 1 + 0.75 * 2) * (n * 2 + 0 + 1) / 16.0 for n in range(N)]
+    want1 = [(0.5 * 2 + 0.5 * 1) * (n * 2 + 1 + 1) / 16.0 for n in range(N)]
+    assert np.array_equal(y[0], want0) and np.array_equal(y[1], want1)
+
+
+def test_moe_rejects_bad_expert_id():
+    import workloads as wl
+    g = np.random.default_rng(1)
+    W = wl.q4_0_matrix(g, 2 * 4, 32)
+    with pytest.raises(ValueError):
+        oracle.qgemv_moe(Q4_0, W, 2, 4, 32, np.ones((1, 32)), np.array([[2]], np.int32), np.ones((1, 1)))
