@@ -1,0 +1,344 @@
+"""Throughput of the block-quantized dequant-GEMV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--nb NB] [--warm]
+
+A step is one pass of the hot path over one batch of synthetic input, with every input already
+resident in HBM.  The default workload is the LFM2-1.2B-like decode MLP (nb = 1): the fused
+RMSNorm + Q4_0 gate/up + SwiGLU launch (8192 x 2048 each), then the Q4_0 down + residual launch
+(2048 x 8192).  Weights are rotated over copies totalling >= 1 GiB so that neither the L2 nor the
+256 MB Infinity Cache can serve them ("cold"); --warm reuses one copy.
+
+Printed: ONE JSON line.  `value` is weight GB/s over the whole step (weight bytes moved per
+step / time per step); `roofline` is the dominant launch's algorithmic bytes over its average
+duration (HIP events on the launch stream), against the 8 TB/s HBM peak; `cpu_baseline` is the
+f64 oracle timed on this host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "weight GB/s and % of HBM peak for Q4 dequant-GEMV, nb=1 and nb=16"
+HBM_PEAK_GBPS = 8000.0
+COLD_BYTES = 1 << 30
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "dequant_gemv_q4_amd", "csrc", "gemv_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Bench:
+    """One workload: R rotated weight copies on the device and the launches of one step."""
+
+    def __init__(self, name, weight_bytes, alg_bytes, dominant, step, dom, cpu, config):
+        self.name, self.weight_bytes, self.alg_bytes = name, weight_bytes, alg_bytes
+        self.dominant, self.step, self.dom, self.cpu, self.config = dominant, step, dom, cpu, config
+
+
+def _copies(total_bytes, warm):
+    return 1 if warm else max(2, -(-COLD_BYTES // total_bytes))
+
+
+def make_decode_mlp(warm):
+    import torch
+    import dequant_gemv_q4_amd as q
+    from dequant_gemv_q4_amd import device as D
+    import workloads as wl
+
+    w = wl.decode_mlp()
+    a = w.arrays
+    H, I, eps = 2048, 8192, w.params["eps"]
+    packed = [D.pack(q.Q4_0, a[k], *s) for k, s in (("Wg", (I, H)), ("Wu", (I, H)), ("Wd", (H, I)))]
+    per_set = sum(p.numel() for p in packed)
+    R = _copies(per_set, warm)
+    sets = [packed] + [[p.clone() for p in packed] for _ in range(R - 1)]
+    x, gamma = D.to_device(a["x"]), D.to_device(a["gamma"])
+    h = torch.empty((1, I), dtype=torch.float32, device="cuda")
+    y = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    wbytes = sum(a[k].nbytes for k in ("Wg", "Wu", "Wd"))
+
+    def gus(i):
+        Wg, Wu, _ = sets[i % R]
+        q.qgemv_gus_nrm(q.Q4_0, Wg, Wu, I, H, x, gamma, eps, 1, h)
+
+    def step(i):
+        gus(i)
+        q.qgemv_res(q.Q4_0, sets[i % R][2], H, I, h, x, 1, y)
+
+    def cpu():
+        import oracle
+        hr = oracle.qgemv_gus_nrm(q.Q4_0, a["Wg"], a["Wu"], I, H, a["x"], a["gamma"], eps)[0]
+        oracle.qgemv_res(q.Q4_0, a["Wd"], H, I, hr, a["x"])
+        return wbytes
+
+    # gate/up launch: both weight matrices, x and gamma read once, h written
+    alg = a["Wg"].nbytes + a["Wu"].nbytes + 2 * H * 4 + I * 4
+    cfg = {"workload": w.name, "nb": 1, "format": "q4_0", "hidden": H, "inter": I,
+           "launches_per_step": 2, "weight_copies": R, "cold": not warm}
+    return Bench(w.name, wbytes, alg, "qgemv_gus_nrm (q4_0, 2 x 8192x2048, nb=1)", step, gus, cpu, cfg)
+
+
+def make_lm_head(warm, nb):
+    import torch
+    import dequant_gemv_q4_amd as q
+    from dequant_gemv_q4_amd import device as D
+    import workloads as wl
+
+    w = wl.lm_head(nb=nb)
+    a = w.arrays
+    Wp = D.pack(q.Q4_0, a["W"], w.N, w.K)
+    R = _copies(Wp.numel(), warm)
+    sets = [Wp] + [Wp.clone() for _ in range(R - 1)]
+    x = D.to_device(a["x"])
+    logits = torch.empty((nb, w.N), dtype=torch.float32, device="cuda")
+    idx = torch.empty((nb,), dtype=torch.int32, device="cuda")
+    ws = D.workspace(q.OP_ARGMAX, q.Q4_0, w.N, w.K, nb)
+
+    def step(i):
+        q.qgemv_argmax(q.Q4_0, sets[i % R], w.N, w.K, x, nb, logits, idx, ws)
+
+    def cpu():
+        import oracle
+        oracle.qgemv_argmax(q.Q4_0, a["W"], w.N, w.K, a["x"])
+        return a["W"].nbytes
+
+    alg = a["W"].nbytes + nb * w.K * 4 + nb * w.N * 4 + nb * 4
+    cfg = {"workload": w.name, "nb": nb, "format": "q4_0", "N": w.N, "K": w.K,
+           "launches_per_step": 1, "weight_copies": R, "cold": not warm}
+    return Bench(w.name, a["W"].nbytes, alg, f"qgemv_argmax (q4_0, {w.N}x{w.K}, nb={nb})", step,
+                 step, cpu, cfg)
+
+
+def make_gemv(warm, nb):
+    """Plain Q4_0 GEMV on the lm_head-sized matrix (65536 x 2048): the nb=1 gate shape."""
+    import torch
+    import dequant_gemv_q4_amd as q
+    from dequant_gemv_q4_amd import device as D
+    import workloads as wl
+
+    w = wl.lm_head(nb=nb)
+    a = w.arrays
+    Wp = D.pack(q.Q4_0, a["W"], w.N, w.K)
+    R = _copies(Wp.numel(), warm)
+    sets = [Wp] + [Wp.clone() for _ in range(R - 1)]
+    x = D.to_device(a["x"])
+    y = torch.empty((nb, w.N), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        q.qgemv(q.Q4_0, sets[i % R], w.N, w.K, x, nb, y)
+
+    def cpu():
+        import oracle
+        oracle.qgemv(q.Q4_0, a["W"], w.N, w.K, a["x"])
+        return a["W"].nbytes
+
+    alg = a["W"].nbytes + nb * w.K * 4 + nb * w.N * 4
+    cfg = {"workload": f"q4_0_gemv_{w.N}x{w.K}_nb{nb}", "nb": nb, "format": "q4_0", "N": w.N,
+           "K": w.K, "launches_per_step": 1, "weight_copies": R, "cold": not warm}
+    return Bench(cfg["workload"], a["W"].nbytes, alg, f"qgemv (q4_0, {w.N}x{w.K}, nb={nb})", step,
+                 step, cpu, cfg)
+
+
+def make_qkv(warm, nb):
+    import torch
+    import dequant_gemv_q4_amd as q
+    from dequant_gemv_q4_amd import device as D
+    import workloads as wl
+
+    w = wl.qkv_q8(nb=nb)
+    a = w.arrays
+    Wp = D.pack(q.Q8_0, a["W"], w.N, w.K)
+    R = _copies(Wp.numel(), warm)
+    sets = [Wp] + [Wp.clone() for _ in range(R - 1)]
+    x, gamma = D.to_device(a["x"]), D.to_device(a["gamma"])
+    y = torch.empty((nb, w.N), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        q.qgemv_nrm(q.Q8_0, sets[i % R], w.N, w.K, x, gamma, w.params["eps"], nb, y)
+
+    def cpu():
+        import oracle
+        oracle.qgemv_nrm(q.Q8_0, a["W"], w.N, w.K, a["x"], a["gamma"], w.params["eps"])
+        return a["W"].nbytes
+
+    alg = a["W"].nbytes + nb * w.K * 4 + w.K * 4 + nb * w.N * 4
+    cfg = {"workload": w.name, "nb": nb, "format": "q8_0", "N": w.N, "K": w.K,
+           "launches_per_step": 1, "weight_copies": R, "cold": not warm}
+    return Bench(w.name, a["W"].nbytes, alg, f"qgemv_nrm (q8_0, {w.N}x{w.K}, nb={nb})", step, step,
+                 cpu, cfg)
+
+
+def make_moe(warm):
+    import torch
+    import dequant_gemv_q4_amd as q
+    from dequant_gemv_q4_amd import device as D
+    import workloads as wl
+
+    w = wl.moe_q4k()
+    a = w.arrays
+    n_exp, topk, nb = w.params["n_exp"], w.params["topk"], w.nb
+    Wp = D.pack(q.Q4_K, a["W"], n_exp * w.N, w.K)
+    R = _copies(Wp.numel(), warm)
+    sets = [Wp] + [Wp.clone() for _ in range(R - 1)]
+    x, ids, p = D.to_device(a["x"]), D.to_device(a["ids"]), D.to_device(a["p"])
+    y = torch.empty((nb, w.N), dtype=torch.float32, device="cuda")
+    ws = D.workspace(q.OP_MOE, q.Q4_K, w.N, w.K, nb, n_exp, topk)
+    touched = len(np.unique(a["ids"]))
+    per_exp = a["W"].nbytes // n_exp
+
+    def step(i):
+        q.qgemv_moe(q.Q4_K, sets[i % R], n_exp, w.N, w.K, x, nb, ids, p, topk, y, ws)
+
+    def cpu():
+        import oracle
+        oracle.qgemv_moe(q.Q4_K, a["W"], n_exp, w.N, w.K, a["x"], a["ids"], a["p"])
+        return touched * per_exp
+
+    wbytes = touched * per_exp
+    alg = wbytes + nb * w.K * 4 + nb * w.N * 4 + 2 * nb * topk * w.N * 4 + 2 * nb * topk * 4
+    cfg = {"workload": w.name, "nb": nb, "format": "q4_k", "N": w.N, "K": w.K, "n_exp": n_exp,
+           "topk": topk, "experts_touched": touched, "launches_per_step": 1,
+           "weight_copies": R, "cold": not warm}
+    return Bench(w.name, wbytes, alg, f"qgemv_moe (q4_k, {touched} of {n_exp} x {w.N}x{w.K}, nb={nb})",
+                 step, step, cpu, cfg)
+
+
+def time_loop(fn, start, count, torch):
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for i in range(count):
+        fn(start + i)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / count   # ms per call
+
+
+def stored_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed PMC summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if rec.get("kernel_sha256") != src:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(b, budget_s):
+    import oracle
+    oracle.build(force=False)
+    b.cpu()                                          # warm-up (page-in, thread pool)
+    t0 = time.perf_counter()
+    reps, moved = 0, 0
+    while True:
+        moved += b.cpu()
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(moved / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{reps} full steps of {b.name} in the f64 oracle ({dt:.1f} s, OpenMP over output rows)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="decode_mlp",
+                    choices=["decode_mlp", "lm_head", "gemv", "qkv", "moe"])
+    ap.add_argument("--nb", type=int, default=None)
+    ap.add_argument("--warm", action="store_true", help="reuse one weight copy (cache-assisted)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the kernels shard by output rows; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dequant_gemv_q4_amd as q
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    q.lib()
+    torch.cuda.set_device(0)
+
+    if args.workload == "decode_mlp":
+        b = make_decode_mlp(args.warm)
+    elif args.workload == "lm_head":
+        b = make_lm_head(args.warm, args.nb or 1)
+    elif args.workload == "gemv":
+        b = make_gemv(args.warm, args.nb or 1)
+    elif args.workload == "qkv":
+        b = make_qkv(args.warm, args.nb or 16)
+    else:
+        b = make_moe(args.warm)
+    log(f"bench: {b.name}, copies={b.config['weight_copies']}, warmup={args.warmup}, steps={args.steps}")
+
+    for i in range(args.warmup):
+        b.step(i)
+    torch.cuda.synchronize()
+    ms_step = time_loop(b.step, args.warmup, args.steps, torch)
+    log(f"bench: {ms_step * 1e3:.2f} us per step")
+    for i in range(args.warmup):
+        b.dom(i)
+    ms_dom = time_loop(b.dom, args.warmup, args.steps, torch)
+    log(f"bench: dominant launch {ms_dom * 1e3:.2f} us")
+
+    value = b.weight_bytes / (ms_step * 1e-3) / 1e9
+    achieved = b.alg_bytes / (ms_dom * 1e-3) / 1e9
+    traffic = stored_traffic(b.name)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "config": b.config,
+        "roofline": {"bound": "hbm", "kernel": b.dominant, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "alg_bytes_per_launch": b.alg_bytes, "us_per_launch": round(ms_dom * 1e3, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        log("bench: timing the f64 oracle on this host")
+        out["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

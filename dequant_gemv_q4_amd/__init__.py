@@ -1,0 +1,12 @@
+"""dequant_gemv_q4_amd -- block-quantized (Q4_0 / Q8_0 / Q4_K) dequant-GEMV for LLM decode on
+MI355X (gfx950): hand-written HIP kernels behind the C ABI of include/qgemv.h.
+
+The functions exported here are the C entry points under the same names (see ``_binding``);
+``device`` holds torch-side plumbing (device buffers for packed weights and workspaces).
+"""
+from ._binding import (  # noqa: F401
+    LIB_PATH, OP_ARGMAX, OP_GEMV, OP_GUS_NRM, OP_MOE, OP_NRM, OP_RES, Q4_0, Q4_K, Q8_0, QgemvError,
+    header_functions, lib, qgemv, qgemv_argmax, qgemv_gus_nrm, qgemv_layout_version, qgemv_moe,
+    qgemv_moe_error, qgemv_nrm, qgemv_pack, qgemv_packed_bytes, qgemv_res, qgemv_status_str,
+    qgemv_workspace_bytes,
+)

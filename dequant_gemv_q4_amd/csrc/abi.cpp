@@ -1,0 +1,442 @@
+// abi.cpp -- the C ABI of libqgemv: argument validation, launch planning, workspace sizing.
+//
+// Every entry point validates all of its arguments on the host before it launches anything, so a
+// failed check returns a status and leaves the stream untouched.  The planner is a pure function
+// of (format, N, K, nb, op): tile length in K, lanes per row, rows per workgroup step and grid.
+#include <hip/hip_runtime.h>
+
+#include <string.h>
+
+#include "../../include/qgemv.h"
+#include "qgemv_internal.h"
+
+#ifndef QG_MAX_GRID
+#define QG_MAX_GRID 1024          // workgroups of the grid-stride GEMV kernels
+#endif
+#ifndef QG_LDS_BUDGET
+#define QG_LDS_BUDGET (64 * 1024)  // staged x bytes per workgroup (two workgroups per CU fit)
+#endif
+
+namespace qg {
+
+static int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
+
+bool fmt_valid(int fmt) { return fmt == FQ4_0 || fmt == FQ8_0 || fmt == FQ4_K; }
+
+bool layout(int fmt, int64_t N, int64_t K, Layout *L)
+{
+    if (!fmt_valid(fmt) || N < 1 || K < 1)
+        return false;
+    const int bw = fmt == FQ4_K ? 256 : 32;
+    const int bb = fmt == FQ4_0 ? 18 : fmt == FQ8_0 ? 34 : 144;
+    if (K % bw != 0 || K > QG_MAX_K)
+        return false;
+    L->block_w = bw;
+    L->block_b = bb;
+    L->qs_row = fmt == FQ8_0 ? K : K / 2;
+    L->sc_row = K / 16;
+    L->sc_off = round256(N * L->qs_row);
+    L->total = L->sc_off + round256(N * L->sc_row);
+    L->gguf_row = K / bw * bb;
+    return true;
+}
+
+struct Plan {
+    int lpr_log2, kt, n_kt, rows_per_step;
+    int64_t n_steps;
+    int grid;
+    size_t lds;
+};
+
+// Tile length: the whole row if its staged x fits the LDS budget, else the smallest number of
+// equal tiles (each a multiple of the format's tile granularity) that fits.
+static bool plan_tiles(int fmt, int64_t K, int nb, Plan *p)
+{
+    const FmtFacts F = fmt_facts(fmt);
+    for (int64_t n_kt = 1; n_kt <= K / F.tile_align; ++n_kt) {
+        if (K % n_kt || (K / n_kt) % F.tile_align)
+            continue;
+        const int kt = (int)(K / n_kt);
+        if (lds_tile_bytes(fmt, nb, kt) <= (size_t)QG_LDS_BUDGET) {
+            p->kt = kt;
+            p->n_kt = (int)n_kt;
+            p->lds = lds_tile_bytes(fmt, nb, kt);
+            const int ct = kt / F.ce;
+            int lpr = 1;
+            while (lpr < 64 && ct % (2 * lpr) == 0)
+                lpr *= 2;   // largest power of two dividing ct, at most 64
+            int lg = 0;
+            while ((1 << lg) < lpr)
+                ++lg;
+            p->lpr_log2 = lg;
+            return true;
+        }
+    }
+    return false;
+}
+
+static bool plan_gemv(int fmt, int64_t N, int64_t K, int nb, int mats, Plan *p)
+{
+    if (!plan_tiles(fmt, K, nb, p))
+        return false;
+    const int G = 64 >> p->lpr_log2;
+    p->rows_per_step = 4 * rows_in_flight(nb, mats) * G;
+    p->n_steps = (N + p->rows_per_step - 1) / p->rows_per_step;
+    p->grid = (int)(p->n_steps < QG_MAX_GRID ? p->n_steps : QG_MAX_GRID);
+    return true;
+}
+
+static bool plan_moe(int fmt, int64_t N, int64_t K, Plan *p)
+{
+    if (!plan_tiles(fmt, K, 4, p))   // groups of up to four routed rows share one staged tile
+        return false;
+    const int G = 64 >> p->lpr_log2;
+    p->rows_per_step = 4 * rows_in_flight(4, 1) * G;
+    const int64_t tile_rows = (int64_t)p->rows_per_step * QG_MOE_STEPS_PER_TILE;
+    p->n_steps = (N + tile_rows - 1) / tile_rows;   // row tiles per expert
+    return true;
+}
+
+}  // namespace qg
+
+using namespace qg;
+
+// ------------------------------------------------------------------------------------ validation
+
+static bool al(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+static bool overlap(const void *a, int64_t na, const void *b, int64_t nb)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+static int check_common(int fmt, const void *W, int64_t N, int64_t K, const float *x, int nb,
+                        const void *y, Layout *L)
+{
+    if (!fmt_valid(fmt))
+        return QG_ERR_FORMAT;
+    if (!W || !x || !y)
+        return QG_ERR_NULL;
+    if (nb < 1 || nb > QG_MAX_NB || N < 1 || N > 0x7fffffffLL || !layout(fmt, N, K, L))
+        return QG_ERR_SHAPE;
+    if (!al(W, 256) || !al(x, 16) || !al(y, 4))
+        return QG_ERR_ALIGN;
+    const int64_t ybytes = (int64_t)nb * N * 4;
+    if (overlap(y, ybytes, x, (int64_t)nb * K * 4) || overlap(y, ybytes, W, L->total))
+        return QG_ERR_ALIAS;
+    return QG_OK;
+}
+
+static int launch_status(int herr) { return herr == 0 ? QG_OK : QG_ERR_LAUNCH; }
+
+static GemvArgs gemv_args(const Layout &L, const Plan &p, const void *W, int64_t N, int64_t K,
+                          const float *x, int nb, float *y)
+{
+    GemvArgs a;
+    memset(&a, 0, sizeof(a));
+    a.qs0 = static_cast<const uint8_t *>(W);
+    a.sc0 = a.qs0 + L.sc_off;
+    a.x = x;
+    a.y = y;
+    a.N = N;
+    a.K = K;
+    a.nb = nb;
+    a.qs_row = L.qs_row;
+    a.sc_row = L.sc_row;
+    a.lpr_log2 = p.lpr_log2;
+    a.kt = p.kt;
+    a.n_kt = p.n_kt;
+    a.rows_per_step = p.rows_per_step;
+    a.n_steps = p.n_steps;
+    return a;
+}
+
+// Workspace layout of argmax: nb 64-bit keys, then the ticket.
+static int64_t ws_argmax_bytes(int nb) { return 256 + ((int64_t)nb * 8 + 255) / 256 * 256; }
+
+// Workspace layout of the routed experts: tickets (one per row tile), the sticky error flag,
+// then the partial outputs [nb][topk][N].
+static int64_t ws_moe_tickets(int64_t n_tiles) { return round256(n_tiles * 4); }
+static int64_t ws_moe_bytes(int64_t n_tiles, int64_t N, int nb, int topk)
+{
+    return ws_moe_tickets(n_tiles) + 256 + round256((int64_t)nb * topk * N * 4);
+}
+
+extern "C" {
+
+int qgemv_layout_version(void) { return 1; }
+
+const char *qgemv_status_str(int status)
+{
+    switch (status) {
+    case QG_OK: return "ok";
+    case QG_ERR_NULL: return "a required pointer is NULL";
+    case QG_ERR_FORMAT: return "unknown format (expected Q4_0=2, Q8_0=8 or Q4_K=12)";
+    case QG_ERR_SHAPE: return "bad shape (N, K, nb, topk or n_exp out of range, or K not a multiple of the block)";
+    case QG_ERR_ALIGN: return "misaligned pointer (W needs 256 B, x and gamma 16 B, other arrays 4 B)";
+    case QG_ERR_WORKSPACE: return "workspace missing or smaller than qgemv_workspace_bytes()";
+    case QG_ERR_LAUNCH: return "HIP launch failed";
+    case QG_ERR_ALIAS: return "an output overlaps an input";
+    default: return "unknown status";
+    }
+}
+
+int64_t qgemv_packed_bytes(int fmt, int64_t N, int64_t K)
+{
+    Layout L;
+    if (!layout(fmt, N, K, &L))
+        return -1;
+    return L.total;
+}
+
+int qgemv_pack(int fmt, const void *w_gguf, int64_t N, int64_t K, void *w_packed, void *stream)
+{
+    if (!fmt_valid(fmt))
+        return QG_ERR_FORMAT;
+    if (!w_gguf || !w_packed)
+        return QG_ERR_NULL;
+    Layout L;
+    if (!layout(fmt, N, K, &L))
+        return QG_ERR_SHAPE;
+    if (!al(w_packed, 256))
+        return QG_ERR_ALIGN;
+    if (overlap(w_gguf, N * L.gguf_row, w_packed, L.total))
+        return QG_ERR_ALIAS;
+    return launch_status(launch_pack(fmt, w_gguf, N, K, w_packed, stream));
+}
+
+int64_t qgemv_workspace_bytes(int op, int fmt, int64_t N, int64_t K, int nb, int64_t n_exp,
+                              int topk)
+{
+    Layout L;
+    if (!layout(fmt, N, K, &L) || nb < 1 || nb > QG_MAX_NB)
+        return -1;
+    switch (op) {
+    case QG_OP_GEMV:
+    case QG_OP_NRM:
+    case QG_OP_GUS_NRM:
+    case QG_OP_RES:
+        return 0;
+    case QG_OP_ARGMAX:
+        return ws_argmax_bytes(nb);
+    case QG_OP_MOE: {
+        Plan p;
+        if (n_exp < 1 || topk < 1 || topk > QG_MAX_TOPK || !plan_moe(fmt, N, K, &p))
+            return -1;
+        return ws_moe_bytes(p.n_steps, N, nb, topk);
+    }
+    default:
+        return -1;
+    }
+}
+
+int qgemv(int fmt, const void *W, int64_t N, int64_t K, const float *x, int nb, float *y,
+          void *ws, size_t ws_bytes, void *stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    Layout L;
+    int st = check_common(fmt, W, N, K, x, nb, y, &L);
+    if (st != QG_OK)
+        return st;
+    Plan p;
+    if (!plan_gemv(fmt, N, K, nb, 1, &p))
+        return QG_ERR_SHAPE;
+    GemvArgs a = gemv_args(L, p, W, N, K, x, nb, y);
+    return launch_status(launch_gemv(fmt, E_STORE, false, a, p.grid, p.lds, stream));
+}
+
+int qgemv_nrm(int fmt, const void *W, int64_t N, int64_t K, const float *x, const float *gamma,
+              float eps, int nb, float *y, void *ws, size_t ws_bytes, void *stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    Layout L;
+    int st = check_common(fmt, W, N, K, x, nb, y, &L);
+    if (st != QG_OK)
+        return st;
+    if (!gamma)
+        return QG_ERR_NULL;
+    if (!al(gamma, 16))
+        return QG_ERR_ALIGN;
+    if (overlap(y, (int64_t)nb * N * 4, gamma, K * 4))
+        return QG_ERR_ALIAS;
+    if (!(eps >= 0.0f))
+        return QG_ERR_SHAPE;
+    Plan p;
+    if (!plan_gemv(fmt, N, K, nb, 1, &p))
+        return QG_ERR_SHAPE;
+    GemvArgs a = gemv_args(L, p, W, N, K, x, nb, y);
+    a.gamma = gamma;
+    a.eps = eps;
+    return launch_status(launch_gemv(fmt, E_STORE, true, a, p.grid, p.lds, stream));
+}
+
+int qgemv_gus_nrm(int fmt, const void *Wg, const void *Wu, int64_t N, int64_t K, const float *x,
+                  const float *gamma, float eps, int nb, float *h, void *ws, size_t ws_bytes,
+                  void *stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    Layout L;
+    int st = check_common(fmt, Wg, N, K, x, nb, h, &L);
+    if (st != QG_OK)
+        return st;
+    if (!Wu || !gamma)
+        return QG_ERR_NULL;
+    if (!al(Wu, 256) || !al(gamma, 16))
+        return QG_ERR_ALIGN;
+    const int64_t hb = (int64_t)nb * N * 4;
+    if (overlap(h, hb, Wu, L.total) || overlap(h, hb, gamma, K * 4))
+        return QG_ERR_ALIAS;
+    if (!(eps >= 0.0f))
+        return QG_ERR_SHAPE;
+    Plan p;
+    if (!plan_gemv(fmt, N, K, nb, 2, &p))
+        return QG_ERR_SHAPE;
+    GemvArgs a = gemv_args(L, p, Wg, N, K, x, nb, h);
+    a.qs1 = static_cast<const uint8_t *>(Wu);
+    a.sc1 = a.qs1 + L.sc_off;
+    a.gamma = gamma;
+    a.eps = eps;
+    return launch_status(launch_gemv(fmt, E_GUS, true, a, p.grid, p.lds, stream));
+}
+
+int qgemv_res(int fmt, const void *W, int64_t N, int64_t K, const float *x, const float *res,
+              int nb, float *y, void *ws, size_t ws_bytes, void *stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    Layout L;
+    int st = check_common(fmt, W, N, K, x, nb, y, &L);
+    if (st != QG_OK)
+        return st;
+    if (!res)
+        return QG_ERR_NULL;
+    if (!al(res, 4))
+        return QG_ERR_ALIGN;
+    const int64_t yb = (int64_t)nb * N * 4;
+    if (res != y && overlap(y, yb, res, yb))
+        return QG_ERR_ALIAS;
+    Plan p;
+    if (!plan_gemv(fmt, N, K, nb, 1, &p))
+        return QG_ERR_SHAPE;
+    GemvArgs a = gemv_args(L, p, W, N, K, x, nb, y);
+    a.res = res;
+    return launch_status(launch_gemv(fmt, E_RES, false, a, p.grid, p.lds, stream));
+}
+
+int qgemv_argmax(int fmt, const void *W, int64_t N, int64_t K, const float *x, int nb,
+                 float *logits, int32_t *idx, void *ws, size_t ws_bytes, void *stream)
+{
+    Layout L;
+    int st = check_common(fmt, W, N, K, x, nb, logits, &L);
+    if (st != QG_OK)
+        return st;
+    if (!idx || !ws)
+        return idx ? QG_ERR_WORKSPACE : QG_ERR_NULL;
+    if (!al(idx, 4) || !al(ws, 256))
+        return QG_ERR_ALIGN;
+    if ((int64_t)ws_bytes < ws_argmax_bytes(nb))
+        return QG_ERR_WORKSPACE;
+    const int64_t lb = (int64_t)nb * N * 4;
+    if (overlap(idx, nb * 4, logits, lb) || overlap(ws, (int64_t)ws_bytes, logits, lb) ||
+        overlap(ws, (int64_t)ws_bytes, idx, nb * 4) || overlap(idx, nb * 4, x, (int64_t)nb * K * 4))
+        return QG_ERR_ALIAS;
+    Plan p;
+    if (!plan_gemv(fmt, N, K, nb, 1, &p))
+        return QG_ERR_SHAPE;
+    GemvArgs a = gemv_args(L, p, W, N, K, x, nb, logits);
+    a.idx = idx;
+    a.ticket = static_cast<unsigned int *>(ws);
+    a.keys = reinterpret_cast<unsigned long long *>(static_cast<uint8_t *>(ws) + 256);
+    return launch_status(launch_gemv(fmt, E_ARGMAX, false, a, p.grid, p.lds, stream));
+}
+
+int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t K, const float *x,
+              int nb, const int32_t *ids, const float *wts, int topk, float *y, void *ws,
+              size_t ws_bytes, void *stream)
+{
+    Layout L;
+    int st = check_common(fmt, W_experts, N, K, x, nb, y, &L);
+    if (st != QG_OK)
+        return st;
+    if (!ids || !wts)
+        return QG_ERR_NULL;
+    if (!ws)
+        return QG_ERR_WORKSPACE;
+    if (n_exp < 1 || topk < 1 || topk > QG_MAX_TOPK || n_exp * N > 0x7fffffffLL)
+        return QG_ERR_SHAPE;
+    Layout LE;   // the expert stack is packed as one matrix of n_exp * N rows
+    if (!layout(fmt, n_exp * N, K, &LE))
+        return QG_ERR_SHAPE;
+    if (!al(ids, 4) || !al(wts, 4) || !al(ws, 256))
+        return QG_ERR_ALIGN;
+    Plan p;
+    if (!plan_moe(fmt, N, K, &p))
+        return QG_ERR_SHAPE;
+    if ((int64_t)ws_bytes < ws_moe_bytes(p.n_steps, N, nb, topk))
+        return QG_ERR_WORKSPACE;
+    const int64_t yb = (int64_t)nb * N * 4;
+    if (overlap(y, yb, W_experts, LE.total) || overlap(y, yb, ws, (int64_t)ws_bytes) ||
+        overlap(y, yb, ids, (int64_t)nb * topk * 4) || overlap(y, yb, wts, (int64_t)nb * topk * 4))
+        return QG_ERR_ALIAS;
+    MoeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.qs = static_cast<const uint8_t *>(W_experts);
+    a.sc = a.qs + LE.sc_off;
+    a.x = x;
+    a.ids = ids;
+    a.wts = wts;
+    a.y = y;
+    uint8_t *w8 = static_cast<uint8_t *>(ws);
+    a.tickets = reinterpret_cast<unsigned int *>(w8);
+    a.err = reinterpret_cast<unsigned int *>(w8 + ws_moe_tickets(p.n_steps));
+    a.part = reinterpret_cast<float *>(w8 + ws_moe_tickets(p.n_steps) + 256);
+    a.n_exp = n_exp;
+    a.N = N;
+    a.K = K;
+    a.qs_row = L.qs_row;
+    a.sc_row = L.sc_row;
+    a.nb = nb;
+    a.topk = topk;
+    a.lpr_log2 = p.lpr_log2;
+    a.kt = p.kt;
+    a.n_kt = p.n_kt;
+    a.rows_per_step = p.rows_per_step;
+    a.n_tiles = p.n_steps;
+    const int64_t grid = n_exp * p.n_steps;
+    if (grid > 0x7fffffffLL)
+        return QG_ERR_SHAPE;
+    return launch_status(launch_moe(fmt, a, (int)grid, p.lds, stream));
+}
+
+int qgemv_moe_error(const void *ws, int64_t n_exp, int64_t N, int64_t K, int fmt, int *flag,
+                    void *stream)
+{
+    if (!ws || !flag)
+        return QG_ERR_NULL;
+    Plan p;
+    if (!fmt_valid(fmt))
+        return QG_ERR_FORMAT;
+    if (n_exp < 1 || !plan_moe(fmt, N, K, &p))
+        return QG_ERR_SHAPE;
+    const uint8_t *errp = static_cast<const uint8_t *>(ws) + ws_moe_tickets(p.n_steps);
+    unsigned int v = 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(&v, errp, 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return QG_ERR_LAUNCH;
+    *flag = (int)v;
+    if (v) {
+        const unsigned int zero = 0;
+        if (hipMemcpyAsync(const_cast<uint8_t *>(errp), &zero, 4, hipMemcpyHostToDevice, s) !=
+                hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return QG_ERR_LAUNCH;
+    }
+    return QG_OK;
+}
+
+}  // extern "C"

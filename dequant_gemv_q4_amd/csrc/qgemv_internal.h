@@ -1,0 +1,109 @@
+// qgemv_internal.h -- library-internal declarations shared by the ABI layer and the kernels.
+// Not installed; the public interface is include/qgemv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qg {
+
+enum Fmt { FQ4_0 = 2, FQ8_0 = 8, FQ4_K = 12 };
+
+// Epilogue kinds of the vector GEMV kernel.
+enum Epi { E_STORE = 0, E_RES = 1, E_GUS = 2, E_ARGMAX = 3 };
+
+// Routed experts: at most this many (row, slot) pairs per call (16 rows x top-8).
+#define QG_PAIRS_MAX 128
+// Routed experts: workgroup steps per output-row tile of one expert.
+#ifndef QG_MOE_STEPS_PER_TILE
+#define QG_MOE_STEPS_PER_TILE 16
+#endif
+
+// Packed device layout of one N x K matrix: a plane of quant bytes (row n at n * qs_row) and a
+// plane of scale bytes (row n at n * sc_row), each starting 256-B aligned.  Same bytes per weight
+// as the GGUF blocks.
+struct Layout {
+    int64_t qs_row;     // quant bytes per row: Q4_0 / Q4_K K/2, Q8_0 K
+    int64_t sc_row;     // scale bytes per row: K/16 for every format
+    int64_t sc_off;     // byte offset of the scale plane (qs plane rounded up to 256 B)
+    int64_t total;      // packed bytes
+    int64_t gguf_row;   // GGUF bytes per row
+    int block_w;        // weights per GGUF block
+    int block_b;        // bytes per GGUF block
+};
+
+// Facts of the 16-byte quant chunk one lane processes: x float4s it multiplies (xf4), x elements
+// (ce), block sums it needs (ns), and the K granularity a tile must keep (tile_align).
+struct FmtFacts {
+    int xf4, ce, ns, tile_align;
+};
+
+__host__ __device__ constexpr FmtFacts fmt_facts(int fmt)
+{
+    return fmt == FQ8_0 ? FmtFacts{4, 16, 1, 32}
+         : fmt == FQ4_K ? FmtFacts{8, 32, 2, 256}
+                        : FmtFacts{8, 32, 1, 32};
+}
+
+// Rows a wave keeps in flight per step of the vector kernel, by row-batch size and matrix count.
+__host__ __device__ constexpr int rows_in_flight(int nb, int mats)
+{
+    return nb == 1 ? (mats == 1 ? 4 : 2) : (nb <= 4 ? (mats == 1 ? 2 : 1) : 1);
+}
+
+// LDS bytes of one staged x tile of nb rows and kt elements (float4 region, then block sums).
+__host__ __device__ constexpr size_t lds_tile_bytes(int fmt, int nb, int kt)
+{
+    return (size_t)nb * kt * 4 + (size_t)nb * (kt / fmt_facts(fmt).ce) * fmt_facts(fmt).ns * 4;
+}
+
+bool fmt_valid(int fmt);
+bool layout(int fmt, int64_t N, int64_t K, Layout *out);
+
+// Arguments of the vector GEMV kernel family, passed by value.
+struct GemvArgs {
+    const uint8_t *qs0, *sc0;   // matrix 0 (the only matrix, or the gate)
+    const uint8_t *qs1, *sc1;   // matrix 1 (the up matrix of the gated product)
+    const float *x;             // [nb][K]
+    const float *gamma;         // [K] (norm prologue)
+    const float *res;           // [nb][N] (residual epilogue)
+    float *y;                   // [nb][N]
+    int32_t *idx;               // [nb] (argmax)
+    unsigned long long *keys;   // [nb] argmax keys in the workspace
+    unsigned int *ticket;       // workgroup ticket in the workspace
+    int64_t N, K;
+    int64_t qs_row, sc_row;
+    float eps;
+    int nb;
+    int lpr_log2;               // log2 of lanes cooperating on one row
+    int kt;                     // K elements per LDS tile
+    int n_kt;                   // tiles per row
+    int rows_per_step;          // rows one workgroup finishes per step
+    int64_t n_steps;            // workgroup steps covering N rows
+};
+
+// Arguments of the routed-expert kernels.
+struct MoeArgs {
+    const uint8_t *qs, *sc;     // packed expert stack: n_exp * N rows
+    const float *x;             // [nb][K]
+    const int32_t *ids;         // [nb][topk]
+    const float *wts;           // [nb][topk]
+    float *y;                   // [nb][N]
+    float *part;                // workspace: [nb][topk][N] partial outputs
+    unsigned int *err;          // workspace: sticky bad-id flag
+    unsigned int *tickets;      // workspace: one ticket per output tile
+    int64_t n_exp, N, K;
+    int64_t qs_row, sc_row;
+    int nb, topk;
+    int lpr_log2, kt, n_kt, rows_per_step;
+    int64_t n_tiles;            // output-row tiles per expert
+};
+
+// Launch helpers (gemv_kernels.hip).  Return a hipError_t value (0 = success).
+int launch_pack(int fmt, const void *src, int64_t N, int64_t K, void *dst, void *stream);
+int launch_gemv(int fmt, int epi, bool nrm, const GemvArgs &a, int grid, size_t lds_bytes,
+                void *stream);
+int launch_moe(int fmt, const MoeArgs &a, int grid, size_t lds_bytes, void *stream);
+
+}  // namespace qg

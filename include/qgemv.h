@@ -1,0 +1,142 @@
+/*
+ * qgemv.h -- C ABI of libqgemv: block-quantized weight GEMV for LLM decode on MI355X (gfx950).
+ *
+ * The operations are the dequant-in-GEMV family of one decode step, for one token or a row
+ * batch of nb <= 16 positions (activations row-major [nb][...], the row-batched steps of
+ * "Module gpu", cherenkov qwen4_exp docs, module summary), fused with the neighbouring steps
+ * "honeycrisp mod.rs" encodes around its quantized matmuls: RMSNorm prologue, gate+up with the
+ * SiLU-gated product, residual add, and greedy argmax of the lm_head.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Formats (GGUF type ids): QG_Q4_0 = 2, QG_Q8_0 = 8, QG_Q4_K = 12.
+ *      Q4_0: 32 weights in 18 B (f16 d, 16 B nibbles), w = (q - 8) * d.
+ *      Q8_0: 32 weights in 34 B (f16 d, 32 x i8),     w = d * q.
+ *      Q4_K: 256 weights in 144 B (f16 d, f16 dmin, 12 B of eight packed 6-bit (scale, min)
+ *            pairs, 128 B nibbles), w = d * sc_j * q - dmin * m_j.
+ *  - W arguments of the compute entry points are in the PACKED device layout written by
+ *    qgemv_pack (same bytes per weight as GGUF, split into planes so every hot load is an
+ *    aligned 16-byte load).  Rows are in output order; K is the reduction length.
+ *  - Every pointer of a compute call is a DEVICE pointer (HIP device memory).  The caller owns
+ *    all memory; the library never allocates or frees and keeps no state between calls.
+ *  - x is f32 [nb][K], outputs f32 [nb][N], all row-major and contiguous.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every call only
+ *    enqueues work on that stream and returns; nothing synchronizes the host.
+ *  - `ws` is a device workspace of at least qgemv_workspace_bytes(...) bytes (may be NULL when
+ *    that is 0).  It must be zero-filled ONCE after allocation; the kernels leave it zeroed
+ *    again after every call (argmax keys and tickets are reset by the last workgroup).  Calls
+ *    that share one workspace must be ordered on one stream.
+ *  - Errors: every argument is validated on the host before anything is launched; a failed
+ *    check returns its status and launches nothing.  QG_ERR_LAUNCH reports a HIP error from the
+ *    launch itself.  qgemv_status_str gives a static description.
+ *  - No CPU fallback: a call the kernels cannot serve is an error, never a host computation.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { QG_Q4_0 = 2, QG_Q8_0 = 8, QG_Q4_K = 12 };
+
+enum {
+    QG_OK = 0,
+    QG_ERR_NULL = 1,       /* a required pointer is NULL */
+    QG_ERR_FORMAT = 2,     /* unknown format id */
+    QG_ERR_SHAPE = 3,      /* N < 1, nb outside [1, 16], K not a positive multiple of the block,
+                              topk outside [1, 8], n_exp < 1, or a size beyond the limits */
+    QG_ERR_ALIGN = 4,      /* W not 256-B aligned, or x / y / other f32 arrays not 16-B aligned */
+    QG_ERR_WORKSPACE = 5,  /* ws smaller than qgemv_workspace_bytes() */
+    QG_ERR_LAUNCH = 6,     /* the HIP launch reported an error */
+    QG_ERR_ALIAS = 7       /* an output overlaps an input in a way the call does not allow */
+};
+
+/* Operation ids for qgemv_workspace_bytes. */
+enum { QG_OP_GEMV = 0, QG_OP_NRM = 1, QG_OP_GUS_NRM = 2, QG_OP_RES = 3, QG_OP_ARGMAX = 4,
+       QG_OP_MOE = 5 };
+
+/* Limits checked by every entry point. */
+#define QG_MAX_NB 16
+#define QG_MAX_TOPK 8
+#define QG_MAX_K 65536
+
+/* Bytes of the packed device layout of an N x K matrix, or -1 if (fmt, N, K) is invalid.
+ * Equal to the GGUF byte count rounded up to 256 B per plane.  Host-only, no HIP call. */
+int64_t qgemv_packed_bytes(int fmt, int64_t N, int64_t K);
+
+/* Re-lay GGUF-native blocks (w_gguf: N rows of K/bs consecutive blocks, the native row order of
+ * "honeycrisp mod.rs", transpose_q8_blocks) into the packed layout (w_packed, at least
+ * qgemv_packed_bytes bytes, 256-B aligned).  A pure byte move, done once per matrix; the
+ * analogue of the pad/re-layout passes of "Crate inferencelayer" (q8_0_pad_blocks,
+ * q6k_pad_blocks).  Both pointers are device pointers and must not overlap.  For Q4_K expert
+ * stacks pass N = n_exp * rows. */
+int qgemv_pack(int fmt, const void *w_gguf, int64_t N, int64_t K, void *w_packed, void *stream);
+
+/* Workspace bytes an operation needs for these sizes (0 if none), or -1 on invalid sizes.
+ * n_exp and topk are read only for QG_OP_MOE.  Host-only. */
+int64_t qgemv_workspace_bytes(int op, int fmt, int64_t N, int64_t K, int nb, int64_t n_exp,
+                              int topk);
+
+/* y[r][n] = sum_k W[n][k] x[r][k].  ("Crate inferencelayer", gemv_q4_k_lcpp_src and its
+ * Q8_0 / Q4_K siblings; "honeycrisp mod.rs", quant_matmul.)  y must not overlap x or W. */
+int qgemv(int fmt, const void *W, int64_t N, int64_t K, const float *x, int nb, float *y,
+          void *ws, size_t ws_bytes, void *stream);
+
+/* y = W rmsnorm(x): n[r][k] = x[r][k] * gamma[k] / sqrt(mean_k x[r][k]^2 + eps), then the GEMV.
+ * ("honeycrisp mod.rs", fused_norm_quant_matmul_multi and the Op::RmsNorm { eps } arm.)
+ * gamma is f32 [K].  A concatenated Q|K|V matrix is passed as one W of N = nq + nk + nv rows. */
+int qgemv_nrm(int fmt, const void *W, int64_t N, int64_t K, const float *x, const float *gamma,
+              float eps, int nb, float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* h[r][n] = silu(g) * u with g = Wg n_r, u = Wu n_r and n = rmsnorm(x) as in qgemv_nrm;
+ * silu(g) = g / (1 + e^-g).  ("honeycrisp mod.rs", fused_norm_swiglu_down: mid = silu(gate) * up;
+ * "Crate inferencelayer", mlp_gate_q8_0n_lcpp_src: act(gate) * up.)  Wg and Wu are two packed
+ * matrices of the same format and shape N x K; h is f32 [nb][N]. */
+int qgemv_gus_nrm(int fmt, const void *Wg, const void *Wu, int64_t N, int64_t K, const float *x,
+                  const float *gamma, float eps, int nb, float *h, void *ws, size_t ws_bytes,
+                  void *stream);
+
+/* y[r][n] = sum_k W[n][k] x[r][k] + res[r][n].  ("honeycrisp mod.rs", fused matmul + residual in
+ * forward_decode_fused_layers.)  res is f32 [nb][N]; y may equal res (in place), no other
+ * overlap is allowed. */
+int qgemv_res(int fmt, const void *W, int64_t N, int64_t K, const float *x, const float *res,
+              int nb, float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* logits[r][n] = sum_k W[n][k] x[r][k] and idx[r] = the lowest n holding the maximum of row r
+ * (greedy argmax on the GPU, no logits read-back: "Module gpu", sampling; "Crate
+ * inferencelayer", crate summary).  idx is int32 [nb].  Needs a workspace. */
+int qgemv_argmax(int fmt, const void *W, int64_t N, int64_t K, const float *x, int nb,
+                 float *logits, int32_t *idx, void *ws, size_t ws_bytes, void *stream);
+
+/* Routed experts: y[r][n] = sum_{t=0..topk-1} wts[r][t] * (W_{ids[r][t]} x_r)[n], the terms added
+ * in ascending t.  ("Module gpu", type alias RouteStep: expert ids and routing weights of one
+ * step; module experts.)  W_experts holds n_exp packed N x K matrices back to back (pack them
+ * as one matrix of n_exp * N rows).  ids int32 [nb][topk]; wts f32 [nb][topk].  An id outside
+ * [0, n_exp) adds nothing to its row and sets a sticky flag in the workspace that
+ * qgemv_moe_error reports.  Needs a workspace. */
+int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t K, const float *x,
+              int nb, const int32_t *ids, const float *wts, int topk, float *y, void *ws,
+              size_t ws_bytes, void *stream);
+
+/* Reads and clears the bad-expert-id flag qgemv_moe leaves in its workspace (*flag = 1 if any id
+ * of an earlier call on this workspace was out of range).  Unlike every other entry point this
+ * one SYNCHRONIZES `stream` (it copies the flag to the host).  The sizes must be those the
+ * workspace was sized for. */
+int qgemv_moe_error(const void *ws, int64_t n_exp, int64_t N, int64_t K, int fmt, int *flag,
+                    void *stream);
+
+/* Static, human-readable text of a status code. */
+const char *qgemv_status_str(int status);
+
+/* Version of the packed layout; changes whenever qgemv_pack's output changes. */
+int qgemv_layout_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

@@ -99,6 +99,8 @@ def route_top_k(z: np.ndarray, topk: int) -> tuple[np.ndarray, np.ndarray]:
 
     This is input preparation upstream of the routed GEMV, which takes (ids, weights) as
     given."""
+    if not 1 <= topk <= z.shape[1]:
+        raise ValueError(f"topk={topk} needs 1 <= topk <= n_exp={z.shape[1]}")
     order = np.argsort(-z, axis=1, kind="stable")[:, :topk]
     zs = np.take_along_axis(z, order, axis=1).astype(np.float64)
     e = np.exp(zs - zs.max(axis=1, keepdims=True))
