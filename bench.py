@@ -214,6 +214,26 @@ def make_moe(warm):
                  step, step, cpu, cfg)
 
 
+def make_copy(warm):
+    """A plain device-to-device copy of 256 MiB (torch's copy kernel): the attainable-bandwidth
+    reference and the known-size kernel that calibrates the HBM byte counters."""
+    import torch
+
+    n = 256 << 20
+    srcs = [torch.empty(n, dtype=torch.uint8, device="cuda").fill_(i + 1) for i in range(4)]
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        dst.copy_(srcs[i % len(srcs)])
+
+    def cpu():
+        return 0
+
+    cfg = {"workload": "device_copy_256MiB", "bytes_read": n, "bytes_written": n,
+           "launches_per_step": 1, "weight_copies": len(srcs), "cold": True}
+    return Bench(cfg["workload"], n, 2 * n, "torch copy_ (256 MiB)", step, step, cpu, cfg)
+
+
 def time_loop(fn, start, count, torch):
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -267,7 +287,7 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode_mlp",
-                    choices=["decode_mlp", "lm_head", "gemv", "qkv", "moe"])
+                    choices=["decode_mlp", "lm_head", "gemv", "qkv", "moe", "copy"])
     ap.add_argument("--nb", type=int, default=None)
     ap.add_argument("--warm", action="store_true", help="reuse one weight copy (cache-assisted)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -296,6 +316,9 @@ def main():
         b = make_gemv(args.warm, args.nb or 1)
     elif args.workload == "qkv":
         b = make_qkv(args.warm, args.nb or 16)
+    elif args.workload == "copy":
+        b = make_copy(args.warm)
+        args.no_cpu = True
     else:
         b = make_moe(args.warm)
     log(f"bench: {b.name}, copies={b.config['weight_copies']}, warmup={args.warmup}, steps={args.steps}")

@@ -3,7 +3,8 @@
     python -m dequant_gemv_q4_amd.build            # build (always recompiles)
     python -m dequant_gemv_q4_amd.build --save-temps DIR   # also keep the gfx950 assembly
 
-Extra preprocessor definitions for tuning sweeps can be passed with ``-D NAME=VALUE``.
+Each source compiles to an object in parallel (``_build/``), then one link.  Extra preprocessor
+definitions for tuning sweeps can be passed with ``-D NAME=VALUE``.
 """
 from __future__ import annotations
 
@@ -12,16 +13,18 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqgemv.so")
-SOURCES = [os.path.join(CSRC, "gemv_kernels.hip"), os.path.join(CSRC, "abi.cpp")]
+BUILD_DIR = os.path.join(ROOT, "_build")
+SOURCES = ["gemv_kernels.hip", "stream_kernels.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed FP32 instructions stay off: the compiler must not form them from float code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
@@ -36,19 +39,31 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build(defines=(), save_temps: str | None = None, out: str = LIB, verbose: bool = False) -> str:
-    cmd = [hipcc(), *HIPCC_FLAGS]
-    for d in defines:
-        cmd += ["-D", d]
+def _compile(src, obj, defines, save_temps, verbose):
+    cmd = [hipcc(), *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if save_temps:
-        os.makedirs(save_temps, exist_ok=True)
-        cmd += ["-save-temps=obj"]
-    tmp = out + ".tmp"
-    cmd += ["-o", tmp, *SOURCES]
+        cmd.append("-save-temps=obj")
     if verbose:
         print(" ".join(cmd), flush=True)
-    cwd = save_temps if save_temps else None
-    subprocess.run(cmd, check=True, cwd=cwd)
+    subprocess.run(cmd, check=True, cwd=save_temps or None)
+    return obj
+
+
+def build(defines=(), save_temps: str | None = None, out: str = LIB, verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    if save_temps:
+        os.makedirs(save_temps, exist_ok=True)
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        list(ex.map(lambda so: _compile(so[0], so[1], defines, save_temps, verbose),
+                    zip(SOURCES, objs)))
+    tmp = out + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp,
+           *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
 

@@ -16,6 +16,7 @@
 #ifndef QG_LDS_BUDGET
 #define QG_LDS_BUDGET (64 * 1024)  // staged x bytes per workgroup (two workgroups per CU fit)
 #endif
+#define QG_ARGMAX_MAX_GRID 4096    // argmax partial keys are kept per workgroup in the workspace
 
 namespace qg {
 
@@ -86,14 +87,69 @@ static bool plan_gemv(int fmt, int64_t N, int64_t K, int nb, int mats, Plan *p)
     return true;
 }
 
-static bool plan_moe(int fmt, int64_t N, int64_t K, Plan *p)
+// Streaming path (whole wave per row): nb <= 4, at most 4 chunks of 16 bytes per lane and row,
+// and the staged row(s) of x in the LDS budget.  Returns the chunks-per-lane class, or 0.
+static int stream_cpl(int fmt, int64_t K, int nb)
 {
-    if (!plan_tiles(fmt, K, 4, p))   // groups of up to four routed rows share one staged tile
+    if (nb > 4)
+        return 0;
+    const int64_t C = (fmt == FQ8_0 ? K : K / 2) / 16;
+    const int cpl = C <= 64 ? 1 : C <= 128 ? 2 : C <= 256 ? 4 : 0;
+    if (!cpl || lds_tile_bytes(fmt, nb, (int)K) > (size_t)QG_LDS_BUDGET)
+        return 0;
+    // the one-pass staging gives each (batch row, chunk) its own thread of the 256
+    if (nb * C > 256)
+        return 0;
+    return cpl;
+}
+
+struct StreamPlan {
+    int cpl;
+    int grid;
+    size_t lds;
+};
+
+static bool plan_stream(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb, StreamPlan *sp)
+{
+    const int cpl = stream_cpl(fmt, K, nb);
+    if (!cpl)
         return false;
-    const int G = 64 >> p->lpr_log2;
-    p->rows_per_step = 4 * rows_in_flight(4, 1) * G;
-    const int64_t tile_rows = (int64_t)p->rows_per_step * QG_MOE_STEPS_PER_TILE;
-    p->n_steps = (N + tile_rows - 1) / tile_rows;   // row tiles per expert
+    const int mats = epi == E_GUS ? 2 : 1;
+    const int R = stream_rows(nb, 1, mats);
+    const int64_t groups = (N + R - 1) / R;
+    const int teams = 4 / cpl;                        // a row's K is split over cpl waves
+    const int64_t want = (groups + teams - 1) / teams;
+    sp->cpl = cpl;
+    sp->lds = lds_tile_bytes(fmt, nb, (int)K);
+    int resident = stream_resident_wgs(fmt, epi, nrm, cpl, nb, sp->lds);
+    if (resident <= 0)
+        resident = QG_MAX_GRID;
+    if (epi == E_ARGMAX && resident > QG_ARGMAX_MAX_GRID)
+        resident = QG_ARGMAX_MAX_GRID;
+    sp->grid = (int)(want < resident ? want : resident);
+    return true;
+}
+
+// Routed experts: chunks per lane (1, 2 or 4 of 16 bytes per row) and how many routed rows are
+// staged together so that they fit the LDS budget.
+static bool plan_moe(int fmt, int64_t N, int64_t K, int *cpl, int *group_max, size_t *lds,
+                     int64_t *n_tiles)
+{
+    const int64_t C = (fmt == FQ8_0 ? K : K / 2) / 16;
+    *cpl = C <= 64 ? 1 : C <= 128 ? 2 : C <= 256 ? 4 : 0;
+    if (!*cpl)
+        return false;
+    // the staging gives every (routed row, chunk) of a group its own thread of the 256
+    *group_max = 4;
+    while (*group_max > 1 && (lds_tile_bytes(fmt, *group_max, (int)K) > (size_t)QG_LDS_BUDGET ||
+                              *group_max * C > 256))
+        *group_max /= 2;
+    if (C > 256)
+        return false;
+    if (lds_tile_bytes(fmt, *group_max, (int)K) > (size_t)QG_LDS_BUDGET)
+        return false;
+    *lds = lds_tile_bytes(fmt, *group_max, (int)K);
+    *n_tiles = (N + QG_MOE_TILE_ROWS - 1) / QG_MOE_TILE_ROWS;
     return true;
 }
 
@@ -130,8 +186,8 @@ static int check_common(int fmt, const void *W, int64_t N, int64_t K, const floa
 
 static int launch_status(int herr) { return herr == 0 ? QG_OK : QG_ERR_LAUNCH; }
 
-static GemvArgs gemv_args(const Layout &L, const Plan &p, const void *W, int64_t N, int64_t K,
-                          const float *x, int nb, float *y)
+static GemvArgs gemv_args(const Layout &L, const void *W, int64_t N, int64_t K, const float *x,
+                          int nb, float *y)
 {
     GemvArgs a;
     memset(&a, 0, sizeof(a));
@@ -144,23 +200,44 @@ static GemvArgs gemv_args(const Layout &L, const Plan &p, const void *W, int64_t
     a.nb = nb;
     a.qs_row = L.qs_row;
     a.sc_row = L.sc_row;
-    a.lpr_log2 = p.lpr_log2;
-    a.kt = p.kt;
-    a.n_kt = p.n_kt;
-    a.rows_per_step = p.rows_per_step;
-    a.n_steps = p.n_steps;
     return a;
 }
 
-// Workspace layout of argmax: nb 64-bit keys, then the ticket.
-static int64_t ws_argmax_bytes(int nb) { return 256 + ((int64_t)nb * 8 + 255) / 256 * 256; }
-
-// Workspace layout of the routed experts: tickets (one per row tile), the sticky error flag,
-// then the partial outputs [nb][topk][N].
-static int64_t ws_moe_tickets(int64_t n_tiles) { return round256(n_tiles * 4); }
-static int64_t ws_moe_bytes(int64_t n_tiles, int64_t N, int nb, int topk)
+// Launch one member of the GEMV family: the streaming kernel when the shape allows it (a whole
+// wave per row), else the tiled kernel (any nb, any K).  An argmax launch is followed by the
+// one-workgroup fold of its per-workgroup partial keys.
+static int run_gemv(int fmt, int epi, bool nrm, GemvArgs a, void *stream)
 {
-    return ws_moe_tickets(n_tiles) + 256 + round256((int64_t)nb * topk * N * 4);
+    int grid = 0, herr = 0;
+    StreamPlan sp;
+    if (plan_stream(fmt, epi, nrm, a.N, a.K, a.nb, &sp)) {
+        grid = sp.grid;
+        herr = launch_stream(fmt, epi, nrm, sp.cpl, a, sp.grid, sp.lds, stream);
+    } else {
+        Plan p;
+        if (!plan_gemv(fmt, a.N, a.K, a.nb, epi == E_GUS ? 2 : 1, &p))
+            return QG_ERR_SHAPE;
+        a.lpr_log2 = p.lpr_log2;
+        a.kt = p.kt;
+        a.n_kt = p.n_kt;
+        a.rows_per_step = p.rows_per_step;
+        a.n_steps = p.n_steps;
+        grid = p.grid;
+        herr = launch_gemv(fmt, epi, nrm, a, p.grid, p.lds, stream);
+    }
+    if (herr == 0 && epi == E_ARGMAX)
+        herr = launch_argmax_fold(a.keys, grid, a.nb, a.idx, stream);
+    return launch_status(herr);
+}
+
+// Workspace of argmax: one 64-bit partial key per workgroup and batch row.
+static int64_t ws_argmax_bytes(int nb) { return (int64_t)QG_ARGMAX_MAX_GRID * nb * 8; }
+
+// Workspace of the routed experts: the sticky bad-id flag, then the partial outputs
+// [nb][topk][N].
+static int64_t ws_moe_bytes(int64_t N, int nb, int topk)
+{
+    return 256 + round256((int64_t)nb * topk * N * 4);
 }
 
 extern "C" {
@@ -221,10 +298,13 @@ int64_t qgemv_workspace_bytes(int op, int fmt, int64_t N, int64_t K, int nb, int
     case QG_OP_ARGMAX:
         return ws_argmax_bytes(nb);
     case QG_OP_MOE: {
-        Plan p;
-        if (n_exp < 1 || topk < 1 || topk > QG_MAX_TOPK || !plan_moe(fmt, N, K, &p))
+        int cpl, gmax;
+        size_t lds;
+        int64_t n_tiles;
+        if (n_exp < 1 || topk < 1 || topk > QG_MAX_TOPK ||
+            !plan_moe(fmt, N, K, &cpl, &gmax, &lds, &n_tiles))
             return -1;
-        return ws_moe_bytes(p.n_steps, N, nb, topk);
+        return ws_moe_bytes(N, nb, topk);
     }
     default:
         return -1;
@@ -240,11 +320,7 @@ int qgemv(int fmt, const void *W, int64_t N, int64_t K, const float *x, int nb, 
     int st = check_common(fmt, W, N, K, x, nb, y, &L);
     if (st != QG_OK)
         return st;
-    Plan p;
-    if (!plan_gemv(fmt, N, K, nb, 1, &p))
-        return QG_ERR_SHAPE;
-    GemvArgs a = gemv_args(L, p, W, N, K, x, nb, y);
-    return launch_status(launch_gemv(fmt, E_STORE, false, a, p.grid, p.lds, stream));
+    return run_gemv(fmt, E_STORE, false, gemv_args(L, W, N, K, x, nb, y), stream);
 }
 
 int qgemv_nrm(int fmt, const void *W, int64_t N, int64_t K, const float *x, const float *gamma,
@@ -264,13 +340,10 @@ int qgemv_nrm(int fmt, const void *W, int64_t N, int64_t K, const float *x, cons
         return QG_ERR_ALIAS;
     if (!(eps >= 0.0f))
         return QG_ERR_SHAPE;
-    Plan p;
-    if (!plan_gemv(fmt, N, K, nb, 1, &p))
-        return QG_ERR_SHAPE;
-    GemvArgs a = gemv_args(L, p, W, N, K, x, nb, y);
+    GemvArgs a = gemv_args(L, W, N, K, x, nb, y);
     a.gamma = gamma;
     a.eps = eps;
-    return launch_status(launch_gemv(fmt, E_STORE, true, a, p.grid, p.lds, stream));
+    return run_gemv(fmt, E_STORE, true, a, stream);
 }
 
 int qgemv_gus_nrm(int fmt, const void *Wg, const void *Wu, int64_t N, int64_t K, const float *x,
@@ -292,15 +365,12 @@ int qgemv_gus_nrm(int fmt, const void *Wg, const void *Wu, int64_t N, int64_t K,
         return QG_ERR_ALIAS;
     if (!(eps >= 0.0f))
         return QG_ERR_SHAPE;
-    Plan p;
-    if (!plan_gemv(fmt, N, K, nb, 2, &p))
-        return QG_ERR_SHAPE;
-    GemvArgs a = gemv_args(L, p, Wg, N, K, x, nb, h);
+    GemvArgs a = gemv_args(L, Wg, N, K, x, nb, h);
     a.qs1 = static_cast<const uint8_t *>(Wu);
     a.sc1 = a.qs1 + L.sc_off;
     a.gamma = gamma;
     a.eps = eps;
-    return launch_status(launch_gemv(fmt, E_GUS, true, a, p.grid, p.lds, stream));
+    return run_gemv(fmt, E_GUS, true, a, stream);
 }
 
 int qgemv_res(int fmt, const void *W, int64_t N, int64_t K, const float *x, const float *res,
@@ -319,12 +389,9 @@ int qgemv_res(int fmt, const void *W, int64_t N, int64_t K, const float *x, cons
     const int64_t yb = (int64_t)nb * N * 4;
     if (res != y && overlap(y, yb, res, yb))
         return QG_ERR_ALIAS;
-    Plan p;
-    if (!plan_gemv(fmt, N, K, nb, 1, &p))
-        return QG_ERR_SHAPE;
-    GemvArgs a = gemv_args(L, p, W, N, K, x, nb, y);
+    GemvArgs a = gemv_args(L, W, N, K, x, nb, y);
     a.res = res;
-    return launch_status(launch_gemv(fmt, E_RES, false, a, p.grid, p.lds, stream));
+    return run_gemv(fmt, E_RES, false, a, stream);
 }
 
 int qgemv_argmax(int fmt, const void *W, int64_t N, int64_t K, const float *x, int nb,
@@ -344,14 +411,10 @@ int qgemv_argmax(int fmt, const void *W, int64_t N, int64_t K, const float *x, i
     if (overlap(idx, nb * 4, logits, lb) || overlap(ws, (int64_t)ws_bytes, logits, lb) ||
         overlap(ws, (int64_t)ws_bytes, idx, nb * 4) || overlap(idx, nb * 4, x, (int64_t)nb * K * 4))
         return QG_ERR_ALIAS;
-    Plan p;
-    if (!plan_gemv(fmt, N, K, nb, 1, &p))
-        return QG_ERR_SHAPE;
-    GemvArgs a = gemv_args(L, p, W, N, K, x, nb, logits);
+    GemvArgs a = gemv_args(L, W, N, K, x, nb, logits);
     a.idx = idx;
-    a.ticket = static_cast<unsigned int *>(ws);
-    a.keys = reinterpret_cast<unsigned long long *>(static_cast<uint8_t *>(ws) + 256);
-    return launch_status(launch_gemv(fmt, E_ARGMAX, false, a, p.grid, p.lds, stream));
+    a.keys = static_cast<unsigned long long *>(ws);
+    return run_gemv(fmt, E_ARGMAX, false, a, stream);
 }
 
 int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t K, const float *x,
@@ -373,15 +436,20 @@ int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t 
         return QG_ERR_SHAPE;
     if (!al(ids, 4) || !al(wts, 4) || !al(ws, 256))
         return QG_ERR_ALIGN;
-    Plan p;
-    if (!plan_moe(fmt, N, K, &p))
+    int cpl, gmax;
+    size_t lds;
+    int64_t n_tiles;
+    if (!plan_moe(fmt, N, K, &cpl, &gmax, &lds, &n_tiles))
         return QG_ERR_SHAPE;
-    if ((int64_t)ws_bytes < ws_moe_bytes(p.n_steps, N, nb, topk))
+    if ((int64_t)ws_bytes < ws_moe_bytes(N, nb, topk))
         return QG_ERR_WORKSPACE;
     const int64_t yb = (int64_t)nb * N * 4;
     if (overlap(y, yb, W_experts, LE.total) || overlap(y, yb, ws, (int64_t)ws_bytes) ||
         overlap(y, yb, ids, (int64_t)nb * topk * 4) || overlap(y, yb, wts, (int64_t)nb * topk * 4))
         return QG_ERR_ALIAS;
+    const int64_t grid = n_exp * n_tiles;
+    if (grid > 0x7fffffffLL)
+        return QG_ERR_SHAPE;
     MoeArgs a;
     memset(&a, 0, sizeof(a));
     a.qs = static_cast<const uint8_t *>(W_experts);
@@ -391,9 +459,8 @@ int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t 
     a.wts = wts;
     a.y = y;
     uint8_t *w8 = static_cast<uint8_t *>(ws);
-    a.tickets = reinterpret_cast<unsigned int *>(w8);
-    a.err = reinterpret_cast<unsigned int *>(w8 + ws_moe_tickets(p.n_steps));
-    a.part = reinterpret_cast<float *>(w8 + ws_moe_tickets(p.n_steps) + 256);
+    a.err = reinterpret_cast<unsigned int *>(w8);
+    a.part = reinterpret_cast<float *>(w8 + 256);
     a.n_exp = n_exp;
     a.N = N;
     a.K = K;
@@ -401,15 +468,10 @@ int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t 
     a.sc_row = L.sc_row;
     a.nb = nb;
     a.topk = topk;
-    a.lpr_log2 = p.lpr_log2;
-    a.kt = p.kt;
-    a.n_kt = p.n_kt;
-    a.rows_per_step = p.rows_per_step;
-    a.n_tiles = p.n_steps;
-    const int64_t grid = n_exp * p.n_steps;
-    if (grid > 0x7fffffffLL)
-        return QG_ERR_SHAPE;
-    return launch_status(launch_moe(fmt, a, (int)grid, p.lds, stream));
+    a.tile_rows = QG_MOE_TILE_ROWS;
+    a.group_max = gmax;
+    a.n_tiles = n_tiles;
+    return launch_status(launch_moe(fmt, cpl, a, (int)grid, lds, stream));
 }
 
 int qgemv_moe_error(const void *ws, int64_t n_exp, int64_t N, int64_t K, int fmt, int *flag,
@@ -417,12 +479,14 @@ int qgemv_moe_error(const void *ws, int64_t n_exp, int64_t N, int64_t K, int fmt
 {
     if (!ws || !flag)
         return QG_ERR_NULL;
-    Plan p;
     if (!fmt_valid(fmt))
         return QG_ERR_FORMAT;
-    if (n_exp < 1 || !plan_moe(fmt, N, K, &p))
+    int cpl, gmax;
+    size_t lds;
+    int64_t n_tiles;
+    if (n_exp < 1 || !plan_moe(fmt, N, K, &cpl, &gmax, &lds, &n_tiles))
         return QG_ERR_SHAPE;
-    const uint8_t *errp = static_cast<const uint8_t *>(ws) + ws_moe_tickets(p.n_steps);
+    const uint8_t *errp = static_cast<const uint8_t *>(ws);
     unsigned int v = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (hipMemcpyAsync(&v, errp, 4, hipMemcpyDeviceToHost, s) != hipSuccess ||

@@ -1,0 +1,379 @@
+// device_common.h -- device helpers shared by the gfx950 kernels of libqgemv: chunk decode,
+// block-offset folding, staging of x into LDS, scale decode, lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "qgemv_internal.h"
+
+namespace qg {
+
+// ------------------------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ float h2f(uint32_t bits16)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+__device__ __forceinline__ float ub0(uint32_t v) { return (float)(v & 0xffu); }
+__device__ __forceinline__ float ub1(uint32_t v) { return (float)((v >> 8) & 0xffu); }
+__device__ __forceinline__ float ub2(uint32_t v) { return (float)((v >> 16) & 0xffu); }
+__device__ __forceinline__ float ub3(uint32_t v) { return (float)(v >> 24); }
+
+__device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+__device__ __forceinline__ uint32_t ucomp(const uint4 &v, int k)
+{
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ float4 f4scale(float4 v, float s, float4 g)
+{
+    return make_float4(v.x * s * g.x, v.y * s * g.y, v.z * s * g.z, v.w * s * g.w);
+}
+
+// Per-format compile-time facts of the chunk (16 bytes of quants) a lane processes.
+template <int FMT> struct Fc {
+    static constexpr int XF4 = fmt_facts(FMT).xf4, CE = fmt_facts(FMT).ce, NS = fmt_facts(FMT).ns;
+};
+
+// Element (within a K tile) of float4 j of chunk i.
+template <int FMT>
+__device__ __forceinline__ int chunk_elem(int i, int j)
+{
+    if constexpr (FMT == FQ4_0) {
+        return 32 * i + 4 * j;             // one 32-weight block per chunk
+    } else if constexpr (FMT == FQ8_0) {
+        return 16 * i + 4 * j;             // half a block per chunk
+    } else {
+        // Q4_K: chunk i is bytes 16q..16q+15 of super-block s's nibbles (q = i % 8).  Its low
+        // nibbles are elements 64c + 16h + 0..15 (sub-block 2c), its high nibbles elements
+        // 64c + 32 + 16h + 0..15 (sub-block 2c + 1), with c = q / 2, h = q % 2.
+        const int s = i >> 3, q = i & 7, c = q >> 1, h = q & 1;
+        const int base = 256 * s + 64 * c + 16 * h;
+        return j < 4 ? base + 4 * j : base + 32 + 4 * (j - 4);
+    }
+}
+
+// ------------------------------------------------------------------------------------ staging
+
+// Stage K-tile t of NB x rows into LDS.  Row r comes from xrow[r] (nullptr = a zero row).  With
+// NRM every element is multiplied by inv[r] and gamma.  Then the per-chunk sums S are formed in
+// exactly the order the dot products consume the elements.
+template <int FMT, int NB, bool NRM>
+__device__ void stage_tile(const float *const *xrow, const float *gamma, const float *inv, int t,
+                           int kt, float4 *X4, float *S)
+{
+    constexpr int XF4 = Fc<FMT>::XF4, CE = Fc<FMT>::CE;
+    const int ct = kt / CE;
+    const int total = NB * ct * XF4;
+    for (int f = threadIdx.x; f < total; f += blockDim.x) {
+        const int j = f % XF4;
+        const int i = (f / XF4) % ct;
+        const int r = f / (XF4 * ct);
+        const int e = t * kt + chunk_elem<FMT>(i, j);
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (xrow[r]) {
+            v = *reinterpret_cast<const float4 *>(xrow[r] + e);
+            if constexpr (NRM)
+                v = f4scale(v, inv[r], *reinterpret_cast<const float4 *>(gamma + e));
+        }
+        X4[(r * XF4 + j) * ct + i] = v;
+    }
+    __syncthreads();
+    for (int f = threadIdx.x; f < NB * ct; f += blockDim.x) {
+        const int r = f / ct, i = f % ct;
+        const float4 *xc = X4 + (size_t)r * XF4 * ct + i;
+        if constexpr (FMT == FQ4_0) {
+            // dot order: for each dword k, its low nibbles (elements 4k..4k+3) then its high
+            // nibbles (elements 16+4k..16+4k+3)
+            float s = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float4 a = xc[k * ct], b = xc[(4 + k) * ct];
+                s += a.x; s += a.y; s += a.z; s += a.w;
+                s += b.x; s += b.y; s += b.z; s += b.w;
+            }
+            S[f] = s;
+        } else if constexpr (FMT == FQ8_0) {
+            float s = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float4 a = xc[k * ct];
+                s += a.x; s += a.y; s += a.z; s += a.w;
+            }
+            S[f] = s;
+        } else {
+            float sa = 0.f, sb = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float4 a = xc[k * ct], b = xc[(4 + k) * ct];
+                sa += a.x; sa += a.y; sa += a.z; sa += a.w;
+                sb += b.x; sb += b.y; sb += b.z; sb += b.w;
+            }
+            S[2 * f] = sa;
+            S[2 * f + 1] = sb;
+        }
+    }
+    __syncthreads();
+}
+
+// 1 / sqrt(mean(x_r^2) + eps) for the NB rows, computed by the whole workgroup in a fixed order.
+template <int NB>
+__device__ void row_inv_rms(const float *const *xrow, int64_t K, float eps, float *inv_out,
+                            float *red /* LDS, NB * 4 floats */)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int r = 0; r < NB; ++r) {
+        float ss = 0.f;
+        if (xrow[r]) {
+            for (int64_t e = 4 * threadIdx.x; e < K; e += 4 * blockDim.x) {
+                const float4 v = *reinterpret_cast<const float4 *>(xrow[r] + e);
+                ss = fmaf(v.x, v.x, ss); ss = fmaf(v.y, v.y, ss);
+                ss = fmaf(v.z, v.z, ss); ss = fmaf(v.w, v.w, ss);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            ss += __shfl_xor(ss, off);
+        if (lane == 0)
+            red[r * 4 + wave] = ss;
+    }
+    __syncthreads();
+    if (threadIdx.x < NB) {
+        const int r = threadIdx.x;
+        const float ss = ((red[r * 4 + 0] + red[r * 4 + 1]) + red[r * 4 + 2]) + red[r * 4 + 3];
+        inv_out[r] = 1.0f / sqrtf(ss / (float)K + eps);
+    }
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------------------------ compute
+
+struct MatPtr {
+    const uint8_t *qs, *sc;
+};
+
+// Scale terms of one chunk of one row: Q4_0/Q8_0 use a (the block scale); Q4_K uses
+// aA, bA (sub-block of the low nibbles) and aB, bB (high nibbles).
+struct ChunkScale {
+    float a, b, a2, b2;
+};
+
+template <int FMT>
+__device__ __forceinline__ ChunkScale chunk_scale(const uint4 &s, int q /* chunk in super-block */)
+{
+    ChunkScale cs;
+    if constexpr (FMT == FQ4_K) {
+        const float d = h2f(s.x & 0xffffu), dmin = h2f(s.x >> 16);
+        const int c = q >> 1;
+        const int jA = 2 * c, jB = 2 * c + 1;
+        uint32_t scA, mA, scB, mB;
+        if (c < 2) {
+            scA = (s.y >> (8 * jA)) & 63u;  mA = (s.z >> (8 * jA)) & 63u;
+            scB = (s.y >> (8 * jB)) & 63u;  mB = (s.z >> (8 * jB)) & 63u;
+        } else {
+            const int kA = jA - 4, kB = jB - 4;
+            scA = ((s.w >> (8 * kA)) & 15u) | (((s.y >> (8 * kA + 6)) & 3u) << 4);
+            mA = ((s.w >> (8 * kA + 4)) & 15u) | (((s.z >> (8 * kA + 6)) & 3u) << 4);
+            scB = ((s.w >> (8 * kB)) & 15u) | (((s.y >> (8 * kB + 6)) & 3u) << 4);
+            mB = ((s.w >> (8 * kB + 4)) & 15u) | (((s.z >> (8 * kB + 6)) & 3u) << 4);
+        }
+        cs.a = d * (float)scA;
+        cs.b = dmin * (float)mA;
+        cs.a2 = d * (float)scB;
+        cs.b2 = dmin * (float)mB;
+    } else {
+        cs.a = h2f(s.x & 0xffffu);
+        cs.b = cs.a2 = cs.b2 = 0.f;
+    }
+    return cs;
+}
+
+// Decode the 16-byte chunk into the per-element factors the dot multiplies (nibble or biased
+// byte values as f32, exact), in dot order.
+template <int FMT>
+__device__ __forceinline__ void decode_chunk(const uint4 &q, float *w)
+{
+    if constexpr (FMT == FQ8_0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t v = ucomp(q, k) ^ 0x80808080u;   // q + 128 as an unsigned byte
+            w[4 * k + 0] = ub0(v); w[4 * k + 1] = ub1(v);
+            w[4 * k + 2] = ub2(v); w[4 * k + 3] = ub3(v);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t v = ucomp(q, k);
+            const uint32_t lo = v & 0x0f0f0f0fu, hi = (v >> 4) & 0x0f0f0f0fu;
+            w[8 * k + 0] = ub0(lo); w[8 * k + 1] = ub1(lo);
+            w[8 * k + 2] = ub2(lo); w[8 * k + 3] = ub3(lo);
+            w[8 * k + 4] = ub0(hi); w[8 * k + 5] = ub1(hi);
+            w[8 * k + 6] = ub2(hi); w[8 * k + 7] = ub3(hi);
+        }
+    }
+}
+
+// Accumulate one decoded chunk against one staged x chunk (xv: XF4 float4s, Sv: NS sums).
+template <int FMT>
+__device__ __forceinline__ float chunk_dot(const float *w, const float4 *xv, const float *Sv,
+                                           const ChunkScale &cs, float acc)
+{
+    if constexpr (FMT == FQ4_0) {
+        float dot = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            dot = fmaf(w[8 * k + 0], xv[k].x, dot);
+            dot = fmaf(w[8 * k + 1], xv[k].y, dot);
+            dot = fmaf(w[8 * k + 2], xv[k].z, dot);
+            dot = fmaf(w[8 * k + 3], xv[k].w, dot);
+            dot = fmaf(w[8 * k + 4], xv[4 + k].x, dot);
+            dot = fmaf(w[8 * k + 5], xv[4 + k].y, dot);
+            dot = fmaf(w[8 * k + 6], xv[4 + k].z, dot);
+            dot = fmaf(w[8 * k + 7], xv[4 + k].w, dot);
+        }
+        return fmaf(cs.a, fmaf(-8.0f, Sv[0], dot), acc);
+    } else if constexpr (FMT == FQ8_0) {
+        float dot = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            dot = fmaf(w[4 * k + 0], xv[k].x, dot);
+            dot = fmaf(w[4 * k + 1], xv[k].y, dot);
+            dot = fmaf(w[4 * k + 2], xv[k].z, dot);
+            dot = fmaf(w[4 * k + 3], xv[k].w, dot);
+        }
+        return fmaf(cs.a, fmaf(-128.0f, Sv[0], dot), acc);
+    } else {
+        float da = 0.f, db = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            da = fmaf(w[8 * k + 0], xv[k].x, da);
+            da = fmaf(w[8 * k + 1], xv[k].y, da);
+            da = fmaf(w[8 * k + 2], xv[k].z, da);
+            da = fmaf(w[8 * k + 3], xv[k].w, da);
+            db = fmaf(w[8 * k + 4], xv[4 + k].x, db);
+            db = fmaf(w[8 * k + 5], xv[4 + k].y, db);
+            db = fmaf(w[8 * k + 6], xv[4 + k].z, db);
+            db = fmaf(w[8 * k + 7], xv[4 + k].w, db);
+        }
+        acc = fmaf(cs.a, da, acc);
+        acc = fmaf(-cs.b, Sv[0], acc);
+        acc = fmaf(cs.a2, db, acc);
+        acc = fmaf(-cs.b2, Sv[1], acc);
+        return acc;
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_chunk(const MatPtr &m, int64_t qs_row, int64_t sc_row,
+                                           int64_t n, int64_t ci, uint4 &q, uint4 &s)
+{
+    q = *reinterpret_cast<const uint4 *>(m.qs + n * qs_row + ci * 16);
+    if constexpr (FMT == FQ4_0) {
+        s = make_uint4(*reinterpret_cast<const uint16_t *>(m.sc + n * sc_row + ci * 2), 0u, 0u, 0u);
+    } else if constexpr (FMT == FQ8_0) {
+        s = make_uint4(*reinterpret_cast<const uint16_t *>(m.sc + n * sc_row + (ci >> 1) * 2), 0u,
+                       0u, 0u);
+    } else {
+        s = *reinterpret_cast<const uint4 *>(m.sc + n * sc_row + (ci >> 3) * 16);
+    }
+}
+
+// One K tile of one wave step: rows row0 + u*G + slot (u < U) of each of MATS matrices against
+// the NB staged x rows.  Lane lir of its LPR-lane group takes chunks lir, lir + lpr, ...
+template <int FMT, int NB, int U, int MATS>
+__device__ __forceinline__ void tile_compute(const MatPtr (&mat)[MATS], int64_t qs_row,
+                                             int64_t sc_row, int64_t row0, int64_t N, int G,
+                                             int slot, int lir, int lpr, int t, int ct,
+                                             const float4 *X4, const float *S,
+                                             float (&acc)[MATS][U][NB])
+{
+    constexpr int XF4 = Fc<FMT>::XF4, CE = Fc<FMT>::CE, NS = Fc<FMT>::NS;
+    for (int i = lir; i < ct; i += lpr) {
+        const int64_t ci = (int64_t)t * ct + i;
+        uint4 q[MATS][U], s[MATS][U];
+#pragma unroll
+        for (int m = 0; m < MATS; ++m)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t n = row0 + (int64_t)u * G + slot;
+                if (n < N) {
+                    load_chunk<FMT>(mat[m], qs_row, sc_row, n, ci, q[m][u], s[m][u]);
+                } else {
+                    q[m][u] = make_uint4(0u, 0u, 0u, 0u);
+                    s[m][u] = make_uint4(0u, 0u, 0u, 0u);
+                }
+            }
+        const int qpos = (int)(ci & 7);
+        if constexpr (NB == 1) {
+            float4 xv[XF4];
+#pragma unroll
+            for (int j = 0; j < XF4; ++j)
+                xv[j] = X4[j * ct + i];
+            float Sv[NS];
+#pragma unroll
+            for (int k = 0; k < NS; ++k)
+                Sv[k] = S[i * NS + k];
+#pragma unroll
+            for (int m = 0; m < MATS; ++m)
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float w[CE];
+                    decode_chunk<FMT>(q[m][u], w);
+                    const ChunkScale cs = chunk_scale<FMT>(s[m][u], qpos);
+                    acc[m][u][0] = chunk_dot<FMT>(w, xv, Sv, cs, acc[m][u][0]);
+                }
+        } else {
+            float w[MATS][U][CE];
+            ChunkScale cs[MATS][U];
+#pragma unroll
+            for (int m = 0; m < MATS; ++m)
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    decode_chunk<FMT>(q[m][u], w[m][u]);
+                    cs[m][u] = chunk_scale<FMT>(s[m][u], qpos);
+                }
+#pragma unroll
+            for (int r = 0; r < NB; ++r) {
+                float4 xv[XF4];
+#pragma unroll
+                for (int j = 0; j < XF4; ++j)
+                    xv[j] = X4[(r * XF4 + j) * ct + i];
+                float Sv[NS];
+#pragma unroll
+                for (int k = 0; k < NS; ++k)
+                    Sv[k] = S[(r * ct + i) * NS + k];
+#pragma unroll
+                for (int m = 0; m < MATS; ++m)
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        acc[m][u][r] = chunk_dot<FMT>(w[m][u], xv, Sv, cs[m][u], acc[m][u][r]);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float group_sum(float v, int lpr)
+{
+    for (int off = lpr >> 1; off > 0; off >>= 1)
+        v += __shfl_xor(v, off);
+    return v;
+}
+
+// Order-preserving key: larger value -> larger key; equal values -> the lower index wins.
+__device__ __forceinline__ unsigned long long argmax_key(float v, int64_t n)
+{
+    const uint32_t b = __float_as_uint(v + 0.0f);   // -0 -> +0
+    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((unsigned long long)ord << 32) | (unsigned long long)(0xffffffffu - (uint32_t)n);
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int off)
+{
+    const uint32_t lo = __shfl_xor((uint32_t)v, off), hi = __shfl_xor((uint32_t)(v >> 32), off);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+
+}  // namespace qg

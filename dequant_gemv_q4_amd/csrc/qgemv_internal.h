@@ -15,9 +15,9 @@ enum Epi { E_STORE = 0, E_RES = 1, E_GUS = 2, E_ARGMAX = 3 };
 
 // Routed experts: at most this many (row, slot) pairs per call (16 rows x top-8).
 #define QG_PAIRS_MAX 128
-// Routed experts: workgroup steps per output-row tile of one expert.
-#ifndef QG_MOE_STEPS_PER_TILE
-#define QG_MOE_STEPS_PER_TILE 16
+// Routed experts: output rows of one expert per workgroup.
+#ifndef QG_MOE_TILE_ROWS
+#define QG_MOE_TILE_ROWS 128
 #endif
 
 // Packed device layout of one N x K matrix: a plane of quant bytes (row n at n * qs_row) and a
@@ -52,6 +52,27 @@ __host__ __device__ constexpr int rows_in_flight(int nb, int mats)
     return nb == 1 ? (mats == 1 ? 4 : 2) : (nb <= 4 ? (mats == 1 ? 2 : 1) : 1);
 }
 
+// Rows one wave of the streaming kernels finishes per group (R), by batch rows, 16-byte chunks
+// per lane and row (CPL), and matrices (2 for the gated product).
+#ifndef QG_R_NB1
+#define QG_R_NB1 2        // rows per group of the single-row-batch streaming kernel
+#endif
+#ifndef QG_OUT_GROUPS
+#define QG_OUT_GROUPS 32  // row groups whose outputs a streaming wave batches before storing
+#endif
+#ifndef QG_WPE_NB1
+#define QG_WPE_NB1 4      // waves per SIMD the single-row-batch streaming kernel is sized for
+#endif
+#ifndef QG_XREG_NB1
+#define QG_XREG_NB1 1     // single-row-batch streaming kernel keeps x in registers
+#endif
+__host__ __device__ constexpr int stream_rows(int nb, int cpl, int mats)
+{
+    return nb == 1 ? ((mats == 1 ? QG_R_NB1 : (QG_R_NB1 + 1) / 2) / cpl > 0
+                          ? (mats == 1 ? QG_R_NB1 : (QG_R_NB1 + 1) / 2) / cpl : 1)
+                   : (cpl == 1 ? 2 : 1);
+}
+
 // LDS bytes of one staged x tile of nb rows and kt elements (float4 region, then block sums).
 __host__ __device__ constexpr size_t lds_tile_bytes(int fmt, int nb, int kt)
 {
@@ -70,8 +91,7 @@ struct GemvArgs {
     const float *res;           // [nb][N] (residual epilogue)
     float *y;                   // [nb][N]
     int32_t *idx;               // [nb] (argmax)
-    unsigned long long *keys;   // [nb] argmax keys in the workspace
-    unsigned int *ticket;       // workgroup ticket in the workspace
+    unsigned long long *keys;   // argmax: partial key per workgroup and batch row (workspace)
     int64_t N, K;
     int64_t qs_row, sc_row;
     float eps;
@@ -92,11 +112,11 @@ struct MoeArgs {
     float *y;                   // [nb][N]
     float *part;                // workspace: [nb][topk][N] partial outputs
     unsigned int *err;          // workspace: sticky bad-id flag
-    unsigned int *tickets;      // workspace: one ticket per output tile
     int64_t n_exp, N, K;
     int64_t qs_row, sc_row;
     int nb, topk;
-    int lpr_log2, kt, n_kt, rows_per_step;
+    int tile_rows;              // output rows of one expert per workgroup
+    int group_max;              // routed rows staged together (1, 2 or 4)
     int64_t n_tiles;            // output-row tiles per expert
 };
 
@@ -104,6 +124,13 @@ struct MoeArgs {
 int launch_pack(int fmt, const void *src, int64_t N, int64_t K, void *dst, void *stream);
 int launch_gemv(int fmt, int epi, bool nrm, const GemvArgs &a, int grid, size_t lds_bytes,
                 void *stream);
-int launch_moe(int fmt, const MoeArgs &a, int grid, size_t lds_bytes, void *stream);
+int launch_stream(int fmt, int epi, bool nrm, int cpl, const GemvArgs &a, int grid,
+                  size_t lds_bytes, void *stream);
+int launch_moe(int fmt, int cpl, const MoeArgs &a, int grid, size_t lds_bytes, void *stream);
+int launch_argmax_fold(const unsigned long long *part, int n_part, int nb, int32_t *idx,
+                       void *stream);
+// Workgroups of a streaming launch that are resident at once on the current device (0 if the
+// query fails).
+int stream_resident_wgs(int fmt, int epi, bool nrm, int cpl, int nb, size_t lds_bytes);
 
 }  // namespace qg

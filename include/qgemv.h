@@ -23,9 +23,11 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every call only
  *    enqueues work on that stream and returns; nothing synchronizes the host.
  *  - `ws` is a device workspace of at least qgemv_workspace_bytes(...) bytes (may be NULL when
- *    that is 0).  It must be zero-filled ONCE after allocation; the kernels leave it zeroed
- *    again after every call (argmax keys and tickets are reset by the last workgroup).  Calls
- *    that share one workspace must be ordered on one stream.
+ *    that is 0).  It is scratch that every call writes before it reads (argmax: one partial key
+ *    per workgroup; experts: partial outputs), except the sticky bad-id flag of qgemv_moe, so a
+ *    qgemv_moe workspace must be zero-filled once after allocation.  Calls that share one
+ *    workspace must be ordered on one stream.  An operation with a workspace runs as two
+ *    launches on `stream` (the main kernel, then a small fold / combine kernel).
  *  - Errors: every argument is validated on the host before anything is launched; a failed
  *    check returns its status and launches nothing.  QG_ERR_LAUNCH reports a HIP error from the
  *    launch itself.  qgemv_status_str gives a static description.

@@ -259,7 +259,6 @@ def test_qgemv_argmax_parity(fmt, N, K, nb):
         idx = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
         q.qgemv_argmax(fmt, Wp, N, K, dev(x), nb, logits, idx, ws)
         _argmax_check(host(logits), host(idx), yr, A, f"argmax fmt={fmt} rep={rep}")
-    assert not host(ws).any()
 
 
 def test_argmax_ties_go_to_lowest_index():
@@ -286,6 +285,8 @@ def test_argmax_ties_go_to_lowest_index():
 @pytest.mark.parametrize("fmt,n_exp,N,K,nb,topk", [(q.Q4_K, 8, 200, 512, 5, 3),
                                                    (q.Q4_0, 10, 129, 1024, 16, 8),
                                                    (q.Q8_0, 4, 300, 1536, 2, 1),
+                                                   (q.Q8_0, 3, 130, 2048, 16, 2),
+                                                   (q.Q4_0, 5, 70, 8192, 7, 3),
                                                    (q.Q4_K, 64, 1024, 2048, 16, 8)])
 def test_qgemv_moe_parity(fmt, n_exp, N, K, nb, topk):
     say(f"moe fmt={fmt} n_exp={n_exp} N={N} K={K} nb={nb} topk={topk}")
