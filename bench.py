@@ -120,14 +120,15 @@ def make_lm_head(warm, nb):
                  step, cpu, cfg)
 
 
-def make_gemv(warm, nb):
-    """Plain Q4_0 GEMV on the lm_head-sized matrix (65536 x 2048): the nb=1 gate shape."""
+def make_gemv(warm, nb, rows=65536, hidden=2048):
+    """Plain Q4_0 GEMV, by default on the lm_head-sized matrix (65536 x 2048): the nb=1 gate
+    shape; --rows / --hidden pick other sizes."""
     import torch
     import dequant_gemv_q4_amd as q
     from dequant_gemv_q4_amd import device as D
     import workloads as wl
 
-    w = wl.lm_head(nb=nb)
+    w = wl.lm_head(nb=nb, vocab=rows, hidden=hidden)
     a = w.arrays
     Wp = D.pack(q.Q4_0, a["W"], w.N, w.K)
     R = _copies(Wp.numel(), warm)
@@ -289,6 +290,8 @@ def main():
     ap.add_argument("--workload", default="decode_mlp",
                     choices=["decode_mlp", "lm_head", "gemv", "qkv", "moe", "copy"])
     ap.add_argument("--nb", type=int, default=None)
+    ap.add_argument("--rows", type=int, default=65536, help="gemv workload: output rows")
+    ap.add_argument("--hidden", type=int, default=2048, help="gemv workload: reduction length")
     ap.add_argument("--warm", action="store_true", help="reuse one weight copy (cache-assisted)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -313,7 +316,7 @@ def main():
     elif args.workload == "lm_head":
         b = make_lm_head(args.warm, args.nb or 1)
     elif args.workload == "gemv":
-        b = make_gemv(args.warm, args.nb or 1)
+        b = make_gemv(args.warm, args.nb or 1, args.rows, args.hidden)
     elif args.workload == "qkv":
         b = make_qkv(args.warm, args.nb or 16)
     elif args.workload == "copy":

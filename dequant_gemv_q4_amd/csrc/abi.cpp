@@ -87,20 +87,15 @@ static bool plan_gemv(int fmt, int64_t N, int64_t K, int nb, int mats, Plan *p)
     return true;
 }
 
-// Streaming path (whole wave per row): nb <= 4, at most 4 chunks of 16 bytes per lane and row,
-// and the staged row(s) of x in the LDS budget.  Returns the chunks-per-lane class, or 0.
+// Streaming path (whole wave per row, x in registers): nb <= 4 and at most 4 chunks of 16 bytes
+// per lane and row (longer rows are split over up to four waves).  Returns the chunks-per-row
+// class (1, 2, 4 = waves per row), or 0.
 static int stream_cpl(int fmt, int64_t K, int nb)
 {
     if (nb > 4)
         return 0;
     const int64_t C = (fmt == FQ8_0 ? K : K / 2) / 16;
-    const int cpl = C <= 64 ? 1 : C <= 128 ? 2 : C <= 256 ? 4 : 0;
-    if (!cpl || lds_tile_bytes(fmt, nb, (int)K) > (size_t)QG_LDS_BUDGET)
-        return 0;
-    // the one-pass staging gives each (batch row, chunk) its own thread of the 256
-    if (nb * C > 256)
-        return 0;
-    return cpl;
+    return C <= 64 ? 1 : C <= 128 ? 2 : C <= 256 ? 4 : 0;
 }
 
 struct StreamPlan {
@@ -120,7 +115,7 @@ static bool plan_stream(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb
     const int teams = 4 / cpl;                        // a row's K is split over cpl waves
     const int64_t want = (groups + teams - 1) / teams;
     sp->cpl = cpl;
-    sp->lds = lds_tile_bytes(fmt, nb, (int)K);
+    sp->lds = 0;
     int resident = stream_resident_wgs(fmt, epi, nrm, cpl, nb, sp->lds);
     if (resident <= 0)
         resident = QG_MAX_GRID;
@@ -131,7 +126,7 @@ static bool plan_stream(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb
 }
 
 // Routed experts: chunks per lane (1, 2 or 4 of 16 bytes per row) and how many routed rows are
-// staged together so that they fit the LDS budget.
+// decoded together (their x sits in registers: rows x chunks <= 4).
 static bool plan_moe(int fmt, int64_t N, int64_t K, int *cpl, int *group_max, size_t *lds,
                      int64_t *n_tiles)
 {
@@ -139,16 +134,8 @@ static bool plan_moe(int fmt, int64_t N, int64_t K, int *cpl, int *group_max, si
     *cpl = C <= 64 ? 1 : C <= 128 ? 2 : C <= 256 ? 4 : 0;
     if (!*cpl)
         return false;
-    // the staging gives every (routed row, chunk) of a group its own thread of the 256
-    *group_max = 4;
-    while (*group_max > 1 && (lds_tile_bytes(fmt, *group_max, (int)K) > (size_t)QG_LDS_BUDGET ||
-                              *group_max * C > 256))
-        *group_max /= 2;
-    if (C > 256)
-        return false;
-    if (lds_tile_bytes(fmt, *group_max, (int)K) > (size_t)QG_LDS_BUDGET)
-        return false;
-    *lds = lds_tile_bytes(fmt, *group_max, (int)K);
+    *group_max = 4 / *cpl;
+    *lds = 0;
     *n_tiles = (N + QG_MOE_TILE_ROWS - 1) / QG_MOE_TILE_ROWS;
     return true;
 }

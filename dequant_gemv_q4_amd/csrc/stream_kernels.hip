@@ -61,100 +61,6 @@ __device__ __forceinline__ void decode_stream(const uint4 &q, float *w)
     }
 }
 
-// Stage the NB x rows for the streaming kernels in one pass.  Thread t < NB * C owns chunk
-// c = t % C of batch row r = t / C (every shape the streaming kernels take has NB * C <= 256):
-// it loads the chunk's x, with NRM the workgroup first forms 1/sqrt(mean x^2 + eps) of each
-// row from per-thread partial sums, and the thread writes the chunk's float4s (Q4_0: u, v) to
-// LDS and its block sums -- formed from its registers in the dot's own order -- to S.
-template <int FMT, int NB, bool NRM>
-__device__ void stage_chunks(const float *const *xrow, const float *gamma, float eps, int64_t K,
-                             int C, float4 *X4, float *S, float *red, float *s_inv)
-{
-    constexpr int XF4 = Fc<FMT>::XF4;
-    const int t = threadIdx.x;
-    const bool act = t < NB * C;
-    const int r = act ? t / C : 0, c = act ? t % C : 0;
-    float4 xv[XF4];
-    float4 gv[NRM ? XF4 : 1];
-#pragma unroll
-    for (int j = 0; j < XF4; ++j) {
-        xv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (act && xrow[r]) {
-            const int e = chunk_elem<FMT>(c, j);
-            xv[j] = *reinterpret_cast<const float4 *>(xrow[r] + e);
-            if constexpr (NRM)
-                gv[j] = *reinterpret_cast<const float4 *>(gamma + e);
-        }
-    }
-    if constexpr (NRM) {
-        float ss = 0.f;
-#pragma unroll
-        for (int j = 0; j < XF4; ++j) {
-            ss = fmaf(xv[j].x, xv[j].x, ss); ss = fmaf(xv[j].y, xv[j].y, ss);
-            ss = fmaf(xv[j].z, xv[j].z, ss); ss = fmaf(xv[j].w, xv[j].w, ss);
-        }
-        red[t] = ss;
-        __syncthreads();
-        const int lane = t & 63, wave = t >> 6;
-        for (int rr = wave; rr < NB; rr += 4) {
-            float sr = 0.f;
-            for (int i = lane; i < C; i += 64)
-                sr += red[rr * C + i];
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1)
-                sr += __shfl_xor(sr, off);
-            if (lane == 0)
-                s_inv[rr] = 1.0f / sqrtf(sr / (float)K + eps);
-        }
-        __syncthreads();
-        if (act && xrow[r]) {
-            const float inv = s_inv[r];
-#pragma unroll
-            for (int j = 0; j < XF4; ++j)
-                xv[j] = f4scale(xv[j], inv, gv[j]);
-        }
-    }
-    if (act) {
-        if constexpr (FMT == FQ4_0) {
-            // float4 j < 4 holds elements 4j..4j+3 (low nibbles), j >= 4 elements 16+4(j-4)..
-            float s = 0.f;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float4 hv = make_float4(xv[4 + k].x * 0.0625f, xv[4 + k].y * 0.0625f,
-                                              xv[4 + k].z * 0.0625f, xv[4 + k].w * 0.0625f);
-                const float4 u = make_float4(xv[k].x - hv.x, xv[k].y - hv.y, xv[k].z - hv.z,
-                                             xv[k].w - hv.w);
-                xv[k] = u;
-                xv[4 + k] = hv;
-                s += u.x; s += u.y; s += u.z; s += u.w;
-                s = fmaf(17.0f, hv.x, s); s = fmaf(17.0f, hv.y, s);
-                s = fmaf(17.0f, hv.z, s); s = fmaf(17.0f, hv.w, s);
-            }
-            S[t] = s;
-        } else if constexpr (FMT == FQ8_0) {
-            float s = 0.f;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                s += xv[k].x; s += xv[k].y; s += xv[k].z; s += xv[k].w;
-            }
-            S[t] = s;
-        } else {
-            float sa = 0.f, sb = 0.f;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                sa += xv[k].x; sa += xv[k].y; sa += xv[k].z; sa += xv[k].w;
-                sb += xv[4 + k].x; sb += xv[4 + k].y; sb += xv[4 + k].z; sb += xv[4 + k].w;
-            }
-            S[2 * t] = sa;
-            S[2 * t + 1] = sb;
-        }
-#pragma unroll
-        for (int j = 0; j < XF4; ++j)
-            X4[(r * XF4 + j) * C + c] = xv[j];
-    }
-    __syncthreads();
-}
-
 // Value of lane (l ^ OFF), every partner exact: OFF 1 and 2 by DPP quad permutes, 8 by DPP
 // row rotation, 4 and 16 by ds_swizzle (bit mode, xor mask), 32 by ds_bpermute (bp32 holds
 // ((l ^ 32) << 2), computed once).
@@ -223,7 +129,6 @@ template <int FMT, int NB, int CPL, int MATS>
 struct SP {
     static constexpr int R = stream_rows(NB, CPL, MATS);
     static constexpr int XF4 = Fc<FMT>::XF4, CE = Fc<FMT>::CE, NS = Fc<FMT>::NS;
-    static constexpr bool XREG = NB == 1 ? (CPL == 1 && QG_XREG_NB1) : NB * CPL <= 4;   // x in registers
     // waves per SIMD the register budget must allow (at most 512 / WPE VGPRs per lane)
     static constexpr int WPE = (NB == 1 && CPL == 1 && FMT != FQ4_K) ? QG_WPE_NB1 : 2;
     static constexpr int ITEMS = R * NB;
@@ -324,18 +229,17 @@ __device__ __forceinline__ ChunkScale scale_of(uint32_t s, int) { ChunkScale cs;
 template <int FMT>
 __device__ __forceinline__ ChunkScale scale_of(const uint4 &s, int qpos) { return chunk_scale<FMT>(s, qpos); }
 
-// x of one chunk slot (i) of one batch row (r): from registers or from LDS.
-template <int FMT, int NB, int CPL, bool XREG>
+// x of the lane's chunk slots (i) of every batch row (r), in registers, with the block sums.
+template <int FMT, int NB, int CPL>
 struct XCache {
-    float4 xv[XREG ? NB : 1][XREG ? CPL : 1][Fc<FMT>::XF4];
-    float sv[XREG ? NB : 1][XREG ? CPL : 1][Fc<FMT>::NS];
+    float4 xv[NB][CPL][Fc<FMT>::XF4];
+    float sv[NB][CPL][Fc<FMT>::NS];
 };
 
 // Decode + FMA of one row group; acc[item][m] with item = u * NB + r.
-template <int FMT, int NB, int CPL, int MATS, int R, int IP, bool XREG>
+template <int FMT, int NB, int CPL, int MATS, int R, int IP>
 __device__ __forceinline__ void compute_group(const GroupBuf<FMT, CPL, MATS, R> &b,
-                                              const XCache<FMT, NB, CPL, XREG> &xc,
-                                              const float4 *X4, const float *S, int C, int lane,
+                                              const XCache<FMT, NB, CPL> &xc, int C, int lane,
                                               float (&acc)[IP][MATS])
 {
     // a slot past the row's C chunks re-reads the last chunk; a zero scale cancels it
@@ -362,46 +266,129 @@ __device__ __forceinline__ void compute_group(const GroupBuf<FMT, CPL, MATS, R> 
                 if (c >= C)
                     cs.a = cs.b = cs.a2 = cs.b2 = 0.f;
 #pragma unroll
-                for (int r = 0; r < NB; ++r) {
-                    if constexpr (XREG) {
-                        acc[u * NB + r][m] = chunk_dot<FMT>(w, xc.xv[r][i], xc.sv[r][i], cs,
-                                                            acc[u * NB + r][m]);
-                    } else {
-                        float4 xv[XF4];
-                        float sv[NS];
-#pragma unroll
-                        for (int j = 0; j < XF4; ++j)
-                            xv[j] = X4[(r * XF4 + j) * C + cx];
-#pragma unroll
-                        for (int k = 0; k < NS; ++k)
-                            sv[k] = S[(r * C + cx) * NS + k];
-                        acc[u * NB + r][m] = chunk_dot<FMT>(w, xv, sv, cs, acc[u * NB + r][m]);
-                    }
-                }
+                for (int r = 0; r < NB; ++r)
+                    acc[u * NB + r][m] = chunk_dot<FMT>(w, xc.xv[r][i], xc.sv[r][i], cs,
+                                                        acc[u * NB + r][m]);
             }
     }
 }
 
-template <int FMT, int NB, int CPL, bool XREG>
-__device__ __forceinline__ void load_xcache(XCache<FMT, NB, CPL, XREG> &xc, const float4 *X4,
-                                            const float *S, int C, int lane)
+// In-register form of one chunk's x as the dot consumes it (Q4_0: u, v), and its block sums in
+// the dot's own order.
+template <int FMT>
+__device__ __forceinline__ void x_chunk_transform(float4 *xv, float *sv)
 {
-    if constexpr (XREG) {
-        constexpr int XF4 = Fc<FMT>::XF4, NS = Fc<FMT>::NS;
+    if constexpr (FMT == FQ4_0) {
+        float sum = 0.f;
 #pragma unroll
-        for (int r = 0; r < NB; ++r)
+        for (int k = 0; k < 4; ++k) {
+            const float4 hv = make_float4(xv[4 + k].x * 0.0625f, xv[4 + k].y * 0.0625f,
+                                          xv[4 + k].z * 0.0625f, xv[4 + k].w * 0.0625f);
+            const float4 u = make_float4(xv[k].x - hv.x, xv[k].y - hv.y, xv[k].z - hv.z,
+                                         xv[k].w - hv.w);
+            xv[k] = u;
+            xv[4 + k] = hv;
+            sum += u.x; sum += u.y; sum += u.z; sum += u.w;
+            sum = fmaf(17.0f, hv.x, sum); sum = fmaf(17.0f, hv.y, sum);
+            sum = fmaf(17.0f, hv.z, sum); sum = fmaf(17.0f, hv.w, sum);
+        }
+        sv[0] = sum;
+    } else if constexpr (FMT == FQ8_0) {
+        float sum = 0.f;
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int c = lane + 64 * i;
-                const int cx = c < C ? c : C - 1;
+        for (int k = 0; k < 4; ++k) {
+            sum += xv[k].x; sum += xv[k].y; sum += xv[k].z; sum += xv[k].w;
+        }
+        sv[0] = sum;
+    } else {
+        float sa = 0.f, sb = 0.f;
 #pragma unroll
-                for (int j = 0; j < XF4; ++j)
-                    xc.xv[r][i][j] = X4[(r * XF4 + j) * C + cx];
-#pragma unroll
-                for (int k = 0; k < NS; ++k)
-                    xc.sv[r][i][k] = S[(r * C + cx) * NS + k];
-            }
+        for (int k = 0; k < 4; ++k) {
+            sa += xv[k].x; sa += xv[k].y; sa += xv[k].z; sa += xv[k].w;
+            sb += xv[4 + k].x; sb += xv[4 + k].y; sb += xv[4 + k].z; sb += xv[4 + k].w;
+        }
+        sv[0] = sa;
+        sv[1] = sb;
     }
+}
+
+// x for this lane's chunk c of every batch row, read straight from global memory into
+// registers (x is a few KB: L1/L2 resident after the first wave), so no LDS staging or
+// workgroup barrier precedes the first row.  With NRM each wave forms 1/sqrt(mean x^2 + eps)
+// itself: its 64 lanes cover the KS chunks of the whole row.  Q4_0 is kept as (u, v) and every
+// block sum is formed in the dot's own order, as in the staging it replaces.
+template <int FMT, int NB, int KS, bool NRM>
+__device__ __forceinline__ void load_x_direct(XCache<FMT, NB, 1> &xc, const float *x,
+                                              const float *gamma, float eps, int64_t K, int C,
+                                              int c, int lane, int bp32)
+{
+    constexpr int XF4 = Fc<FMT>::XF4;
+    const int cx = c < C ? c : C - 1;
+#pragma unroll
+    for (int r = 0; r < NB; ++r)
+#pragma unroll
+        for (int j = 0; j < XF4; ++j)
+            xc.xv[r][0][j] = *reinterpret_cast<const float4 *>(x + r * K + chunk_elem<FMT>(cx, j));
+    if constexpr (NRM) {
+        float4 gv[XF4];
+#pragma unroll
+        for (int j = 0; j < XF4; ++j)
+            gv[j] = *reinterpret_cast<const float4 *>(gamma + chunk_elem<FMT>(cx, j));
+#pragma unroll
+        for (int r = 0; r < NB; ++r) {
+            float ss = 0.f;
+#pragma unroll
+            for (int q = 0; q < KS; ++q) {
+                const int cq = q * 64 + lane;
+                if (cq < C) {
+#pragma unroll
+                    for (int j = 0; j < XF4; ++j) {
+                        const float4 v = q * 64 == c - lane
+                                             ? xc.xv[r][0][j]
+                                             : *reinterpret_cast<const float4 *>(
+                                                   x + r * K + chunk_elem<FMT>(cq, j));
+                        ss = fmaf(v.x, v.x, ss); ss = fmaf(v.y, v.y, ss);
+                        ss = fmaf(v.z, v.z, ss); ss = fmaf(v.w, v.w, ss);
+                    }
+                }
+            }
+            ss += xor_lane<32>(ss, bp32);
+            ss += xor_lane<16>(ss, bp32);
+            ss += xor_lane<8>(ss, bp32);
+            ss += xor_lane<4>(ss, bp32);
+            ss += xor_lane<2>(ss, bp32);
+            ss += xor_lane<1>(ss, bp32);
+            const float inv = 1.0f / sqrtf(ss / (float)K + eps);
+#pragma unroll
+            for (int j = 0; j < XF4; ++j)
+                xc.xv[r][0][j] = f4scale(xc.xv[r][0][j], inv, gv[j]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NB; ++r)
+        x_chunk_transform<FMT>(xc.xv[r][0], xc.sv[r][0]);
+}
+
+// x of CPL chunk slots (lane + 64 i) of NB gathered rows (xrow[r] == nullptr: a zero row),
+// straight into registers; no norm.
+template <int FMT, int NB, int CPL>
+__device__ __forceinline__ void load_x_rows(XCache<FMT, NB, CPL> &xc,
+                                            const float *const *xrow, int C, int lane)
+{
+    constexpr int XF4 = Fc<FMT>::XF4;
+#pragma unroll
+    for (int r = 0; r < NB; ++r)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            const int cx = c < C ? c : C - 1;
+#pragma unroll
+            for (int j = 0; j < XF4; ++j)
+                xc.xv[r][i][j] = xrow[r] ? *reinterpret_cast<const float4 *>(
+                                               xrow[r] + chunk_elem<FMT>(cx, j))
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+            x_chunk_transform<FMT>(xc.xv[r][i], xc.sv[r][i]);
+        }
 }
 
 // ------------------------------------------------------------------------------------ GEMV family
@@ -418,13 +405,10 @@ void k_stream(GemvArgs a)
 {
     constexpr int MATS = EPI == E_GUS ? 2 : 1;
     using P = SP<FMT, NB, 1, MATS>;
-    constexpr int R = P::R, IP = P::IP, XF4 = P::XF4;
+    constexpr int R = P::R, IP = P::IP;
     constexpr int LG = IP == 1 ? 0 : IP == 2 ? 1 : IP == 4 ? 2 : IP == 8 ? 3 : IP == 16 ? 4 : 5;
     constexpr int TEAMS = 4 / KS;
 
-    extern __shared__ float4 lds4[];
-    __shared__ float s_inv[NB];
-    __shared__ float s_red[256];
     __shared__ unsigned long long s_key[NB * 4];
     __shared__ float s_comb[KS > 1 ? 2 : 1][4][IP][MATS];
     __shared__ float s_out[4][QG_OUT_GROUPS][IP];
@@ -433,8 +417,6 @@ void k_stream(GemvArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ks = wave % KS, team = wave / KS;
     const int C = (int)(a.qs_row / 16);
-    float4 *X4 = lds4;
-    float *S = reinterpret_cast<float *>(lds4 + (size_t)NB * XF4 * C);
 
     const uint32_t qbytes = (uint32_t)(a.N * a.qs_row), sbytes = (uint32_t)(a.N * a.sc_row);
     BufMat mat[MATS];
@@ -465,21 +447,17 @@ void k_stream(GemvArgs a)
         }
     };
 
+    const int cme = ks * 64 + lane;   // this lane's chunk of the row
+    const int bp32 = (lane ^ 32) << 2;
+    // x first (its loads retire first), then the first two row groups
+    XCache<FMT, NB, 1> xc;
+    load_x_direct<FMT, NB, KS, NRM>(xc, a.x, a.gamma, a.eps, a.K, C, cme, lane, bp32);
+
     GroupBuf<FMT, 1, MATS, R> bufA, bufB;
     load_group(bufA, mat, qrow, srow, a.N, lo, g0);
     float resA = load_res(g0);
     load_group(bufB, mat, qrow, srow, a.N, lo, g0 + W);
     float resB = load_res(g0 + W);
-
-    const float *xrow[NB];
-#pragma unroll
-    for (int r = 0; r < NB; ++r)
-        xrow[r] = a.x + (int64_t)r * a.K;
-    stage_chunks<FMT, NB, NRM>(xrow, a.gamma, a.eps, a.K, C, X4, S, s_red, s_inv);
-    XCache<FMT, NB, 1, P::XREG> xc;
-    load_xcache(xc, X4, S, C, ks * 64 + lane);
-    // x of this wave's K slice, as chunk index (clamped like the weight slots)
-    const int cme = ks * 64 + lane;
 
     // the item this lane reports after the reduction, and whether it writes it
     const int my_item = lane >> (6 - LG);
@@ -490,7 +468,6 @@ void k_stream(GemvArgs a)
     // Outputs wait in a small per-wave LDS buffer and leave in batches: a vector store among
     // the in-flight weight loads would make the compiler wait for every load (one counter
     // tracks both on this target).
-    const int bp32 = (lane ^ 32) << 2;
     int nout = 0;
     int64_t gout = g0;
     auto flush = [&]() {
@@ -560,7 +537,7 @@ void k_stream(GemvArgs a)
     for (int64_t it = 0; KS > 1 ? it < steps : g < T; ++it) {
         {
             float acc[IP][MATS];
-            compute_group<FMT, NB, 1, MATS, R, IP, P::XREG>(bufA, xc, X4, S, C, cme, acc);
+            compute_group<FMT, NB, 1, MATS, R, IP>(bufA, xc, C, cme, acc);
             const float res = resA;
             load_group(bufA, mat, qrow, srow, a.N, lo, g + 2 * W);
             resA = load_res(g + 2 * W);
@@ -572,7 +549,7 @@ void k_stream(GemvArgs a)
             break;
         {
             float acc[IP][MATS];
-            compute_group<FMT, NB, 1, MATS, R, IP, P::XREG>(bufB, xc, X4, S, C, cme, acc);
+            compute_group<FMT, NB, 1, MATS, R, IP>(bufB, xc, C, cme, acc);
             const float res = resB;
             load_group(bufB, mat, qrow, srow, a.N, lo, g + 2 * W);
             resB = load_res(g + 2 * W);
@@ -638,8 +615,7 @@ __global__ __launch_bounds__(256) void k_argmax_fold(const unsigned long long *p
 template <int FMT, int NB, int CPL>
 __device__ void moe_stream(const MoeArgs &a, const uint8_t *eq, const uint8_t *es, const int *pr,
                            const int *pt, int np,
-                           int64_t row0, int64_t rows, float4 *X4, float *S, float *red,
-                           float *s_inv)
+                           int64_t row0, int64_t rows)
 {
     using P = SP<FMT, NB, CPL, 1>;
     constexpr int R = P::R, IP = P::IP;
@@ -660,13 +636,11 @@ __device__ void moe_stream(const MoeArgs &a, const uint8_t *eq, const uint8_t *e
                                   (uint32_t)(rows * a.qs_row), (uint32_t)(rows * a.sc_row))};
     const LaneOff<CPL> lo = lane_offsets<FMT, CPL>(lane, C);
     const uint32_t qrow = (uint32_t)a.qs_row, srow = (uint32_t)a.sc_row;
+    XCache<FMT, NB, CPL> xc;
+    load_x_rows<FMT, NB, CPL>(xc, xrow, C, lane);
     GroupBuf<FMT, CPL, 1, R> bufA, bufB;
     load_group(bufA, tm, qrow, srow, rows, lo, g);
     load_group(bufB, tm, qrow, srow, rows, lo, g + W);
-    __syncthreads();   // the previous group may still read LDS
-    stage_chunks<FMT, NB, false>(xrow, nullptr, 0.f, a.K, C, X4, S, red, s_inv);
-    XCache<FMT, NB, CPL, P::XREG> xc;
-    load_xcache(xc, X4, S, C, lane);
 
     const int my_item = lane >> (6 - LG);
     const bool writer = (lane & ((64 >> LG) - 1)) == 0 && my_item < P::ITEMS;
@@ -680,7 +654,7 @@ __device__ void moe_stream(const MoeArgs &a, const uint8_t *eq, const uint8_t *e
     while (g < T) {
         {
             float acc[IP][1];
-            compute_group<FMT, NB, CPL, 1, R, IP, P::XREG>(bufA, xc, X4, S, C, lane, acc);
+            compute_group<FMT, NB, CPL, 1, R, IP>(bufA, xc, C, lane, acc);
             load_group(bufA, tm, qrow, srow, rows, lo, g + 2 * W);
             finish(acc, g);
         }
@@ -689,7 +663,7 @@ __device__ void moe_stream(const MoeArgs &a, const uint8_t *eq, const uint8_t *e
             break;
         {
             float acc[IP][1];
-            compute_group<FMT, NB, CPL, 1, R, IP, P::XREG>(bufB, xc, X4, S, C, lane, acc);
+            compute_group<FMT, NB, CPL, 1, R, IP>(bufB, xc, C, lane, acc);
             load_group(bufB, tm, qrow, srow, rows, lo, g + 2 * W);
             finish(acc, g);
         }
@@ -701,12 +675,9 @@ template <int FMT, int CPL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void k_moe_stream(MoeArgs a)
 {
-    extern __shared__ float4 lds4[];
     __shared__ int s_pr[QG_PAIRS_MAX];
     __shared__ int s_pt[QG_PAIRS_MAX];
     __shared__ int s_cnt[QG_PAIRS_MAX / 64];
-    __shared__ float s_red[256];
-    __shared__ float s_inv[4];
 
     const int64_t e = blockIdx.x % a.n_exp;
     const int64_t tile = blockIdx.x / a.n_exp;
@@ -741,19 +712,17 @@ void k_moe_stream(MoeArgs a)
         np += s_cnt[w];
 
     const uint8_t *eq = a.qs + e * a.N * a.qs_row, *es = a.sc + e * a.N * a.sc_row;
-    const int C = (int)(a.qs_row / 16);
-    float4 *X4 = lds4;
     for (int g0 = 0; g0 < np; g0 += a.group_max) {
         const int ng = np - g0 < a.group_max ? np - g0 : a.group_max;
+        // group_max = 4 / CPL keeps rows x chunks <= 4 (x held in registers)
         if (ng == 1) {
-            float *S = reinterpret_cast<float *>(lds4 + (size_t)1 * Fc<FMT>::XF4 * C);
-            moe_stream<FMT, 1, CPL>(a, eq, es, s_pr + g0, s_pt + g0, ng, row0, rows, X4, S, s_red, s_inv);
-        } else if (ng == 2) {
-            float *S = reinterpret_cast<float *>(lds4 + (size_t)2 * Fc<FMT>::XF4 * C);
-            moe_stream<FMT, 2, CPL>(a, eq, es, s_pr + g0, s_pt + g0, ng, row0, rows, X4, S, s_red, s_inv);
-        } else {
-            float *S = reinterpret_cast<float *>(lds4 + (size_t)4 * Fc<FMT>::XF4 * C);
-            moe_stream<FMT, 4, CPL>(a, eq, es, s_pr + g0, s_pt + g0, ng, row0, rows, X4, S, s_red, s_inv);
+            moe_stream<FMT, 1, CPL>(a, eq, es, s_pr + g0, s_pt + g0, ng, row0, rows);
+        } else if constexpr (CPL <= 2) {
+            if (ng == 2) {
+                moe_stream<FMT, 2, CPL>(a, eq, es, s_pr + g0, s_pt + g0, ng, row0, rows);
+            } else if constexpr (CPL == 1) {
+                moe_stream<FMT, 4, CPL>(a, eq, es, s_pr + g0, s_pt + g0, ng, row0, rows);
+            }
         }
     }
 }
