@@ -10,6 +10,9 @@
 #include "../../include/qgemv.h"
 #include "qgemv_internal.h"
 
+#ifndef QG_POOL_LDS
+#define QG_POOL_LDS 32768         // most LDS bytes of results one streaming workgroup holds
+#endif
 #ifndef QG_MAX_GRID
 #define QG_MAX_GRID 1024          // workgroups of the grid-stride GEMV kernels
 #endif
@@ -99,7 +102,8 @@ static int stream_cpl(int fmt, int64_t K, int nb)
 }
 
 struct StreamPlan {
-    int cpl;
+    int cpl;     // waves a row's K is split over
+    int pd;      // row groups in flight per wave
     int grid;
     size_t lds;
 };
@@ -112,17 +116,53 @@ static bool plan_stream(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb
     const int mats = epi == E_GUS ? 2 : 1;
     const int R = stream_rows(nb, 1, mats);
     const int64_t groups = (N + R - 1) / R;
-    const int teams = 4 / cpl;                        // a row's K is split over cpl waves
-    const int64_t want = (groups + teams - 1) / teams;
+    const int64_t items = (int64_t)R * nb;            // results per row group
+    const int64_t n_tiles = (groups + QG_TILE_GROUPS - 1) / QG_TILE_GROUPS;
+    // LDS: x of the nb rows (norm: x * gamma), one f32 max |.| per 4 (norm: and one square
+    // sum per 4), then the results of the workgroup's pool of row groups
+    const size_t x_lds = (size_t)nb * K * 4 + (size_t)nb * K + (nrm ? (size_t)nb * K : 0);
     sp->cpl = cpl;
-    sp->lds = 0;
-    int resident = stream_resident_wgs(fmt, epi, nrm, cpl, nb, sp->lds);
-    if (resident <= 0)
-        resident = QG_MAX_GRID;
-    if (epi == E_ARGMAX && resident > QG_ARGMAX_MAX_GRID)
-        resident = QG_ARGMAX_MAX_GRID;
-    sp->grid = (int)(want < resident ? want : resident);
-    return true;
+    // The deepest prefetch whose own grid (one pass of resident workgroups) still gives every
+    // team that many groups.  Each variant has its own register use, hence its own residency.
+    const int pd_max = nb == 1 ? QG_PD_MAX : 2;
+    for (int pd = pd_max; pd >= 1; pd /= 2) {
+        int waves = 0;
+        // residency with the largest pool this grid could need (results of pool_max groups)
+        int resident = stream_resident_wgs(fmt, epi, nrm, cpl, nb, pd, x_lds, &waves);
+        if (resident <= 0)
+            continue;
+        const int teams = waves / cpl;                // a row's K is split over cpl waves
+        int64_t want = (groups + teams - 1) / teams;
+        if (want > n_tiles)
+            want = n_tiles;
+        int grid = (int)(want < resident ? want : resident);
+        if (epi == E_ARGMAX && grid > QG_ARGMAX_MAX_GRID)
+            grid = QG_ARGMAX_MAX_GRID;
+        // keep a pool's results within QG_POOL_LDS (more, smaller pools for very tall matrices)
+        const int64_t min_grid = (groups * items * 4 + QG_POOL_LDS - 1) / QG_POOL_LDS;
+        if (grid < min_grid) {
+            if (epi == E_ARGMAX && min_grid > QG_ARGMAX_MAX_GRID)
+                return false;
+            grid = (int)min_grid;
+        }
+        const int64_t pool_max = (n_tiles + grid - 1) / grid * QG_TILE_GROUPS;
+        const size_t lds = x_lds + (size_t)pool_max * items * 4;
+        const int64_t per_team = (n_tiles / grid) * QG_TILE_GROUPS / teams;
+        if (pd > 1 && per_team < pd)
+            continue;
+        const int fit = stream_resident_wgs(fmt, epi, nrm, cpl, nb, pd, lds, &waves);
+        if (fit <= 0)
+            continue;
+        if (fit < grid && grid <= resident && fit >= min_grid)
+            grid = fit;                               // the pool's LDS lowered the residency
+        sp->pd = pd;
+        sp->grid = grid;
+        sp->lds = x_lds + (size_t)((n_tiles + grid - 1) / grid * QG_TILE_GROUPS) * items * 4;
+        if (stream_resident_wgs(fmt, epi, nrm, cpl, nb, pd, sp->lds, &waves) <= 0)
+            continue;
+        return true;
+    }
+    return false;   // too much LDS for every variant: the tiled kernel takes the call
 }
 
 // Routed experts: chunks per lane (1, 2 or 4 of 16 bytes per row) and how many routed rows are
@@ -199,7 +239,7 @@ static int run_gemv(int fmt, int epi, bool nrm, GemvArgs a, void *stream)
     StreamPlan sp;
     if (plan_stream(fmt, epi, nrm, a.N, a.K, a.nb, &sp)) {
         grid = sp.grid;
-        herr = launch_stream(fmt, epi, nrm, sp.cpl, a, sp.grid, sp.lds, stream);
+        herr = launch_stream(fmt, epi, nrm, sp.cpl, sp.pd, a, sp.grid, sp.lds, stream);
     } else {
         Plan p;
         if (!plan_gemv(fmt, a.N, a.K, a.nb, epi == E_GUS ? 2 : 1, &p))

@@ -57,14 +57,17 @@ __host__ __device__ constexpr int rows_in_flight(int nb, int mats)
 #ifndef QG_R_NB1
 #define QG_R_NB1 2        // rows per group of the single-row-batch streaming kernel
 #endif
-#ifndef QG_OUT_GROUPS
-#define QG_OUT_GROUPS 32  // row groups whose outputs a streaming wave batches before storing
-#endif
 #ifndef QG_WPE_NB1
 #define QG_WPE_NB1 4      // waves per SIMD the single-row-batch streaming kernel is sized for
 #endif
-#ifndef QG_XREG_NB1
-#define QG_XREG_NB1 1     // single-row-batch streaming kernel keeps x in registers
+#ifndef QG_X_LEAD
+#define QG_X_LEAD 1       // row groups a streaming wave issues before x is published in LDS
+#endif
+#ifndef QG_TILE_GROUPS
+#define QG_TILE_GROUPS 8  // consecutive row groups a streaming workgroup takes at a time
+#endif
+#ifndef QG_PD_MAX
+#define QG_PD_MAX 4       // most row groups a single-row-batch streaming wave keeps in flight
 #endif
 __host__ __device__ constexpr int stream_rows(int nb, int cpl, int mats)
 {
@@ -124,13 +127,14 @@ struct MoeArgs {
 int launch_pack(int fmt, const void *src, int64_t N, int64_t K, void *dst, void *stream);
 int launch_gemv(int fmt, int epi, bool nrm, const GemvArgs &a, int grid, size_t lds_bytes,
                 void *stream);
-int launch_stream(int fmt, int epi, bool nrm, int cpl, const GemvArgs &a, int grid,
+int launch_stream(int fmt, int epi, bool nrm, int cpl, int pd, const GemvArgs &a, int grid,
                   size_t lds_bytes, void *stream);
 int launch_moe(int fmt, int cpl, const MoeArgs &a, int grid, size_t lds_bytes, void *stream);
 int launch_argmax_fold(const unsigned long long *part, int n_part, int nb, int32_t *idx,
                        void *stream);
 // Workgroups of a streaming launch that are resident at once on the current device (0 if the
 // query fails).
-int stream_resident_wgs(int fmt, int epi, bool nrm, int cpl, int nb, size_t lds_bytes);
+int stream_resident_wgs(int fmt, int epi, bool nrm, int cpl, int nb, int pd, size_t lds_bytes,
+                        int *waves);
 
 }  // namespace qg

@@ -19,47 +19,12 @@
 
 #include "device_common.h"
 
+#include <mutex>
+#include <vector>
+
 namespace qg {
 
 // ------------------------------------------------------------------------------------ helpers
-
-// v & m as an opaque instruction, so the compiler keeps the byte structure and converts each
-// byte with v_cvt_f32_ubyteN instead of re-extracting single nibbles.
-__device__ __forceinline__ uint32_t and_opaque(uint32_t v, uint32_t m)
-{
-    uint32_t r;
-    asm("v_and_b32 %0, %1, %2" : "=v"(r) : "s"(m), "v"(v));
-    return r;
-}
-
-template <int FMT>
-__device__ __forceinline__ void decode_stream(const uint4 &q, float *w)
-{
-    if constexpr (FMT == FQ4_0) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t v = ucomp(q, k);
-            const uint32_t lo = and_opaque(v, 0x0f0f0f0fu);
-            w[8 * k + 0] = ub0(lo); w[8 * k + 1] = ub1(lo);
-            w[8 * k + 2] = ub2(lo); w[8 * k + 3] = ub3(lo);
-            w[8 * k + 4] = ub0(v); w[8 * k + 5] = ub1(v);
-            w[8 * k + 6] = ub2(v); w[8 * k + 7] = ub3(v);
-        }
-    } else if constexpr (FMT == FQ4_K) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t v = ucomp(q, k);
-            const uint32_t lo = and_opaque(v, 0x0f0f0f0fu);
-            const uint32_t hi = and_opaque(v >> 4, 0x0f0f0f0fu);
-            w[8 * k + 0] = ub0(lo); w[8 * k + 1] = ub1(lo);
-            w[8 * k + 2] = ub2(lo); w[8 * k + 3] = ub3(lo);
-            w[8 * k + 4] = ub0(hi); w[8 * k + 5] = ub1(hi);
-            w[8 * k + 6] = ub2(hi); w[8 * k + 7] = ub3(hi);
-        }
-    } else {
-        decode_chunk<FMT>(q, w);
-    }
-}
 
 // Value of lane (l ^ OFF), every partner exact: OFF 1 and 2 by DPP quad permutes, 8 by DPP
 // row rotation, 4 and 16 by ds_swizzle (bit mode, xor mask), 32 by ds_bpermute (bp32 holds
@@ -133,11 +98,15 @@ struct SP {
     static constexpr int WPE = (NB == 1 && CPL == 1 && FMT != FQ4_K) ? QG_WPE_NB1 : 2;
     static constexpr int ITEMS = R * NB;
     static constexpr int IP = pow2_ceil(ITEMS);
+    // GEMV family: one workgroup fills a CU (WPE waves on each of its 4 SIMDs)
+    static constexpr int WV = 4 * WPE, NT = 64 * WV;
 };
 
+// Raw scale bytes as loaded: one f16 (kept 16-bit, so nothing has to mask a load's result before
+// it is used), or the 16-byte Q4_K header.
 template <int FMT>
 struct ScaleT {
-    using T = uint32_t;
+    using T = uint16_t;
 };
 template <>
 struct ScaleT<FQ4_K> {
@@ -225,25 +194,322 @@ __device__ __forceinline__ void load_group(GroupBuf<FMT, CPL, MATS, R> &b, const
 }
 
 template <int FMT>
-__device__ __forceinline__ ChunkScale scale_of(uint32_t s, int) { ChunkScale cs; cs.a = h2f(s & 0xffffu); cs.b = cs.a2 = cs.b2 = 0.f; return cs; }
+__device__ __forceinline__ ChunkScale scale_of(uint16_t s, int) { ChunkScale cs; cs.a = (float)__builtin_bit_cast(_Float16, s); cs.b = cs.a2 = cs.b2 = 0.f; return cs; }
 template <int FMT>
 __device__ __forceinline__ ChunkScale scale_of(const uint4 &s, int qpos) { return chunk_scale<FMT>(s, qpos); }
 
-// x of the lane's chunk slots (i) of every batch row (r), in registers, with the block sums.
-template <int FMT, int NB, int CPL>
-struct XCache {
-    float4 xv[NB][CPL][Fc<FMT>::XF4];
-    float sv[NB][CPL][Fc<FMT>::NS];
+// Workgroup-shared x.  Each thread loads a few float4s of the NB rows (and of gamma); the caller
+// then issues its first weight loads, and only after that are the x values written to LDS
+// (natural [row][K] order).  Loads retire in order, so the wait for the x loads leaves the
+// later weight loads in flight.  With NRM the stored value is x * gamma, and beside it the sum
+// of squares of each float4 of raw x, so every wave can form a row's norm in a fixed order.
+template <int NB, bool NRM, int XPT>
+struct XStage {
+    float4 v[XPT];
+    float4 g[NRM ? XPT : 1];
 };
 
-// Decode + FMA of one row group; acc[item][m] with item = u * NB + r.
-template <int FMT, int NB, int CPL, int MATS, int R, int IP>
-__device__ __forceinline__ void compute_group(const GroupBuf<FMT, CPL, MATS, R> &b,
-                                              const XCache<FMT, NB, CPL> &xc, int C, int lane,
-                                              float (&acc)[IP][MATS])
+template <int NB, bool NRM, int XPT, int NT>
+__device__ __forceinline__ void xstage_issue(XStage<NB, NRM, XPT> &st, const float *x,
+                                             const float *gamma, int K4)
 {
-    // a slot past the row's C chunks re-reads the last chunk; a zero scale cancels it
-    constexpr int XF4 = Fc<FMT>::XF4, CE = Fc<FMT>::CE, NS = Fc<FMT>::NS;
+    const int tot = NB * K4;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const int f = (int)threadIdx.x + NT * i;
+        const int fc = f < tot ? f : tot - 1;
+        st.v[i] = reinterpret_cast<const float4 *>(x)[fc];
+        if constexpr (NRM)
+            st.g[i] = reinterpret_cast<const float4 *>(gamma)[NB == 1 ? fc : fc % K4];
+    }
+}
+
+// Threads past the end store at the last index the value loaded for it (the same value as the
+// thread that owns it), so the stores, and the loads before them, are unconditional: a load
+// used only under a branch would be sunk below the weight loads.
+template <int NB, bool NRM, int XPT, int NT>
+__device__ __forceinline__ void xstage_store(const XStage<NB, NRM, XPT> &st, int K4, float4 *X4,
+                                             float *SS, float *MX)
+{
+    const int tot = NB * K4;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const int f = (int)threadIdx.x + NT * i;
+        const int fc = f < tot ? f : tot - 1;
+        float4 v = st.v[i];
+        if constexpr (NRM) {
+            float q = v.x * v.x;
+            q = fmaf(v.y, v.y, q);
+            q = fmaf(v.z, v.z, q);
+            q = fmaf(v.w, v.w, q);
+            SS[fc] = q;
+            const float4 g = st.g[i];
+            v = make_float4(v.x * g.x, v.y * g.y, v.z * g.z, v.w * g.w);
+        }
+        X4[fc] = v;
+        MX[fc] = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    }
+}
+
+// ------------------------------------------------------------------------------------ f16 pairs
+//
+// The streaming GEMV forms its dot products with v_dot2_f32_f16: two f16 products (exact in
+// f32) added to an f32 accumulator.  Weights: a nibble n placed in the mantissa of the f16
+// 0x6400 (1024.0) reads as 1024 + n, and a nibble in mantissa bits 4..7 as 1024 + 16 n, so one
+// and-or per dword yields two weights (exact); the x operand of a high-nibble pair carries a
+// factor 1/16.  x: each row is scaled by a power of two that puts its largest |value| in
+// [2^14, 2^15), then rounded to f16 (relative error at most 2^-11, far inside the stated
+// 1e-3 * sum|w x| bound); the scale is undone, exactly, on the row sums.  The 1024 offsets (and
+// Q4_0's -8, Q8_0's +128 bias) are removed by subtracting the same dot chain run on the constant
+// weight pattern (n = 8, u = 128, n = 0), in the same order, so all-offset blocks give exactly 0.
+typedef _Float16 qg_h2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float c)
+{
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(qg_h2, w), __builtin_bit_cast(qg_h2, x), c,
+                                  false);
+}
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b)
+{
+    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// x of a lane's CPL chunk slots for every batch row, as f16 pairs in dot order, and the offset
+// sums of each slot.
+template <int FMT, int NB, int CPL = 1>
+struct XH {
+    static constexpr int NP = FMT == FQ8_0 ? 8 : 16;   // pairs per 16-byte chunk
+    static constexpr int NZ = FMT == FQ4_K ? 4 : 1;
+    uint32_t p[NB][CPL][NP];
+    float z[NB][CPL][NZ];   // Q4_0: chain(n = 8); Q8_0: chain(u = 128); Q4_K: chain_A(0), chain_B(0), S_A, S_B
+};
+
+// (v & m) | c in one instruction.  A three-operand instruction of this target takes no literal
+// and one scalar operand at most, so the masks and the constant live in VGPRs (set once).
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t m, uint32_t c)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(m), "v"(c));
+    return r;
+}
+
+// Loop-invariant operands of w_pairs, kept in VGPRs.
+struct WConst {
+    uint32_t m_lo, m_hi, c;
+};
+
+template <int FMT>
+__device__ __forceinline__ WConst w_const()
+{
+    WConst k;
+    k.m_lo = FMT == FQ8_0 ? 0x00FF00FFu : 0x000F000Fu;
+    k.m_hi = 0x00F000F0u;
+    k.c = 0x64006400u;
+    asm volatile("" : "+v"(k.m_lo), "+v"(k.m_hi), "+v"(k.c));
+    return k;
+}
+
+// Weight pairs of one dword of a 16-byte chunk, in dot order.
+template <int FMT>
+__device__ __forceinline__ void w_pairs(uint32_t q, const WConst &k, uint32_t *w)
+{
+    if constexpr (FMT == FQ8_0) {
+        const uint32_t u = q ^ 0x80808080u;                 // q + 128 as unsigned bytes
+        w[0] = and_or(u, k.m_lo, k.c);                      // bytes 0, 2
+        w[1] = and_or(u >> 8, k.m_lo, k.c);                 // bytes 1, 3
+    } else {
+        const uint32_t t = q >> 8;
+        w[0] = and_or(q, k.m_lo, k.c);                      // low nibbles of bytes 0, 2
+        w[1] = and_or(q, k.m_hi, k.c);                      // high nibbles of bytes 0, 2 (x16)
+        w[2] = and_or(t, k.m_lo, k.c);                      // low nibbles of bytes 1, 3
+        w[3] = and_or(t, k.m_hi, k.c);                      // high nibbles of bytes 1, 3 (x16)
+    }
+}
+
+// Dot chains of one chunk for one batch row: d[0] (Q4_K: low-nibble chain d[0], high d[1]).
+template <int FMT>
+__device__ __forceinline__ void chunk_chains(const uint32_t (&w)[FMT == FQ8_0 ? 8 : 16],
+                                             const uint32_t *x, float *d)
+{
+    if constexpr (FMT == FQ8_0) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            a = dot2(w[i], x[i], a);
+        d[0] = a;
+    } else if constexpr (FMT == FQ4_0) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            a = dot2(w[i], x[i], a);
+        d[0] = a;
+    } else {
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a = dot2(w[4 * i + 0], x[4 * i + 0], a);
+            b = dot2(w[4 * i + 1], x[4 * i + 1], b);
+            a = dot2(w[4 * i + 2], x[4 * i + 2], a);
+            b = dot2(w[4 * i + 3], x[4 * i + 3], b);
+        }
+        d[0] = a;
+        d[1] = b;
+    }
+}
+
+// x pairs of one chunk (its float4s xv in chunk_elem order), scaled by sc, and the offset sums.
+template <int FMT>
+__device__ __forceinline__ void x_pairs(const float4 *xv, float sc, uint32_t *p, float *z)
+{
+    if constexpr (FMT == FQ8_0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[2 * i + 0] = pack_h2(xv[i].x * sc, xv[i].z * sc);
+            p[2 * i + 1] = pack_h2(xv[i].y * sc, xv[i].w * sc);
+        }
+        uint32_t wz[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            wz[i] = 0x64806480u;                            // u = 128 (q = 0)
+        chunk_chains<FMT>(wz, p, z);
+    } else {
+        const float sh = sc * 0.0625f;                       // high-nibble pairs carry 1/16
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[4 * i + 0] = pack_h2(xv[i].x * sc, xv[i].z * sc);
+            p[4 * i + 1] = pack_h2(xv[4 + i].x * sh, xv[4 + i].z * sh);
+            p[4 * i + 2] = pack_h2(xv[i].y * sc, xv[i].w * sc);
+            p[4 * i + 3] = pack_h2(xv[4 + i].y * sh, xv[4 + i].w * sh);
+        }
+        uint32_t wz[16];
+        if constexpr (FMT == FQ4_0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                wz[4 * i + 0] = wz[4 * i + 2] = 0x64086408u;   // n = 8
+                wz[4 * i + 1] = wz[4 * i + 3] = 0x64806480u;   // 16 n = 128
+            }
+            chunk_chains<FMT>(wz, p, z);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                wz[i] = 0x64006400u;                          // n = 0
+            chunk_chains<FMT>(wz, p, z);
+            // S_A, S_B: the sums of the (rounded, scaled) x of the two sub-blocks
+            float sa = 0.f, sb = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const qg_h2 a0 = __builtin_bit_cast(qg_h2, p[4 * i + 0]);
+                const qg_h2 a1 = __builtin_bit_cast(qg_h2, p[4 * i + 2]);
+                const qg_h2 b0 = __builtin_bit_cast(qg_h2, p[4 * i + 1]);
+                const qg_h2 b1 = __builtin_bit_cast(qg_h2, p[4 * i + 3]);
+                sa += (float)a0.x; sa += (float)a0.y; sa += (float)a1.x; sa += (float)a1.y;
+                sb += (float)b0.x; sb += (float)b0.y; sb += (float)b1.x; sb += (float)b1.y;
+            }
+            z[2] = sa;
+            z[3] = sb * 16.0f;
+        }
+    }
+}
+
+// The lane's chunk c of every batch row as f16 pairs, and the factor that undoes each row's
+// scale (rs[r], exact: a power of two).  With NRM the row's 1/sqrt(mean x^2 + eps) is formed
+// from the staged per-float4 squares (lane-strided partial sums, then a butterfly: the same order
+// whatever the batch size) and folded into the scale.
+template <int FMT, int NB, bool NRM>
+__device__ __forceinline__ void xh_from_lds(XH<FMT, NB> &xh, float (&rs)[NB], const float4 *X4,
+                                            const float *SS, const float *MX, float eps, int K4,
+                                            int C, int c, int lane, int bp32)
+{
+    constexpr int XF4 = Fc<FMT>::XF4;
+    const int cx = c < C ? c : C - 1;
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+        float inv = 1.0f;
+        if constexpr (NRM) {
+            float ss = 0.f;
+            for (int e = lane; e < K4; e += 64)
+                ss += SS[r * K4 + e];
+            ss += xor_lane<32>(ss, bp32);
+            ss += xor_lane<16>(ss, bp32);
+            ss += xor_lane<8>(ss, bp32);
+            ss += xor_lane<4>(ss, bp32);
+            ss += xor_lane<2>(ss, bp32);
+            ss += xor_lane<1>(ss, bp32);
+            inv = 1.0f / sqrtf(ss / (float)(4 * K4) + eps);
+        }
+        float mx = 0.f;
+        for (int e = lane; e < K4; e += 64)
+            mx = fmaxf(mx, MX[r * K4 + e]);
+        mx = fmaxf(mx, xor_lane<32>(mx, bp32));
+        mx = fmaxf(mx, xor_lane<16>(mx, bp32));
+        mx = fmaxf(mx, xor_lane<8>(mx, bp32));
+        mx = fmaxf(mx, xor_lane<4>(mx, bp32));
+        mx = fmaxf(mx, xor_lane<2>(mx, bp32));
+        mx = fmaxf(mx, xor_lane<1>(mx, bp32));
+        int e2 = 0;
+        frexpf(mx * inv, &e2);                              // max |x| = f 2^e2, f in [0.5, 1)
+        const float s = ldexpf(1.0f, 15 - e2);
+        rs[r] = ldexpf(1.0f, e2 - 15);
+        float4 xv[XF4];
+#pragma unroll
+        for (int j = 0; j < XF4; ++j)
+            xv[j] = X4[(size_t)r * K4 + chunk_elem<FMT>(cx, j) / 4];
+        x_pairs<FMT>(xv, inv * s, xh.p[r][0], xh.z[r][0]);
+    }
+}
+
+// x of CPL chunk slots (lane + 64 i) of NB gathered rows (xrow[r] == nullptr: a zero row),
+// straight from global memory, as f16 pairs; the row scale comes from the row's largest |x|
+// (the lanes' slots cover the row), as in xh_from_lds.
+template <int FMT, int NB, int CPL>
+__device__ __forceinline__ void xh_rows(XH<FMT, NB, CPL> &xh, float (&rs)[NB],
+                                        const float *const *xrow, int C, int lane, int bp32)
+{
+    constexpr int XF4 = Fc<FMT>::XF4;
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+        float4 xv[CPL][XF4];
+        float mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            const int cx = c < C ? c : C - 1;
+#pragma unroll
+            for (int j = 0; j < XF4; ++j) {
+                xv[i][j] = xrow[r] ? *reinterpret_cast<const float4 *>(
+                                         xrow[r] + chunk_elem<FMT>(cx, j))
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[i][j].x), fabsf(xv[i][j].y)),
+                                     fmaxf(fabsf(xv[i][j].z), fabsf(xv[i][j].w))));
+            }
+        }
+        mx = fmaxf(mx, xor_lane<32>(mx, bp32));
+        mx = fmaxf(mx, xor_lane<16>(mx, bp32));
+        mx = fmaxf(mx, xor_lane<8>(mx, bp32));
+        mx = fmaxf(mx, xor_lane<4>(mx, bp32));
+        mx = fmaxf(mx, xor_lane<2>(mx, bp32));
+        mx = fmaxf(mx, xor_lane<1>(mx, bp32));
+        int e2 = 0;
+        frexpf(mx, &e2);
+        const float s = ldexpf(1.0f, 15 - e2);
+        rs[r] = ldexpf(1.0f, e2 - 15);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            x_pairs<FMT>(xv[i], s, xh.p[r][i], xh.z[r][i]);
+    }
+}
+
+// Decode + dot of one row group with f16 pairs; acc[item][m] with item = u * NB + r, in the
+// scaled domain of each batch row.
+template <int FMT, int NB, int CPL, int MATS, int R, int IP>
+__device__ __forceinline__ void compute_group_h(const GroupBuf<FMT, CPL, MATS, R> &b,
+                                                const XH<FMT, NB, CPL> &xh, const WConst &k,
+                                                int C, int c0, float (&acc)[IP][MATS])
+{
+    constexpr int NP = XH<FMT, NB, CPL>::NP;
 #pragma unroll
     for (int it = 0; it < IP; ++it)
 #pragma unroll
@@ -251,172 +517,82 @@ __device__ __forceinline__ void compute_group(const GroupBuf<FMT, CPL, MATS, R> 
             acc[it][m] = 0.f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        if (i > 0)
-            __builtin_amdgcn_sched_barrier(0);   // one chunk slot's x and decode live at a time
-        const int c = lane + 64 * i;
-        const int cx = c < C ? c : C - 1;   // slots past the row hold zero weights and scales
-        const int qpos = cx & 7;
+    if (i > 0)
+        __builtin_amdgcn_sched_barrier(0);   // one chunk slot's pairs and decode live at a time
+    const int c = c0 + 64 * i;
+    const int cx = c < C ? c : C - 1;   // a slot past the row's chunks gets zero scales
+    const int qpos = cx & 7;
 #pragma unroll
-        for (int m = 0; m < MATS; ++m)
+    for (int m = 0; m < MATS; ++m)
 #pragma unroll
-            for (int u = 0; u < R; ++u) {
-                float w[CE];
-                decode_stream<FMT>(b.q[m][u][i], w);
-                ChunkScale cs = scale_of<FMT>(b.s[m][u][i], qpos);
-                if (c >= C)
-                    cs.a = cs.b = cs.a2 = cs.b2 = 0.f;
+        for (int u = 0; u < R; ++u) {
+            ChunkScale cs = scale_of<FMT>(b.s[m][u][i], qpos);
+            if (c >= C)
+                cs.a = cs.b = cs.a2 = cs.b2 = 0.f;
+            uint32_t w[NP];
+            const uint4 q = b.q[m][u][i];
+            w_pairs<FMT>(q.x, k, w + 0 * (NP / 4));
+            w_pairs<FMT>(q.y, k, w + 1 * (NP / 4));
+            w_pairs<FMT>(q.z, k, w + 2 * (NP / 4));
+            w_pairs<FMT>(q.w, k, w + 3 * (NP / 4));
 #pragma unroll
-                for (int r = 0; r < NB; ++r)
-                    acc[u * NB + r][m] = chunk_dot<FMT>(w, xc.xv[r][i], xc.sv[r][i], cs,
-                                                        acc[u * NB + r][m]);
-            }
-    }
-}
-
-// In-register form of one chunk's x as the dot consumes it (Q4_0: u, v), and its block sums in
-// the dot's own order.
-template <int FMT>
-__device__ __forceinline__ void x_chunk_transform(float4 *xv, float *sv)
-{
-    if constexpr (FMT == FQ4_0) {
-        float sum = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float4 hv = make_float4(xv[4 + k].x * 0.0625f, xv[4 + k].y * 0.0625f,
-                                          xv[4 + k].z * 0.0625f, xv[4 + k].w * 0.0625f);
-            const float4 u = make_float4(xv[k].x - hv.x, xv[k].y - hv.y, xv[k].z - hv.z,
-                                         xv[k].w - hv.w);
-            xv[k] = u;
-            xv[4 + k] = hv;
-            sum += u.x; sum += u.y; sum += u.z; sum += u.w;
-            sum = fmaf(17.0f, hv.x, sum); sum = fmaf(17.0f, hv.y, sum);
-            sum = fmaf(17.0f, hv.z, sum); sum = fmaf(17.0f, hv.w, sum);
-        }
-        sv[0] = sum;
-    } else if constexpr (FMT == FQ8_0) {
-        float sum = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            sum += xv[k].x; sum += xv[k].y; sum += xv[k].z; sum += xv[k].w;
-        }
-        sv[0] = sum;
-    } else {
-        float sa = 0.f, sb = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            sa += xv[k].x; sa += xv[k].y; sa += xv[k].z; sa += xv[k].w;
-            sb += xv[4 + k].x; sb += xv[4 + k].y; sb += xv[4 + k].z; sb += xv[4 + k].w;
-        }
-        sv[0] = sa;
-        sv[1] = sb;
-    }
-}
-
-// x for this lane's chunk c of every batch row, read straight from global memory into
-// registers (x is a few KB: L1/L2 resident after the first wave), so no LDS staging or
-// workgroup barrier precedes the first row.  With NRM each wave forms 1/sqrt(mean x^2 + eps)
-// itself: its 64 lanes cover the KS chunks of the whole row.  Q4_0 is kept as (u, v) and every
-// block sum is formed in the dot's own order, as in the staging it replaces.
-template <int FMT, int NB, int KS, bool NRM>
-__device__ __forceinline__ void load_x_direct(XCache<FMT, NB, 1> &xc, const float *x,
-                                              const float *gamma, float eps, int64_t K, int C,
-                                              int c, int lane, int bp32)
-{
-    constexpr int XF4 = Fc<FMT>::XF4;
-    const int cx = c < C ? c : C - 1;
-#pragma unroll
-    for (int r = 0; r < NB; ++r)
-#pragma unroll
-        for (int j = 0; j < XF4; ++j)
-            xc.xv[r][0][j] = *reinterpret_cast<const float4 *>(x + r * K + chunk_elem<FMT>(cx, j));
-    if constexpr (NRM) {
-        float4 gv[XF4];
-#pragma unroll
-        for (int j = 0; j < XF4; ++j)
-            gv[j] = *reinterpret_cast<const float4 *>(gamma + chunk_elem<FMT>(cx, j));
-#pragma unroll
-        for (int r = 0; r < NB; ++r) {
-            float ss = 0.f;
-#pragma unroll
-            for (int q = 0; q < KS; ++q) {
-                const int cq = q * 64 + lane;
-                if (cq < C) {
-#pragma unroll
-                    for (int j = 0; j < XF4; ++j) {
-                        const float4 v = q * 64 == c - lane
-                                             ? xc.xv[r][0][j]
-                                             : *reinterpret_cast<const float4 *>(
-                                                   x + r * K + chunk_elem<FMT>(cq, j));
-                        ss = fmaf(v.x, v.x, ss); ss = fmaf(v.y, v.y, ss);
-                        ss = fmaf(v.z, v.z, ss); ss = fmaf(v.w, v.w, ss);
-                    }
+            for (int r = 0; r < NB; ++r) {
+                float d[2];
+                chunk_chains<FMT>(w, xh.p[r][i], d);
+                float &a = acc[u * NB + r][m];
+                if constexpr (FMT == FQ4_K) {
+                    a = fmaf(cs.a, d[0] - xh.z[r][i][0], a);
+                    a = fmaf(-cs.b, xh.z[r][i][2], a);
+                    a = fmaf(cs.a2, d[1] - xh.z[r][i][1], a);
+                    a = fmaf(-cs.b2, xh.z[r][i][3], a);
+                } else {
+                    a = fmaf(cs.a, d[0] - xh.z[r][i][0], a);
                 }
             }
-            ss += xor_lane<32>(ss, bp32);
-            ss += xor_lane<16>(ss, bp32);
-            ss += xor_lane<8>(ss, bp32);
-            ss += xor_lane<4>(ss, bp32);
-            ss += xor_lane<2>(ss, bp32);
-            ss += xor_lane<1>(ss, bp32);
-            const float inv = 1.0f / sqrtf(ss / (float)K + eps);
-#pragma unroll
-            for (int j = 0; j < XF4; ++j)
-                xc.xv[r][0][j] = f4scale(xc.xv[r][0][j], inv, gv[j]);
         }
     }
-#pragma unroll
-    for (int r = 0; r < NB; ++r)
-        x_chunk_transform<FMT>(xc.xv[r][0], xc.sv[r][0]);
-}
-
-// x of CPL chunk slots (lane + 64 i) of NB gathered rows (xrow[r] == nullptr: a zero row),
-// straight into registers; no norm.
-template <int FMT, int NB, int CPL>
-__device__ __forceinline__ void load_x_rows(XCache<FMT, NB, CPL> &xc,
-                                            const float *const *xrow, int C, int lane)
-{
-    constexpr int XF4 = Fc<FMT>::XF4;
-#pragma unroll
-    for (int r = 0; r < NB; ++r)
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int c = lane + 64 * i;
-            const int cx = c < C ? c : C - 1;
-#pragma unroll
-            for (int j = 0; j < XF4; ++j)
-                xc.xv[r][i][j] = xrow[r] ? *reinterpret_cast<const float4 *>(
-                                               xrow[r] + chunk_elem<FMT>(cx, j))
-                                         : make_float4(0.f, 0.f, 0.f, 0.f);
-            x_chunk_transform<FMT>(xc.xv[r][i], xc.sv[r][i]);
-        }
 }
 
 // ------------------------------------------------------------------------------------ GEMV family
 
-// Grid-stride over row groups with prefetch distance 2: group g is decoded while the team's
-// next two groups are in flight, using two register buffers.  A row of C chunks is split over
-// KS = ceil(C / 64) waves (KS in {1, 2, 4}); each wave takes one 16-byte chunk per lane of its
-// K slice, and the KS waves of a team combine their row sums in LDS (slices added in order)
-// before one of them runs the epilogue.
-template <int FMT, int NB, int KS, int EPI, bool NRM>
-__global__ __launch_bounds__(256)
+// Workgroup b streams a pool of row groups: the tiles (TG consecutive groups) b, b + grid,
+// b + 2 grid, ... so that at any time the grid reads one dense window of the matrix (pools of
+// contiguous rows would put hundreds of streams a power-of-two stride apart, on the same memory
+// channels).  Each wave keeps PD groups in flight in PD register buffers: group g is decoded while
+// the next PD - 1 stream in.  With KS = 1 a wave takes a whole row group (one 16-byte chunk per
+// lane) and, after its first PD groups, claims the next group of the pool from an LDS counter,
+// so that waves whose loads the memory system serves early take more groups and all waves of
+// the CU finish together.  With KS > 1 a row's C chunks are split over KS waves (a team) that
+// walk the pool in a fixed order and combine their row sums in LDS (slices added in order).
+// Results wait in LDS and leave in one coalesced pass at the end, so the loop holds no stores
+// (one counter tracks loads and stores on this target: a store among the in-flight loads would
+// make the compiler wait for all of them).  x is staged in LDS once per workgroup.
+template <int FMT, int NB, int KS, int EPI, bool NRM, int PD>
+__global__ __launch_bounds__((SP<FMT, NB, 1, EPI == E_GUS ? 2 : 1>::NT))
 __attribute__((amdgpu_waves_per_eu(SP<FMT, NB, 1, EPI == E_GUS ? 2 : 1>::WPE)))
 void k_stream(GemvArgs a)
 {
     constexpr int MATS = EPI == E_GUS ? 2 : 1;
     using P = SP<FMT, NB, 1, MATS>;
-    constexpr int R = P::R, IP = P::IP;
+    constexpr int R = P::R, IP = P::IP, WV = P::WV, NT = P::NT, ITEMS = P::ITEMS;
     constexpr int LG = IP == 1 ? 0 : IP == 2 ? 1 : IP == 4 ? 2 : IP == 8 ? 3 : IP == 16 ? 4 : 5;
-    constexpr int TEAMS = 4 / KS;
+    constexpr int TEAMS = WV / KS;
+    constexpr int XPT = (NB * KS * 64 * Fc<FMT>::XF4 + NT - 1) / NT;
 
-    __shared__ unsigned long long s_key[NB * 4];
-    __shared__ float s_comb[KS > 1 ? 2 : 1][4][IP][MATS];
-    __shared__ float s_out[4][QG_OUT_GROUPS][IP];
+    extern __shared__ float4 lds4[];
+    __shared__ unsigned long long s_key[NB * WV];
+    __shared__ float s_comb[KS > 1 ? 2 : 1][WV][IP][MATS];
+    __shared__ int s_next;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ks = wave % KS, team = wave / KS;
     const int C = (int)(a.qs_row / 16);
+    const int K4 = (int)(a.K / 4);
+    float4 *X4 = lds4;                                              // x (norm: x * gamma)
+    float *MX = reinterpret_cast<float *>(lds4 + (size_t)NB * K4);  // max |.| of each float4
+    float *SS = MX + NB * K4;                                       // norm: float4 squares
+    float *s_out = SS + (NRM ? NB * K4 : 0);                        // [pool][ITEMS] results
 
     const uint32_t qbytes = (uint32_t)(a.N * a.qs_row), sbytes = (uint32_t)(a.N * a.sc_row);
     BufMat mat[MATS];
@@ -426,22 +602,30 @@ void k_stream(GemvArgs a)
     const LaneOff<1> lo = lane_offsets<FMT, 1>(ks * 64 + lane, C);
     const uint32_t qrow = (uint32_t)a.qs_row, srow = (uint32_t)a.sc_row;
 
+    // this workgroup's pool of row groups: pool-local index c is group gmap(c); indices at or
+    // past `pool` (and groups past T in the last tile) carry no result
+    constexpr int TG = QG_TILE_GROUPS;
     const int64_t T = (a.N + R - 1) / R;
-    const int64_t W = (int64_t)gridDim.x * TEAMS;
-    const int64_t g0 = (int64_t)blockIdx.x * TEAMS + team;
-    // every wave of the workgroup runs the same number of steps (the combine has barriers)
-    const int64_t steps = KS > 1 ? (T - (int64_t)blockIdx.x * TEAMS + W - 1) / W : 0;
+    const int64_t n_tiles = (T + TG - 1) / TG;
+    const int pool = blockIdx.x < n_tiles
+                         ? (int)((n_tiles - 1 - blockIdx.x) / gridDim.x + 1) * TG : 0;
+    auto gmap = [&](int c) -> int64_t {
+        return ((int64_t)(c / TG) * gridDim.x + blockIdx.x) * TG + (c % TG);
+    };
+    // a group that exists, for loads whose results are dropped
+    auto gclamp = [&](int c) -> int64_t {
+        const int64_t g = gmap(c < pool ? c : pool - 1);
+        return g < T ? g : T - 1;
+    };
 
-    // the first two groups of this wave are in flight while x is staged
-    // residual operand of the (row, batch row) this lane writes, fetched with its group
-    const int lg_items = IP == 1 ? 0 : IP == 2 ? 1 : IP == 4 ? 2 : IP == 8 ? 3 : IP == 16 ? 4 : 5;
-    const int item0 = lane >> (6 - lg_items);
-    const int64_t res_col = (int64_t)(item0 % NB) * a.N;
-    const int res_u = item0 / NB;
-    auto load_res = [&](int64_t gg) -> float {
+    // residual operand of the (row, batch row) this lane reports, fetched with its group
+    const int my_item = lane >> (6 - LG);
+    const bool writer = (lane & ((64 >> LG) - 1)) == 0 && my_item < ITEMS;
+    const int my_u = my_item / NB, my_r = my_item % NB;
+    auto load_res = [&](int gl) -> float {
         if constexpr (EPI == E_RES) {
-            const int64_t nr = gg * R + res_u;
-            return a.res[res_col + (nr < a.N ? nr : a.N - 1)];
+            const int64_t nr = gclamp(gl) * R + my_u;   // rows past N re-read row N - 1
+            return a.res[(int64_t)my_r * a.N + (nr < a.N ? nr : a.N - 1)];
         } else {
             return 0.f;
         }
@@ -449,38 +633,55 @@ void k_stream(GemvArgs a)
 
     const int cme = ks * 64 + lane;   // this lane's chunk of the row
     const int bp32 = (lane ^ 32) << 2;
-    // x first (its loads retire first), then the first two row groups
-    XCache<FMT, NB, 1> xc;
-    load_x_direct<FMT, NB, KS, NRM>(xc, a.x, a.gamma, a.eps, a.K, C, cme, lane, bp32);
+    // First group of each buffer: KS = 1, wave w takes p * WV + w; KS > 1, team t takes
+    // t + p * TEAMS (its steps are t + k * TEAMS).
+    auto first_group = [&](int p) -> int { return KS == 1 ? p * WV + wave : team + p * TEAMS; };
+    if (threadIdx.x == 0)
+        s_next = PD * WV;
 
-    GroupBuf<FMT, 1, MATS, R> bufA, bufB;
-    load_group(bufA, mat, qrow, srow, a.N, lo, g0);
-    float resA = load_res(g0);
-    load_group(bufB, mat, qrow, srow, a.N, lo, g0 + W);
-    float resB = load_res(g0 + W);
+    // x (and gamma) first.  The workgroup barrier that publishes x in LDS comes before most of
+    // the weight stream: a wave that issues loads into full memory queues stalls at issue, and a
+    // barrier after its weight loads would hold the whole workgroup for its slowest issuer.
+    // QG_X_LEAD groups per wave are issued ahead of the barrier to cover the x latency.
+    XStage<NB, NRM, XPT> xs;
+    xstage_issue<NB, NRM, XPT, NT>(xs, a.x, a.gamma, K4);
+    __builtin_amdgcn_sched_barrier(0);
+    GroupBuf<FMT, 1, MATS, R> buf[PD];
+    float resv[PD];
+    int gcur[PD];
+    constexpr int LEAD = QG_X_LEAD < PD ? QG_X_LEAD : PD;
+    // issued group by group, in the order the loop re-issues them, so that the wait counts the
+    // compiler derives at the loop head hold on the first round too
+#pragma unroll
+    for (int p = 0; p < LEAD; ++p) {
+        gcur[p] = first_group(p);
+        load_group(buf[p], mat, qrow, srow, a.N, lo, gclamp(gcur[p]));
+        resv[p] = load_res(gcur[p]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    xstage_store<NB, NRM, XPT, NT>(xs, K4, X4, SS, MX);
+    __syncthreads();
+    XH<FMT, NB> xh;
+    const WConst wk = w_const<FMT>();
+    float rs[NB];
+    xh_from_lds<FMT, NB, NRM>(xh, rs, X4, SS, MX, a.eps, K4, C, cme, lane, bp32);
+    // the scale this lane's reported item undoes
+    float my_rs = rs[0];
+#pragma unroll
+    for (int r = 1; r < NB; ++r)
+        my_rs = my_r == r ? rs[r] : my_rs;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = LEAD; p < PD; ++p) {
+        gcur[p] = first_group(p);
+        load_group(buf[p], mat, qrow, srow, a.N, lo, gclamp(gcur[p]));
+        resv[p] = load_res(gcur[p]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
-    // the item this lane reports after the reduction, and whether it writes it
-    const int my_item = lane >> (6 - LG);
-    const bool writer = (lane & ((64 >> LG) - 1)) == 0 && my_item < P::ITEMS;
-    const int my_u = my_item / NB, my_r = my_item % NB;
     unsigned long long best = 0ull;
-
-    // Outputs wait in a small per-wave LDS buffer and leave in batches: a vector store among
-    // the in-flight weight loads would make the compiler wait for every load (one counter
-    // tracks both on this target).
-    int nout = 0;
-    int64_t gout = g0;
-    auto flush = [&]() {
-        for (int L = lane; L < nout * P::ITEMS; L += 64) {
-            const int k = L / P::ITEMS, item = L % P::ITEMS;
-            const int64_t n = (gout + (int64_t)k * W) * R + item / NB;
-            if (n < a.N)
-                a.y[(int64_t)(item % NB) * a.N + n] = s_out[wave][k][item];
-        }
-    };
     // the value this lane's item contributes to y (residual, gated product), argmax bookkeeping
-    auto epilogue = [&](const float (&v)[MATS], int64_t gg, float res) {
-        const int64_t n = gg * R + my_u;
+    auto epilogue = [&](const float (&v)[MATS], int gl, float res) {
         float out;
         if constexpr (EPI == E_RES) {
             out = v[0] + res;
@@ -490,27 +691,32 @@ void k_stream(GemvArgs a)
         } else {
             out = v[0];
         }
-        if constexpr (EPI == E_ARGMAX) {
-            if (writer && n < a.N) {
-                const unsigned long long k = argmax_key(out, n);
-                best = k > best ? k : best;
+        if (writer) {
+            s_out[gl * ITEMS + my_item] = out;
+            if constexpr (EPI == E_ARGMAX) {
+                const int64_t n = gmap(gl) * R + my_u;
+                if (n < a.N) {
+                    const unsigned long long k = argmax_key(out, n);
+                    best = k > best ? k : best;
+                }
             }
         }
-        if (writer)
-            s_out[wave][nout][my_item] = out;
     };
-    // reduce one computed group; with KS > 1 combine the slices through LDS (buffer `par`)
-    auto finish = [&](float (&acc)[IP][MATS], int64_t gg, int par, float res) {
+    // reduce one computed group (gl in the pool); with KS > 1 combine the slices through LDS
+    auto finish = [&](float (&acc)[IP][MATS], int gl, int par, float res) {
         xpose_reduce<IP, MATS>(acc, lane, bp32);
+#pragma unroll
+        for (int m = 0; m < MATS; ++m)
+            acc[0][m] *= my_rs;
         if constexpr (KS == 1) {
-            epilogue(acc[0], gg, res);
+            epilogue(acc[0], gl, res);
         } else {
             if (writer)
 #pragma unroll
                 for (int m = 0; m < MATS; ++m)
                     s_comb[par][wave][my_item][m] = acc[0][m];
             __syncthreads();
-            if (ks == 0) {
+            if (ks == 0 && gl < pool) {
                 float v[MATS];
 #pragma unroll
                 for (int m = 0; m < MATS; ++m) {
@@ -519,46 +725,83 @@ void k_stream(GemvArgs a)
                         for (int q = 0; q < KS; ++q)
                             v[m] += s_comb[par][wave + q][my_item][m];
                 }
-                epilogue(v, gg, res);
+                epilogue(v, gl, res);
             }
-        }
-        if (++nout == QG_OUT_GROUPS) {
-            if (KS == 1 || ks == 0)
-                flush();
-            // retire the stores here (vmcnt 0, other counters untouched), so that only loads
-            // are outstanding where the loop continues and the compiler's waits stay exact
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-            nout = 0;
-            gout = gg + W;
         }
     };
 
-    int64_t g = g0;
-    for (int64_t it = 0; KS > 1 ? it < steps : g < T; ++it) {
-        {
-            float acc[IP][MATS];
-            compute_group<FMT, NB, 1, MATS, R, IP>(bufA, xc, C, cme, acc);
-            const float res = resA;
-            load_group(bufA, mat, qrow, srow, a.N, lo, g + 2 * W);
-            resA = load_res(g + 2 * W);
-            finish(acc, g, 0, res);
+    if constexpr (KS == 1) {
+        // Rounds of PD groups; the loop has one exit, at the end of a round (an exit edge back
+        // through the loop head would make the compiler's wait counts there assume the newest
+        // buffer is the next one).  Claims are increasing, so once the first claim of a round
+        // is past the pool every buffer is.  A buffer past the pool is re-loaded (clamped, no
+        // result) so that every round issues the same loads.
+        if (gcur[0] < pool) {
+            for (;;) {
+#pragma unroll
+                for (int p = 0; p < PD; ++p) {
+                    const int gl = gcur[p];
+                    float acc[IP][MATS];
+                    if (gl < pool)
+                        compute_group_h<FMT, NB, 1, MATS, R, IP>(buf[p], xh, wk, C, cme, acc);
+                    int nx = 0;
+                    if (lane == 0)
+                        nx = atomicAdd(&s_next, 1);
+                    nx = __builtin_amdgcn_readfirstlane(nx);
+                    const float res = resv[p];
+                    load_group(buf[p], mat, qrow, srow, a.N, lo, gclamp(nx < pool ? nx : gl));
+                    resv[p] = load_res(nx < pool ? nx : gl);
+                    if (gl < pool)
+                        finish(acc, gl, 0, res);
+                    gcur[p] = nx;
+                }
+                if (gcur[0] >= pool)
+                    break;
+            }
         }
-        g += W;
-        ++it;
-        if (KS > 1 ? it >= steps : g >= T)
-            break;
-        {
-            float acc[IP][MATS];
-            compute_group<FMT, NB, 1, MATS, R, IP>(bufB, xc, C, cme, acc);
-            const float res = resB;
-            load_group(bufB, mat, qrow, srow, a.N, lo, g + 2 * W);
-            resB = load_res(g + 2 * W);
-            finish(acc, g, 1, res);
+    } else {
+        // the team's steps t + k * TEAMS, k < steps (the same count for every wave: the combine
+        // has barriers); whole rounds of PD, then the last steps % PD with no further loads
+        const int steps = (pool + TEAMS - 1) / TEAMS;
+        const int rounds = steps / PD, rem = steps - rounds * PD;
+        int k = 0, par = 0;
+        for (int rd = 0; rd < rounds; ++rd) {
+#pragma unroll
+            for (int p = 0; p < PD; ++p) {
+                const int gl = team + k * TEAMS;
+                float acc[IP][MATS];
+                compute_group_h<FMT, NB, 1, MATS, R, IP>(buf[p], xh, wk, C, cme, acc);
+                const float res = resv[p];
+                const int gn = gl + PD * TEAMS;
+                load_group(buf[p], mat, qrow, srow, a.N, lo, gclamp(gn));
+                resv[p] = load_res(gn);
+                finish(acc, gl, par, res);
+                par ^= 1;
+                ++k;
+            }
         }
-        g += W;
+#pragma unroll
+        for (int p = 0; p < PD - 1; ++p) {
+            if (p < rem) {
+                const int gl = team + k * TEAMS;
+                float acc[IP][MATS];
+                compute_group_h<FMT, NB, 1, MATS, R, IP>(buf[p], xh, wk, C, cme, acc);
+                finish(acc, gl, par, resv[p]);
+                par ^= 1;
+                ++k;
+            }
+        }
     }
-    if (KS == 1 || ks == 0)
-        flush();
+
+    // all results of the pool are in LDS: write them out, row-contiguous within each tile
+    __syncthreads();
+    const int prow = pool * R;
+    for (int i = threadIdx.x; i < NB * prow; i += NT) {
+        const int r = i / prow, nl = i - r * prow;
+        const int64_t n = gmap(nl / R) * R + nl % R;
+        if (n < a.N)
+            a.y[(int64_t)r * a.N + n] = s_out[(nl / R) * ITEMS + (nl % R) * NB + r];
+    }
 
     if constexpr (EPI == E_ARGMAX) {
         // per batch row: wave max over the writer lanes of that row, then the workgroup's
@@ -572,14 +815,14 @@ void k_stream(GemvArgs a)
                 k = o > k ? o : k;
             }
             if (lane == 0)
-                s_key[r * 4 + wave] = k;
+                s_key[r * WV + wave] = k;
         }
         __syncthreads();
         if (threadIdx.x < NB) {
             const int r = threadIdx.x;
-            unsigned long long k = s_key[r * 4];
-            for (int w = 1; w < 4; ++w)
-                k = s_key[r * 4 + w] > k ? s_key[r * 4 + w] : k;
+            unsigned long long k = s_key[r * WV];
+            for (int w = 1; w < WV; ++w)
+                k = s_key[r * WV + w] > k ? s_key[r * WV + w] : k;
             a.keys[(int64_t)blockIdx.x * NB + r] = k;
         }
     }
@@ -636,8 +879,11 @@ __device__ void moe_stream(const MoeArgs &a, const uint8_t *eq, const uint8_t *e
                                   (uint32_t)(rows * a.qs_row), (uint32_t)(rows * a.sc_row))};
     const LaneOff<CPL> lo = lane_offsets<FMT, CPL>(lane, C);
     const uint32_t qrow = (uint32_t)a.qs_row, srow = (uint32_t)a.sc_row;
-    XCache<FMT, NB, CPL> xc;
-    load_x_rows<FMT, NB, CPL>(xc, xrow, C, lane);
+    const int bp32 = (lane ^ 32) << 2;
+    XH<FMT, NB, CPL> xh;
+    float rs[NB];
+    xh_rows<FMT, NB, CPL>(xh, rs, xrow, C, lane, bp32);
+    const WConst wk = w_const<FMT>();
     GroupBuf<FMT, CPL, 1, R> bufA, bufB;
     load_group(bufA, tm, qrow, srow, rows, lo, g);
     load_group(bufB, tm, qrow, srow, rows, lo, g + W);
@@ -645,16 +891,20 @@ __device__ void moe_stream(const MoeArgs &a, const uint8_t *eq, const uint8_t *e
     const int my_item = lane >> (6 - LG);
     const bool writer = (lane & ((64 >> LG) - 1)) == 0 && my_item < P::ITEMS;
     const int my_u = my_item / NB, my_r = my_item % NB;
+    float my_rs = rs[0];
+#pragma unroll
+    for (int r = 1; r < NB; ++r)
+        my_rs = my_r == r ? rs[r] : my_rs;
     auto finish = [&](float (&acc)[IP][1], int64_t gg) {
-        xpose_reduce<IP, 1>(acc, lane, (lane ^ 32) << 2);
+        xpose_reduce<IP, 1>(acc, lane, bp32);
         const int64_t n = gg * R + my_u;
         if (writer && n < rows && my_r < np)
-            a.part[((int64_t)pr[my_r] * a.topk + pt[my_r]) * a.N + row0 + n] = acc[0][0];
+            a.part[((int64_t)pr[my_r] * a.topk + pt[my_r]) * a.N + row0 + n] = acc[0][0] * my_rs;
     };
     while (g < T) {
         {
             float acc[IP][1];
-            compute_group<FMT, NB, CPL, 1, R, IP>(bufA, xc, C, lane, acc);
+            compute_group_h<FMT, NB, CPL, 1, R, IP>(bufA, xh, wk, C, lane, acc);
             load_group(bufA, tm, qrow, srow, rows, lo, g + 2 * W);
             finish(acc, g);
         }
@@ -663,7 +913,7 @@ __device__ void moe_stream(const MoeArgs &a, const uint8_t *eq, const uint8_t *e
             break;
         {
             float acc[IP][1];
-            compute_group<FMT, NB, CPL, 1, R, IP>(bufB, xc, C, lane, acc);
+            compute_group_h<FMT, NB, CPL, 1, R, IP>(bufB, xh, wk, C, lane, acc);
             load_group(bufB, tm, qrow, srow, rows, lo, g + 2 * W);
             finish(acc, g);
         }
@@ -750,60 +1000,80 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float *part, const in
 
 // ------------------------------------------------------------------------------------ launchers
 
-template <int FMT, int EPI, bool NRM, int CPL>
-static int launch_stream_nb(const GemvArgs &a, int grid, size_t lds, hipStream_t s)
+template <int FMT, int NB, int EPI>
+constexpr int stream_threads() { return SP<FMT, NB, 1, EPI == E_GUS ? 2 : 1>::NT; }
+
+// Kernel of one streaming variant, and its workgroup size.
+struct StreamFn {
+    const void *fn;
+    int threads;
+};
+
+template <int FMT, int NB, int KS, int EPI, bool NRM>
+static StreamFn stream_fn_pd(int pd)
 {
-    switch (a.nb) {
-    case 1: hipLaunchKernelGGL((k_stream<FMT, 1, CPL, EPI, NRM>), dim3(grid), dim3(256), lds, s, a); break;
-    case 2: hipLaunchKernelGGL((k_stream<FMT, 2, CPL, EPI, NRM>), dim3(grid), dim3(256), lds, s, a); break;
-    case 3: hipLaunchKernelGGL((k_stream<FMT, 3, CPL, EPI, NRM>), dim3(grid), dim3(256), lds, s, a); break;
-    case 4: hipLaunchKernelGGL((k_stream<FMT, 4, CPL, EPI, NRM>), dim3(grid), dim3(256), lds, s, a); break;
-    default: return (int)hipErrorInvalidValue;
+    constexpr int T = stream_threads<FMT, NB, EPI>();
+    switch (pd) {
+    case 1: return {reinterpret_cast<const void *>(&k_stream<FMT, NB, KS, EPI, NRM, 1>), T};
+    case 2: return {reinterpret_cast<const void *>(&k_stream<FMT, NB, KS, EPI, NRM, 2>), T};
+    case 4:
+        if constexpr (NB == 1)
+            return {reinterpret_cast<const void *>(&k_stream<FMT, NB, KS, EPI, NRM, 4>), T};
+        return {nullptr, 0};
+    default: return {nullptr, 0};
     }
-    return (int)hipGetLastError();
+}
+
+template <int FMT, int KS, int EPI, bool NRM>
+static StreamFn stream_fn_nb(int nb, int pd)
+{
+    switch (nb) {
+    case 1: return stream_fn_pd<FMT, 1, KS, EPI, NRM>(pd);
+    case 2: return stream_fn_pd<FMT, 2, KS, EPI, NRM>(pd);
+    case 3: return stream_fn_pd<FMT, 3, KS, EPI, NRM>(pd);
+    case 4: return stream_fn_pd<FMT, 4, KS, EPI, NRM>(pd);
+    default: return {nullptr, 0};
+    }
 }
 
 template <int FMT, int EPI, bool NRM>
-static int launch_stream_cpl(int cpl, const GemvArgs &a, int grid, size_t lds, hipStream_t s)
+static StreamFn stream_fn_ks(int ks, int nb, int pd)
 {
-    switch (cpl) {
-    case 1: return launch_stream_nb<FMT, EPI, NRM, 1>(a, grid, lds, s);
-    case 2: return launch_stream_nb<FMT, EPI, NRM, 2>(a, grid, lds, s);
-    case 4: return launch_stream_nb<FMT, EPI, NRM, 4>(a, grid, lds, s);
-    default: return (int)hipErrorInvalidValue;
-    }
+    return ks == 1 ? stream_fn_nb<FMT, 1, EPI, NRM>(nb, pd)
+         : ks == 2 ? stream_fn_nb<FMT, 2, EPI, NRM>(nb, pd)
+         : ks == 4 ? stream_fn_nb<FMT, 4, EPI, NRM>(nb, pd) : StreamFn{nullptr, 0};
 }
 
 template <int FMT>
-static int launch_stream_fmt(int epi, bool nrm, int cpl, const GemvArgs &a, int grid, size_t lds,
-                             hipStream_t s)
+static StreamFn stream_fn_fmt(int epi, bool nrm, int ks, int nb, int pd)
 {
     switch (epi) {
     case E_STORE:
-        return nrm ? launch_stream_cpl<FMT, E_STORE, true>(cpl, a, grid, lds, s)
-                   : launch_stream_cpl<FMT, E_STORE, false>(cpl, a, grid, lds, s);
-    case E_RES:
-        return launch_stream_cpl<FMT, E_RES, false>(cpl, a, grid, lds, s);
-    case E_GUS:
-        return launch_stream_cpl<FMT, E_GUS, true>(cpl, a, grid, lds, s);
-    case E_ARGMAX:
-        return launch_stream_cpl<FMT, E_ARGMAX, false>(cpl, a, grid, lds, s);
-    default:
-        return (int)hipErrorInvalidValue;
+        return nrm ? stream_fn_ks<FMT, E_STORE, true>(ks, nb, pd)
+                   : stream_fn_ks<FMT, E_STORE, false>(ks, nb, pd);
+    case E_RES: return stream_fn_ks<FMT, E_RES, false>(ks, nb, pd);
+    case E_GUS: return stream_fn_ks<FMT, E_GUS, true>(ks, nb, pd);
+    case E_ARGMAX: return stream_fn_ks<FMT, E_ARGMAX, false>(ks, nb, pd);
+    default: return {nullptr, 0};
     }
 }
 
-int launch_stream(int fmt, int epi, bool nrm, int cpl, const GemvArgs &a, int grid,
+static StreamFn stream_fn(int fmt, int epi, bool nrm, int ks, int nb, int pd)
+{
+    return fmt == FQ4_0 ? stream_fn_fmt<FQ4_0>(epi, nrm, ks, nb, pd)
+         : fmt == FQ8_0 ? stream_fn_fmt<FQ8_0>(epi, nrm, ks, nb, pd)
+         : fmt == FQ4_K ? stream_fn_fmt<FQ4_K>(epi, nrm, ks, nb, pd) : StreamFn{nullptr, 0};
+}
+
+int launch_stream(int fmt, int epi, bool nrm, int cpl, int pd, const GemvArgs &a, int grid,
                   size_t lds_bytes, void *stream)
 {
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (fmt == FQ4_0)
-        return launch_stream_fmt<FQ4_0>(epi, nrm, cpl, a, grid, lds_bytes, s);
-    if (fmt == FQ8_0)
-        return launch_stream_fmt<FQ8_0>(epi, nrm, cpl, a, grid, lds_bytes, s);
-    if (fmt == FQ4_K)
-        return launch_stream_fmt<FQ4_K>(epi, nrm, cpl, a, grid, lds_bytes, s);
-    return (int)hipErrorInvalidValue;
+    const StreamFn f = stream_fn(fmt, epi, nrm, cpl, a.nb, pd);
+    if (!f.fn)
+        return (int)hipErrorInvalidValue;
+    void *args[] = {const_cast<GemvArgs *>(&a)};
+    return (int)hipLaunchKernel(f.fn, dim3(grid), dim3(f.threads), args, lds_bytes,
+                                static_cast<hipStream_t>(stream));
 }
 
 template <int FMT>
@@ -847,53 +1117,48 @@ int launch_argmax_fold(const unsigned long long *part, int n_part, int nb, int32
 
 // ------------------------------------------------------------------------------------ occupancy
 
-template <int FMT, int EPI, bool NRM, int CPL>
-static const void *stream_fn_nb(int nb)
+// Workgroups of this streaming variant that fit on the device at once with lds_bytes of dynamic
+// LDS (0 if it does not fit at all or the query fails), and its waves per workgroup.  Cached per
+// device and variant.
+int stream_resident_wgs(int fmt, int epi, bool nrm, int cpl, int nb, int pd, size_t lds_bytes,
+                        int *waves)
 {
-    switch (nb) {
-    case 1: return reinterpret_cast<const void *>(&k_stream<FMT, 1, CPL, EPI, NRM>);
-    case 2: return reinterpret_cast<const void *>(&k_stream<FMT, 2, CPL, EPI, NRM>);
-    case 3: return reinterpret_cast<const void *>(&k_stream<FMT, 3, CPL, EPI, NRM>);
-    case 4: return reinterpret_cast<const void *>(&k_stream<FMT, 4, CPL, EPI, NRM>);
-    default: return nullptr;
-    }
-}
-
-template <int FMT, int EPI, bool NRM>
-static const void *stream_fn_cpl(int cpl, int nb)
-{
-    return cpl == 1 ? stream_fn_nb<FMT, EPI, NRM, 1>(nb)
-         : cpl == 2 ? stream_fn_nb<FMT, EPI, NRM, 2>(nb)
-         : cpl == 4 ? stream_fn_nb<FMT, EPI, NRM, 4>(nb) : nullptr;
-}
-
-template <int FMT>
-static const void *stream_fn_fmt(int epi, bool nrm, int cpl, int nb)
-{
-    switch (epi) {
-    case E_STORE:
-        return nrm ? stream_fn_cpl<FMT, E_STORE, true>(cpl, nb)
-                   : stream_fn_cpl<FMT, E_STORE, false>(cpl, nb);
-    case E_RES: return stream_fn_cpl<FMT, E_RES, false>(cpl, nb);
-    case E_GUS: return stream_fn_cpl<FMT, E_GUS, true>(cpl, nb);
-    case E_ARGMAX: return stream_fn_cpl<FMT, E_ARGMAX, false>(cpl, nb);
-    default: return nullptr;
-    }
-}
-
-int stream_resident_wgs(int fmt, int epi, bool nrm, int cpl, int nb, size_t lds_bytes)
-{
-    const void *fn = fmt == FQ4_0 ? stream_fn_fmt<FQ4_0>(epi, nrm, cpl, nb)
-                   : fmt == FQ8_0 ? stream_fn_fmt<FQ8_0>(epi, nrm, cpl, nb)
-                   : fmt == FQ4_K ? stream_fn_fmt<FQ4_K>(epi, nrm, cpl, nb) : nullptr;
-    if (!fn)
+    const StreamFn f = stream_fn(fmt, epi, nrm, cpl, nb, pd);
+    if (!f.fn)
         return 0;
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds_bytes) != hipSuccess)
+    *waves = f.threads / 64;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
         return 0;
-    return cus * per_cu;
+    struct Entry {
+        const void *fn;
+        int dev;
+        size_t lds;
+        int resident;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        for (const Entry &e : cache)
+            if (e.fn == f.fn && e.dev == dev && e.lds == lds_bytes)
+                return e.resident;
+    }
+    int cus = 0, per_cu = 0, max_lds = 0;
+    hipFuncAttributes attr;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess ||
+        hipFuncGetAttributes(&attr, f.fn) != hipSuccess)
+        return 0;
+    int resident = 0;
+    if (attr.sharedSizeBytes + lds_bytes <= (size_t)max_lds &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f.fn, f.threads, lds_bytes) ==
+            hipSuccess)
+        resident = cus * per_cu;
+    std::lock_guard<std::mutex> lk(mu);
+    cache.push_back({f.fn, dev, lds_bytes, resident});
+    return resident;
 }
 
 }  // namespace qg
