@@ -31,7 +31,7 @@ METRIC = "weight GB/s and % of HBM peak for Q4 dequant-GEMV, nb=1 and nb=16"
 HBM_PEAK_GBPS = 8000.0
 COLD_BYTES = 1 << 30
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "dequant_gemv_q4_amd", "csrc", "gemv_kernels.hip")
+KERNEL_DIR = os.path.join(ROOT, "dequant_gemv_q4_amd", "csrc")
 
 
 def log(*a):
@@ -259,10 +259,20 @@ def stored_traffic(workload):
         return None
     if not rec:
         return None
-    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if rec.get("kernel_sha256") != src:
+    if rec.get("kernel_sha256") != kernel_sha256():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def kernel_sha256():
+    """One hash over every kernel and library source: a counter reading is only valid for the
+    code it was taken on."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_DIR)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(KERNEL_DIR, name), "rb").read())
+    return h.hexdigest()
 
 
 def cpu_baseline(b, budget_s):
@@ -350,7 +360,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16xf16->f32",
         "data": "synthetic",
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "config": b.config,
