@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqgemv.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["gemv_kernels.hip", "stream_kernels.hip", "abi.cpp"]
+SOURCES = ["gemv_kernels.hip", "stream_kernels.hip", "mfma_kernels.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

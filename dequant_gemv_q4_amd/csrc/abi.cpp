@@ -10,6 +10,9 @@
 #include "../../include/qgemv.h"
 #include "qgemv_internal.h"
 
+#ifndef QG_MFMA_MIN_NB
+#define QG_MFMA_MIN_NB 5          // batch rows from which the matrix-core kernel takes a call
+#endif
 #ifndef QG_POOL_LDS
 #define QG_POOL_LDS 32768         // most LDS bytes of results one streaming workgroup holds
 #endif
@@ -237,7 +240,12 @@ static int run_gemv(int fmt, int epi, bool nrm, GemvArgs a, void *stream)
 {
     int grid = 0, herr = 0;
     StreamPlan sp;
-    if (plan_stream(fmt, epi, nrm, a.N, a.K, a.nb, &sp)) {
+    MfmaPlan mp;
+    if (a.nb >= QG_MFMA_MIN_NB && plan_mfma(fmt, epi, nrm, a.N, a.K, a.nb, &mp) &&
+        mp.grid <= QG_ARGMAX_MAX_GRID) {
+        grid = mp.grid;
+        herr = launch_mfma(fmt, epi, nrm, mp, a, stream);
+    } else if (plan_stream(fmt, epi, nrm, a.N, a.K, a.nb, &sp)) {
         grid = sp.grid;
         herr = launch_stream(fmt, epi, nrm, sp.cpl, sp.pd, a, sp.grid, sp.lds, stream);
     } else {

@@ -1,0 +1,501 @@
+// mfma_kernels.hip -- row-batch (5 <= nb <= 16) dequant GEMV on the gfx950 matrix cores.
+//
+// With a batch of up to 16 activation rows the product is a small dense contraction, so it runs
+// on v_mfma_f32_16x16x32_f16: D[b][n] = sum_k X[b][k] W[n][k] over one quant block of 32 k at a
+// time, b the batch row (padded to 16) and n one of 16 weight rows.  The weights sit in the B
+// operand, so each lane's four results belong to a single weight row and take a single block
+// scale: acc += d * D (f32, VALU).  Same arithmetic as the vector path:
+//  - weights: nibbles (or Q8_0 bytes + 128) are placed in the mantissa of 1024.0 (f16 0x6400) by
+//    one and-or per pair, then the offset (1032, or 1152 for a high nibble held x16 and for Q8_0)
+//    is subtracted with one packed f16 add: exact q - 8 (16 (q - 8)) or exact q;
+//  - x: each batch row scaled by a power of two that puts its largest |x| in [2^14, 2^15),
+//    rounded to f16 (relative error <= 2^-11); x at a high-nibble position carries 1/16.  The row
+//    scale is undone, exactly, on the results.
+// Operand layouts (CDNA4 16x16x32 f16): lane l holds A[l % 16][8 (l / 16) + 0..7] and
+// B[8 (l / 16) + 0..7][l % 16], and D[4 (l / 16) + 0..3][l % 16].  A k position may be any
+// element as long as A and B agree, so the eight halves a lane holds for one block are the eight
+// elements of one dword of quant bytes (Q4_0: bytes 4j..4j+3, their low and high nibbles; Q8_0:
+// bytes 4j..4j+3 of both 16-byte halves of the block).
+//
+// Loads: lane (row i = l % 16, c = l / 16) reads the 16-byte chunk 4 s + c of weight row i for
+// step s; a 4 x 4 transpose of dwords across the four 16-lane rows (v_permlane32_swap, then
+// v_permlane16_swap) leaves in lane (i, j) dword j of each of the four chunks: the B operands of
+// the step's four blocks (Q4_0) or two blocks (Q8_0).
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+
+#include <mutex>
+#include <vector>
+
+namespace qg {
+
+typedef _Float16 mh2 __attribute__((ext_vector_type(2)));
+typedef _Float16 mh8 __attribute__((ext_vector_type(8)));
+typedef float mf4 __attribute__((ext_vector_type(4)));
+
+constexpr int MF_WAVES = 16;             // waves per workgroup: one per batch row in the prologue
+constexpr int MF_THREADS = 64 * MF_WAVES;
+constexpr int MF_KMAX = 4096;            // longest row the staged x fits (x2 K classes)
+
+__device__ __forceinline__ uint32_t mf_and_or(uint32_t v, uint32_t m, uint32_t c)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(m), "v"(c));
+    return r;
+}
+
+__device__ __forceinline__ uint32_t mf_hadd(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(mh2, a) + __builtin_bit_cast(mh2, b));
+}
+
+struct MfConst {
+    uint32_t m_lo, m_hi, c, off_lo, off_hi;
+};
+
+template <int FMT>
+__device__ __forceinline__ MfConst mf_const()
+{
+    MfConst k;
+    k.m_lo = FMT == FQ8_0 ? 0x00FF00FFu : 0x000F000Fu;
+    k.m_hi = 0x00F000F0u;
+    k.c = 0x64006400u;
+    k.off_lo = FMT == FQ8_0 ? 0xE480E480u : 0xE408E408u;   // -1152 (Q8_0) / -1032 (n - 8)
+    k.off_hi = 0xE480E480u;                                // -1152: 16 n - 128
+    asm volatile("" : "+v"(k.m_lo), "+v"(k.m_hi), "+v"(k.c), "+v"(k.off_lo), "+v"(k.off_hi));
+    return k;
+}
+
+// B operand (eight exact f16 weights) of one block from the lane's dword(s).
+template <int FMT>
+__device__ __forceinline__ mh8 mf_bop(uint32_t q0, uint32_t q1, const MfConst &k)
+{
+    uint32_t w[4];
+    if constexpr (FMT == FQ8_0) {
+        const uint32_t u0 = q0 ^ 0x80808080u, u1 = q1 ^ 0x80808080u;
+        w[0] = mf_hadd(mf_and_or(u0, k.m_lo, k.c), k.off_lo);          // bytes 0, 2 (half 0)
+        w[1] = mf_hadd(mf_and_or(u0 >> 8, k.m_lo, k.c), k.off_lo);     // bytes 1, 3
+        w[2] = mf_hadd(mf_and_or(u1, k.m_lo, k.c), k.off_lo);          // bytes 0, 2 (half 1)
+        w[3] = mf_hadd(mf_and_or(u1 >> 8, k.m_lo, k.c), k.off_lo);     // bytes 1, 3
+    } else {
+        const uint32_t t = q0 >> 8;
+        w[0] = mf_hadd(mf_and_or(q0, k.m_lo, k.c), k.off_lo);   // low nibbles of bytes 0, 2
+        w[1] = mf_hadd(mf_and_or(q0, k.m_hi, k.c), k.off_hi);   // high nibbles of bytes 0, 2 (x16)
+        w[2] = mf_hadd(mf_and_or(t, k.m_lo, k.c), k.off_lo);    // low nibbles of bytes 1, 3
+        w[3] = mf_hadd(mf_and_or(t, k.m_hi, k.c), k.off_hi);    // high nibbles of bytes 1, 3 (x16)
+    }
+    struct W4 {
+        uint32_t v[4];
+    } p = {{w[0], w[1], w[2], w[3]}};
+    return __builtin_bit_cast(mh8, p);
+}
+
+// Position (dword j of the block, half h of the lane's eight) of block element eb (0..31), and
+// whether it carries the 1/16 of a high nibble.
+template <int FMT>
+__device__ __forceinline__ void mf_slot(int eb, int &j, int &h, bool &hi)
+{
+    const int second = eb >= 16, e = eb & 15, t = e & 3;
+    j = e >> 2;
+    if constexpr (FMT == FQ8_0) {
+        // halves: [b0, b2, b1, b3] of half 0, then of half 1
+        h = 4 * second + (t == 0 ? 0 : t == 2 ? 1 : t == 1 ? 2 : 3);
+        hi = false;
+    } else {
+        // halves: [lo b0, lo b2, hi b0, hi b2, lo b1, lo b3, hi b1, hi b3]
+        h = (t & 1) * 4 + second * 2 + (t >> 1);
+        hi = second;
+    }
+}
+
+// 4 x 4 transpose of dwords across the four 16-lane rows: register r of lane row c holds dword
+// c of row r's chunk afterwards.
+__device__ __forceinline__ void mf_xpose(uint32_t (&v)[4])
+{
+    auto s0 = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+    auto s1 = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+    auto t0 = __builtin_amdgcn_permlane16_swap(s0[0], s1[0], false, false);
+    auto t1 = __builtin_amdgcn_permlane16_swap(s0[1], s1[1], false, false);
+    v[0] = t0[0];
+    v[1] = t0[1];
+    v[2] = t1[0];
+    v[3] = t1[1];
+}
+
+template <int OFF>
+__device__ __forceinline__ float mf_xor(float v)
+{
+    return __shfl_xor(v, OFF);
+}
+
+// Persistent workgroups of 16 waves; x (the 16 padded batch rows, all of K) is staged once per
+// workgroup.  Work comes in groups of TPW consecutive 16-row tiles (group g = blockIdx.x,
+// blockIdx.x + gridDim.x, ...: the grid reads one dense window).  In a group, wave w takes tile
+// w / KS and K slice w % KS (KS = 16 / TPW waves per tile), i.e. steps slice, slice + KS, ...,
+// streamed through two register buffers.  With KS > 1 the slices' partial tiles are added in LDS
+// in slice order.  K class KC: K <= 2048 KC (x: 8 KC float4s per lane).
+template <int FMT, int EPI, bool NRM, int KC, int TPW>
+__global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
+{
+    constexpr int MATS = EPI == E_GUS ? 2 : 1;
+    constexpr int BPS = FMT == FQ8_0 ? 2 : 4;   // blocks per step
+    constexpr int MF_XR = 8 * KC;                // float4s of x a lane stages
+    constexpr int KS = MF_WAVES / TPW;           // waves per tile
+    constexpr int PD = TPW >= 8 && MATS == 1 ? 4 : 2;   // steps in flight per wave
+    extern __shared__ float4 mf_lds[];
+    __shared__ float s_rs[16];
+    __shared__ unsigned long long s_best[16];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int C = (int)(a.qs_row / 16), S = (C + 3) / 4, KB = (int)(a.K / 32);
+    const int K4 = (int)(a.K / 4);
+    uint8_t *XA = reinterpret_cast<uint8_t *>(mf_lds);                   // [KB][4][16] x 16 B
+    float *PART = reinterpret_cast<float *>(XA + (size_t)KB * 1024);    // [16][MATS][4][64]
+
+    // ---- x loads (this lane's float4s of batch row `wave`) and gamma
+    const int bx = wave;   // the batch row this wave stages
+    const bool xrow = bx < a.nb;
+    float4 xv[MF_XR];
+#pragma unroll
+    for (int i = 0; i < MF_XR; ++i) {
+        const int f = lane + 64 * i;
+        const int fc = f < K4 ? f : K4 - 1;
+        xv[i] = reinterpret_cast<const float4 *>(a.x)[(int64_t)(xrow ? bx : 0) * K4 + fc];
+    }
+    // gamma (norm): K4 <= 512 float4s, one per thread, staged in the (not yet used) result area
+    float4 gone = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (NRM)
+        gone = reinterpret_cast<const float4 *>(a.gamma)[tid < K4 ? tid : K4 - 1];
+    float4 *G4 = reinterpret_cast<float4 *>(PART);
+    if (tid < 16)
+        s_best[tid] = 0ull;
+
+    const int ir = lane & 15, lc = lane >> 4;
+    const uint32_t qbytes = (uint32_t)(a.N * a.qs_row), sbytes = (uint32_t)(a.N * a.sc_row);
+    __amdgpu_buffer_rsrc_t rq[MATS], rsc[MATS];
+    rq[0] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.qs0), (short)0, (int)qbytes, 0x00020000);
+    rsc[0] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.sc0), (short)0, (int)sbytes, 0x00020000);
+    if constexpr (MATS == 2) {
+        rq[1] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.qs1), (short)0, (int)qbytes, 0x00020000);
+        rsc[1] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.sc1), (short)0, (int)sbytes, 0x00020000);
+    }
+    const int64_t NT = (a.N + 15) / 16, G = (NT + TPW - 1) / TPW;
+    const int my_t = wave / KS, slice = wave % KS;
+    const int nst = S > slice ? (S - 1 - slice) / KS + 1 : 0;   // this wave's steps per tile
+
+    // one step's loads: the lane's 16-byte chunk of its row and the step's block scales
+    struct StepBuf {
+        uint32_t q[MATS][4];
+        uint16_t s[MATS][BPS];
+    };
+    auto load_step = [&](StepBuf &sb, int64_t n, int k) {
+        const int kk = k < nst ? k : nst - 1;              // past the wave's steps: its last
+        const int st = slice + KS * (kk > 0 ? kk : 0);      // (a wave with none: a clamped chunk)
+        const int ch = 4 * st + lc < C ? 4 * st + lc : C - 1;
+#pragma unroll
+        for (int m = 0; m < MATS; ++m) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+                rq[m], (int)((uint32_t)n * (uint32_t)a.qs_row + 16u * (uint32_t)ch), 0, 0);
+            sb.q[m][0] = v[0]; sb.q[m][1] = v[1]; sb.q[m][2] = v[2]; sb.q[m][3] = v[3];
+#pragma unroll
+            for (int b = 0; b < BPS; ++b) {
+                const int blk = BPS * st + b < KB ? BPS * st + b : KB - 1;
+                sb.s[m][b] = __builtin_amdgcn_raw_buffer_load_b16(
+                    rsc[m], (int)((uint32_t)n * (uint32_t)a.sc_row + 2u * (uint32_t)blk), 0, 0);
+            }
+        }
+    };
+    auto tile_row = [&](int64_t grp) -> int64_t {
+        const int64_t t = grp * TPW + my_t;
+        const int64_t r = t * 16 + ir;
+        return r < a.N ? r : a.N - 1;
+    };
+    // the first group's first PD steps go out before x is converted
+    StepBuf sbuf[PD];
+    const int64_t grp0 = blockIdx.x;
+#pragma unroll
+    for (int p = 0; p < PD; ++p) {
+        load_step(sbuf[p], tile_row(grp0), p);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NRM) {
+        if (tid < K4)
+            G4[tid] = gone;
+        __syncthreads();
+    }
+
+    // ---- batch row `wave`: norm, scale, f16 pairs into the A layout
+    {
+        float ss = 0.f, mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < MF_XR; ++i) {
+            const int f = lane + 64 * i;
+            float4 v = xv[i];
+            if (f >= K4 || !xrow)
+                v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if constexpr (NRM) {
+                float q = v.x * v.x;
+                q = fmaf(v.y, v.y, q);
+                q = fmaf(v.z, v.z, q);
+                q = fmaf(v.w, v.w, q);
+                ss += q;
+                const float4 g = G4[f < K4 ? f : K4 - 1];
+                v = make_float4(v.x * g.x, v.y * g.y, v.z * g.z, v.w * g.w);
+            }
+            xv[i] = v;
+            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+        float inv = 1.0f;
+        if constexpr (NRM) {
+            ss += mf_xor<32>(ss);
+            ss += mf_xor<16>(ss);
+            ss += mf_xor<8>(ss);
+            ss += mf_xor<4>(ss);
+            ss += mf_xor<2>(ss);
+            ss += mf_xor<1>(ss);
+            inv = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+        }
+        mx = fmaxf(mx, mf_xor<32>(mx));
+        mx = fmaxf(mx, mf_xor<16>(mx));
+        mx = fmaxf(mx, mf_xor<8>(mx));
+        mx = fmaxf(mx, mf_xor<4>(mx));
+        mx = fmaxf(mx, mf_xor<2>(mx));
+        mx = fmaxf(mx, mf_xor<1>(mx));
+        int e2 = 0;
+        frexpf(mx * inv, &e2);
+        const int sk = 15 - e2 < 127 ? 15 - e2 : 127;       // 2^sk stays a finite f32
+        const float sc = inv * ldexpf(1.0f, sk), sh = sc * 0.0625f;
+        if (lane == 0)
+            s_rs[wave] = ldexpf(1.0f, -sk);
+#pragma unroll
+        for (int i = 0; i < MF_XR; ++i) {
+            const int f = lane + 64 * i;
+            if (f < K4) {
+                const float e[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int el = 4 * f + t, blk = el >> 5;
+                    int j, h;
+                    bool hi;
+                    mf_slot<FMT>(el & 31, j, h, hi);
+                    const _Float16 hv = (_Float16)(e[t] * (hi ? sh : sc));
+                    *reinterpret_cast<_Float16 *>(XA + (((size_t)(blk * 4 + j) * 16 + bx) * 8 + h) * 2) = hv;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const MfConst kc = mf_const<FMT>();
+    // one step: transpose, B operands, one MFMA per block, scaled accumulation
+    auto compute = [&](const StepBuf &sb, int k, float (&acc)[MATS][4]) {
+        const int st = slice + KS * k;
+#pragma unroll
+        for (int m = 0; m < MATS; ++m) {
+            uint32_t q[4] = {sb.q[m][0], sb.q[m][1], sb.q[m][2], sb.q[m][3]};
+            mf_xpose(q);
+#pragma unroll
+            for (int b = 0; b < BPS; ++b) {
+                const int blk = BPS * st + b;
+                const float d = blk < KB ? (float)__builtin_bit_cast(_Float16, sb.s[m][b]) : 0.f;
+                const mh8 bop = FMT == FQ8_0 ? mf_bop<FMT>(q[2 * b], q[2 * b + 1], kc)
+                                             : mf_bop<FMT>(q[b], 0u, kc);
+                const int blc = blk < KB ? blk : KB - 1;
+                const mh8 aop = *reinterpret_cast<const mh8 *>(
+                    XA + ((size_t)(blc * 4 + lc) * 16 + ir) * 16);
+                const mf4 zero = {0.f, 0.f, 0.f, 0.f};
+                const mf4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, zero, 0, 0, 0);
+                acc[m][0] = fmaf(d, D[0], acc[m][0]);
+                acc[m][1] = fmaf(d, D[1], acc[m][1]);
+                acc[m][2] = fmaf(d, D[2], acc[m][2]);
+                acc[m][3] = fmaf(d, D[3], acc[m][3]);
+            }
+        }
+    };
+    // result of (batch row b, tile row nn) from the summed, row-scaled values v
+    auto epilogue = [&](const float (&v)[MATS], int b, int64_t nn) {
+        const bool ok = b < a.nb && nn < a.N;
+        float out;
+        if constexpr (EPI == E_GUS) {
+            out = v[0] / (1.0f + expf(-v[0])) * v[MATS - 1];
+        } else if constexpr (EPI == E_RES) {
+            out = v[0] + (ok ? a.res[(int64_t)b * a.N + nn] : 0.f);
+        } else {
+            out = v[0];
+        }
+        if (ok) {
+            a.y[(int64_t)b * a.N + nn] = out;
+            if constexpr (EPI == E_ARGMAX)
+                atomicMax(&s_best[b], argmax_key(out, nn));
+        }
+    };
+
+    for (int64_t grp = grp0; grp < G; grp += gridDim.x) {
+        const int64_t n = tile_row(grp);
+        float acc[MATS][4];
+#pragma unroll
+        for (int m = 0; m < MATS; ++m)
+            acc[m][0] = acc[m][1] = acc[m][2] = acc[m][3] = 0.f;
+        if (grp != grp0) {
+#pragma unroll
+            for (int p = 0; p < PD; ++p)
+                load_step(sbuf[p], n, p);
+        }
+        // rounds of PD steps (the loop has one exit, at the end of a round); a step past the
+        // wave's own is skipped, its buffer re-loaded with the wave's last step
+        for (int k = 0; k < nst; k += PD) {
+#pragma unroll
+            for (int p = 0; p < PD; ++p) {
+                float t[MATS][4];
+#pragma unroll
+                for (int m = 0; m < MATS; ++m)
+                    t[m][0] = t[m][1] = t[m][2] = t[m][3] = 0.f;
+                if (k + p < nst)
+                    compute(sbuf[p], k + p, t);
+#pragma unroll
+                for (int m = 0; m < MATS; ++m)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[m][r] += t[m][r];
+                load_step(sbuf[p], n, k + p + PD);
+            }
+        }
+        const int64_t tile = grp * TPW + my_t;
+        if constexpr (KS == 1) {
+            // the wave owns its tile: lane l holds batch rows 4 (l / 16) + r of row l % 16
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int b = 4 * lc + r;
+                float v[MATS];
+#pragma unroll
+                for (int m = 0; m < MATS; ++m)
+                    v[m] = acc[m][r] * s_rs[b];
+                epilogue(v, b, tile * 16 + ir);
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < MATS; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    PART[((wave * MATS + m) * 4 + r) * 64 + lane] = acc[m][r];
+            __syncthreads();
+            for (int e = tid; e < TPW * 256; e += MF_THREADS) {
+                const int tt = e >> 8, b = (e >> 4) & 15, ri = e & 15;
+                const int src = (b >> 2) * 16 + ri, r = b & 3;
+                float v[MATS];
+#pragma unroll
+                for (int m = 0; m < MATS; ++m) {
+                    float sum = 0.f;
+                    for (int q = 0; q < KS; ++q)
+                        sum += PART[(((tt * KS + q) * MATS + m) * 4 + r) * 64 + src];
+                    v[m] = sum * s_rs[b];
+                }
+                epilogue(v, b, (grp * TPW + tt) * 16 + ri);
+            }
+            __syncthreads();
+        }
+    }
+
+    if constexpr (EPI == E_ARGMAX) {
+        __syncthreads();
+        if (tid < a.nb)
+            a.keys[(int64_t)blockIdx.x * a.nb + tid] = s_best[tid];
+    }
+}
+
+// ------------------------------------------------------------------------------------ host side
+
+// The norm variants take K <= 2048 only: with the longer class x, its statistics and the weight
+// loads do not fit in the 128 registers a lane has at 1024 threads.
+template <int FMT, int EPI, bool NRM, int KC>
+static const void *mfma_fn_tpw(int tpw)
+{
+    switch (tpw) {
+    case 1: return reinterpret_cast<const void *>(&k_mfma<FMT, EPI, NRM, KC, 1>);
+    case 2: return reinterpret_cast<const void *>(&k_mfma<FMT, EPI, NRM, KC, 2>);
+    case 4: return reinterpret_cast<const void *>(&k_mfma<FMT, EPI, NRM, KC, 4>);
+    case 8: return reinterpret_cast<const void *>(&k_mfma<FMT, EPI, NRM, KC, 8>);
+    case 16: return reinterpret_cast<const void *>(&k_mfma<FMT, EPI, NRM, KC, 16>);
+    default: return nullptr;
+    }
+}
+
+template <int FMT, int EPI, bool NRM>
+static const void *mfma_fn_ns(int kc, int tpw)
+{
+    if (kc == 1)
+        return mfma_fn_tpw<FMT, EPI, NRM, 1>(tpw);
+    if constexpr (!NRM) {
+        if (kc == 2)
+            return mfma_fn_tpw<FMT, EPI, NRM, 2>(tpw);
+    }
+    return nullptr;
+}
+
+template <int FMT>
+static const void *mfma_fn_fmt(int epi, bool nrm, int kc, int tpw)
+{
+    switch (epi) {
+    case E_STORE:
+        return nrm ? mfma_fn_ns<FMT, E_STORE, true>(kc, tpw)
+                   : mfma_fn_ns<FMT, E_STORE, false>(kc, tpw);
+    case E_RES: return mfma_fn_ns<FMT, E_RES, false>(kc, tpw);
+    case E_GUS: return mfma_fn_ns<FMT, E_GUS, true>(kc, tpw);
+    case E_ARGMAX: return mfma_fn_ns<FMT, E_ARGMAX, false>(kc, tpw);
+    default: return nullptr;
+    }
+}
+
+static const void *mfma_fn(int fmt, int epi, bool nrm, int kc, int tpw)
+{
+    return fmt == FQ4_0 ? mfma_fn_fmt<FQ4_0>(epi, nrm, kc, tpw)
+         : fmt == FQ8_0 ? mfma_fn_fmt<FQ8_0>(epi, nrm, kc, tpw) : nullptr;
+}
+
+// Plan of the row-batch kernel: K class (1: K <= 2048, 2: K <= 4096), tiles per group (16 / waves
+// per tile), grid and LDS bytes; false if the kernel does not take these sizes (format, K too long
+// for the staged x, LDS).
+bool plan_mfma(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb, MfmaPlan *p)
+{
+    if (fmt != FQ4_0 && fmt != FQ8_0)
+        return false;
+    if (nb < 1 || nb > 16 || K > MF_KMAX || N < 1)
+        return false;
+    p->kc = K <= 2048 ? 1 : 2;
+    const int mats = epi == E_GUS ? 2 : 1;
+    p->lds = (size_t)(K / 32) * 1024 + (size_t)MF_WAVES * mats * 4 * 64 * 4;
+    // one workgroup per CU; enough tiles per group that the groups fill the CUs once, at most
+    // one wave per tile
+    int dev = 0, cus = 0, max_lds = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess)
+        return false;
+    const int64_t NT = (N + 15) / 16;
+    int tpw = 1;
+    while (tpw < 16 && NT >= (int64_t)cus * tpw * 2)
+        tpw *= 2;
+    p->tpw = tpw;
+    const int64_t groups = (NT + tpw - 1) / tpw;
+    p->grid = (int)(groups < cus ? groups : cus);
+    const void *fn = mfma_fn(fmt, epi, nrm, p->kc, p->tpw);
+    hipFuncAttributes attr;
+    if (!fn || hipFuncGetAttributes(&attr, fn) != hipSuccess)
+        return false;
+    return attr.sharedSizeBytes + p->lds <= (size_t)max_lds;
+}
+
+int launch_mfma(int fmt, int epi, bool nrm, const MfmaPlan &p, const GemvArgs &a, void *stream)
+{
+    const void *fn = mfma_fn(fmt, epi, nrm, p.kc, p.tpw);
+    if (!fn)
+        return (int)hipErrorInvalidValue;
+    void *args[] = {const_cast<GemvArgs *>(&a)};
+    return (int)hipLaunchKernel(fn, dim3(p.grid), dim3(MF_THREADS), args, p.lds,
+                                static_cast<hipStream_t>(stream));
+}
+
+}  // namespace qg

@@ -130,6 +130,16 @@ int launch_gemv(int fmt, int epi, bool nrm, const GemvArgs &a, int grid, size_t 
 int launch_stream(int fmt, int epi, bool nrm, int cpl, int pd, const GemvArgs &a, int grid,
                   size_t lds_bytes, void *stream);
 int launch_moe(int fmt, int cpl, const MoeArgs &a, int grid, size_t lds_bytes, void *stream);
+// Row-batch kernel on the matrix cores (mfma_kernels.hip): persistent workgroups over groups of
+// 16-row tiles.
+struct MfmaPlan {
+    int kc;       // K class: 1 (K <= 2048) or 2 (K <= 4096)
+    int tpw;      // tiles per group (16 / waves per tile)
+    int grid;
+    size_t lds;
+};
+bool plan_mfma(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb, MfmaPlan *p);
+int launch_mfma(int fmt, int epi, bool nrm, const MfmaPlan &p, const GemvArgs &a, void *stream);
 int launch_argmax_fold(const unsigned long long *part, int n_part, int nb, int32_t *idx,
                        void *stream);
 // Workgroups of a streaming launch that are resident at once on the current device (0 if the

@@ -451,8 +451,9 @@ __device__ __forceinline__ void xh_from_lds(XH<FMT, NB> &xh, float (&rs)[NB], co
         mx = fmaxf(mx, xor_lane<1>(mx, bp32));
         int e2 = 0;
         frexpf(mx * inv, &e2);                              // max |x| = f 2^e2, f in [0.5, 1)
-        const float s = ldexpf(1.0f, 15 - e2);
-        rs[r] = ldexpf(1.0f, e2 - 15);
+        const int sk = 15 - e2 < 127 ? 15 - e2 : 127;       // 2^sk stays a finite f32
+        const float s = ldexpf(1.0f, sk);
+        rs[r] = ldexpf(1.0f, -sk);
         float4 xv[XF4];
 #pragma unroll
         for (int j = 0; j < XF4; ++j)
@@ -494,8 +495,9 @@ __device__ __forceinline__ void xh_rows(XH<FMT, NB, CPL> &xh, float (&rs)[NB],
         mx = fmaxf(mx, xor_lane<1>(mx, bp32));
         int e2 = 0;
         frexpf(mx, &e2);
-        const float s = ldexpf(1.0f, 15 - e2);
-        rs[r] = ldexpf(1.0f, e2 - 15);
+        const int sk = 15 - e2 < 127 ? 15 - e2 : 127;       // 2^sk stays a finite f32
+        const float s = ldexpf(1.0f, sk);
+        rs[r] = ldexpf(1.0f, -sk);
 #pragma unroll
         for (int i = 0; i < CPL; ++i)
             x_pairs<FMT>(xv[i], s, xh.p[r][i], xh.z[r][i]);

@@ -153,6 +153,44 @@ def test_repeated_launches_are_bitwise_identical():
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
+@pytest.mark.parametrize("fmt,N,K,nb", [(q.Q4_0, 8209, 512, 16), (q.Q4_0, 16411, 256, 8),
+                                        (q.Q8_0, 33000, 256, 13), (q.Q4_0, 65573, 256, 16),
+                                        (q.Q8_0, 8200, 3072, 7), (q.Q4_0, 1000, 4096, 16)])
+def test_row_batch_tile_groups(fmt, N, K, nb):
+    """Row batches of 5..16 on tall matrices: several 16-row tiles per work group and fewer waves
+    per tile (K split 8, 4, 2 ways, or one wave per tile), ragged last group, and the long-K
+    class (K > 2048)."""
+    say(f"row batch fmt={fmt} N={N} K={K} nb={nb}")
+    g = wl.rng(700 + fmt, N + nb)
+    W = wl.matrix(fmt, g, N, K)
+    x = wl.normal_f32(g, (nb, K))
+    y = _run_gemv(fmt, gpu_matrix(fmt, W, N, K), N, K, x)
+    yr, A = oracle.gemv(fmt, W, N, K, x)
+    assert_within(y, yr, tol_gemv(A, yr), f"row batch fmt={fmt} N={N}")
+
+
+def test_x_scale_extremes():
+    """x rows spanning many binades (and one row of zeros, one tiny, one huge): the per-row
+    power-of-two scaling keeps every path inside its bound."""
+    say("x scale extremes")
+    N, K = 300, 2048
+    g = np.random.default_rng(31)
+    W = wl.q4_0_matrix(g, N, K)
+    Wp = gpu_matrix(q.Q4_0, W, N, K)
+    base = wl.normal_f32(g, (16, K))
+    mags = np.float32(2.0) ** g.integers(-12, 13, size=(16, K)).astype(np.float32)
+    x = (base * mags).astype(np.float32)
+    x[1] = 0.0
+    x[2] *= np.float32(1e-36)
+    x[3] *= np.float32(1e25)
+    for nb in (1, 3, 16):
+        xs = np.ascontiguousarray(x[:nb])
+        y = _run_gemv(q.Q4_0, Wp, N, K, xs)
+        yr, A = oracle.gemv(q.Q4_0, W, N, K, xs)
+        assert np.all(np.isfinite(y))
+        assert_within(y, yr, tol_gemv(A, yr), f"x extremes nb={nb}")
+
+
 # ------------------------------------------------------------------------------------ fused ops
 
 @pytest.mark.parametrize("fmt,N,K,nb", [(q.Q4_0, 515, 2048, 1), (q.Q8_0, 2048, 1536, 4),
@@ -205,7 +243,9 @@ def test_gus_zero_gate_gives_zero():
 @pytest.mark.parametrize("fmt,N,K,nb,inplace", [(q.Q4_0, 2048, 8192, 1, False),
                                                 (q.Q4_0, 500, 2048, 2, True),
                                                 (q.Q8_0, 300, 1536, 4, True),
-                                                (q.Q4_K, 129, 2048, 1, False)])
+                                                (q.Q4_K, 129, 2048, 1, False),
+                                                (q.Q4_0, 333, 2048, 11, True),
+                                                (q.Q8_0, 9001, 1024, 16, False)])
 def test_qgemv_res_parity(fmt, N, K, nb, inplace):
     say(f"res fmt={fmt} N={N} K={K} nb={nb} inplace={inplace}")
     g = wl.rng(400 + fmt, N + nb)
@@ -245,7 +285,8 @@ def _argmax_check(logits, idx, yr, A, what):
 
 
 @pytest.mark.parametrize("fmt,N,K,nb", [(q.Q4_0, 5000, 2048, 1), (q.Q4_0, 4097, 1024, 4),
-                                        (q.Q8_0, 999, 1536, 2), (q.Q4_K, 777, 2048, 16)])
+                                        (q.Q8_0, 999, 1536, 2), (q.Q4_K, 777, 2048, 16),
+                                        (q.Q4_0, 20011, 512, 16), (q.Q8_0, 1500, 1024, 6)])
 def test_qgemv_argmax_parity(fmt, N, K, nb):
     say(f"argmax fmt={fmt} N={N} K={K} nb={nb}")
     g = wl.rng(500 + fmt, N + nb)
