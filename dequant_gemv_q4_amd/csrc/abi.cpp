@@ -10,6 +10,9 @@
 #include "../../include/qgemv.h"
 #include "qgemv_internal.h"
 
+#ifndef QG_BUF_MAX
+#define QG_BUF_MAX (1LL << 31)     // largest plane the buffer-addressed kernels take
+#endif
 #ifndef QG_MFMA_MIN_NB
 #define QG_MFMA_MIN_NB 5          // batch rows from which the matrix-core kernel takes a call
 #endif
@@ -241,11 +244,13 @@ static int run_gemv(int fmt, int epi, bool nrm, GemvArgs a, void *stream)
     int grid = 0, herr = 0;
     StreamPlan sp;
     MfmaPlan mp;
-    if (a.nb >= QG_MFMA_MIN_NB && plan_mfma(fmt, epi, nrm, a.N, a.K, a.nb, &mp) &&
+    // the streaming and matrix kernels address each plane with 32-bit buffer offsets
+    const bool small = a.N * a.qs_row < QG_BUF_MAX && a.N * a.sc_row < QG_BUF_MAX;
+    if (small && a.nb >= QG_MFMA_MIN_NB && plan_mfma(fmt, epi, nrm, a.N, a.K, a.nb, &mp) &&
         mp.grid <= QG_ARGMAX_MAX_GRID) {
         grid = mp.grid;
         herr = launch_mfma(fmt, epi, nrm, mp, a, stream);
-    } else if (plan_stream(fmt, epi, nrm, a.N, a.K, a.nb, &sp)) {
+    } else if (small && plan_stream(fmt, epi, nrm, a.N, a.K, a.nb, &sp)) {
         grid = sp.grid;
         herr = launch_stream(fmt, epi, nrm, sp.cpl, sp.pd, a, sp.grid, sp.lds, stream);
     } else {

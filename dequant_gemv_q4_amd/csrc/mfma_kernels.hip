@@ -197,13 +197,13 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
 #pragma unroll
         for (int m = 0; m < MATS; ++m) {
             const auto v = __builtin_amdgcn_raw_buffer_load_b128(
-                rq[m], (int)((uint32_t)n * (uint32_t)a.qs_row + 16u * (uint32_t)ch), 0, 0);
+                rq[m], (int)((uint32_t)n * (uint32_t)a.qs_row + 16u * (uint32_t)ch), 0, QG_WCPOL);
             sb.q[m][0] = v[0]; sb.q[m][1] = v[1]; sb.q[m][2] = v[2]; sb.q[m][3] = v[3];
 #pragma unroll
             for (int b = 0; b < BPS; ++b) {
                 const int blk = BPS * st + b < KB ? BPS * st + b : KB - 1;
                 sb.s[m][b] = __builtin_amdgcn_raw_buffer_load_b16(
-                    rsc[m], (int)((uint32_t)n * (uint32_t)a.sc_row + 2u * (uint32_t)blk), 0, 0);
+                    rsc[m], (int)((uint32_t)n * (uint32_t)a.sc_row + 2u * (uint32_t)blk), 0, QG_WCPOL);
             }
         }
     };

@@ -60,14 +60,17 @@ __host__ __device__ constexpr int rows_in_flight(int nb, int mats)
 #ifndef QG_WPE_NB1
 #define QG_WPE_NB1 4      // waves per SIMD the single-row-batch streaming kernel is sized for
 #endif
-#ifndef QG_X_LEAD
-#define QG_X_LEAD 1       // row groups a streaming wave issues before x is published in LDS
+#ifndef QG_WCPOL
+#define QG_WCPOL 0        // cache policy bits of the matrix-core kernel's weight loads
+#endif
+#ifndef QG_WCPOL_STREAM
+#define QG_WCPOL_STREAM 2 // the vector kernels' weight loads: non-temporal (x and gamma stay cached)
 #endif
 #ifndef QG_TILE_GROUPS
 #define QG_TILE_GROUPS 8  // consecutive row groups a streaming workgroup takes at a time
 #endif
 #ifndef QG_PD_MAX
-#define QG_PD_MAX 4       // most row groups a single-row-batch streaming wave keeps in flight
+#define QG_PD_MAX 2       // most row groups a single-row-batch streaming wave keeps in flight
 #endif
 __host__ __device__ constexpr int stream_rows(int nb, int cpl, int mats)
 {

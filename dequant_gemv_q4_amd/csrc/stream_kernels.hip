@@ -122,14 +122,20 @@ struct GroupBuf {
 
 // A packed matrix seen through two buffer resources (quant plane, scale plane).  Row offsets
 // are wave-uniform and go in the scalar offset; a lane's chunk offset is a constant VGPR.
+// A load whose (vector) offset is at or past the plane's size returns zeros without a memory
+// request: q_end / s_end (the sizes) are added to the offsets of loads that must move no data.
+// Row offsets go in the vector offset too, so that every load is range-checked.
 struct BufMat {
     __amdgpu_buffer_rsrc_t q, s;
+    uint32_t q_end, s_end;
 };
 
 __device__ __forceinline__ BufMat buf_mat(const uint8_t *qs, const uint8_t *sc, uint32_t q_bytes,
                                           uint32_t s_bytes)
 {
     BufMat m;
+    m.q_end = q_bytes;
+    m.s_end = s_bytes;
     m.q = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(qs), (short)0, (int)q_bytes,
                                             0x00020000);
     m.s = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(sc), (short)0, (int)s_bytes,
@@ -161,7 +167,8 @@ __device__ __forceinline__ LaneOff<CPL> lane_offsets(int lane, int C)
 }
 
 // Loads of one row group, unconditional so the compiler can count them exactly in its
-// s_waitcnt: rows past N reload row N - 1 (their results are dropped by the epilogue).
+// s_waitcnt.  A row outside [0, N) (a group index < 0 marks a group with no result) is loaded
+// out of range: zeros, no memory traffic; its results are dropped by the epilogue.
 template <int FMT, int CPL, int MATS, int R>
 __device__ __forceinline__ void load_group(GroupBuf<FMT, CPL, MATS, R> &b, const BufMat (&mat)[MATS],
                                            uint32_t qs_row, uint32_t sc_row, int64_t N,
@@ -170,24 +177,26 @@ __device__ __forceinline__ void load_group(GroupBuf<FMT, CPL, MATS, R> &b, const
 #pragma unroll
     for (int u = 0; u < R; ++u) {
         const int64_t nr = g * R + u;   // wave-uniform
-        const uint32_t n = (uint32_t)(nr < N ? nr : N - 1);
-        const uint32_t soq = n * qs_row, sos = n * sc_row;
+        const bool in = nr >= 0 && nr < N;
+        const uint32_t n = (uint32_t)(in ? nr : 0);
 #pragma unroll
         for (int m = 0; m < MATS; ++m)
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
-                const auto v = __builtin_amdgcn_raw_buffer_load_b128(mat[m].q, (int)lo.q[i],
-                                                                     (int)soq, 0);
+                const uint32_t roq = in ? n * qs_row : mat[m].q_end;
+                const uint32_t ros = in ? n * sc_row : mat[m].s_end;
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(mat[m].q,
+                                                                     (int)(lo.q[i] + roq), 0, QG_WCPOL_STREAM);
                 b.q[m][u][i] = make_uint4(v[0], v[1], v[2], v[3]);
                 // raw scale bytes: the lane mask is applied where they are used, so that no
                 // instruction touches a load's result before its group is decoded
                 if constexpr (FMT == FQ4_K) {
-                    const auto w = __builtin_amdgcn_raw_buffer_load_b128(mat[m].s, (int)lo.s[i],
-                                                                         (int)sos, 0);
+                    const auto w = __builtin_amdgcn_raw_buffer_load_b128(
+                        mat[m].s, (int)(lo.s[i] + ros), 0, QG_WCPOL_STREAM);
                     b.s[m][u][i] = make_uint4(w[0], w[1], w[2], w[3]);
                 } else {
-                    b.s[m][u][i] = __builtin_amdgcn_raw_buffer_load_b16(mat[m].s, (int)lo.s[i],
-                                                                         (int)sos, 0);
+                    b.s[m][u][i] = __builtin_amdgcn_raw_buffer_load_b16(
+                        mat[m].s, (int)(lo.s[i] + ros), 0, QG_WCPOL_STREAM);
                 }
             }
     }
@@ -198,25 +207,24 @@ __device__ __forceinline__ ChunkScale scale_of(uint16_t s, int) { ChunkScale cs;
 template <int FMT>
 __device__ __forceinline__ ChunkScale scale_of(const uint4 &s, int qpos) { return chunk_scale<FMT>(s, qpos); }
 
-// Workgroup-shared x.  Each thread loads a few float4s of the NB rows (and of gamma); the caller
-// then issues its first weight loads, and only after that are the x values written to LDS
-// (natural [row][K] order).  Loads retire in order, so the wait for the x loads leaves the
-// later weight loads in flight.  With NRM the stored value is x * gamma, and beside it the sum
-// of squares of each float4 of raw x, so every wave can form a row's norm in a fixed order.
+// Workgroup-shared x.  A few loader waves each load float4s base + stride * i of the NB rows
+// (and of gamma) and write them to LDS (natural [row][K] order).  With NRM the stored value is
+// x * gamma, and beside it the sum of squares of each float4 of raw x, so every wave can form a
+// row's norm in a fixed order; every float4 also gets its largest |value| (the row scale).
 template <int NB, bool NRM, int XPT>
 struct XStage {
     float4 v[XPT];
     float4 g[NRM ? XPT : 1];
 };
 
-template <int NB, bool NRM, int XPT, int NT>
+template <int NB, bool NRM, int XPT>
 __device__ __forceinline__ void xstage_issue(XStage<NB, NRM, XPT> &st, const float *x,
-                                             const float *gamma, int K4)
+                                             const float *gamma, int K4, int base, int stride)
 {
     const int tot = NB * K4;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-        const int f = (int)threadIdx.x + NT * i;
+        const int f = base + stride * i;
         const int fc = f < tot ? f : tot - 1;
         st.v[i] = reinterpret_cast<const float4 *>(x)[fc];
         if constexpr (NRM)
@@ -227,14 +235,14 @@ __device__ __forceinline__ void xstage_issue(XStage<NB, NRM, XPT> &st, const flo
 // Threads past the end store at the last index the value loaded for it (the same value as the
 // thread that owns it), so the stores, and the loads before them, are unconditional: a load
 // used only under a branch would be sunk below the weight loads.
-template <int NB, bool NRM, int XPT, int NT>
-__device__ __forceinline__ void xstage_store(const XStage<NB, NRM, XPT> &st, int K4, float4 *X4,
-                                             float *SS, float *MX)
+template <int NB, bool NRM, int XPT>
+__device__ __forceinline__ void xstage_store(const XStage<NB, NRM, XPT> &st, int K4, int base,
+                                             int stride, float4 *X4, float *SS, float *MX)
 {
     const int tot = NB * K4;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-        const int f = (int)threadIdx.x + NT * i;
+        const int f = base + stride * i;
         const int fc = f < tot ? f : tot - 1;
         float4 v = st.v[i];
         if constexpr (NRM) {
@@ -579,12 +587,16 @@ void k_stream(GemvArgs a)
     constexpr int R = P::R, IP = P::IP, WV = P::WV, NT = P::NT, ITEMS = P::ITEMS;
     constexpr int LG = IP == 1 ? 0 : IP == 2 ? 1 : IP == 4 ? 2 : IP == 8 ? 3 : IP == 16 ? 4 : 5;
     constexpr int TEAMS = WV / KS;
-    constexpr int XPT = (NB * KS * 64 * Fc<FMT>::XF4 + NT - 1) / NT;
+    // float4s of x each loader lane fetches: at least 4, and enough for 16 (8) waves to cover the
+    // longest row of this K class
+    constexpr int XPL0 = (NB * KS * Fc<FMT>::XF4 + WV - 1) / WV;
+    constexpr int XPL = XPL0 > 4 ? XPL0 : 4;
 
     extern __shared__ float4 lds4[];
     __shared__ unsigned long long s_key[NB * WV];
     __shared__ float s_comb[KS > 1 ? 2 : 1][WV][IP][MATS];
     __shared__ int s_next;
+    __shared__ int s_xcnt;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -614,10 +626,12 @@ void k_stream(GemvArgs a)
     auto gmap = [&](int c) -> int64_t {
         return ((int64_t)(c / TG) * gridDim.x + blockIdx.x) * TG + (c % TG);
     };
-    // a group that exists, for loads whose results are dropped
+    // the group of pool index c, or -1 (loaded out of range: no traffic, no result)
     auto gclamp = [&](int c) -> int64_t {
-        const int64_t g = gmap(c < pool ? c : pool - 1);
-        return g < T ? g : T - 1;
+        if (c >= pool)
+            return -1;
+        const int64_t g = gmap(c);
+        return g < T ? g : -1;
     };
 
     // residual operand of the (row, batch row) this lane reports, fetched with its group
@@ -626,7 +640,7 @@ void k_stream(GemvArgs a)
     const int my_u = my_item / NB, my_r = my_item % NB;
     auto load_res = [&](int gl) -> float {
         if constexpr (EPI == E_RES) {
-            const int64_t nr = gclamp(gl) * R + my_u;   // rows past N re-read row N - 1
+            const int64_t g = gclamp(gl), nr = (g < 0 ? 0 : g) * R + my_u;
             return a.res[(int64_t)my_r * a.N + (nr < a.N ? nr : a.N - 1)];
         } else {
             return 0.f;
@@ -638,31 +652,50 @@ void k_stream(GemvArgs a)
     // First group of each buffer: KS = 1, wave w takes p * WV + w; KS > 1, team t takes
     // t + p * TEAMS (its steps are t + k * TEAMS).
     auto first_group = [&](int p) -> int { return KS == 1 ? p * WV + wave : team + p * TEAMS; };
-    if (threadIdx.x == 0)
-        s_next = PD * WV;
 
-    // x (and gamma) first.  The workgroup barrier that publishes x in LDS comes before most of
-    // the weight stream: a wave that issues loads into full memory queues stalls at issue, and a
-    // barrier after its weight loads would hold the whole workgroup for its slowest issuer.
-    // QG_X_LEAD groups per wave are issued ahead of the barrier to cover the x latency.
-    XStage<NB, NRM, XPT> xs;
-    xstage_issue<NB, NRM, XPT, NT>(xs, a.x, a.gamma, K4);
-    __builtin_amdgcn_sched_barrier(0);
+    // x: the first xw waves fetch it (XPL float4s per lane) and publish it in LDS, counting
+    // themselves in s_xcnt; the other waves issue their weight loads at once and only then wait
+    // for the count, so the x latency runs under the weight latency.  (A workgroup barrier here
+    // would hold every wave until the slowest one had issued its weight loads.)
+    const int xw = (NB * K4 + 64 * XPL - 1) / (64 * XPL);
+    const bool xloader = wave < xw;
+    if (threadIdx.x == 0) {
+        s_next = PD * WV;
+        s_xcnt = 0;
+    }
+    __syncthreads();   // the counters are set (no memory wait: nothing is in flight yet)
     GroupBuf<FMT, 1, MATS, R> buf[PD];
     float resv[PD];
     int gcur[PD];
-    constexpr int LEAD = QG_X_LEAD < PD ? QG_X_LEAD : PD;
     // issued group by group, in the order the loop re-issues them, so that the wait counts the
     // compiler derives at the loop head hold on the first round too
+    auto issue_first = [&]() {
 #pragma unroll
-    for (int p = 0; p < LEAD; ++p) {
-        gcur[p] = first_group(p);
-        load_group(buf[p], mat, qrow, srow, a.N, lo, gclamp(gcur[p]));
-        resv[p] = load_res(gcur[p]);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int p = 0; p < PD; ++p) {
+            gcur[p] = first_group(p);
+            load_group(buf[p], mat, qrow, srow, a.N, lo, gclamp(gcur[p]));
+            resv[p] = load_res(gcur[p]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // Each path issues its own weight loads, so that no path inherits pending x loads from the
+    // other (the compiler's wait counts merge paths conservatively).
+    if (!xloader)
+        issue_first();
+    if (xloader) {
+        XStage<NB, NRM, XPL> xs;
+        xstage_issue<NB, NRM, XPL>(xs, a.x, a.gamma, K4, lane + 64 * wave, 64 * xw);
+        xstage_store<NB, NRM, XPL>(xs, K4, lane + 64 * wave, 64 * xw, X4, SS, MX);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0)
+            __hip_atomic_fetch_add(&s_xcnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        issue_first();
     }
-    xstage_store<NB, NRM, XPT, NT>(xs, K4, X4, SS, MX);
-    __syncthreads();
+    // wait for x: relaxed polling (an acquire would also wait for this wave's weight loads); LDS
+    // accesses of a wave complete in order, and every loader finished its stores before counting
+    while (__hip_atomic_load(&s_xcnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < xw)
+        __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
     XH<FMT, NB> xh;
     const WConst wk = w_const<FMT>();
     float rs[NB];
@@ -672,14 +705,6 @@ void k_stream(GemvArgs a)
 #pragma unroll
     for (int r = 1; r < NB; ++r)
         my_rs = my_r == r ? rs[r] : my_rs;
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int p = LEAD; p < PD; ++p) {
-        gcur[p] = first_group(p);
-        load_group(buf[p], mat, qrow, srow, a.N, lo, gclamp(gcur[p]));
-        resv[p] = load_res(gcur[p]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
 
     unsigned long long best = 0ull;
     // the value this lane's item contributes to y (residual, gated product), argmax bookkeeping
@@ -751,8 +776,8 @@ void k_stream(GemvArgs a)
                         nx = atomicAdd(&s_next, 1);
                     nx = __builtin_amdgcn_readfirstlane(nx);
                     const float res = resv[p];
-                    load_group(buf[p], mat, qrow, srow, a.N, lo, gclamp(nx < pool ? nx : gl));
-                    resv[p] = load_res(nx < pool ? nx : gl);
+                    load_group(buf[p], mat, qrow, srow, a.N, lo, gclamp(nx));
+                    resv[p] = load_res(nx);
                     if (gl < pool)
                         finish(acc, gl, 0, res);
                     gcur[p] = nx;
