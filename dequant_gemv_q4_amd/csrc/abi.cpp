@@ -110,6 +110,7 @@ static int stream_cpl(int fmt, int64_t K, int nb)
 struct StreamPlan {
     int cpl;     // waves a row's K is split over
     int pd;      // row groups in flight per wave
+    int tg_log2; // log2 of the row groups per tile
     int grid;
     size_t lds;
 };
@@ -123,7 +124,17 @@ static bool plan_stream(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb
     const int R = stream_rows(nb, 1, mats);
     const int64_t groups = (N + R - 1) / R;
     const int64_t items = (int64_t)R * nb;            // results per row group
-    const int64_t n_tiles = (groups + QG_TILE_GROUPS - 1) / QG_TILE_GROUPS;
+    // tiles of up to QG_TILE_GROUPS groups, smaller when that leaves CUs without a tile
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return false;
+    int tgl = 0;
+    while ((1 << (tgl + 1)) <= QG_TILE_GROUPS && (groups >> (tgl + 1)) >= cus)
+        ++tgl;
+    sp->tg_log2 = tgl;
+    const int64_t TGr = (int64_t)1 << tgl;
+    const int64_t n_tiles = (groups + TGr - 1) / TGr;
     // LDS: x of the nb rows (norm: x * gamma), one f32 max |.| per 4 (norm: and one square
     // sum per 4), then the results of the workgroup's pool of row groups
     const size_t x_lds = (size_t)nb * K * 4 + (size_t)nb * K + (nrm ? (size_t)nb * K : 0);
@@ -151,9 +162,9 @@ static bool plan_stream(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb
                 return false;
             grid = (int)min_grid;
         }
-        const int64_t pool_max = (n_tiles + grid - 1) / grid * QG_TILE_GROUPS;
+        const int64_t pool_max = (n_tiles + grid - 1) / grid * TGr;
         const size_t lds = x_lds + (size_t)pool_max * items * 4;
-        const int64_t per_team = (n_tiles / grid) * QG_TILE_GROUPS / teams;
+        const int64_t per_team = (n_tiles / grid) * TGr / teams;
         if (pd > 1 && per_team < pd)
             continue;
         const int fit = stream_resident_wgs(fmt, epi, nrm, cpl, nb, pd, lds, &waves);
@@ -163,7 +174,7 @@ static bool plan_stream(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb
             grid = fit;                               // the pool's LDS lowered the residency
         sp->pd = pd;
         sp->grid = grid;
-        sp->lds = x_lds + (size_t)((n_tiles + grid - 1) / grid * QG_TILE_GROUPS) * items * 4;
+        sp->lds = x_lds + (size_t)((n_tiles + grid - 1) / grid * TGr) * items * 4;
         if (stream_resident_wgs(fmt, epi, nrm, cpl, nb, pd, sp->lds, &waves) <= 0)
             continue;
         return true;
@@ -252,6 +263,7 @@ static int run_gemv(int fmt, int epi, bool nrm, GemvArgs a, void *stream)
         herr = launch_mfma(fmt, epi, nrm, mp, a, stream);
     } else if (small && plan_stream(fmt, epi, nrm, a.N, a.K, a.nb, &sp)) {
         grid = sp.grid;
+        a.tg_log2 = sp.tg_log2;
         herr = launch_stream(fmt, epi, nrm, sp.cpl, sp.pd, a, sp.grid, sp.lds, stream);
     } else {
         Plan p;

@@ -67,7 +67,7 @@ __host__ __device__ constexpr int rows_in_flight(int nb, int mats)
 #define QG_WCPOL_STREAM 2 // the vector kernels' weight loads: non-temporal (x and gamma stay cached)
 #endif
 #ifndef QG_TILE_GROUPS
-#define QG_TILE_GROUPS 8  // consecutive row groups a streaming workgroup takes at a time
+#define QG_TILE_GROUPS 8  // most consecutive row groups a streaming workgroup takes at a time
 #endif
 #ifndef QG_PD_MAX
 #define QG_PD_MAX 2       // most row groups a single-row-batch streaming wave keeps in flight
@@ -107,6 +107,7 @@ struct GemvArgs {
     int n_kt;                   // tiles per row
     int rows_per_step;          // rows one workgroup finishes per step
     int64_t n_steps;            // workgroup steps covering N rows
+    int tg_log2;                // streaming kernels: log2 of the row groups per tile
 };
 
 // Arguments of the routed-expert kernels.

@@ -618,13 +618,13 @@ void k_stream(GemvArgs a)
 
     // this workgroup's pool of row groups: pool-local index c is group gmap(c); indices at or
     // past `pool` (and groups past T in the last tile) carry no result
-    constexpr int TG = QG_TILE_GROUPS;
+    const int tgl = a.tg_log2, TG = 1 << tgl;    // groups per tile (1..8, set by the host)
     const int64_t T = (a.N + R - 1) / R;
-    const int64_t n_tiles = (T + TG - 1) / TG;
-    const int pool = blockIdx.x < n_tiles
-                         ? (int)((n_tiles - 1 - blockIdx.x) / gridDim.x + 1) * TG : 0;
+    const int n_tiles = (int)((T + TG - 1) >> tgl);
+    const int pool = (int)blockIdx.x < n_tiles
+                         ? ((n_tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1) << tgl : 0;
     auto gmap = [&](int c) -> int64_t {
-        return ((int64_t)(c / TG) * gridDim.x + blockIdx.x) * TG + (c % TG);
+        return ((int64_t)((c >> tgl) * (int)gridDim.x + (int)blockIdx.x) << tgl) + (c & (TG - 1));
     };
     // the group of pool index c, or -1 (loaded out of range: no traffic, no result)
     auto gclamp = [&](int c) -> int64_t {
