@@ -182,18 +182,54 @@ static bool plan_stream(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb
     return false;   // too much LDS for every variant: the tiled kernel takes the call
 }
 
-// Routed experts: chunks per lane (1, 2 or 4 of 16 bytes per row) and how many routed rows are
-// decoded together (their x sits in registers: rows x chunks <= 4).
-static bool plan_moe(int fmt, int64_t N, int64_t K, int *cpl, int *group_max, size_t *lds,
-                     int64_t *n_tiles)
+// Routed experts: 16-byte chunks per lane (1, 2 or 4 per row; the kernel holds 4 / cpl x rows
+// per set in registers), groups in flight per wave, workgroups, result slots and LDS.  The grid
+// has at least nb * topk workgroups, so that a workgroup's range (at most nb * topk sets of GS
+// row groups, split evenly) spans at most two sets; at least the resident count; and enough that
+// a range's results fit the result LDS.  query = false skips the device query (validation only).
+struct MoePlan {
+    int cpl, pd, grid, pool_max;
+    size_t lds;
+};
+
+static bool plan_moe(int fmt, int64_t n_exp, int64_t N, int64_t K, int nb, int topk, bool query,
+                     MoePlan *p)
 {
-    const int64_t C = (fmt == FQ8_0 ? K : K / 2) / 16;
-    *cpl = C <= 64 ? 1 : C <= 128 ? 2 : C <= 256 ? 4 : 0;
-    if (!*cpl)
+    if (n_exp < 1 || n_exp > QG_MOE_EXPERTS_MAX)   // the per-expert counts live in LDS
         return false;
-    *group_max = 4 / *cpl;
-    *lds = 0;
-    *n_tiles = (N + QG_MOE_TILE_ROWS - 1) / QG_MOE_TILE_ROWS;
+    const int64_t C = (fmt == FQ8_0 ? K : K / 2) / 16;
+    p->cpl = C <= 64 ? 1 : C <= 128 ? 2 : C <= 256 ? 4 : 0;
+    if (!p->cpl)
+        return false;
+    const int nbx = 4 / p->cpl;
+    const int R = stream_rows(nbx, p->cpl, 1);
+    const int64_t GS = (N + R - 1) / R;
+    const int64_t P = (int64_t)nb * topk;
+    if (P * GS > 0x7fffffffLL)
+        return false;
+    p->pd = QG_MOE_PD;
+    // expert pair masks and set bases; two sets' x rows as f16 pairs and offset sums (uint4s per
+    // row, chunk slot and lane: NP / 4 + 1 with NP = 16 pairs per chunk, 8 for Q8_0); then the
+    // rows' raw copies, whose space the results reuse
+    const int nq4 = (fmt == FQ8_0 ? 8 : 16) / 4 + 1;
+    const size_t fixed_lds = (size_t)n_exp * 16 + (size_t)(n_exp + 3) / 4 * 16 +
+                             (size_t)2 * nbx * p->cpl * nq4 * 64 * 16;
+    const size_t raw_lds = (size_t)2 * nbx * (K / 4) * 16;
+    const int64_t itx = (int64_t)R * nbx;
+    const int64_t budget = QG_MOE_POOL_LDS / (itx * 4);   // result groups the LDS may hold
+    const int resident = query ? moe_resident_wgs(fmt, p->cpl, p->pd,
+                                                  fixed_lds + (raw_lds > QG_MOE_POOL_LDS
+                                                                   ? raw_lds : QG_MOE_POOL_LDS))
+                               : 0;
+    int64_t grid = resident > P ? resident : P;
+    const int64_t need = (P * GS + budget - 1) / budget;
+    grid = grid > need ? grid : need;
+    if (grid > 0x7fffffffLL)
+        return false;
+    p->grid = (int)grid;
+    p->pool_max = (int)((P * GS + grid - 1) / grid);
+    const size_t pool_lds = (size_t)p->pool_max * itx * 4;
+    p->lds = fixed_lds + (raw_lds > pool_lds ? raw_lds : pool_lds);
     return true;
 }
 
@@ -350,11 +386,9 @@ int64_t qgemv_workspace_bytes(int op, int fmt, int64_t N, int64_t K, int nb, int
     case QG_OP_ARGMAX:
         return ws_argmax_bytes(nb);
     case QG_OP_MOE: {
-        int cpl, gmax;
-        size_t lds;
-        int64_t n_tiles;
+        MoePlan mp;
         if (n_exp < 1 || topk < 1 || topk > QG_MAX_TOPK ||
-            !plan_moe(fmt, N, K, &cpl, &gmax, &lds, &n_tiles))
+            !plan_moe(fmt, n_exp, N, K, nb, topk, false, &mp))
             return -1;
         return ws_moe_bytes(N, nb, topk);
     }
@@ -488,10 +522,10 @@ int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t 
         return QG_ERR_SHAPE;
     if (!al(ids, 4) || !al(wts, 4) || !al(ws, 256))
         return QG_ERR_ALIGN;
-    int cpl, gmax;
-    size_t lds;
-    int64_t n_tiles;
-    if (!plan_moe(fmt, N, K, &cpl, &gmax, &lds, &n_tiles))
+    MoePlan mp;
+    // every expert's planes are addressed through 32-bit buffer offsets
+    if (N * L.qs_row >= QG_BUF_MAX || N * L.sc_row >= QG_BUF_MAX ||
+        !plan_moe(fmt, n_exp, N, K, nb, topk, true, &mp))
         return QG_ERR_SHAPE;
     if ((int64_t)ws_bytes < ws_moe_bytes(N, nb, topk))
         return QG_ERR_WORKSPACE;
@@ -499,9 +533,6 @@ int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t 
     if (overlap(y, yb, W_experts, LE.total) || overlap(y, yb, ws, (int64_t)ws_bytes) ||
         overlap(y, yb, ids, (int64_t)nb * topk * 4) || overlap(y, yb, wts, (int64_t)nb * topk * 4))
         return QG_ERR_ALIAS;
-    const int64_t grid = n_exp * n_tiles;
-    if (grid > 0x7fffffffLL)
-        return QG_ERR_SHAPE;
     MoeArgs a;
     memset(&a, 0, sizeof(a));
     a.qs = static_cast<const uint8_t *>(W_experts);
@@ -520,10 +551,8 @@ int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t 
     a.sc_row = L.sc_row;
     a.nb = nb;
     a.topk = topk;
-    a.tile_rows = QG_MOE_TILE_ROWS;
-    a.group_max = gmax;
-    a.n_tiles = n_tiles;
-    return launch_status(launch_moe(fmt, cpl, a, (int)grid, lds, stream));
+    a.pool_max = mp.pool_max;
+    return launch_status(launch_moe(fmt, mp.cpl, mp.pd, a, mp.grid, mp.lds, stream));
 }
 
 int qgemv_moe_error(const void *ws, int64_t n_exp, int64_t N, int64_t K, int fmt, int *flag,
@@ -533,10 +562,8 @@ int qgemv_moe_error(const void *ws, int64_t n_exp, int64_t N, int64_t K, int fmt
         return QG_ERR_NULL;
     if (!fmt_valid(fmt))
         return QG_ERR_FORMAT;
-    int cpl, gmax;
-    size_t lds;
-    int64_t n_tiles;
-    if (n_exp < 1 || !plan_moe(fmt, N, K, &cpl, &gmax, &lds, &n_tiles))
+    MoePlan mp;
+    if (!plan_moe(fmt, n_exp, N, K, 1, 1, false, &mp))
         return QG_ERR_SHAPE;
     const uint8_t *errp = static_cast<const uint8_t *>(ws);
     unsigned int v = 0;

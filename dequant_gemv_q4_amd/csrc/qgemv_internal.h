@@ -15,9 +15,22 @@ enum Epi { E_STORE = 0, E_RES = 1, E_GUS = 2, E_ARGMAX = 3 };
 
 // Routed experts: at most this many (row, slot) pairs per call (16 rows x top-8).
 #define QG_PAIRS_MAX 128
-// Routed experts: output rows of one expert per workgroup.
-#ifndef QG_MOE_TILE_ROWS
-#define QG_MOE_TILE_ROWS 128
+// Routed experts: threads per workgroup and the waves per SIMD the register budget allows.
+#ifndef QG_MOE_THREADS
+#define QG_MOE_THREADS 512
+#endif
+#ifndef QG_MOE_WPE
+#define QG_MOE_WPE 2
+#endif
+#ifndef QG_MOE_PD
+#define QG_MOE_PD 2       // row groups a routed-expert wave keeps in flight (2 or 4)
+#endif
+// Routed experts: most experts a call may have (a 128-bit pair mask and a count per expert are
+// kept in LDS; at most 4 experts per thread in the scan).
+#define QG_MOE_EXPERTS_MAX 1024
+// Routed experts: most LDS bytes for the results a workgroup collects.
+#ifndef QG_MOE_POOL_LDS
+#define QG_MOE_POOL_LDS 32768
 #endif
 
 // Packed device layout of one N x K matrix: a plane of quant bytes (row n at n * qs_row) and a
@@ -118,13 +131,11 @@ struct MoeArgs {
     const float *wts;           // [nb][topk]
     float *y;                   // [nb][N]
     float *part;                // workspace: [nb][topk][N] partial outputs
-    unsigned int *err;          // workspace: sticky bad-id flag
+    unsigned int *err;          // workspace: sticky flag (bit 0: an expert id out of range)
     int64_t n_exp, N, K;
     int64_t qs_row, sc_row;
     int nb, topk;
-    int tile_rows;              // output rows of one expert per workgroup
-    int group_max;              // routed rows staged together (1, 2 or 4)
-    int64_t n_tiles;            // output-row tiles per expert
+    int pool_max;               // most row groups one workgroup's range may hold
 };
 
 // Launch helpers (gemv_kernels.hip).  Return a hipError_t value (0 = success).
@@ -133,7 +144,10 @@ int launch_gemv(int fmt, int epi, bool nrm, const GemvArgs &a, int grid, size_t 
                 void *stream);
 int launch_stream(int fmt, int epi, bool nrm, int cpl, int pd, const GemvArgs &a, int grid,
                   size_t lds_bytes, void *stream);
-int launch_moe(int fmt, int cpl, const MoeArgs &a, int grid, size_t lds_bytes, void *stream);
+// Routed experts: the expert kernel (x rows per set 4 / cpl, pd groups in flight per wave), then
+// the combine.
+int launch_moe(int fmt, int cpl, int pd, const MoeArgs &a, int grid, size_t lds_bytes,
+               void *stream);
 // Row-batch kernel on the matrix cores (mfma_kernels.hip): persistent workgroups over groups of
 // 16-row tiles.
 struct MfmaPlan {
@@ -150,5 +164,6 @@ int launch_argmax_fold(const unsigned long long *part, int n_part, int nb, int32
 // query fails).
 int stream_resident_wgs(int fmt, int epi, bool nrm, int cpl, int nb, int pd, size_t lds_bytes,
                         int *waves);
+int moe_resident_wgs(int fmt, int cpl, int pd, size_t lds_bytes);
 
 }  // namespace qg

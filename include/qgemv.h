@@ -119,13 +119,15 @@ int qgemv_argmax(int fmt, const void *W, int64_t N, int64_t K, const float *x, i
  * step; module experts.)  W_experts holds n_exp packed N x K matrices back to back (pack them
  * as one matrix of n_exp * N rows).  ids int32 [nb][topk]; wts f32 [nb][topk].  An id outside
  * [0, n_exp) adds nothing to its row and sets a sticky flag in the workspace that
- * qgemv_moe_error reports.  Needs a workspace. */
+ * qgemv_moe_error reports.  Limits: n_exp <= 1024 (QG_ERR_SHAPE beyond), and each expert's
+ * quant plane (N * K/2 bytes, Q8_0 N * K) under 2 GiB.  Needs a workspace. */
 int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t K, const float *x,
               int nb, const int32_t *ids, const float *wts, int topk, float *y, void *ws,
               size_t ws_bytes, void *stream);
 
 /* Reads and clears the bad-expert-id flag qgemv_moe leaves in its workspace (*flag = 1 if any id
- * of an earlier call on this workspace was out of range).  Unlike every other entry point this
+ * of an earlier call on this workspace was out of range; any other nonzero value means a launch
+ * broke the kernel's own sizing contract, a library bug).  Unlike every other entry point this
  * one SYNCHRONIZES `stream` (it copies the flag to the host).  The sizes must be those the
  * workspace was sized for. */
 int qgemv_moe_error(const void *ws, int64_t n_exp, int64_t N, int64_t K, int fmt, int *flag,
