@@ -135,9 +135,9 @@ static bool plan_stream(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb
     sp->tg_log2 = tgl;
     const int64_t TGr = (int64_t)1 << tgl;
     const int64_t n_tiles = (groups + TGr - 1) / TGr;
-    // LDS: x of the nb rows (norm: x * gamma), one f32 max |.| per 4 (norm: and one square
-    // sum per 4), then the results of the workgroup's pool of row groups
-    const size_t x_lds = (size_t)nb * K * 4 + (size_t)nb * K + (nrm ? (size_t)nb * K : 0);
+    // LDS: x of the nb rows (norm: x * gamma; and one f32 square sum per 4), then the results
+    // of the workgroup's pool of row groups
+    const size_t x_lds = (size_t)nb * K * 4 + (nrm ? (size_t)nb * K : 0);
     sp->cpl = cpl;
     // The deepest prefetch whose own grid (one pass of resident workgroups) still gives every
     // team that many groups.  Each variant has its own register use, hence its own residency.

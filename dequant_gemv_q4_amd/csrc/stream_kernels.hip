@@ -1,20 +1,19 @@
 // stream_kernels.hip -- the streaming dequant-GEMV kernels of libqgemv for gfx950.
 //
-// One wave64 owns whole rows: lane l takes the 16-byte chunks l, l + 64, ... (CPL per row) of
-// R rows at a time, so every global load instruction reads 1 KB contiguous.  Each wave
-// double-buffers its loads: the quants and scales of its next row group are in flight while
-// it decodes and FMAs the current one.  x (or rmsnorm(x)) is staged once per workgroup in
-// LDS and, when small enough, held in registers for the whole kernel.  R x NB partial sums
-// leave the wave through a transposed butterfly (each exchange halves the number of values a
-// lane carries), and one lane per (row, batch row) runs the epilogue.
+// One wave64 owns whole rows: lane l takes the 16-byte quant chunk l (and l + 64, ... when a
+// row is split over several waves) of R rows at a time, so every weight load instruction reads
+// 1 KB contiguous.  Each wave keeps PD row groups in flight: the quants and scales of its next
+// groups stream in while it decodes the current one.  x (or x * gamma for the norm prologue) is
+// staged once per workgroup in LDS; each lane turns its own chunk of x into f16 pairs once.
+// R x NB partial sums leave the wave through a transposed butterfly (each exchange halves the
+// number of values a lane carries), and one lane per (row, batch row) runs the epilogue.
 //
-// Q4_0 decode: byte b_j of a block holds element j (low nibble lo_j) and element j + 16 (high
-// nibble hi_j).  Since hi_j = (b_j - lo_j) / 16,
-//     lo_j x_j + hi_j x_{j+16} = lo_j u_j + b_j v_j,  u_j = x_j - x_{j+16}/16,  v_j = x_{j+16}/16,
-// so a dword of nibbles costs one mask and eight byte converts (v_cvt_f32_ubyteN) before its
-// eight FMAs.  x is staged as (u, v).  The -8 offset of Q4_0 ("Crate inferencelayer" docs,
-// q4_0_to_q8_0n: q8 = nib - 8) is folded into S' = sum_j (u_j + 17 v_j), accumulated in the
-// dot's own order, so eight-valued nibbles (b = 0x88) give exactly 0.
+// Decode: a Q4_0 byte holds element j in its low nibble and element j + 16 in its high nibble
+// (GGUF order).  Nibbles become exact f16 weights by an and-or into the mantissa of 1024.0, two
+// per instruction, and meet x through v_dot2_f32_f16 (two f16 products, exact in f32, added to an
+// f32 accumulator).  The -8 offset of Q4_0 ("Crate inferencelayer" docs, q4_0_to_q8_0n:
+// q8 = nib - 8) and the 1024 mantissa offset are removed by subtracting the same dot chain run
+// on the constant weight pattern, so eight-valued nibbles (b = 0x88) give exactly 0.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -238,7 +237,7 @@ __device__ __forceinline__ void xstage_issue(XStage<NB, NRM, XPT> &st, const flo
 // used only under a branch would be sunk below the weight loads.
 template <int NB, bool NRM, int XPT>
 __device__ __forceinline__ void xstage_store(const XStage<NB, NRM, XPT> &st, int K4, int base,
-                                             int stride, float4 *X4, float *SS, float *MX)
+                                             int stride, float4 *X4, float *SS)
 {
     const int tot = NB * K4;
 #pragma unroll
@@ -256,7 +255,6 @@ __device__ __forceinline__ void xstage_store(const XStage<NB, NRM, XPT> &st, int
             v = make_float4(v.x * g.x, v.y * g.y, v.z * g.z, v.w * g.w);
         }
         X4[fc] = v;
-        MX[fc] = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
     }
 }
 
@@ -266,9 +264,10 @@ __device__ __forceinline__ void xstage_store(const XStage<NB, NRM, XPT> &st, int
 // f32) added to an f32 accumulator.  Weights: a nibble n placed in the mantissa of the f16
 // 0x6400 (1024.0) reads as 1024 + n, and a nibble in mantissa bits 4..7 as 1024 + 16 n, so one
 // and-or per dword yields two weights (exact); the x operand of a high-nibble pair carries a
-// factor 1/16.  x: each row is scaled by a power of two that puts its largest |value| in
-// [2^14, 2^15), then rounded to f16 (relative error at most 2^-11, far inside the stated
-// 1e-3 * sum|w x| bound); the scale is undone, exactly, on the row sums.  The 1024 offsets (and
+// factor 1/16.  x: the values of each chunk (the 16 or 32 x elements one 16-byte quant chunk
+// multiplies) are scaled by a power of two that puts their largest |value| in [2^14, 2^15), then
+// rounded to f16 (relative error at most 2^-11, far inside the stated 1e-3 * sum|w x| bound); the
+// scale is undone, exactly, on the chunk's partial sums.  The 1024 offsets (and
 // Q4_0's -8, Q8_0's +128 bias) are removed by subtracting the same dot chain run on the constant
 // weight pattern (n = 8, u = 128, n = 0), in the same order, so all-offset blocks give exactly 0.
 typedef _Float16 qg_h2 __attribute__((ext_vector_type(2)));
@@ -423,51 +422,55 @@ __device__ __forceinline__ void x_pairs(const float4 *xv, float sc, uint32_t *p,
     }
 }
 
-// The lane's chunk c of every batch row as f16 pairs, and the factor that undoes each row's
-// scale (rs[r], exact: a power of two).  With NRM the row's 1/sqrt(mean x^2 + eps) is formed
-// from the staged per-float4 squares (lane-strided partial sums, then a butterfly: the same order
-// whatever the batch size) and folded into the scale.
-template <int FMT, int NB, bool NRM>
-__device__ __forceinline__ void xh_from_lds(XH<FMT, NB> &xh, float (&rs)[NB], const float4 *X4,
-                                            const float *SS, const float *MX, float eps, int K4,
-                                            int C, int c, int lane, int bp32)
+// The lane's chunk c of every batch row as f16 pairs, each chunk scaled by the power of two that
+// puts its largest |value| in [2^14, 2^15), and the factor that undoes that scale (un[r], exact).
+// The scale depends on the chunk's own 16 or 32 values only, so no wave waits for a reduction
+// over the row before its first dot product.
+template <int FMT, int NB>
+__device__ __forceinline__ void xh_from_lds(XH<FMT, NB> &xh, float (&un)[NB], const float4 *X4,
+                                            int K4, int C, int c)
 {
     constexpr int XF4 = Fc<FMT>::XF4;
     const int cx = c < C ? c : C - 1;
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
-        float inv = 1.0f;
-        if constexpr (NRM) {
-            float ss = 0.f;
-            for (int e = lane; e < K4; e += 64)
-                ss += SS[r * K4 + e];
-            ss += xor_lane<32>(ss, bp32);
-            ss += xor_lane<16>(ss, bp32);
-            ss += xor_lane<8>(ss, bp32);
-            ss += xor_lane<4>(ss, bp32);
-            ss += xor_lane<2>(ss, bp32);
-            ss += xor_lane<1>(ss, bp32);
-            inv = 1.0f / sqrtf(ss / (float)(4 * K4) + eps);
-        }
-        float mx = 0.f;
-        for (int e = lane; e < K4; e += 64)
-            mx = fmaxf(mx, MX[r * K4 + e]);
-        mx = fmaxf(mx, xor_lane<32>(mx, bp32));
-        mx = fmaxf(mx, xor_lane<16>(mx, bp32));
-        mx = fmaxf(mx, xor_lane<8>(mx, bp32));
-        mx = fmaxf(mx, xor_lane<4>(mx, bp32));
-        mx = fmaxf(mx, xor_lane<2>(mx, bp32));
-        mx = fmaxf(mx, xor_lane<1>(mx, bp32));
-        int e2 = 0;
-        frexpf(mx * inv, &e2);                              // max |x| = f 2^e2, f in [0.5, 1)
-        const int sk = 15 - e2 < 127 ? 15 - e2 : 127;       // 2^sk stays a finite f32
-        const float s = ldexpf(1.0f, sk);
-        rs[r] = ldexpf(1.0f, -sk);
         float4 xv[XF4];
 #pragma unroll
         for (int j = 0; j < XF4; ++j)
             xv[j] = X4[(size_t)r * K4 + chunk_elem<FMT>(cx, j) / 4];
-        x_pairs<FMT>(xv, inv * s, xh.p[r][0], xh.z[r][0]);
+        float mx = 0.f;
+#pragma unroll
+        for (int j = 0; j < XF4; ++j)
+            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[j].x), fabsf(xv[j].y)),
+                                 fmaxf(fabsf(xv[j].z), fabsf(xv[j].w))));
+        int e2 = 0;
+        frexpf(mx, &e2);                                    // max |x| = f 2^e2, f in [0.5, 1)
+        const int sk = 15 - e2 < 127 ? 15 - e2 : 127;       // 2^sk stays a finite f32
+        un[r] = ldexpf(1.0f, -sk);
+        x_pairs<FMT>(xv, ldexpf(1.0f, sk), xh.p[r][0], xh.z[r][0]);
+    }
+}
+
+// 1 / sqrt(mean x^2 + eps) of each batch row, from the staged per-float4 squares: lane-strided
+// partial sums, then a butterfly, so the order is the same whatever the batch size and every wave
+// gets the same value.
+template <int NB>
+__device__ __forceinline__ void row_inv_rms(float (&inv)[NB], const float *SS, float eps, int K4,
+                                            int lane, int bp32)
+{
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+        float ss = 0.f;
+#pragma unroll 4
+        for (int e = lane; e < K4; e += 64)
+            ss += SS[r * K4 + e];
+        ss += xor_lane<32>(ss, bp32);
+        ss += xor_lane<16>(ss, bp32);
+        ss += xor_lane<8>(ss, bp32);
+        ss += xor_lane<4>(ss, bp32);
+        ss += xor_lane<2>(ss, bp32);
+        ss += xor_lane<1>(ss, bp32);
+        inv[r] = 1.0f / sqrtf(ss / (float)(4 * K4) + eps);
     }
 }
 
@@ -564,8 +567,7 @@ void k_stream(GemvArgs a)
     const int C = (int)(a.qs_row / 16);
     const int K4 = (int)(a.K / 4);
     float4 *X4 = lds4;                                              // x (norm: x * gamma)
-    float *MX = reinterpret_cast<float *>(lds4 + (size_t)NB * K4);  // max |.| of each float4
-    float *SS = MX + NB * K4;                                       // norm: float4 squares
+    float *SS = reinterpret_cast<float *>(lds4 + (size_t)NB * K4);  // norm: float4 squares
     float *s_out = SS + (NRM ? NB * K4 : 0);                        // [pool][ITEMS] results
 
     const uint32_t qbytes = (uint32_t)(a.N * a.qs_row), sbytes = (uint32_t)(a.N * a.sc_row);
@@ -645,7 +647,7 @@ void k_stream(GemvArgs a)
     if (xloader) {
         XStage<NB, NRM, XPL> xs;
         xstage_issue<NB, NRM, XPL>(xs, a.x, a.gamma, K4, lane + 64 * wave, 64 * xw);
-        xstage_store<NB, NRM, XPL>(xs, K4, lane + 64 * wave, 64 * xw, X4, SS, MX);
+        xstage_store<NB, NRM, XPL>(xs, K4, lane + 64 * wave, 64 * xw, X4, SS);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         if (lane == 0)
             __hip_atomic_fetch_add(&s_xcnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -658,13 +660,18 @@ void k_stream(GemvArgs a)
     asm volatile("" ::: "memory");
     XH<FMT, NB> xh;
     const WConst wk = w_const<FMT>();
-    float rs[NB];
-    xh_from_lds<FMT, NB, NRM>(xh, rs, X4, SS, MX, a.eps, K4, C, cme, lane, bp32);
-    // the scale this lane's reported item undoes
-    float my_rs = rs[0];
+    float un[NB];   // factor undoing the scale of this lane's x chunk, per batch row
+    xh_from_lds<FMT, NB>(xh, un, X4, K4, C, cme);
+    // the row factor this lane's reported item takes: 1 / rms of its batch row with the norm
+    float my_inv = 1.0f;
+    if constexpr (NRM) {
+        float inv[NB];
+        row_inv_rms<NB>(inv, SS, a.eps, K4, lane, bp32);
+        my_inv = inv[0];
 #pragma unroll
-    for (int r = 1; r < NB; ++r)
-        my_rs = my_r == r ? rs[r] : my_rs;
+        for (int r = 1; r < NB; ++r)
+            my_inv = my_r == r ? inv[r] : my_inv;
+    }
 
     unsigned long long best = 0ull;
     // the value this lane's item contributes to y (residual, gated product), argmax bookkeeping
@@ -691,10 +698,19 @@ void k_stream(GemvArgs a)
     };
     // reduce one computed group (gl in the pool); with KS > 1 combine the slices through LDS
     auto finish = [&](float (&acc)[IP][MATS], int gl, int par, float res) {
-        xpose_reduce<IP, MATS>(acc, lane, bp32);
+        // undo the chunk scales (exact: powers of two), then sum over the lanes
 #pragma unroll
-        for (int m = 0; m < MATS; ++m)
-            acc[0][m] *= my_rs;
+        for (int u = 0; u < R; ++u)
+#pragma unroll
+            for (int r = 0; r < NB; ++r)
+#pragma unroll
+                for (int m = 0; m < MATS; ++m)
+                    acc[u * NB + r][m] *= un[r];
+        xpose_reduce<IP, MATS>(acc, lane, bp32);
+        if constexpr (NRM)
+#pragma unroll
+            for (int m = 0; m < MATS; ++m)
+                acc[0][m] *= my_inv;
         if constexpr (KS == 1) {
             epilogue(acc[0], gl, res);
         } else {
