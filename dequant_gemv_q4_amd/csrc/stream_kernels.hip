@@ -560,6 +560,9 @@ void k_stream(GemvArgs a)
     __shared__ float s_comb[KS > 1 ? 2 : 1][WV][IP][MATS];
     __shared__ int s_next;
     __shared__ int s_xcnt;
+    // norm: bits of 1 / rms of each batch row with the sign bit flipped, published by the last
+    // loader wave; 0 = not yet (1 / sqrt(y) is never -0.0, so the value is its own ready flag)
+    __shared__ unsigned s_inv[NB];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -624,6 +627,9 @@ void k_stream(GemvArgs a)
     if (threadIdx.x == 0) {
         s_next = PD * WV;
         s_xcnt = 0;
+#pragma unroll
+        for (int r = 0; r < NB; ++r)
+            s_inv[r] = 0u;
     }
     __syncthreads();   // the counters are set (no memory wait: nothing is in flight yet)
     GroupBuf<FMT, 1, MATS, R> buf[PD];
@@ -649,9 +655,27 @@ void k_stream(GemvArgs a)
         xstage_issue<NB, NRM, XPL>(xs, a.x, a.gamma, K4, lane + 64 * wave, 64 * xw);
         xstage_store<NB, NRM, XPL>(xs, K4, lane + 64 * wave, 64 * xw, X4, SS);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        int seen = 0;
         if (lane == 0)
-            __hip_atomic_fetch_add(&s_xcnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            seen = __hip_atomic_fetch_add(&s_xcnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        seen = __builtin_amdgcn_readfirstlane(seen);
         issue_first();
+        if constexpr (NRM) {
+            // The last loader to count forms every row's 1 / rms once, after its weight loads are
+            // out; the other waves need it only at their first epilogue.  Every other loader
+            // finished its stores before counting, and LDS accesses complete in order.
+            if (seen == xw - 1) {
+                asm volatile("" ::: "memory");
+                float inv[NB];
+                row_inv_rms<NB>(inv, SS, a.eps, K4, lane, bp32);
+                if (lane == 0)
+#pragma unroll
+                    for (int r = 0; r < NB; ++r)
+                        __hip_atomic_store(&s_inv[r], __float_as_uint(inv[r]) ^ 0x80000000u,
+                                           __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
     }
     // wait for x: relaxed polling (an acquire would also wait for this wave's weight loads); LDS
     // accesses of a wave complete in order, and every loader finished its stores before counting
@@ -662,16 +686,10 @@ void k_stream(GemvArgs a)
     const WConst wk = w_const<FMT>();
     float un[NB];   // factor undoing the scale of this lane's x chunk, per batch row
     xh_from_lds<FMT, NB>(xh, un, X4, K4, C, cme);
-    // the row factor this lane's reported item takes: 1 / rms of its batch row with the norm
+    // the row factor this lane's reported item takes: 1 / rms of its batch row with the norm,
+    // read at the first epilogue (my_inv_ready)
     float my_inv = 1.0f;
-    if constexpr (NRM) {
-        float inv[NB];
-        row_inv_rms<NB>(inv, SS, a.eps, K4, lane, bp32);
-        my_inv = inv[0];
-#pragma unroll
-        for (int r = 1; r < NB; ++r)
-            my_inv = my_r == r ? inv[r] : my_inv;
-    }
+    bool my_inv_ready = !NRM;
 
     unsigned long long best = 0ull;
     // the value this lane's item contributes to y (residual, gated product), argmax bookkeeping
@@ -707,10 +725,24 @@ void k_stream(GemvArgs a)
                 for (int m = 0; m < MATS; ++m)
                     acc[u * NB + r][m] *= un[r];
         xpose_reduce<IP, MATS>(acc, lane, bp32);
-        if constexpr (NRM)
+        if constexpr (NRM) {
+            if (!my_inv_ready) {   // wave-uniform
+                unsigned bits[NB];
+#pragma unroll
+                for (int r = 0; r < NB; ++r)
+                    while ((bits[r] = __hip_atomic_load(&s_inv[r], __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_WORKGROUP)) == 0u)
+                        __builtin_amdgcn_s_sleep(1);
+                my_inv = __uint_as_float(bits[0] ^ 0x80000000u);
+#pragma unroll
+                for (int r = 1; r < NB; ++r)
+                    my_inv = my_r == r ? __uint_as_float(bits[r] ^ 0x80000000u) : my_inv;
+                my_inv_ready = true;
+            }
 #pragma unroll
             for (int m = 0; m < MATS; ++m)
                 acc[0][m] *= my_inv;
+        }
         if constexpr (KS == 1) {
             epilogue(acc[0], gl, res);
         } else {
