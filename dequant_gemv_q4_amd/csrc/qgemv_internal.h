@@ -15,12 +15,14 @@ enum Epi { E_STORE = 0, E_RES = 1, E_GUS = 2, E_ARGMAX = 3 };
 
 // Routed experts: at most this many (row, slot) pairs per call (16 rows x top-8).
 #define QG_PAIRS_MAX 128
-// Routed experts: threads per workgroup and the waves per SIMD the register budget allows.
+// Routed experts: threads per workgroup and the waves per SIMD the register budget allows.  The
+// Q4_K variant needs about 160 VGPRs (four x rows held as f16 pairs), so three waves fit on a
+// SIMD: 12 waves per workgroup, one workgroup per CU.
 #ifndef QG_MOE_THREADS
-#define QG_MOE_THREADS 512
+#define QG_MOE_THREADS 768
 #endif
 #ifndef QG_MOE_WPE
-#define QG_MOE_WPE 2
+#define QG_MOE_WPE 3
 #endif
 #ifndef QG_MOE_PD
 #define QG_MOE_PD 2       // row groups a routed-expert wave keeps in flight (2 or 4)
