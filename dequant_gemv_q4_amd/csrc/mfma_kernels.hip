@@ -134,8 +134,10 @@ __device__ __forceinline__ float mf_xor(float v)
 // blockIdx.x + gridDim.x, ...: the grid reads one dense window).  In a group, wave w takes tile
 // w / KS and K slice w % KS (KS = 16 / TPW waves per tile), i.e. steps slice, slice + KS, ...,
 // streamed through two register buffers.  With KS > 1 the slices' partial tiles are added in LDS
-// in slice order.  K class KC: K <= 2048 KC (x: 8 KC float4s per lane).
-template <int FMT, int EPI, bool NRM, int KC, int TPW>
+// in slice order.  K class KC: K <= 2048 KC (x: 8 KC float4s per lane).  SV: a step's block
+// scales of a row are contiguous and aligned (K a multiple of 128 for Q4_0, 64 for Q8_0), so one
+// 8- or 4-byte load per lane fetches them (else one 2-byte load per block).
+template <int FMT, int EPI, bool NRM, int KC, int TPW, bool SV>
 __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
 {
     constexpr int MATS = EPI == E_GUS ? 2 : 1;
@@ -188,7 +190,8 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
     // one step's loads: the lane's 16-byte chunk of its row and the step's block scales
     struct StepBuf {
         uint32_t q[MATS][4];
-        uint16_t s[MATS][BPS];
+        uint16_t s[MATS][BPS];        // per-block scale loads
+        uint32_t sw[MATS][BPS / 2];   // SV: the step's scales as loaded (two f16 per dword)
     };
     auto load_step = [&](StepBuf &sb, int64_t n, int k) {
         const int kk = k < nst ? k : nst - 1;              // past the wave's steps: its last
@@ -199,11 +202,25 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
             const auto v = __builtin_amdgcn_raw_buffer_load_b128(
                 rq[m], (int)((uint32_t)n * (uint32_t)a.qs_row + 16u * (uint32_t)ch), 0, QG_WCPOL);
             sb.q[m][0] = v[0]; sb.q[m][1] = v[1]; sb.q[m][2] = v[2]; sb.q[m][3] = v[3];
+            if constexpr (SV) {
+                // raw dwords: halves are split where they are used, so that no instruction
+                // touches the load's result before its step is computed
+                const int so = (int)((uint32_t)n * (uint32_t)a.sc_row + 2u * BPS * (uint32_t)st);
+                if constexpr (BPS == 4) {
+                    const auto w = __builtin_amdgcn_raw_buffer_load_b64(rsc[m], so, 0, QG_WCPOL);
+                    sb.sw[m][0] = w[0];
+                    sb.sw[m][1] = w[1];
+                } else {
+                    sb.sw[m][0] = __builtin_amdgcn_raw_buffer_load_b32(rsc[m], so, 0, QG_WCPOL);
+                }
+            } else {
 #pragma unroll
-            for (int b = 0; b < BPS; ++b) {
-                const int blk = BPS * st + b < KB ? BPS * st + b : KB - 1;
-                sb.s[m][b] = __builtin_amdgcn_raw_buffer_load_b16(
-                    rsc[m], (int)((uint32_t)n * (uint32_t)a.sc_row + 2u * (uint32_t)blk), 0, QG_WCPOL);
+                for (int b = 0; b < BPS; ++b) {
+                    const int blk = BPS * st + b < KB ? BPS * st + b : KB - 1;
+                    sb.s[m][b] = __builtin_amdgcn_raw_buffer_load_b16(
+                        rsc[m], (int)((uint32_t)n * (uint32_t)a.sc_row + 2u * (uint32_t)blk), 0,
+                        QG_WCPOL);
+                }
             }
         }
     };
@@ -299,7 +316,9 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
 #pragma unroll
             for (int b = 0; b < BPS; ++b) {
                 const int blk = BPS * st + b;
-                const float d = blk < KB ? (float)__builtin_bit_cast(_Float16, sb.s[m][b]) : 0.f;
+                const uint16_t sbits = SV ? (uint16_t)(sb.sw[m][b >> 1] >> (16 * (b & 1)))
+                                          : sb.s[m][b];
+                const float d = blk < KB ? (float)__builtin_bit_cast(_Float16, sbits) : 0.f;
                 const mh8 bop = FMT == FQ8_0 ? mf_bop<FMT>(q[2 * b], q[2 * b + 1], kc)
                                              : mf_bop<FMT>(q[b], 0u, kc);
                 const int blc = blk < KB ? blk : KB - 1;
@@ -409,49 +428,55 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
 
 // The norm variants take K <= 2048 only: with the longer class x, its statistics and the weight
 // loads do not fit in the 128 registers a lane has at 1024 threads.
-template <int FMT, int EPI, bool NRM, int KC>
+template <int FMT, int EPI, bool NRM, int KC, bool SV>
 static const void *mfma_fn_tpw(int tpw)
 {
     switch (tpw) {
-    case 1: return reinterpret_cast<const void *>(&k_mfma<FMT, EPI, NRM, KC, 1>);
-    case 2: return reinterpret_cast<const void *>(&k_mfma<FMT, EPI, NRM, KC, 2>);
-    case 4: return reinterpret_cast<const void *>(&k_mfma<FMT, EPI, NRM, KC, 4>);
-    case 8: return reinterpret_cast<const void *>(&k_mfma<FMT, EPI, NRM, KC, 8>);
-    case 16: return reinterpret_cast<const void *>(&k_mfma<FMT, EPI, NRM, KC, 16>);
+    case 1: return reinterpret_cast<const void *>(&k_mfma<FMT, EPI, NRM, KC, 1, SV>);
+    case 2: return reinterpret_cast<const void *>(&k_mfma<FMT, EPI, NRM, KC, 2, SV>);
+    case 4: return reinterpret_cast<const void *>(&k_mfma<FMT, EPI, NRM, KC, 4, SV>);
+    case 8: return reinterpret_cast<const void *>(&k_mfma<FMT, EPI, NRM, KC, 8, SV>);
+    case 16: return reinterpret_cast<const void *>(&k_mfma<FMT, EPI, NRM, KC, 16, SV>);
     default: return nullptr;
     }
 }
 
+template <int FMT, int EPI, bool NRM, int KC>
+static const void *mfma_fn_sv(bool sv, int tpw)
+{
+    return sv ? mfma_fn_tpw<FMT, EPI, NRM, KC, true>(tpw) : mfma_fn_tpw<FMT, EPI, NRM, KC, false>(tpw);
+}
+
 template <int FMT, int EPI, bool NRM>
-static const void *mfma_fn_ns(int kc, int tpw)
+static const void *mfma_fn_ns(int kc, bool sv, int tpw)
 {
     if (kc == 1)
-        return mfma_fn_tpw<FMT, EPI, NRM, 1>(tpw);
+        return mfma_fn_sv<FMT, EPI, NRM, 1>(sv, tpw);
     if constexpr (!NRM) {
         if (kc == 2)
-            return mfma_fn_tpw<FMT, EPI, NRM, 2>(tpw);
+            return mfma_fn_sv<FMT, EPI, NRM, 2>(sv, tpw);
     }
     return nullptr;
 }
 
 template <int FMT>
-static const void *mfma_fn_fmt(int epi, bool nrm, int kc, int tpw)
+static const void *mfma_fn_fmt(int epi, bool nrm, int kc, bool sv, int tpw)
 {
     switch (epi) {
     case E_STORE:
-        return nrm ? mfma_fn_ns<FMT, E_STORE, true>(kc, tpw)
-                   : mfma_fn_ns<FMT, E_STORE, false>(kc, tpw);
-    case E_RES: return mfma_fn_ns<FMT, E_RES, false>(kc, tpw);
-    case E_GUS: return mfma_fn_ns<FMT, E_GUS, true>(kc, tpw);
-    case E_ARGMAX: return mfma_fn_ns<FMT, E_ARGMAX, false>(kc, tpw);
+        return nrm ? mfma_fn_ns<FMT, E_STORE, true>(kc, sv, tpw)
+                   : mfma_fn_ns<FMT, E_STORE, false>(kc, sv, tpw);
+    case E_RES: return mfma_fn_ns<FMT, E_RES, false>(kc, sv, tpw);
+    case E_GUS: return mfma_fn_ns<FMT, E_GUS, true>(kc, sv, tpw);
+    case E_ARGMAX: return mfma_fn_ns<FMT, E_ARGMAX, false>(kc, sv, tpw);
     default: return nullptr;
     }
 }
 
-static const void *mfma_fn(int fmt, int epi, bool nrm, int kc, int tpw)
+static const void *mfma_fn(int fmt, int epi, bool nrm, int kc, bool sv, int tpw)
 {
-    return fmt == FQ4_0 ? mfma_fn_fmt<FQ4_0>(epi, nrm, kc, tpw)
-         : fmt == FQ8_0 ? mfma_fn_fmt<FQ8_0>(epi, nrm, kc, tpw) : nullptr;
+    return fmt == FQ4_0 ? mfma_fn_fmt<FQ4_0>(epi, nrm, kc, sv, tpw)
+         : fmt == FQ8_0 ? mfma_fn_fmt<FQ8_0>(epi, nrm, kc, sv, tpw) : nullptr;
 }
 
 // Plan of the row-batch kernel: K class (1: K <= 2048, 2: K <= 4096), tiles per group (16 / waves
@@ -464,6 +489,7 @@ bool plan_mfma(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb, MfmaPla
     if (nb < 1 || nb > 16 || K > MF_KMAX || N < 1)
         return false;
     p->kc = K <= 2048 ? 1 : 2;
+    p->sv = fmt == FQ4_0 ? K % 128 == 0 : K % 64 == 0;
     const int mats = epi == E_GUS ? 2 : 1;
     p->lds = (size_t)(K / 32) * 1024 + (size_t)MF_WAVES * mats * 4 * 64 * 4;
     // one workgroup per CU; enough tiles per group that the groups fill the CUs once, at most
@@ -481,7 +507,7 @@ bool plan_mfma(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb, MfmaPla
     p->tpw = tpw;
     const int64_t groups = (NT + tpw - 1) / tpw;
     p->grid = (int)(groups < cus ? groups : cus);
-    const void *fn = mfma_fn(fmt, epi, nrm, p->kc, p->tpw);
+    const void *fn = mfma_fn(fmt, epi, nrm, p->kc, p->sv, p->tpw);
     hipFuncAttributes attr;
     if (!fn || hipFuncGetAttributes(&attr, fn) != hipSuccess)
         return false;
@@ -490,7 +516,7 @@ bool plan_mfma(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb, MfmaPla
 
 int launch_mfma(int fmt, int epi, bool nrm, const MfmaPlan &p, const GemvArgs &a, void *stream)
 {
-    const void *fn = mfma_fn(fmt, epi, nrm, p.kc, p.tpw);
+    const void *fn = mfma_fn(fmt, epi, nrm, p.kc, p.sv, p.tpw);
     if (!fn)
         return (int)hipErrorInvalidValue;
     void *args[] = {const_cast<GemvArgs *>(&a)};

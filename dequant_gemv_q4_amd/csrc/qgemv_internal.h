@@ -154,6 +154,7 @@ int launch_moe(int fmt, int cpl, int pd, const MoeArgs &a, int grid, size_t lds_
 // 16-row tiles.
 struct MfmaPlan {
     int kc;       // K class: 1 (K <= 2048) or 2 (K <= 4096)
+    bool sv;      // one load per lane fetches a step's block scales (aligned scale rows)
     int tpw;      // tiles per group (16 / waves per tile)
     int grid;
     size_t lds;

@@ -54,6 +54,8 @@ GEMV_CASES = [
     (q.Q4_0, 1, 32, 1), (q.Q4_0, 37, 32, 3), (q.Q4_0, 1037, 1024, 1), (q.Q4_0, 517, 2048, 1),
     (q.Q4_0, 300, 8192, 1), (q.Q4_0, 129, 96, 2), (q.Q4_0, 201, 2048, 4), (q.Q4_0, 77, 1536, 5),
     (q.Q4_0, 150, 2048, 7), (q.Q4_0, 100, 2048, 8), (q.Q4_0, 65, 2048, 16), (q.Q4_0, 33, 4096, 12),
+    # row batches whose scale rows are not 8 (Q4_0) / 4 (Q8_0) byte aligned: per-block scale loads
+    (q.Q4_0, 40, 96, 8), (q.Q4_0, 29, 1120, 16), (q.Q8_0, 45, 96, 6),
     (q.Q8_0, 1, 32, 1), (q.Q8_0, 301, 1536, 1), (q.Q8_0, 2048 + 5, 1536, 4), (q.Q8_0, 99, 1536, 16),
     (q.Q8_0, 45, 4096, 3), (q.Q8_0, 70, 2048, 9),
     (q.Q4_K, 1, 256, 1), (q.Q4_K, 61, 2048, 1), (q.Q4_K, 130, 768, 2), (q.Q4_K, 90, 2048, 16),
