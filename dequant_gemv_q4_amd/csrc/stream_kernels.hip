@@ -118,6 +118,7 @@ template <int FMT, int CPL, int MATS, int R>
 struct GroupBuf {
     uint4 q[MATS][R][CPL];
     typename ScaleT<FMT>::T s[MATS][R][CPL];
+    uint32_t sw;   // one-load scales: dword `lane` of the group's scale bytes, as loaded
 };
 
 // A packed matrix seen through two buffer resources (quant plane, scale plane).  Row offsets
@@ -148,6 +149,7 @@ __device__ __forceinline__ BufMat buf_mat(const uint8_t *qs, const uint8_t *sc, 
 template <int CPL>
 struct LaneOff {
     uint32_t q[CPL], s[CPL];
+    uint32_t w4;   // 4 * lane: the lane's dword of a group's scale bytes (one-load scales)
     bool ok[CPL];
 };
 
@@ -155,6 +157,7 @@ template <int FMT, int CPL>
 __device__ __forceinline__ LaneOff<CPL> lane_offsets(int lane, int C)
 {
     LaneOff<CPL> o;
+    o.w4 = 4u * (uint32_t)(lane & 63);
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = lane + 64 * i;
@@ -169,11 +172,16 @@ __device__ __forceinline__ LaneOff<CPL> lane_offsets(int lane, int C)
 // Loads of one row group, unconditional so the compiler can count them exactly in its
 // s_waitcnt.  A row outside [0, N) (a group index < 0 marks a group with no result) is loaded
 // out of range: zeros, no memory traffic; its results are dropped by the epilogue.
-template <int FMT, int CPL, int MATS, int R>
+// SCW (one-load scales; one matrix, rows of at most 64 chunks): the scale bytes of all R rows of
+// the group are contiguous and at most 256, so each lane loads one dword of them and the block
+// scales reach their lanes by a cross-lane permute when the group is decoded (one load
+// instruction instead of R two-byte loads).
+template <int FMT, int CPL, int MATS, int R, bool SCW = false>
 __device__ __forceinline__ void load_group(GroupBuf<FMT, CPL, MATS, R> &b, const BufMat (&mat)[MATS],
                                            uint32_t qs_row, uint32_t sc_row, int64_t N,
                                            const LaneOff<CPL> &lo, int64_t g)
 {
+    static_assert(!SCW || (MATS == 1 && CPL == 1), "one-load scales: one matrix, one chunk slot");
 #pragma unroll
     for (int u = 0; u < R; ++u) {
         const int64_t nr = g * R + u;   // wave-uniform
@@ -190,7 +198,9 @@ __device__ __forceinline__ void load_group(GroupBuf<FMT, CPL, MATS, R> &b, const
                 b.q[m][u][i] = make_uint4(v[0], v[1], v[2], v[3]);
                 // raw scale bytes: the lane mask is applied where they are used, so that no
                 // instruction touches a load's result before its group is decoded
-                if constexpr (FMT == FQ4_K) {
+                if constexpr (SCW) {
+                    (void)ros;
+                } else if constexpr (FMT == FQ4_K) {
                     const auto w = __builtin_amdgcn_raw_buffer_load_b128(
                         mat[m].s, (int)(lo.s[i] + ros), 0, QG_WCPOL_STREAM);
                     b.s[m][u][i] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -199,6 +209,11 @@ __device__ __forceinline__ void load_group(GroupBuf<FMT, CPL, MATS, R> &b, const
                         mat[m].s, (int)(lo.s[i] + ros), 0, QG_WCPOL_STREAM);
                 }
             }
+    }
+    if constexpr (SCW) {
+        const bool gin = g >= 0 && g * R < N;
+        const uint32_t so = gin ? (uint32_t)(g * R) * sc_row + lo.w4 : mat[0].s_end;
+        b.sw = __builtin_amdgcn_raw_buffer_load_b32(mat[0].s, (int)so, 0, QG_WCPOL_STREAM);
     }
 }
 
@@ -573,13 +588,27 @@ void k_stream(GemvArgs a)
     float *SS = reinterpret_cast<float *>(lds4 + (size_t)NB * K4);  // norm: float4 squares
     float *s_out = SS + (NRM ? NB * K4 : 0);                        // [pool][ITEMS] results
 
-    const uint32_t qbytes = (uint32_t)(a.N * a.qs_row), sbytes = (uint32_t)(a.N * a.sc_row);
+    // the scale plane's range rounded up to whole dwords (one-load scales read dwords; the packed
+    // layout pads each plane to 256 bytes)
+    const uint32_t qbytes = (uint32_t)(a.N * a.qs_row),
+                   sbytes = ((uint32_t)(a.N * a.sc_row) + 3u) & ~3u;
     BufMat mat[MATS];
     mat[0] = buf_mat(a.qs0, a.sc0, qbytes, sbytes);
     if constexpr (MATS == 2)
         mat[MATS - 1] = buf_mat(a.qs1, a.sc1, qbytes, sbytes);
     const LaneOff<1> lo = lane_offsets<FMT, 1>(ks * 64 + lane, C);
     const uint32_t qrow = (uint32_t)a.qs_row, srow = (uint32_t)a.sc_row;
+    // one-load scales (see load_group): this lane's block scale of row u of a group is half
+    // ssh[u] / 16 of the dword that lane sbp[u] / 4 loaded
+    constexpr bool SCW = KS == 1 && MATS == 1 && R == 2 && (FMT == FQ4_0 || FMT == FQ8_0);
+    uint32_t sbp[R], ssh[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const uint32_t cx = (uint32_t)(lane < C ? lane : C - 1);
+        const uint32_t byte = u * srow + 2u * (FMT == FQ8_0 ? cx >> 1 : cx);
+        sbp[u] = byte & ~3u;
+        ssh[u] = (byte & 2u) * 8u;
+    }
 
     // this workgroup's pool of row groups: pool-local index c is group gmap(c); indices at or
     // past `pool` (and groups past T in the last tile) carry no result
@@ -641,7 +670,7 @@ void k_stream(GemvArgs a)
 #pragma unroll
         for (int p = 0; p < PD; ++p) {
             gcur[p] = first_group(p);
-            load_group(buf[p], mat, qrow, srow, a.N, lo, gclamp(gcur[p]));
+            load_group<FMT, 1, MATS, R, SCW>(buf[p], mat, qrow, srow, a.N, lo, gclamp(gcur[p]));
             resv[p] = load_res(gcur[p]);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -777,14 +806,21 @@ void k_stream(GemvArgs a)
                 for (int p = 0; p < PD; ++p) {
                     const int gl = gcur[p];
                     float acc[IP][MATS];
-                    if (gl < pool)
+                    if (gl < pool) {
+                        if constexpr (SCW)
+#pragma unroll
+                            for (int u = 0; u < R; ++u)
+                                buf[p].s[0][u][0] = (uint16_t)(
+                                    (uint32_t)__builtin_amdgcn_ds_bpermute((int)sbp[u], (int)buf[p].sw) >>
+                                    ssh[u]);
                         compute_group_h<FMT, NB, 1, MATS, R, IP>(buf[p], xh, wk, C, cme, acc);
+                    }
                     int nx = 0;
                     if (lane == 0)
                         nx = atomicAdd(&s_next, 1);
                     nx = __builtin_amdgcn_readfirstlane(nx);
                     const float res = resv[p];
-                    load_group(buf[p], mat, qrow, srow, a.N, lo, gclamp(nx));
+                    load_group<FMT, 1, MATS, R, SCW>(buf[p], mat, qrow, srow, a.N, lo, gclamp(nx));
                     resv[p] = load_res(nx);
                     if (gl < pool)
                         finish(acc, gl, 0, res);
