@@ -16,7 +16,9 @@
  *            pairs, 128 B nibbles), w = d * sc_j * q - dmin * m_j.
  *  - W arguments of the compute entry points are in the PACKED device layout written by
  *    qgemv_pack (same bytes per weight as GGUF, split into planes so every hot load is an
- *    aligned 16-byte load).  Rows are in output order; K is the reduction length.
+ *    aligned 16-byte load).  Rows are in output order; K is the reduction length.  A W buffer
+ *    must span the whole qgemv_packed_bytes(fmt, N, K): the kernels may read into the padding
+ *    after each plane (whole dwords of the scale plane), never past it.
  *  - Every pointer of a compute call is a DEVICE pointer (HIP device memory).  The caller owns
  *    all memory; the library never allocates or frees and keeps no state between calls.
  *  - x is f32 [nb][K], outputs f32 [nb][N], all row-major and contiguous.
