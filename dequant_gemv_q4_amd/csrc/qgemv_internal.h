@@ -15,15 +15,19 @@ enum Epi { E_STORE = 0, E_RES = 1, E_GUS = 2, E_ARGMAX = 3 };
 
 // Routed experts: at most this many (row, slot) pairs per call (16 rows x top-8).
 #define QG_PAIRS_MAX 128
-// Routed experts: threads per workgroup and the waves per SIMD the register budget allows.  The
-// Q4_K variant needs about 160 VGPRs (four x rows held as f16 pairs), so three waves fit on a
-// SIMD: 12 waves per workgroup, one workgroup per CU.
+// Routed experts: threads per workgroup of the common variants, and of the variants that hold
+// more in registers.  The Q4_K variant with one chunk slot per lane needs about 160 VGPRs (four x
+// rows held as f16 pairs), so three waves fit on a SIMD: 12 waves per workgroup, one workgroup
+// per CU.  Q4_K with four chunk slots per lane (rows of 8192) and the variants with four groups
+// in flight need more than 168 VGPRs and keep two waves per SIMD (8 waves per workgroup).
 #ifndef QG_MOE_THREADS
 #define QG_MOE_THREADS 768
 #endif
-#ifndef QG_MOE_WPE
-#define QG_MOE_WPE 3
-#endif
+#define QG_MOE_THREADS_WIDE 512
+__host__ __device__ constexpr int moe_threads(int fmt, int cpl, int pd)
+{
+    return (fmt == FQ4_K && cpl >= 4) || pd >= 4 ? QG_MOE_THREADS_WIDE : QG_MOE_THREADS;
+}
 #ifndef QG_MOE_PD
 #define QG_MOE_PD 2       // row groups a routed-expert wave keeps in flight (2 or 4)
 #endif

@@ -89,13 +89,17 @@ __device__ __forceinline__ void xpose_reduce(float (&v)[IP][P], int lane, int bp
 
 constexpr int pow2_ceil(int v) { return v <= 1 ? 1 : 2 * pow2_ceil((v + 1) / 2); }
 
-// Compile-time shape of the streaming kernels.
-template <int FMT, int NB, int CPL, int MATS>
+// Compile-time shape of the streaming kernels.  KS: waves that share one row.
+template <int FMT, int NB, int CPL, int MATS, int KS = 1>
 struct SP {
     static constexpr int R = stream_rows(NB, CPL, MATS);
     static constexpr int XF4 = Fc<FMT>::XF4, CE = Fc<FMT>::CE, NS = Fc<FMT>::NS;
-    // waves per SIMD the register budget must allow (at most 512 / WPE VGPRs per lane)
-    static constexpr int WPE = (NB == 1 && CPL == 1 && FMT != FQ4_K) ? QG_WPE_NB1 : 2;
+    // waves per SIMD the register budget must allow (at most 512 / WPE VGPRs per lane): a row
+    // batch of 2..4 on one matrix with one wave per row holds its x pairs in about 120 VGPRs,
+    // so three waves fit (more waves to hide the longer decode of several batch rows); rows
+    // split over several waves are short, and fewer, smaller workgroups start sooner there
+    static constexpr int WPE = (NB == 1 && CPL == 1 && FMT != FQ4_K) ? QG_WPE_NB1
+                             : (NB > 1 && KS == 1 && MATS == 1 && FMT != FQ4_K) ? 3 : 2;
     static constexpr int ITEMS = R * NB;
     static constexpr int IP = pow2_ceil(ITEMS);
     // GEMV family: one workgroup fills a CU (WPE waves on each of its 4 SIMDs)
@@ -556,12 +560,12 @@ __device__ __forceinline__ void compute_group_h(const GroupBuf<FMT, CPL, MATS, R
 // (one counter tracks loads and stores on this target: a store among the in-flight loads would
 // make the compiler wait for all of them).  x is staged in LDS once per workgroup.
 template <int FMT, int NB, int KS, int EPI, bool NRM, int PD>
-__global__ __launch_bounds__((SP<FMT, NB, 1, EPI == E_GUS ? 2 : 1>::NT))
-__attribute__((amdgpu_waves_per_eu(SP<FMT, NB, 1, EPI == E_GUS ? 2 : 1>::WPE)))
+__global__ __launch_bounds__((SP<FMT, NB, 1, EPI == E_GUS ? 2 : 1, KS>::NT))
+__attribute__((amdgpu_waves_per_eu(SP<FMT, NB, 1, EPI == E_GUS ? 2 : 1, KS>::WPE)))
 void k_stream(GemvArgs a)
 {
     constexpr int MATS = EPI == E_GUS ? 2 : 1;
-    using P = SP<FMT, NB, 1, MATS>;
+    using P = SP<FMT, NB, 1, MATS, KS>;
     constexpr int R = P::R, IP = P::IP, WV = P::WV, NT = P::NT, ITEMS = P::ITEMS;
     constexpr int LG = IP == 1 ? 0 : IP == 2 ? 1 : IP == 4 ? 2 : IP == 8 ? 3 : IP == 16 ? 4 : 5;
     constexpr int TEAMS = WV / KS;
@@ -934,14 +938,15 @@ __global__ __launch_bounds__(256) void k_argmax_fold(const unsigned long long *p
 // when a claim crosses into the second set.  Results collect in LDS and leave in one pass to
 // part[pair][n]; k_moe_combine then forms y[r][n] = sum_t wts[r][t] part[r][t][n], t ascending.
 template <int FMT, int CPL, int PD>
-__global__ __launch_bounds__(QG_MOE_THREADS) __attribute__((amdgpu_waves_per_eu(QG_MOE_WPE)))
+__global__ __launch_bounds__(moe_threads(FMT, CPL, PD))
+__attribute__((amdgpu_waves_per_eu(moe_threads(FMT, CPL, PD) / 256)))
 void k_moe(MoeArgs a)
 {
     constexpr int NBX = 4 / CPL;                  // x rows a wave holds in registers
     constexpr int R = stream_rows(NBX, CPL, 1);
     constexpr int ITX = R * NBX, IPX = pow2_ceil(ITX);
     constexpr int LG = IPX == 1 ? 0 : IPX == 2 ? 1 : IPX == 4 ? 2 : IPX == 8 ? 3 : 4;
-    constexpr int WV = QG_MOE_THREADS / 64, NT = QG_MOE_THREADS;
+    constexpr int NT = moe_threads(FMT, CPL, PD), WV = NT / 64;
     constexpr int XF4 = Fc<FMT>::XF4;
     constexpr int XPL = 8;   // float4s in flight per loader lane while a row is copied
     extern __shared__ float4 lds4[];
@@ -1316,8 +1321,8 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float *part, const in
 
 // ------------------------------------------------------------------------------------ launchers
 
-template <int FMT, int NB, int EPI>
-constexpr int stream_threads() { return SP<FMT, NB, 1, EPI == E_GUS ? 2 : 1>::NT; }
+template <int FMT, int NB, int EPI, int KS>
+constexpr int stream_threads() { return SP<FMT, NB, 1, EPI == E_GUS ? 2 : 1, KS>::NT; }
 
 // Kernel of one streaming variant, and its workgroup size.
 struct StreamFn {
@@ -1328,7 +1333,7 @@ struct StreamFn {
 template <int FMT, int NB, int KS, int EPI, bool NRM>
 static StreamFn stream_fn_pd(int pd)
 {
-    constexpr int T = stream_threads<FMT, NB, EPI>();
+    constexpr int T = stream_threads<FMT, NB, EPI, KS>();
     switch (pd) {
     case 1: return {reinterpret_cast<const void *>(&k_stream<FMT, NB, KS, EPI, NRM, 1>), T};
     case 2: return {reinterpret_cast<const void *>(&k_stream<FMT, NB, KS, EPI, NRM, 2>), T};
@@ -1424,7 +1429,8 @@ int launch_moe(int fmt, int cpl, int pd, const MoeArgs &a, int grid, size_t lds_
     if (!fn)
         return (int)hipErrorInvalidValue;
     void *args[] = {const_cast<MoeArgs *>(&a)};
-    const hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(QG_MOE_THREADS), args, lds_bytes, s);
+    const hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(moe_threads(fmt, cpl, pd)), args,
+                                           lds_bytes, s);
     if (err != hipSuccess)
         return (int)err;
     const int64_t quads = (int64_t)a.nb * ((a.N + 3) / 4);
@@ -1496,7 +1502,7 @@ int stream_resident_wgs(int fmt, int epi, bool nrm, int cpl, int nb, int pd, siz
 
 int moe_resident_wgs(int fmt, int cpl, int pd, size_t lds_bytes)
 {
-    return resident_wgs(moe_fn(fmt, cpl, pd), QG_MOE_THREADS, lds_bytes);
+    return resident_wgs(moe_fn(fmt, cpl, pd), moe_threads(fmt, cpl, pd), lds_bytes);
 }
 
 }  // namespace qg
