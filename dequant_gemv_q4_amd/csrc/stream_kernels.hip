@@ -903,16 +903,25 @@ void k_stream(GemvArgs a)
     }
 }
 
-// idx[r] from the per-workgroup partial keys [n_part][nb] of an argmax launch (one workgroup).
-__global__ __launch_bounds__(256) void k_argmax_fold(const unsigned long long *part, int n_part,
-                                                     int nb, int32_t *idx)
+// idx[r] from the per-workgroup partial keys [n_part][nb] of an argmax launch (one workgroup of
+// 16 waves, one batch row per wave).  A lane's keys are loaded eight at a time, all issued before
+// the first compare, so a row of up to 512 partial keys costs one memory latency.
+__global__ __launch_bounds__(1024) void k_argmax_fold(const unsigned long long *part, int n_part,
+                                                      int nb, int32_t *idx)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int r = wave; r < nb; r += 4) {
+    for (int r = wave; r < nb; r += 16) {
         unsigned long long k = 0ull;
-        for (int b = lane; b < n_part; b += 64) {
-            const unsigned long long o = part[(int64_t)b * nb + r];
-            k = o > k ? o : k;
+        for (int b0 = lane; b0 < n_part; b0 += 64 * 8) {
+            unsigned long long o[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int b = b0 + 64 * u;
+                o[u] = b < n_part ? part[(int64_t)b * nb + r] : 0ull;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                k = o[u] > k ? o[u] : k;
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
@@ -1442,7 +1451,7 @@ int launch_moe(int fmt, int cpl, int pd, const MoeArgs &a, int grid, size_t lds_
 int launch_argmax_fold(const unsigned long long *part, int n_part, int nb, int32_t *idx,
                        void *stream)
 {
-    hipLaunchKernelGGL(k_argmax_fold, dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream),
+    hipLaunchKernelGGL(k_argmax_fold, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream),
                        part, n_part, nb, idx);
     return (int)hipGetLastError();
 }
