@@ -330,7 +330,10 @@ def test_argmax_ties_go_to_lowest_index():
                                                    (q.Q8_0, 4, 300, 1536, 2, 1),
                                                    (q.Q8_0, 3, 130, 2048, 16, 2),
                                                    (q.Q4_0, 5, 70, 8192, 7, 3),
-                                                   (q.Q4_K, 64, 1024, 2048, 16, 8)])
+                                                   (q.Q4_K, 64, 1024, 2048, 16, 8),
+                                                   # Q4_K rows of two and four chunks per lane
+                                                   (q.Q4_K, 6, 100, 4096, 4, 2),
+                                                   (q.Q4_K, 5, 64, 8192, 3, 2)])
 def test_qgemv_moe_parity(fmt, n_exp, N, K, nb, topk):
     say(f"moe fmt={fmt} n_exp={n_exp} N={N} K={K} nb={nb} topk={topk}")
     g = wl.rng(600 + fmt, n_exp + N + nb)
