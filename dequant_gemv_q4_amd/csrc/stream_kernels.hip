@@ -569,10 +569,11 @@ void k_stream(GemvArgs a)
     constexpr int R = P::R, IP = P::IP, WV = P::WV, NT = P::NT, ITEMS = P::ITEMS;
     constexpr int LG = IP == 1 ? 0 : IP == 2 ? 1 : IP == 4 ? 2 : IP == 8 ? 3 : IP == 16 ? 4 : 5;
     constexpr int TEAMS = WV / KS;
-    // float4s of x each loader lane fetches: at least 4, and enough for 16 (8) waves to cover the
-    // longest row of this K class
+    // float4s of x each loader lane fetches: at least 2 (more loader waves, each with fewer loads,
+    // publish x sooner; measured against 1, 4 and 8), and enough for the workgroup's waves to
+    // cover the longest row of this K class
     constexpr int XPL0 = (NB * KS * Fc<FMT>::XF4 + WV - 1) / WV;
-    constexpr int XPL = XPL0 > 4 ? XPL0 : 4;
+    constexpr int XPL = XPL0 > 2 ? XPL0 : 2;
 
     extern __shared__ float4 lds4[];
     __shared__ unsigned long long s_key[NB * WV];
