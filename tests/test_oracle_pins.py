@@ -439,3 +439,110 @@ def test_moe_rejects_bad_expert_id():
     W = wl.q4_0_matrix(g, 2 * 4, 32)
     with pytest.raises(ValueError):
         oracle.qgemv_moe(Q4_0, W, 2, 4, 32, np.ones((1, 32)), np.array([[2]], np.int32), np.ones((1, 1)))
+
+
+# ----------------------------------------------------------------------------- gate / up roles
+
+def test_gus_nrm_gate_and_up_take_their_own_roles():
+    """x = e_0 with K = 64, gamma = 1, eps = 0 normalizes to exactly 8 e_0, so row n of each
+    matrix contributes 8 w[n][0].  Weights are built so that (g, u) per row is a hand-chosen
+    pair of small integers; h must be silu(g) u ("honeycrisp mod.rs", fused_norm_swiglu_down:
+    silu on the gate), and every pair is chosen so that the swapped composite silu(u) g differs.
+    The values use logistic(1) and logistic(2) only."""
+    K = 64
+    pairs = [(1, 2), (2, 1), (-1, 2), (2, -1), (0, 3)]
+    want = [2 * SIGMA_1, 2 * SIGMA_2, -2 * (1 - SIGMA_1), -2 * SIGMA_2, 0.0]
+    # silu(u) g, the composite with the roles swapped, for the first four pairs
+    swapped = [2 * SIGMA_2, 2 * SIGMA_1, -2 * SIGMA_2, -2 * (1 - SIGMA_1)]
+    N = len(pairs)
+
+    def mat(vals):
+        # d = 1/8 (f16 0x3000); element 0 of row n has nibble 8 + v (so w = v / 8), others 8
+        out = bytearray()
+        for v in vals:
+            for b in range(K // 32):
+                nib = [8] * 32
+                if b == 0:
+                    nib[0] = 8 + v
+                out += f16_bytes(0.125) + bytes(nib[j] | (nib[j + 16] << 4) for j in range(16))
+        return np.frombuffer(bytes(out), dtype=np.uint8)
+
+    Wg = mat([p[0] for p in pairs])
+    Wu = mat([p[1] for p in pairs])
+    x = np.zeros((1, K))
+    x[0, 0] = 1.0
+    h, g, u, Ag, Au = oracle.qgemv_gus_nrm(Q4_0, Wg, Wu, N, K, x, np.ones(K), 0.0)
+    assert np.array_equal(g[0], [p[0] for p in pairs])
+    assert np.array_equal(u[0], [p[1] for p in pairs])
+    assert np.array_equal(Ag[0], np.abs(g[0])) and np.array_equal(Au[0], np.abs(u[0]))
+    for n in range(N):
+        assert abs(h[0, n] - want[n]) <= 1e-15, (n, h[0, n], want[n])
+        if n < 4:
+            assert abs(h[0, n] - swapped[n]) > 0.1, n
+
+
+# ----------------------------------------------------------------------------- brute force
+
+def _blocks_from_nibbles(d_bits, nib):
+    """Q4_0 bytes of one row: per block the f16 bits of d, then byte j = nib[j] | nib[j+16] << 4."""
+    out = bytearray()
+    for b in range(len(d_bits)):
+        out += int(d_bits[b]).to_bytes(2, "little")
+        q = nib[32 * b:32 * b + 32]
+        out += bytes(int(q[j]) | (int(q[j + 16]) << 4) for j in range(16))
+    return bytes(out)
+
+
+@pytest.mark.parametrize("K", [32, 64])
+def test_q4_0_brute_force_second_form(K):
+    """Every row of up to 16 with random nibbles, small-integer x and d = 2^-k: the oracle equals,
+    exactly, the block form d (sum_j q_j x_j - 8 sum_j x_j) worked in integers here, and
+    A = sum |w x| equals d sum |q - 8| |x| (every value is a dyadic rational that f64 holds)."""
+    g = np.random.default_rng(40 + K)
+    for trial in range(20):
+        N = int(g.integers(1, 17))
+        nb = int(g.integers(1, 4))
+        nblk = K // 32
+        kexp = g.integers(1, 9, size=(N, nblk))                 # d = 2^-k
+        nib = g.integers(0, 16, size=(N, K))
+        x = g.integers(-9, 10, size=(nb, K))
+        W = bytearray()
+        for n in range(N):
+            dbits = [int(np.array([2.0 ** -int(k)], "<f2").view("<u2")[0]) for k in kexp[n]]
+            W += _blocks_from_nibbles(dbits, nib[n])
+        y, A = oracle.gemv(Q4_0, np.frombuffer(bytes(W), np.uint8), N, K, x.astype(np.float64))
+        for r in range(nb):
+            for n in range(N):
+                s = 0.0
+                a = 0.0
+                for b in range(nblk):
+                    qx = sum(int(nib[n, 32 * b + j]) * int(x[r, 32 * b + j]) for j in range(32))
+                    sx = sum(int(x[r, 32 * b + j]) for j in range(32))
+                    ab = sum(abs(int(nib[n, 32 * b + j]) - 8) * abs(int(x[r, 32 * b + j]))
+                             for j in range(32))
+                    d = 2.0 ** -int(kexp[n, b])
+                    s += d * (qx - 8 * sx)
+                    a += d * ab
+                assert y[r, n] == s, (trial, r, n, y[r, n], s)
+                assert A[r, n] == a, (trial, r, n)
+
+
+def test_q8_0_brute_force_integer_form():
+    """Q8_0 with every signed byte (including -128) and small-integer x: y = d sum q x exactly."""
+    g = np.random.default_rng(77)
+    for K in (32, 64):
+        N, nb = 16, 2
+        q8 = g.integers(-128, 128, size=(N, K))
+        q8[0, :32] = -128
+        kexp = g.integers(1, 9, size=(N, K // 32))
+        x = g.integers(-9, 10, size=(nb, K))
+        W = bytearray()
+        for n in range(N):
+            for b in range(K // 32):
+                W += np.array([2.0 ** -int(kexp[n, b])], "<f2").tobytes()
+                W += q8[n, 32 * b:32 * b + 32].astype(np.int8).tobytes()
+        y, _ = oracle.gemv(Q8_0, np.frombuffer(bytes(W), np.uint8), N, K, x.astype(np.float64))
+        for r in range(nb):
+            for n in range(N):
+                s = sum(2.0 ** -int(kexp[n, j // 32]) * int(q8[n, j]) * int(x[r, j]) for j in range(K))
+                assert y[r, n] == s, (K, r, n)
