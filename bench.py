@@ -1,21 +1,25 @@
 """Throughput of the block-quantized dequant-GEMV hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--nb NB] [--warm]
+                    [--no-extras] [--no-cpu]
 
 A step is one pass of the hot path over one batch of synthetic input, with every input already
-resident in HBM.  The default workload is the LFM2-1.2B-like decode MLP (nb = 1): the fused
-RMSNorm + Q4_0 gate/up + SwiGLU launch (8192 x 2048 each), then the Q4_0 down + residual launch
-(2048 x 8192).  Weights are rotated over copies totalling >= 1 GiB so that neither the L2 nor the
-256 MB Infinity Cache can serve them ("cold"); --warm reuses one copy.
+resident in HBM.  The default workload is the metric's gate: one Q4_0 GEMV at nb = 1 on the
+lm_head-sized matrix W[65536 x 2048] (75.5 MB of weights, K = hidden 2048).  Weights are rotated
+over copies totalling >= 1 GiB so that neither the L2 nor the 256 MB Infinity Cache can serve
+them ("cold"); --warm reuses one copy (cache-assisted, labelled as such).
 
-The K timed steps are captured once in a HIP graph and replayed under HIP events (the launches
-run back to back, without per-launch host work); the same steps issued eagerly from Python are
-reported as `ms_per_step_eager` (--eager times those instead).
+The K timed steps are captured once in a HIP graph and replayed under HIP events on the launch
+stream (the launches run back to back, without per-launch host work); the same steps issued
+eagerly from Python are reported as `ms_per_step_eager`.
 
-Printed: ONE JSON line.  `value` is weight GB/s over the whole step (weight bytes moved per
-step / time per step); `roofline` is the dominant launch's algorithmic bytes over its average
-duration (HIP events on the launch stream), against the 8 TB/s HBM peak; `cpu_baseline` is the
-f64 oracle timed on this host on a bounded sample of the same workload.
+Printed: ONE JSON line.  `value` is weight GB/s (weight bytes per step / time per step);
+`roofline` is the dominant launch's algorithmic bytes over its average duration against the
+8 TB/s HBM peak; `cpu_baseline` is the f64 oracle on this host's cores (all of them and one).
+`extras` holds the other configurations of the metric measured the same way in the same run:
+the nb = 16 row batch on the same matrix, the routed Q4_K experts (nb = 16), the Q8_0 QKV with
+the norm prologue (nb = 16), the decode MLP step, lm_head + argmax, the warm (cache-assisted)
+gate, and the attainable read rate of a plain 16-byte-load kernel on the same box.
 """
 from __future__ import annotations
 
@@ -23,6 +27,8 @@ import argparse
 import hashlib
 import json
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -33,9 +39,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "weight GB/s and % of HBM peak for Q4 dequant-GEMV, nb=1 and nb=16"
 HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
 COLD_BYTES = 1 << 30
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_DIR = os.path.join(ROOT, "dequant_gemv_q4_amd", "csrc")
+# The pages' end-to-end figure for the LFM2 WebGPU demo ("Crate inferencelayer", crate summary);
+# the hardware is not given, so it is context, not a target.
+PAGES_CONTEXT = {"value": 1400, "unit": "tok/s",
+                 "what": "LFM2 WebGPU demo decode (Q4_0 dequant-in-GEMV), hardware not given; "
+                         "context only, not comparable"}
 
 
 def log(*a):
@@ -43,15 +55,21 @@ def log(*a):
 
 
 class Bench:
-    """One workload: R rotated weight copies on the device and the launches of one step."""
+    """One workload: rotated weight copies on the device and the launches of one step."""
 
-    def __init__(self, name, weight_bytes, alg_bytes, dominant, step, dom, cpu, config):
+    def __init__(self, name, weight_bytes, alg_bytes, dominant, step, dom, cpu, config,
+                 flops=0):
         self.name, self.weight_bytes, self.alg_bytes = name, weight_bytes, alg_bytes
         self.dominant, self.step, self.dom, self.cpu, self.config = dominant, step, dom, cpu, config
+        self.flops = flops
 
 
 def _copies(total_bytes, warm):
     return 1 if warm else max(2, -(-COLD_BYTES // total_bytes))
+
+
+def _rotated(t, R):
+    return [t] + [t.clone() for _ in range(R - 1)]
 
 
 def make_decode_mlp(warm):
@@ -90,7 +108,8 @@ def make_decode_mlp(warm):
     alg = a["Wg"].nbytes + a["Wu"].nbytes + 2 * H * 4 + I * 4
     cfg = {"workload": w.name, "nb": 1, "format": "q4_0", "hidden": H, "inter": I,
            "launches_per_step": 2, "weight_copies": R, "cold": not warm}
-    return Bench(w.name, wbytes, alg, "qgemv_gus_nrm (q4_0, 2 x 8192x2048, nb=1)", step, gus, cpu, cfg)
+    return Bench(w.name, wbytes, alg, "qgemv_gus_nrm (q4_0, 2 x 8192x2048, nb=1)", step, gus,
+                 cpu, cfg, flops=2 * 3 * H * I)
 
 
 def make_lm_head(warm, nb):
@@ -103,7 +122,7 @@ def make_lm_head(warm, nb):
     a = w.arrays
     Wp = D.pack(q.Q4_0, a["W"], w.N, w.K)
     R = _copies(Wp.numel(), warm)
-    sets = [Wp] + [Wp.clone() for _ in range(R - 1)]
+    sets = _rotated(Wp, R)
     x = D.to_device(a["x"])
     logits = torch.empty((nb, w.N), dtype=torch.float32, device="cuda")
     idx = torch.empty((nb,), dtype=torch.int32, device="cuda")
@@ -119,9 +138,9 @@ def make_lm_head(warm, nb):
 
     alg = a["W"].nbytes + nb * w.K * 4 + nb * w.N * 4 + nb * 4
     cfg = {"workload": w.name, "nb": nb, "format": "q4_0", "N": w.N, "K": w.K,
-           "launches_per_step": 1, "weight_copies": R, "cold": not warm}
+           "launches_per_step": 2, "weight_copies": R, "cold": not warm}
     return Bench(w.name, a["W"].nbytes, alg, f"qgemv_argmax (q4_0, {w.N}x{w.K}, nb={nb})", step,
-                 step, cpu, cfg)
+                 step, cpu, cfg, flops=2 * nb * w.N * w.K)
 
 
 def make_gemv(warm, nb, rows=65536, hidden=2048):
@@ -136,7 +155,7 @@ def make_gemv(warm, nb, rows=65536, hidden=2048):
     a = w.arrays
     Wp = D.pack(q.Q4_0, a["W"], w.N, w.K)
     R = _copies(Wp.numel(), warm)
-    sets = [Wp] + [Wp.clone() for _ in range(R - 1)]
+    sets = _rotated(Wp, R)
     x = D.to_device(a["x"])
     y = torch.empty((nb, w.N), dtype=torch.float32, device="cuda")
 
@@ -149,10 +168,11 @@ def make_gemv(warm, nb, rows=65536, hidden=2048):
         return a["W"].nbytes
 
     alg = a["W"].nbytes + nb * w.K * 4 + nb * w.N * 4
-    cfg = {"workload": f"q4_0_gemv_{w.N}x{w.K}_nb{nb}", "nb": nb, "format": "q4_0", "N": w.N,
-           "K": w.K, "launches_per_step": 1, "weight_copies": R, "cold": not warm}
-    return Bench(cfg["workload"], a["W"].nbytes, alg, f"qgemv (q4_0, {w.N}x{w.K}, nb={nb})", step,
-                 step, cpu, cfg)
+    name = f"q4_0_gemv_{w.N}x{w.K}_nb{nb}"
+    cfg = {"workload": name, "nb": nb, "format": "q4_0", "N": w.N, "K": w.K,
+           "launches_per_step": 1, "weight_copies": R, "cold": not warm}
+    return Bench(name, a["W"].nbytes, alg, f"qgemv (q4_0, {w.N}x{w.K}, nb={nb})", step, step, cpu,
+                 cfg, flops=2 * nb * w.N * w.K)
 
 
 def make_qkv(warm, nb):
@@ -165,7 +185,7 @@ def make_qkv(warm, nb):
     a = w.arrays
     Wp = D.pack(q.Q8_0, a["W"], w.N, w.K)
     R = _copies(Wp.numel(), warm)
-    sets = [Wp] + [Wp.clone() for _ in range(R - 1)]
+    sets = _rotated(Wp, R)
     x, gamma = D.to_device(a["x"]), D.to_device(a["gamma"])
     y = torch.empty((nb, w.N), dtype=torch.float32, device="cuda")
 
@@ -181,7 +201,7 @@ def make_qkv(warm, nb):
     cfg = {"workload": w.name, "nb": nb, "format": "q8_0", "N": w.N, "K": w.K,
            "launches_per_step": 1, "weight_copies": R, "cold": not warm}
     return Bench(w.name, a["W"].nbytes, alg, f"qgemv_nrm (q8_0, {w.N}x{w.K}, nb={nb})", step, step,
-                 cpu, cfg)
+                 cpu, cfg, flops=2 * nb * w.N * w.K)
 
 
 def make_moe(warm):
@@ -195,7 +215,7 @@ def make_moe(warm):
     n_exp, topk, nb = w.params["n_exp"], w.params["topk"], w.nb
     Wp = D.pack(q.Q4_K, a["W"], n_exp * w.N, w.K)
     R = _copies(Wp.numel(), warm)
-    sets = [Wp] + [Wp.clone() for _ in range(R - 1)]
+    sets = _rotated(Wp, R)
     x, ids, p = D.to_device(a["x"]), D.to_device(a["ids"]), D.to_device(a["p"])
     y = torch.empty((nb, w.N), dtype=torch.float32, device="cuda")
     ws = D.workspace(q.OP_MOE, q.Q4_K, w.N, w.K, nb, n_exp, topk)
@@ -213,15 +233,38 @@ def make_moe(warm):
     wbytes = touched * per_exp
     alg = wbytes + nb * w.K * 4 + nb * w.N * 4 + 2 * nb * topk * w.N * 4 + 2 * nb * topk * 4
     cfg = {"workload": w.name, "nb": nb, "format": "q4_k", "N": w.N, "K": w.K, "n_exp": n_exp,
-           "topk": topk, "experts_touched": touched, "launches_per_step": 1,
+           "topk": topk, "experts_touched": touched, "launches_per_step": 2,
            "weight_copies": R, "cold": not warm}
     return Bench(w.name, wbytes, alg, f"qgemv_moe (q4_k, {touched} of {n_exp} x {w.N}x{w.K}, nb={nb})",
-                 step, step, cpu, cfg)
+                 step, step, cpu, cfg, flops=2 * nb * topk * w.N * w.K)
+
+
+def make_read(warm, nbytes=75497472, shape=(256, 1024)):
+    """The attainable read rate: the plain 16-byte-load read kernel (libqgbw.so) over the same
+    number of bytes as the gate's weights, rotated over >= 1 GiB like the GEMV, at one launch
+    shape."""
+    import torch
+    from dequant_gemv_q4_amd import bwref
+
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(7)
+    R = _copies(nbytes, warm)
+    sets = _rotated(buf, R)
+    grid, threads = shape
+    out = torch.empty(grid * threads // 64, dtype=torch.int32, device="cuda")
+
+    def step(i):
+        bwref.read(sets[i % R], nbytes, out, grid, threads)
+
+    name = f"read_{nbytes}B_{grid}x{threads}"
+    cfg = {"workload": name, "bytes": nbytes, "grid": grid, "threads": threads,
+           "launches_per_step": 1, "weight_copies": R, "cold": not warm}
+    return Bench(name, nbytes, nbytes, f"plain 16-byte read ({grid} x {threads})", step, step,
+                 lambda: 0, cfg)
 
 
 def make_copy(warm):
-    """A plain device-to-device copy of 256 MiB (torch's copy kernel): the attainable-bandwidth
-    reference and the known-size kernel that calibrates the HBM byte counters."""
+    """A plain device-to-device copy of 256 MiB (torch's copy kernel): the known-size kernel that
+    calibrates the HBM byte counters."""
     import torch
 
     n = 256 << 20
@@ -231,12 +274,9 @@ def make_copy(warm):
     def step(i):
         dst.copy_(srcs[i % len(srcs)])
 
-    def cpu():
-        return 0
-
     cfg = {"workload": "device_copy_256MiB", "bytes_read": n, "bytes_written": n,
            "launches_per_step": 1, "weight_copies": len(srcs), "cold": True}
-    return Bench(cfg["workload"], n, 2 * n, "torch copy_ (256 MiB)", step, step, cpu, cfg)
+    return Bench(cfg["workload"], n, 2 * n, "torch copy_ (256 MiB)", step, step, lambda: 0, cfg)
 
 
 def time_loop(fn, start, count, torch):
@@ -296,27 +336,96 @@ def kernel_sha256():
     code it was taken on."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_DIR)):
-        if name.endswith((".hip", ".h", ".cpp")):
+        if name.endswith((".hip", ".h", ".cpp")) and name != "bw_read.hip":
             h.update(name.encode())
             h.update(open(os.path.join(KERNEL_DIR, name), "rb").read())
     return h.hexdigest()
 
 
-def cpu_baseline(b, budget_s):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(b, reps=5):
+    """The f64 oracle on the same workload: 1 warm-up, then the median of `reps` full steps, with
+    all host threads and again with one."""
     import oracle
     oracle.build(force=False)
-    b.cpu()                                          # warm-up (page-in, thread pool)
-    t0 = time.perf_counter()
-    reps, moved = 0, 0
-    while True:
-        moved += b.cpu()
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(moved / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
+    out = {}
+    all_threads = oracle.threads()
+    for label, n in (("all", all_threads), ("one", 1)):
+        used = oracle.set_threads(n)
+        b.cpu()
+        ts = []
+        moved = 0
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            moved = b.cpu()
+            ts.append(time.perf_counter() - t0)
+        med = statistics.median(ts)
+        out[label] = {"threads": used, "median_s": med, "gbps": moved / med / 1e9}
+    oracle.set_threads(all_threads)
+    return {"value": round(out["all"]["gbps"], 4), "unit": "GB/s", "cores": out["all"]["threads"],
             "kind": "oracle",
-            "sample": f"{reps} full steps of {b.name} in the f64 oracle ({dt:.1f} s, OpenMP over output rows)"}
+            "sample": f"full steps of {b.name} in the f64 oracle, median of {reps} after one "
+                      f"warm-up (OpenMP over output rows)",
+            "ms_median": round(out["all"]["median_s"] * 1e3, 3),
+            "value_1thread": round(out["one"]["gbps"], 4),
+            "ms_median_1thread": round(out["one"]["median_s"] * 1e3, 3),
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "label": "f64 oracle (correctness reference, not a tuned CPU GEMV)"}
+
+
+def measure(b, steps, warmup, eager, torch):
+    """(ms per step graph-replayed, ms per step eager, ms per dominant launch)."""
+    for i in range(warmup):
+        b.step(i)
+    torch.cuda.synchronize()
+    ms_eager = time_loop(b.step, warmup, steps, torch)
+    ms_step = ms_eager if eager else time_graph(b.step, warmup, steps, torch)
+    if b.dom is b.step:
+        ms_dom = ms_step
+    else:
+        for i in range(warmup):
+            b.dom(i)
+        ms_dom = (time_loop if eager else time_graph)(b.dom, warmup, steps, torch)
+    return ms_step, ms_eager, ms_dom
+
+
+def summary(b, ms_step, ms_eager, ms_dom):
+    value = b.weight_bytes / (ms_step * 1e-3) / 1e9
+    achieved = b.alg_bytes / (ms_dom * 1e-3) / 1e9
+    out = {"workload": b.name, "value": round(value, 2), "unit": "GB/s",
+           "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+           "us_per_step": round(ms_step * 1e3, 3), "us_per_step_eager": round(ms_eager * 1e3, 3),
+           "roofline": {"bound": "hbm", "kernel": b.dominant, "achieved": round(achieved, 2),
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                        "traffic": stored_traffic(b.name), "alg_bytes_per_launch": b.alg_bytes,
+                        "us_per_launch": round(ms_dom * 1e3, 3)},
+           "config": b.config}
+    if b.flops:
+        out["tflops"] = round(b.flops / (ms_step * 1e-3) / 1e12, 3)
+    return out
+
+
+def run_extra(name, factory, steps, warmup, torch):
+    log(f"bench: extra {name}")
+    b = factory()
+    ms_step, ms_eager, ms_dom = measure(b, steps, warmup, False, torch)
+    out = summary(b, ms_step, ms_eager, ms_dom)
+    log(f"bench:   {out['us_per_step']:.2f} us/step, {out['value']:.0f} GB/s "
+        f"({out['pct_of_hbm_peak']:.1f}% of 8 TB/s)")
+    del b
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -324,14 +433,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="decode_mlp",
-                    choices=["decode_mlp", "lm_head", "gemv", "qkv", "moe", "copy"])
+    ap.add_argument("--workload", default="gemv",
+                    choices=["gemv", "decode_mlp", "lm_head", "qkv", "moe", "read", "copy"])
     ap.add_argument("--nb", type=int, default=None)
     ap.add_argument("--rows", type=int, default=65536, help="gemv workload: output rows")
     ap.add_argument("--hidden", type=int, default=2048, help="gemv workload: reduction length")
     ap.add_argument("--warm", action="store_true", help="reuse one weight copy (cache-assisted)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--extra-steps", type=int, default=200)
     ap.add_argument("--eager", action="store_true",
                     help="time launches issued from Python instead of one HIP graph replay")
     args = ap.parse_args()
@@ -350,43 +460,32 @@ def main():
     q.lib()
     torch.cuda.set_device(0)
 
-    if args.workload == "decode_mlp":
+    wl_name = args.workload
+    if wl_name == "decode_mlp":
         b = make_decode_mlp(args.warm)
-    elif args.workload == "lm_head":
+    elif wl_name == "lm_head":
         b = make_lm_head(args.warm, args.nb or 1)
-    elif args.workload == "gemv":
+    elif wl_name == "gemv":
         b = make_gemv(args.warm, args.nb or 1, args.rows, args.hidden)
-    elif args.workload == "qkv":
+    elif wl_name == "qkv":
         b = make_qkv(args.warm, args.nb or 16)
-    elif args.workload == "copy":
+    elif wl_name == "read":
+        b = make_read(args.warm)
+        args.no_cpu = True
+    elif wl_name == "copy":
         b = make_copy(args.warm)
         args.no_cpu = True
     else:
         b = make_moe(args.warm)
     log(f"bench: {b.name}, copies={b.config['weight_copies']}, warmup={args.warmup}, steps={args.steps}")
 
-    for i in range(args.warmup):
-        b.step(i)
-    torch.cuda.synchronize()
-    # the timed steps: captured in one HIP graph and replayed (launches back to back, no
-    # per-launch host work); the same steps issued eagerly from Python are reported beside them
-    ms_eager = time_loop(b.step, args.warmup, args.steps, torch)
-    if args.eager:
-        ms_step = ms_eager
-    else:
-        ms_step = time_graph(b.step, args.warmup, args.steps, torch)
-    log(f"bench: {ms_step * 1e3:.2f} us per step ({ms_eager * 1e3:.2f} us issued eagerly)")
-    for i in range(args.warmup):
-        b.dom(i)
-    ms_dom = (time_loop if args.eager else time_graph)(b.dom, args.warmup, args.steps, torch)
-    log(f"bench: dominant launch {ms_dom * 1e3:.2f} us")
-
-    value = b.weight_bytes / (ms_step * 1e-3) / 1e9
-    achieved = b.alg_bytes / (ms_dom * 1e-3) / 1e9
-    traffic = stored_traffic(b.name)
+    ms_step, ms_eager, ms_dom = measure(b, args.steps, args.warmup, args.eager, torch)
+    log(f"bench: {ms_step * 1e3:.2f} us per step ({ms_eager * 1e3:.2f} us issued eagerly), "
+        f"dominant launch {ms_dom * 1e3:.2f} us")
+    s = summary(b, ms_step, ms_eager, ms_dom)
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": s["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -399,17 +498,43 @@ def main():
         "vs_baseline": None,
         "dtype": "f16xf16->f32",
         "data": "synthetic",
-        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "pct_of_hbm_peak": s["pct_of_hbm_peak"],
         "config": b.config,
-        "roofline": {"bound": "hbm", "kernel": b.dominant, "achieved": round(achieved, 2),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "alg_bytes_per_launch": b.alg_bytes, "us_per_launch": round(ms_dom * 1e3, 3)},
+        "roofline": s["roofline"],
         "cpu_baseline": None,
+        "pages_context": PAGES_CONTEXT,
     }
+    if "tflops" in s:
+        out["tflops"] = s["tflops"]
+
+    cpu_b = Bench(b.name, 0, 0, "", None, None, b.cpu, {})   # the oracle needs host arrays only
+    if not args.no_extras and wl_name == "gemv" and not args.warm and args.nb in (None, 1):
+        del b
+        torch.cuda.empty_cache()
+        es, ew = args.extra_steps, min(args.warmup, 20)
+        extras = {}
+        extras["gemv_nb16"] = run_extra("gemv nb=16", lambda: make_gemv(False, 16), es, ew, torch)
+        extras["moe_q4k_nb16"] = run_extra("moe", lambda: make_moe(False), es, ew, torch)
+        extras["qkv_q8_nb16"] = run_extra("qkv nb=16", lambda: make_qkv(False, 16), es, ew, torch)
+        extras["decode_mlp"] = run_extra("decode mlp", lambda: make_decode_mlp(False), es, ew, torch)
+        extras["lm_head_nb1"] = run_extra("lm_head", lambda: make_lm_head(False, 1), es, ew, torch)
+        w = run_extra("gemv warm", lambda: make_gemv(True, 1), es, ew, torch)
+        w["label"] = "cache-assisted: one weight copy reused, served in part by the 256 MB MALL"
+        extras["gemv_nb1_warm"] = w
+        # attainable: the plain read kernel over the gate's bytes at a few launch shapes (best kept)
+        best = None
+        for shape in ((256, 1024), (512, 1024), (1024, 512), (2048, 256)):
+            r = run_extra(f"read {shape}", lambda: make_read(False, shape=shape), es, ew, torch)
+            if best is None or r["value"] > best["value"]:
+                best = r
+        best["label"] = "plain 16-byte non-temporal read of the same bytes, best launch shape"
+        extras["read_attainable"] = best
+        out["attainable_read_gbps"] = best["value"]
+        out["pct_of_attainable"] = round(100 * out["value"] / best["value"], 2)
+        out["extras"] = extras
     if not args.no_cpu:
         log("bench: timing the f64 oracle on this host")
-        out["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(cpu_b)
     print(json.dumps(out), flush=True)
 
 

@@ -19,6 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqgemv.so")
+BW_LIB = os.path.join(PKG, "libqgbw.so")       # the benchmark's bandwidth reference (bw_read.hip)
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["gemv_kernels.hip", "stream_kernels.hip", "mfma_kernels.hip", "abi.cpp"]
 ARCH = "gfx950"
@@ -65,7 +66,20 @@ def build(defines=(), save_temps: str | None = None, out: str = LIB, verbose: bo
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
+    if out == LIB:
+        build_bw(verbose)
     return out
+
+
+def build_bw(verbose: bool = False) -> str:
+    """The bandwidth-reference read kernel bench.py times (a library of its own)."""
+    tmp = BW_LIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-shared", "-o", tmp, os.path.join(CSRC, "bw_read.hip")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, BW_LIB)
+    return BW_LIB
 
 
 def main(argv=None):

@@ -25,7 +25,6 @@
 #ifndef QG_LDS_BUDGET
 #define QG_LDS_BUDGET (64 * 1024)  // staged x bytes per workgroup (two workgroups per CU fit)
 #endif
-#define QG_ARGMAX_MAX_GRID 4096    // argmax partial keys are kept per workgroup in the workspace
 
 namespace qg {
 
@@ -493,9 +492,10 @@ int qgemv_argmax(int fmt, const void *W, int64_t N, int64_t K, const float *x, i
         return QG_ERR_ALIGN;
     if ((int64_t)ws_bytes < ws_argmax_bytes(nb))
         return QG_ERR_WORKSPACE;
-    const int64_t lb = (int64_t)nb * N * 4;
-    if (overlap(idx, nb * 4, logits, lb) || overlap(ws, (int64_t)ws_bytes, logits, lb) ||
-        overlap(ws, (int64_t)ws_bytes, idx, nb * 4) || overlap(idx, nb * 4, x, (int64_t)nb * K * 4))
+    const int64_t lb = (int64_t)nb * N * 4, xb = (int64_t)nb * K * 4, wsb = (int64_t)ws_bytes;
+    if (overlap(idx, nb * 4, logits, lb) || overlap(ws, wsb, logits, lb) ||
+        overlap(ws, wsb, idx, nb * 4) || overlap(idx, nb * 4, x, xb) ||
+        overlap(idx, nb * 4, W, L.total) || overlap(ws, wsb, x, xb) || overlap(ws, wsb, W, L.total))
         return QG_ERR_ALIAS;
     GemvArgs a = gemv_args(L, W, N, K, x, nb, logits);
     a.idx = idx;
@@ -529,9 +529,11 @@ int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t 
         return QG_ERR_SHAPE;
     if ((int64_t)ws_bytes < ws_moe_bytes(N, nb, topk))
         return QG_ERR_WORKSPACE;
-    const int64_t yb = (int64_t)nb * N * 4;
-    if (overlap(y, yb, W_experts, LE.total) || overlap(y, yb, ws, (int64_t)ws_bytes) ||
-        overlap(y, yb, ids, (int64_t)nb * topk * 4) || overlap(y, yb, wts, (int64_t)nb * topk * 4))
+    const int64_t yb = (int64_t)nb * N * 4, wsb = (int64_t)ws_bytes, rb = (int64_t)nb * topk * 4;
+    if (overlap(y, yb, W_experts, LE.total) || overlap(y, yb, ws, wsb) || overlap(y, yb, ids, rb) ||
+        overlap(y, yb, wts, rb) || overlap(ws, wsb, W_experts, LE.total) ||
+        overlap(ws, wsb, x, (int64_t)nb * K * 4) || overlap(ws, wsb, ids, rb) ||
+        overlap(ws, wsb, wts, rb))
         return QG_ERR_ALIAS;
     MoeArgs a;
     memset(&a, 0, sizeof(a));

@@ -190,27 +190,42 @@ __device__ __forceinline__ ChunkScale chunk_scale(const uint4 &s, int q /* chunk
     return cs;
 }
 
-// Decode the 16-byte chunk into the per-element factors the dot multiplies (nibble or biased
-// byte values as f32, exact), in dot order.
+// Q4_K sub-block centre.  With a = d sc and b = dmin m the weights are w = a n - b =
+// a (n - c) + (a c - b) for any integer c; c = the integer nearest b / a, kept in [0, 63], makes
+// a |n - c| at most about 2 |w| for every n != c and |a c - b| at most about |w| for every weight,
+// so a dot over (n - c) and the term (a c - b) sum x carry no cancellation: their rounding is
+// relative to sum |w x| (for b / a outside [0, 63] every |w| is already at least 48 a).  a = 0 or
+// NaN ratios give c = 0 (any c is exact there).
+__device__ __forceinline__ float k_center(float a, float b)
+{
+    return fminf(fmaxf(rintf(b * __builtin_amdgcn_rcpf(a)), 0.f), 63.f);
+}
+
+// Decode the 16-byte chunk into the per-element factors the dot multiplies, exact in f32 and in
+// dot order: Q4_0 the signed q - 8, Q8_0 the signed byte, Q4_K the nibble (its -dmin m term is
+// applied to the chunk's x sums).  The Q4_0 and Q8_0 dots then hold no offset to cancel.
 template <int FMT>
 __device__ __forceinline__ void decode_chunk(const uint4 &q, float *w)
 {
     if constexpr (FMT == FQ8_0) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const uint32_t v = ucomp(q, k) ^ 0x80808080u;   // q + 128 as an unsigned byte
-            w[4 * k + 0] = ub0(v); w[4 * k + 1] = ub1(v);
-            w[4 * k + 2] = ub2(v); w[4 * k + 3] = ub3(v);
+            const uint32_t v = ucomp(q, k);
+            w[4 * k + 0] = (float)(int8_t)(v & 0xffu);
+            w[4 * k + 1] = (float)(int8_t)((v >> 8) & 0xffu);
+            w[4 * k + 2] = (float)(int8_t)((v >> 16) & 0xffu);
+            w[4 * k + 3] = (float)(int8_t)(v >> 24);
         }
     } else {
+        const float off = FMT == FQ4_0 ? 8.0f : 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const uint32_t v = ucomp(q, k);
             const uint32_t lo = v & 0x0f0f0f0fu, hi = (v >> 4) & 0x0f0f0f0fu;
-            w[8 * k + 0] = ub0(lo); w[8 * k + 1] = ub1(lo);
-            w[8 * k + 2] = ub2(lo); w[8 * k + 3] = ub3(lo);
-            w[8 * k + 4] = ub0(hi); w[8 * k + 5] = ub1(hi);
-            w[8 * k + 6] = ub2(hi); w[8 * k + 7] = ub3(hi);
+            w[8 * k + 0] = ub0(lo) - off; w[8 * k + 1] = ub1(lo) - off;
+            w[8 * k + 2] = ub2(lo) - off; w[8 * k + 3] = ub3(lo) - off;
+            w[8 * k + 4] = ub0(hi) - off; w[8 * k + 5] = ub1(hi) - off;
+            w[8 * k + 6] = ub2(hi) - off; w[8 * k + 7] = ub3(hi) - off;
         }
     }
 }
@@ -233,7 +248,7 @@ __device__ __forceinline__ float chunk_dot(const float *w, const float4 *xv, con
             dot = fmaf(w[8 * k + 6], xv[4 + k].z, dot);
             dot = fmaf(w[8 * k + 7], xv[4 + k].w, dot);
         }
-        return fmaf(cs.a, fmaf(-8.0f, Sv[0], dot), acc);
+        return fmaf(cs.a, dot, acc);
     } else if constexpr (FMT == FQ8_0) {
         float dot = 0.f;
 #pragma unroll
@@ -243,24 +258,26 @@ __device__ __forceinline__ float chunk_dot(const float *w, const float4 *xv, con
             dot = fmaf(w[4 * k + 2], xv[k].z, dot);
             dot = fmaf(w[4 * k + 3], xv[k].w, dot);
         }
-        return fmaf(cs.a, fmaf(-128.0f, Sv[0], dot), acc);
+        return fmaf(cs.a, dot, acc);
     } else {
+        // centred sub-blocks (k_center): dots over n - c, then the (a c - b) sum x terms
+        const float cA = k_center(cs.a, cs.b), cB = k_center(cs.a2, cs.b2);
         float da = 0.f, db = 0.f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            da = fmaf(w[8 * k + 0], xv[k].x, da);
-            da = fmaf(w[8 * k + 1], xv[k].y, da);
-            da = fmaf(w[8 * k + 2], xv[k].z, da);
-            da = fmaf(w[8 * k + 3], xv[k].w, da);
-            db = fmaf(w[8 * k + 4], xv[4 + k].x, db);
-            db = fmaf(w[8 * k + 5], xv[4 + k].y, db);
-            db = fmaf(w[8 * k + 6], xv[4 + k].z, db);
-            db = fmaf(w[8 * k + 7], xv[4 + k].w, db);
+            da = fmaf(w[8 * k + 0] - cA, xv[k].x, da);
+            da = fmaf(w[8 * k + 1] - cA, xv[k].y, da);
+            da = fmaf(w[8 * k + 2] - cA, xv[k].z, da);
+            da = fmaf(w[8 * k + 3] - cA, xv[k].w, da);
+            db = fmaf(w[8 * k + 4] - cB, xv[4 + k].x, db);
+            db = fmaf(w[8 * k + 5] - cB, xv[4 + k].y, db);
+            db = fmaf(w[8 * k + 6] - cB, xv[4 + k].z, db);
+            db = fmaf(w[8 * k + 7] - cB, xv[4 + k].w, db);
         }
         acc = fmaf(cs.a, da, acc);
-        acc = fmaf(-cs.b, Sv[0], acc);
+        acc = fmaf(fmaf(cs.a, cA, -cs.b), Sv[0], acc);
         acc = fmaf(cs.a2, db, acc);
-        acc = fmaf(-cs.b2, Sv[1], acc);
+        acc = fmaf(fmaf(cs.a2, cB, -cs.b2), Sv[1], acc);
         return acc;
     }
 }

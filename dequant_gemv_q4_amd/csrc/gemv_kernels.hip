@@ -4,9 +4,9 @@
 //   * x (or rmsnorm(x)) is staged once per workgroup in LDS as float4s laid out
 //     [row][float4-in-chunk][chunk], so lane i of a wave reads float4 i: conflict-free ds_read_b128.
 //   * each lane issues one aligned 16-byte global load per chunk and row (32 Q4 weights or 16 Q8
-//     weights), decodes in registers (byte masks + v_cvt_f32_ubyteN) and FMAs in f32.
-//   * the block offset (Q4_0's -8, Q8_0's +128 bias, Q4_K's -dmin*m) is folded into a per-chunk
-//     sum S of x, summed in the SAME order as the dot, so all-zero weights give an exact 0.
+//     weights), decodes in registers to the exact signed weights (q - 8, the signed byte, or the
+//     Q4_K nibble) and FMAs in f32.
+//   * Q4_K's -dmin*m term multiplies a per-chunk sum S of x, summed in the order the dot uses.
 //   * a lane-group butterfly reduces the LPR partials; every lane holds the bitwise same total.
 //
 // Formats and formulas ("Crate inferencelayer" docs): Q4_0 w = (q - 8) d (q4_0_to_q8_0n);

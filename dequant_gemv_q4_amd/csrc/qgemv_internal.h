@@ -13,6 +13,10 @@ enum Fmt { FQ4_0 = 2, FQ8_0 = 8, FQ4_K = 12 };
 // Epilogue kinds of the vector GEMV kernel.
 enum Epi { E_STORE = 0, E_RES = 1, E_GUS = 2, E_ARGMAX = 3 };
 
+// Argmax: partial keys are kept per workgroup (and batch row), so its launches have at most this
+// many workgroups.
+#define QG_ARGMAX_MAX_GRID 4096
+
 // Routed experts: at most this many (row, slot) pairs per call (16 rows x top-8).
 #define QG_PAIRS_MAX 128
 // Routed experts: threads per workgroup of the common variants, and of the variants that hold

@@ -10,10 +10,10 @@
 //
 // Decode: a Q4_0 byte holds element j in its low nibble and element j + 16 in its high nibble
 // (GGUF order).  Nibbles become exact f16 weights by an and-or into the mantissa of 1024.0, two
-// per instruction, and meet x through v_dot2_f32_f16 (two f16 products, exact in f32, added to an
-// f32 accumulator).  The -8 offset of Q4_0 ("Crate inferencelayer" docs, q4_0_to_q8_0n:
-// q8 = nib - 8) and the 1024 mantissa offset are removed by subtracting the same dot chain run
-// on the constant weight pattern, so eight-valued nibbles (b = 0x88) give exactly 0.
+// per instruction, then one packed f16 add removes the 1024 mantissa offset together with the
+// format's own offset (Q4_0's -8, "Crate inferencelayer" docs, q4_0_to_q8_0n: q8 = nib - 8), so
+// the dot operands are the exact signed weights; they meet x through v_dot2_f32_f16 (two f16
+// products, exact in f32, added to an f32 accumulator).  No offset is cancelled in the sums.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -286,9 +286,10 @@ __device__ __forceinline__ void xstage_store(const XStage<NB, NRM, XPT> &st, int
 // factor 1/16.  x: the values of each chunk (the 16 or 32 x elements one 16-byte quant chunk
 // multiplies) are scaled by a power of two that puts their largest |value| in [2^14, 2^15), then
 // rounded to f16 (relative error at most 2^-11, far inside the stated 1e-3 * sum|w x| bound); the
-// scale is undone, exactly, on the chunk's partial sums.  The 1024 offsets (and
-// Q4_0's -8, Q8_0's +128 bias) are removed by subtracting the same dot chain run on the constant
-// weight pattern (n = 8, u = 128, n = 0), in the same order, so all-offset blocks give exactly 0.
+// scale is undone, exactly, on the chunk's partial sums.  The 1024 mantissa offset, and Q4_0's
+// -8 and Q8_0's +128 bias, are removed from every weight pair by one exact packed f16 add before
+// the dot, so a dot sums exact products of the true weights: its rounding error is relative to
+// sum |w x|, whatever the weights (a weight pattern of mostly-zero weights cancels nothing).
 typedef _Float16 qg_h2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float c)
@@ -309,9 +310,9 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b)
 template <int FMT, int NB, int CPL = 1>
 struct XH {
     static constexpr int NP = FMT == FQ8_0 ? 8 : 16;   // pairs per 16-byte chunk
-    static constexpr int NZ = FMT == FQ4_K ? 4 : 1;
+    static constexpr int NZ = FMT == FQ4_K ? 2 : 1;
     uint32_t p[NB][CPL][NP];
-    float z[NB][CPL][NZ];   // Q4_0: chain(n = 8); Q8_0: chain(u = 128); Q4_K: chain_A(0), chain_B(0), S_A, S_B
+    float z[NB][CPL][NZ];   // Q4_K: S_A, S_B, the x sums of the two sub-blocks (others: unused)
 };
 
 // (v & m) | c in one instruction.  A three-operand instruction of this target takes no literal
@@ -323,9 +324,10 @@ __device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t m, uint32_t c)
     return r;
 }
 
-// Loop-invariant operands of w_pairs, kept in VGPRs.
+// Loop-invariant operands of w_pairs, kept in VGPRs: the masks, the 1024.0 pair, and the f16
+// pairs added to remove the offsets (low nibble / byte, high nibble held x16).
 struct WConst {
-    uint32_t m_lo, m_hi, c;
+    uint32_t m_lo, m_hi, c, off_lo, off_hi;
 };
 
 template <int FMT>
@@ -335,24 +337,41 @@ __device__ __forceinline__ WConst w_const()
     k.m_lo = FMT == FQ8_0 ? 0x00FF00FFu : 0x000F000Fu;
     k.m_hi = 0x00F000F0u;
     k.c = 0x64006400u;
-    asm volatile("" : "+v"(k.m_lo), "+v"(k.m_hi), "+v"(k.c));
+    // Q4_0: -1032 (1024 + n -> n - 8), -1152 (1024 + 16 n -> 16 (n - 8)); Q8_0: -1152
+    // (1024 + q + 128 -> q); Q4_K: set per sub-block from its centre (see compute_group_h)
+    k.off_lo = FMT == FQ4_0 ? 0xE408E408u : FMT == FQ8_0 ? 0xE480E480u : 0xE400E400u;
+    k.off_hi = FMT == FQ4_0 ? 0xE480E480u : 0xE400E400u;
+    asm volatile("" : "+v"(k.m_lo), "+v"(k.m_hi), "+v"(k.c), "+v"(k.off_lo), "+v"(k.off_hi));
     return k;
 }
 
-// Weight pairs of one dword of a 16-byte chunk, in dot order.
+// Exact packed f16 sum of two pairs (every result here is a small integer times a power of two).
+__device__ __forceinline__ uint32_t h2_add(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(qg_h2, a) + __builtin_bit_cast(qg_h2, b));
+}
+
+// The f16 value v (exact: an integer below 2048 in magnitude) in both halves of a pair.
+__device__ __forceinline__ uint32_t h2_splat(float v)
+{
+    const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)v);
+    return h | (h << 16);
+}
+
+// Exact signed weight pairs of one dword of a 16-byte chunk, in dot order.
 template <int FMT>
 __device__ __forceinline__ void w_pairs(uint32_t q, const WConst &k, uint32_t *w)
 {
     if constexpr (FMT == FQ8_0) {
-        const uint32_t u = q ^ 0x80808080u;                 // q + 128 as unsigned bytes
-        w[0] = and_or(u, k.m_lo, k.c);                      // bytes 0, 2
-        w[1] = and_or(u >> 8, k.m_lo, k.c);                 // bytes 1, 3
+        const uint32_t u = q ^ 0x80808080u;                          // q + 128 as unsigned bytes
+        w[0] = h2_add(and_or(u, k.m_lo, k.c), k.off_lo);             // bytes 0, 2
+        w[1] = h2_add(and_or(u >> 8, k.m_lo, k.c), k.off_lo);        // bytes 1, 3
     } else {
         const uint32_t t = q >> 8;
-        w[0] = and_or(q, k.m_lo, k.c);                      // low nibbles of bytes 0, 2
-        w[1] = and_or(q, k.m_hi, k.c);                      // high nibbles of bytes 0, 2 (x16)
-        w[2] = and_or(t, k.m_lo, k.c);                      // low nibbles of bytes 1, 3
-        w[3] = and_or(t, k.m_hi, k.c);                      // high nibbles of bytes 1, 3 (x16)
+        w[0] = h2_add(and_or(q, k.m_lo, k.c), k.off_lo);   // low nibbles of bytes 0, 2
+        w[1] = h2_add(and_or(q, k.m_hi, k.c), k.off_hi);   // high nibbles of bytes 0, 2 (x16)
+        w[2] = h2_add(and_or(t, k.m_lo, k.c), k.off_lo);   // low nibbles of bytes 1, 3
+        w[3] = h2_add(and_or(t, k.m_hi, k.c), k.off_hi);   // high nibbles of bytes 1, 3 (x16)
     }
 }
 
@@ -387,7 +406,8 @@ __device__ __forceinline__ void chunk_chains(const uint32_t (&w)[FMT == FQ8_0 ? 
     }
 }
 
-// x pairs of one chunk (its float4s xv in chunk_elem order), scaled by sc, and the offset sums.
+// x pairs of one chunk (its float4s xv in chunk_elem order), scaled by sc; Q4_K also the sums of
+// the two sub-blocks' rounded, scaled x (the -dmin m terms multiply them).
 template <int FMT>
 __device__ __forceinline__ void x_pairs(const float4 *xv, float sc, uint32_t *p, float *z)
 {
@@ -397,11 +417,7 @@ __device__ __forceinline__ void x_pairs(const float4 *xv, float sc, uint32_t *p,
             p[2 * i + 0] = pack_h2(xv[i].x * sc, xv[i].z * sc);
             p[2 * i + 1] = pack_h2(xv[i].y * sc, xv[i].w * sc);
         }
-        uint32_t wz[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            wz[i] = 0x64806480u;                            // u = 128 (q = 0)
-        chunk_chains<FMT>(wz, p, z);
+        z[0] = 0.f;
     } else {
         const float sh = sc * 0.0625f;                       // high-nibble pairs carry 1/16
 #pragma unroll
@@ -411,19 +427,9 @@ __device__ __forceinline__ void x_pairs(const float4 *xv, float sc, uint32_t *p,
             p[4 * i + 2] = pack_h2(xv[i].y * sc, xv[i].w * sc);
             p[4 * i + 3] = pack_h2(xv[4 + i].y * sh, xv[4 + i].w * sh);
         }
-        uint32_t wz[16];
         if constexpr (FMT == FQ4_0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                wz[4 * i + 0] = wz[4 * i + 2] = 0x64086408u;   // n = 8
-                wz[4 * i + 1] = wz[4 * i + 3] = 0x64806480u;   // 16 n = 128
-            }
-            chunk_chains<FMT>(wz, p, z);
+            z[0] = 0.f;
         } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                wz[i] = 0x64006400u;                          // n = 0
-            chunk_chains<FMT>(wz, p, z);
             // S_A, S_B: the sums of the (rounded, scaled) x of the two sub-blocks
             float sa = 0.f, sb = 0.f;
 #pragma unroll
@@ -435,8 +441,8 @@ __device__ __forceinline__ void x_pairs(const float4 *xv, float sc, uint32_t *p,
                 sa += (float)a0.x; sa += (float)a0.y; sa += (float)a1.x; sa += (float)a1.y;
                 sb += (float)b0.x; sb += (float)b0.y; sb += (float)b1.x; sb += (float)b1.y;
             }
-            z[2] = sa;
-            z[3] = sb * 16.0f;
+            z[0] = sa;
+            z[1] = sb * 16.0f;
         }
     }
 }
@@ -523,22 +529,33 @@ __device__ __forceinline__ void compute_group_h(const GroupBuf<FMT, CPL, MATS, R
                 cs.a = cs.b = cs.a2 = cs.b2 = 0.f;
             uint32_t w[NP];
             const uint4 q = b.q[m][u][i];
-            w_pairs<FMT>(q.x, k, w + 0 * (NP / 4));
-            w_pairs<FMT>(q.y, k, w + 1 * (NP / 4));
-            w_pairs<FMT>(q.z, k, w + 2 * (NP / 4));
-            w_pairs<FMT>(q.w, k, w + 3 * (NP / 4));
+            WConst kk = k;
+            float resA = 0.f, resB = 0.f;
+            if constexpr (FMT == FQ4_K) {
+                // centred sub-blocks (k_center): the pairs hold n - c (16 (n - c) for the high
+                // nibbles) exactly, and (a c - b) multiplies the sub-block's x sum
+                const float cA = k_center(cs.a, cs.b), cB = k_center(cs.a2, cs.b2);
+                kk.off_lo = h2_splat(-1024.0f - cA);
+                kk.off_hi = h2_splat(-1024.0f - 16.0f * cB);
+                resA = fmaf(cs.a, cA, -cs.b);
+                resB = fmaf(cs.a2, cB, -cs.b2);
+            }
+            w_pairs<FMT>(q.x, kk, w + 0 * (NP / 4));
+            w_pairs<FMT>(q.y, kk, w + 1 * (NP / 4));
+            w_pairs<FMT>(q.z, kk, w + 2 * (NP / 4));
+            w_pairs<FMT>(q.w, kk, w + 3 * (NP / 4));
 #pragma unroll
             for (int r = 0; r < NB; ++r) {
                 float d[2];
                 chunk_chains<FMT>(w, xh.p[r][i], d);
                 float &a = acc[u * NBX + r][m];
                 if constexpr (FMT == FQ4_K) {
-                    a = fmaf(cs.a, d[0] - xh.z[r][i][0], a);
-                    a = fmaf(-cs.b, xh.z[r][i][2], a);
-                    a = fmaf(cs.a2, d[1] - xh.z[r][i][1], a);
-                    a = fmaf(-cs.b2, xh.z[r][i][3], a);
+                    a = fmaf(cs.a, d[0], a);
+                    a = fmaf(resA, xh.z[r][i][0], a);
+                    a = fmaf(cs.a2, d[1], a);
+                    a = fmaf(resB, xh.z[r][i][1], a);
                 } else {
-                    a = fmaf(cs.a, d[0] - xh.z[r][i][0], a);
+                    a = fmaf(cs.a, d[0], a);
                 }
             }
         }
@@ -957,7 +974,6 @@ void k_moe(MoeArgs a)
     constexpr int ITX = R * NBX, IPX = pow2_ceil(ITX);
     constexpr int LG = IPX == 1 ? 0 : IPX == 2 ? 1 : IPX == 4 ? 2 : IPX == 8 ? 3 : 4;
     constexpr int NT = moe_threads(FMT, CPL, PD), WV = NT / 64;
-    constexpr int XF4 = Fc<FMT>::XF4;
     constexpr int XPL = 8;   // float4s in flight per loader lane while a row is copied
     extern __shared__ float4 lds4[];
     __shared__ int s_pair[QG_PAIRS_MAX][NBX];
@@ -1169,11 +1185,8 @@ void k_moe(MoeArgs a)
                 dst[k * 64] = make_uint4(pp[4 * k], pp[4 * k + 1], pp[4 * k + 2], pp[4 * k + 3]);
             uint4 zq = make_uint4(0u, 0u, 0u, 0u);
             zq.x = __float_as_uint(zz[0]);
-            if constexpr (NZ == 4) {
+            if constexpr (NZ == 2)
                 zq.y = __float_as_uint(zz[1]);
-                zq.z = __float_as_uint(zz[2]);
-                zq.w = __float_as_uint(zz[3]);
-            }
             dst[(NP / 4) * 64] = zq;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -1222,11 +1235,8 @@ void k_moe(MoeArgs a)
                                     }
                                     const uint4 zq = src[(NP / 4) * 64];
                                     xh.z[r][i][0] = __uint_as_float(zq.x);
-                                    if constexpr (NZ == 4) {
+                                    if constexpr (NZ == 2)
                                         xh.z[r][i][1] = __uint_as_float(zq.y);
-                                        xh.z[r][i][2] = __uint_as_float(zq.z);
-                                        xh.z[r][i][3] = __uint_as_float(zq.w);
-                                    }
                                 }
                         my_rs = s_rs[ls * NBX + (my_r < nbc ? my_r : 0)];
                     }

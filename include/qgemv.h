@@ -20,7 +20,8 @@
  *    must span the whole qgemv_packed_bytes(fmt, N, K): the kernels may read into the padding
  *    after each plane (whole dwords of the scale plane), never past it.
  *  - Every pointer of a compute call is a DEVICE pointer (HIP device memory).  The caller owns
- *    all memory; the library never allocates or frees and keeps no state between calls.
+ *    all memory; the library never allocates or frees and carries no data from one call to the
+ *    next (on the host it caches per-device occupancy queries, which only shape launches).
  *  - x is f32 [nb][K], outputs f32 [nb][N], all row-major and contiguous.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every call only
  *    enqueues work on that stream and returns; nothing synchronizes the host.
@@ -53,7 +54,8 @@ enum {
     QG_ERR_FORMAT = 2,     /* unknown format id */
     QG_ERR_SHAPE = 3,      /* N < 1, nb outside [1, 16], K not a positive multiple of the block,
                               topk outside [1, 8], n_exp < 1, or a size beyond the limits */
-    QG_ERR_ALIGN = 4,      /* W not 256-B aligned, or x / y / other f32 arrays not 16-B aligned */
+    QG_ERR_ALIGN = 4,      /* W or a workspace not 256-B aligned, x or gamma not 16-B aligned, or
+                              an output, residual, id or weight array not 4-B aligned */
     QG_ERR_WORKSPACE = 5,  /* ws smaller than qgemv_workspace_bytes() */
     QG_ERR_LAUNCH = 6,     /* the HIP launch reported an error */
     QG_ERR_ALIAS = 7       /* an output overlaps an input in a way the call does not allow */

@@ -29,6 +29,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+int orc_threads(void);
+
 #define ORC_Q4_0 2
 #define ORC_Q8_0 8
 #define ORC_Q4_K 12
@@ -324,6 +326,20 @@ int orc_moe(int fmt, const uint8_t *W, int64_t n_exp, int64_t N, int64_t K, cons
     free(ye);
     free(ae);
     return err;
+}
+
+/* Sets the number of OpenMP threads later parallel loops use (the bench times the oracle with
+ * one thread and with all of them); returns the number now in effect. */
+int orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return orc_threads();
 }
 
 /* Number of OpenMP threads the oracle's parallel loops use. */

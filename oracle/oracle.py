@@ -85,6 +85,11 @@ def threads() -> int:
     return int(_load().orc_threads())
 
 
+def set_threads(n: int) -> int:
+    """Use n OpenMP threads from now on; returns the count in effect."""
+    return int(_load().orc_set_threads(int(n)))
+
+
 def f16(bits: int) -> float:
     return float(_load().orc_f16(int(bits) & 0xFFFF))
 

@@ -57,9 +57,11 @@ def assert_within(got, ref, tol, what=""):
 
 
 def gus_tol(g, u, Ag, Au):
-    """Tolerance of h = silu(g) u from the tolerances of g and u (|silu'| <= 1.1)."""
+    """Tolerance of h = silu(g) u propagated from the per-output bounds of g and u,
+    |dg| <= 1e-3 Ag and |du| <= 1e-3 Au: |dh| <= |silu'| |dg| |u| + |silu(g)| |du| + |silu'| |dg| |du|
+    with sup |silu'| < 1.1."""
     sg = g / (1.0 + np.exp(-g))
-    return REL * (1.1 * Ag * np.abs(u) + np.abs(sg) * Au) + 1e-6 * 1.1 * Ag * Au + 2.0 ** -22 * np.abs(sg * u)
+    return REL * (1.1 * Ag * np.abs(u) + np.abs(sg) * Au) + REL * REL * 1.1 * Ag * Au
 
 
 def gpu_matrix(fmt, W_gguf, N, K):
