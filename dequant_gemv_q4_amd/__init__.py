@@ -6,7 +6,7 @@ The functions exported here are the C entry points under the same names (see ``_
 """
 from ._binding import (  # noqa: F401
     LIB_PATH, OP_ARGMAX, OP_GEMV, OP_GUS_NRM, OP_MOE, OP_NRM, OP_RES, Q4_0, Q4_K, Q8_0, QgemvError,
-    header_functions, lib, qgemv, qgemv_argmax, qgemv_gus_nrm, qgemv_layout_version, qgemv_moe,
+    header_functions, lib, qgemv, qgemv_argmax, qgemv_argmax_noalloc, qgemv_gus_nrm, qgemv_layout_version, qgemv_moe,
     qgemv_moe_error, qgemv_nrm, qgemv_pack, qgemv_packed_bytes, qgemv_res, qgemv_status_str,
     qgemv_workspace_bytes,
 )

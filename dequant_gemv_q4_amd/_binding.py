@@ -39,6 +39,7 @@ _SIGS = {
     "qgemv_gus_nrm": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _vp, _f32, _i32, _vp, _vp, _sz, _vp]),
     "qgemv_res": (_i32, [_i32, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "qgemv_argmax": (_i32, [_i32, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "qgemv_argmax_noalloc": (_i32, [_i32, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp]),
     "qgemv_moe": (_i32, [_i32, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "qgemv_moe_error": (_i32, [_vp, _i64, _i64, _i64, _i32, ctypes.POINTER(ctypes.c_int), _vp]),
     "qgemv_status_str": (ctypes.c_char_p, [_i32]),
@@ -148,6 +149,11 @@ def qgemv_argmax(fmt, W, N, K, x, nb, logits, idx, ws, ws_bytes=None, stream=Non
     _check("qgemv_argmax", lib().qgemv_argmax(fmt, _p(W), N, K, _p(x), nb, _p(logits), _p(idx),
                                               _p(ws), _nbytes(ws) if ws_bytes is None else ws_bytes,
                                               _stream(stream)))
+
+
+def qgemv_argmax_noalloc(fmt, W, N, K, x, nb, logits, idx, stream=None):
+    _check("qgemv_argmax_noalloc", lib().qgemv_argmax_noalloc(fmt, _p(W), N, K, _p(x), nb,
+                                                              _p(logits), _p(idx), _stream(stream)))
 
 
 def qgemv_moe(fmt, W_experts, n_exp, N, K, x, nb, ids, wts, topk, y, ws, ws_bytes=None,

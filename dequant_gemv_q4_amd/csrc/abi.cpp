@@ -503,6 +503,36 @@ int qgemv_argmax(int fmt, const void *W, int64_t N, int64_t K, const float *x, i
     return run_gemv(fmt, E_ARGMAX, false, a, stream);
 }
 
+int qgemv_argmax_noalloc(int fmt, const void *W, int64_t N, int64_t K, const float *x, int nb,
+                         float *logits, int32_t *idx, void *stream)
+{
+    Layout L;
+    int st = check_common(fmt, W, N, K, x, nb, logits, &L);
+    if (st != QG_OK)
+        return st;
+    if (!idx)
+        return QG_ERR_NULL;
+    if (!al(idx, 4))
+        return QG_ERR_ALIGN;
+    const int64_t lb = (int64_t)nb * N * 4;
+    if (overlap(idx, nb * 4, logits, lb) || overlap(idx, nb * 4, x, (int64_t)nb * K * 4) ||
+        overlap(idx, nb * 4, W, L.total))
+        return QG_ERR_ALIAS;
+    // every argmax launch has at most QG_ARGMAX_MAX_GRID workgroups, so its partial keys fit
+    if (ws_argmax_bytes(nb) > (int64_t)((size_t)QG_ARGMAX_MAX_GRID * QG_MAX_NB * 8))
+        return QG_ERR_SHAPE;
+    void *sp = nullptr;
+    size_t sbytes = 0;
+    if (noalloc_scratch(&sp, &sbytes) != 0)
+        return QG_ERR_LAUNCH;
+    if ((int64_t)sbytes < ws_argmax_bytes(nb))
+        return QG_ERR_WORKSPACE;
+    GemvArgs a = gemv_args(L, W, N, K, x, nb, logits);
+    a.idx = idx;
+    a.keys = static_cast<unsigned long long *>(sp);
+    return run_gemv(fmt, E_ARGMAX, false, a, stream);
+}
+
 int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t K, const float *x,
               int nb, const int32_t *ids, const float *wts, int topk, float *y, void *ws,
               size_t ws_bytes, void *stream)

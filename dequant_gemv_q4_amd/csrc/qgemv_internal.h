@@ -171,6 +171,9 @@ bool plan_mfma(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb, MfmaPla
 int launch_mfma(int fmt, int epi, bool nrm, const MfmaPlan &p, const GemvArgs &a, void *stream);
 int launch_argmax_fold(const unsigned long long *part, int n_part, int nb, int32_t *idx,
                        void *stream);
+// Device address of this device's copy of the library's fixed scratch array (the argmax partial
+// keys of the no-allocation entry point) and its size; looked up once per device.  0 = ok.
+int noalloc_scratch(void **ptr, size_t *bytes);
 // Workgroups of a streaming launch that are resident at once on the current device (0 if the
 // query fails).
 int stream_resident_wgs(int fmt, int epi, bool nrm, int cpl, int nb, int pd, size_t lds_bytes,

@@ -1459,6 +1459,33 @@ int launch_moe(int fmt, int cpl, int pd, const MoeArgs &a, int grid, size_t lds_
     return (int)hipGetLastError();
 }
 
+// The fixed scratch of the no-allocation argmax entry point: one partial key per workgroup and
+// batch row at the largest grid and batch an argmax launch may have (512 KiB per device, held
+// until the process ends).  Host code never passes the array's name to a kernel: on the host it
+// is a stand-in, not a device address; noalloc_scratch looks the device address up once per
+// device and every launch takes that pointer.
+static __device__ __align__(256) unsigned long long scratch[QG_ARGMAX_MAX_GRID * QG_MAX_NB];
+
+int noalloc_scratch(void **ptr, size_t *bytes)
+{
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static void *dev_ptr[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev)
+        return -1;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!dev_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return -1;
+        dev_ptr[dev] = p;
+    }
+    *ptr = dev_ptr[dev];
+    *bytes = sizeof(scratch);
+    return 0;
+}
+
 int launch_argmax_fold(const unsigned long long *part, int n_part, int nb, int32_t *idx,
                        void *stream)
 {

@@ -118,6 +118,17 @@ int qgemv_res(int fmt, const void *W, int64_t N, int64_t K, const float *x, cons
 int qgemv_argmax(int fmt, const void *W, int64_t N, int64_t K, const float *x, int nb,
                  float *logits, int32_t *idx, void *ws, size_t ws_bytes, void *stream);
 
+/* qgemv_argmax without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels, with the partial keys in a fixed scratch array the library holds on each device
+ * it runs on (512 KiB, from the first call until the process ends).  The call itself allocates
+ * nothing.  The array is shared by every call on that device and keeps the last call's partial
+ * keys (each launch writes every key it reads, so nothing needs clearing): calls that may overlap
+ * on one device (different streams, or concurrent graph replays) race and must be ordered by the
+ * caller.  Sizes and errors as qgemv_argmax; the scratch covers every accepted size. */
+int qgemv_argmax_noalloc(int fmt, const void *W, int64_t N, int64_t K, const float *x, int nb,
+                         float *logits, int32_t *idx, void *stream);
+
 /* Routed experts: y[r][n] = sum_{t=0..topk-1} wts[r][t] * (W_{ids[r][t]} x_r)[n], the terms added
  * in ascending t.  ("Module gpu", type alias RouteStep: expert ids and routing weights of one
  * step; module experts.)  W_experts holds n_exp packed N x K matrices back to back (pack them
