@@ -24,6 +24,7 @@
  * Parallelism: output rows are independent, so an OpenMP loop runs over them.
  * The order of the K-sum inside one output is the plain ascending k order.
  */
+#define _GNU_SOURCE
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -241,6 +242,55 @@ void orc_swiglu(const double *g, const double *u, int64_t n, double *h)
 {
     for (int64_t i = 0; i < n; ++i)
         h[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
+}
+
+/* GELU-gated product h = gelu(g) * u with the tanh form of GELU,
+ * gelu(g) = g/2 (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))).  [Honey] pipeline
+ * field pipe_q8_large4_gus_nrm_gelu, the "GeluTanh variant" of the fused
+ * gate/up + norm step; the tanh form is the one the variant's name gives. */
+void orc_gelu_tanh_gate(const double *g, const double *u, int64_t n, double *h)
+{
+    const double k0 = sqrt(2.0 / M_PI);
+    for (int64_t i = 0; i < n; ++i) {
+        double x = g[i];
+        h[i] = 0.5 * x * (1.0 + tanh(k0 * (x + 0.044715 * x * x * x))) * u[i];
+    }
+}
+
+/* Per-head QK RMSNorm + RoPE in place on y[nb][(nq + 2 nkv) hd] ([Honey] the
+ * QK-norm + RoPE step of the fused QKV chain: one group per head over the Q
+ * heads then the K heads, with q_norm / k_norm weights, rope_half, eps, and
+ * cos / sin tables of rope_half values per position).  Q head h is normalized
+ * by 1/sqrt(mean of its squares + eps) and scaled by qg (K heads by kg; a NULL
+ * gamma skips the normalization), then each pair (j, j + rh), j < rh, is
+ * rotated by the angle whose cosine / sine are cs[r][j] / sn[r][j].  The pair
+ * layout (j with j + rh) is a reading: the page gives only the half size.
+ * V heads are not touched. */
+void orc_qk_norm_rope(double *y, int64_t nb, int64_t nq, int64_t nkv, int64_t hd, int64_t rh,
+                      const double *qg, const double *kg, double eps, const double *cs,
+                      const double *sn)
+{
+    int64_t row = (nq + 2 * nkv) * hd;
+    for (int64_t r = 0; r < nb; ++r) {
+        for (int64_t h = 0; h < nq + nkv; ++h) {
+            double *v = y + r * row + h * hd;
+            const double *gam = h < nq ? qg : kg;
+            if (gam) {
+                double ss = 0.0;
+                for (int64_t k = 0; k < hd; ++k)
+                    ss += v[k] * v[k];
+                double inv = 1.0 / sqrt(ss / (double)hd + eps);
+                for (int64_t k = 0; k < hd; ++k)
+                    v[k] = v[k] * inv * gam[k];
+            }
+            for (int64_t j = 0; j < rh; ++j) {
+                double c = cs[r * rh + j], s = sn[r * rh + j];
+                double a = v[j], b = v[j + rh];
+                v[j] = a * c - b * s;
+                v[j + rh] = b * c + a * s;
+            }
+        }
+    }
 }
 
 /* y = W v + r.  [Honey] forward_decode_fused_layers, the fused matmul +

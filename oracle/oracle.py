@@ -65,6 +65,10 @@ def _load():
         lib.orc_rmsnorm.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, _dp]
         lib.orc_swiglu.argtypes = [_dp, _dp, ctypes.c_int64, _dp]
         lib.orc_argmax.argtypes = [_dp, ctypes.c_int64, ctypes.c_int64, _i64p]
+        lib.orc_gelu_tanh_gate.argtypes = [_dp, _dp, ctypes.c_int64, _dp]
+        lib.orc_qk_norm_rope.argtypes = [_dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_int64, _dp, _dp,
+                                         ctypes.c_double, _dp, _dp]
         lib.orc_moe.argtypes = [ctypes.c_int, _u8p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                 _dp, ctypes.c_int64, _i32p, _dp, ctypes.c_int64, _i64p,
                                 ctypes.c_int64, _dp, _dp]
@@ -167,6 +171,32 @@ def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     return h
 
 
+def gelu_tanh_gate(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    g = _c(g, np.float64)
+    u = _c(u, np.float64)
+    assert g.shape == u.shape
+    h = np.empty_like(g)
+    _load().orc_gelu_tanh_gate(_ptr(g, _dp), _ptr(u, _dp), g.size, _ptr(h, _dp))
+    return h
+
+
+def qk_norm_rope(qkv: np.ndarray, n_q_heads: int, n_kv_heads: int, head_dim: int, rope_half: int,
+                 q_gamma, k_gamma, eps: float, rope_cos: np.ndarray, rope_sin: np.ndarray):
+    """Per-head QK RMSNorm + RoPE of a QKV output [nb][(nq + 2 nkv) hd]; returns a new array."""
+    row = (n_q_heads + 2 * n_kv_heads) * head_dim
+    y = _c(qkv, np.float64).reshape(-1, row).copy()
+    nb = y.shape[0]
+    cs = _c(rope_cos, np.float64).reshape(nb, rope_half)
+    sn = _c(rope_sin, np.float64).reshape(nb, rope_half)
+    qg = None if q_gamma is None else _c(q_gamma, np.float64)
+    kg = None if k_gamma is None else _c(k_gamma, np.float64)
+    _load().orc_qk_norm_rope(_ptr(y, _dp), nb, n_q_heads, n_kv_heads, head_dim, rope_half,
+                             None if qg is None else _ptr(qg, _dp),
+                             None if kg is None else _ptr(kg, _dp), float(eps),
+                             _ptr(cs, _dp), _ptr(sn, _dp))
+    return y
+
+
 def argmax(y: np.ndarray) -> np.ndarray:
     y = _c(y, np.float64)
     y2 = y.reshape(-1, y.shape[-1])
@@ -206,6 +236,23 @@ def qgemv_gus_nrm(fmt, Wg, Wu, N, K, x, gamma, eps, rows=None):
     g, Ag = gemv(fmt, Wg, N, K, n, rows)
     u, Au = gemv(fmt, Wu, N, K, n, rows)
     return swiglu(g, u), g, u, Ag, Au
+
+
+def qgemv_nrm_bias(fmt, W, N, K, x, gamma, eps, bias, rows=None):
+    """y = W rmsnorm(x) + bias ("honeycrisp mod.rs", pipe_q8_nrm_mb64_bias: bias[row] added at
+    the output); A as for the GEMV."""
+    y, A = gemv(fmt, W, N, K, rmsnorm(x, gamma, eps), rows)
+    b = _c(bias, np.float64)
+    return y + (b if rows is None else b[np.asarray(rows)])[None, :], A
+
+
+def qgemv_gus_act_nrm(fmt, Wg, Wu, N, K, x, gamma, eps, act, rows=None):
+    """Returns (h, g, u, Ag, Au) with h = act(g) * u; act 0 = silu, 1 = GELU (tanh form)."""
+    n = rmsnorm(x, gamma, eps)
+    g, Ag = gemv(fmt, Wg, N, K, n, rows)
+    u, Au = gemv(fmt, Wu, N, K, n, rows)
+    h = swiglu(g, u) if act == 0 else gelu_tanh_gate(g, u)
+    return h, g, u, Ag, Au
 
 
 def qgemv_argmax(fmt, W, N, K, x):

@@ -546,3 +546,108 @@ def test_q8_0_brute_force_integer_form():
             for n in range(N):
                 s = sum(2.0 ** -int(kexp[n, j // 32]) * int(q8[n, j]) * int(x[r, j]) for j in range(K))
                 assert y[r, n] == s, (K, r, n)
+
+
+# ----------------------------------------------------------------------------- GELU (tanh form)
+
+def test_gelu_tanh_closed_forms_and_erf_form():
+    """gelu(0) = 0; gelu(g) - gelu(-g) = g (the tanh term is odd); gelu(g) -> g for large g and
+    -> 0 for very negative g; and the tanh form stays within 1e-3 of the exact g Phi(g) (Phi
+    from math.erf, independent of the oracle) over [-6, 6]; a missing 1/2, a wrong sign or a
+    wrong cubic coefficient fails one of these."""
+    g = np.linspace(-6, 6, 241)
+    h = oracle.gelu_tanh_gate(g, np.ones_like(g))
+    hm = oracle.gelu_tanh_gate(-g, np.ones_like(g))
+    assert oracle.gelu_tanh_gate(np.zeros(1), np.ones(1))[0] == 0.0
+    assert np.all(np.abs((h - hm) - g) <= 1e-13 * (1 + np.abs(g)))
+    big = oracle.gelu_tanh_gate(np.array([30.0, -30.0]), np.array([1.0, 1.0]))
+    assert abs(big[0] - 30.0) < 1e-12 and abs(big[1]) < 1e-12
+    exact = np.array([x * 0.5 * (1 + math.erf(x / math.sqrt(2))) for x in g])
+    assert np.max(np.abs(h - exact)) < 1e-3
+    # u multiplies linearly
+    u = np.linspace(-2, 2, 241)
+    assert np.allclose(oracle.gelu_tanh_gate(g, u), h * u, rtol=1e-15, atol=0)
+
+
+def test_gus_act_gelu_uses_the_gate():
+    """The same hand-built (g, u) rows as the SiLU roles pin, through the GELU composite: the
+    gate's GELU multiplies the up value (GELU values at 1 and 2 from the erf form agree with the
+    tanh form within 1e-3, and the swapped composite differs by far more)."""
+    K = 64
+    pairs = [(1, 2), (2, 1), (2, -1)]
+
+    def mat(vals):
+        out = bytearray()
+        for v in vals:
+            for b in range(K // 32):
+                nib = [8] * 32
+                if b == 0:
+                    nib[0] = 8 + v
+                out += f16_bytes(0.125) + bytes(nib[j] | (nib[j + 16] << 4) for j in range(16))
+        return np.frombuffer(bytes(out), dtype=np.uint8)
+
+    x = np.zeros((1, K))
+    x[0, 0] = 1.0
+    h, g, u, _, _ = oracle.qgemv_gus_act_nrm(Q4_0, mat([p[0] for p in pairs]),
+                                              mat([p[1] for p in pairs]), len(pairs), K, x,
+                                              np.ones(K), 0.0, 1)
+    phi = lambda t: 0.5 * (1 + math.erf(t / math.sqrt(2)))
+    for n, (gv, uv) in enumerate(pairs):
+        assert abs(h[0, n] - gv * phi(gv) * uv) < 1e-3 * abs(uv)
+        assert abs(h[0, n] - uv * phi(uv) * gv) > 0.1
+
+
+# ----------------------------------------------------------------------------- QK norm + RoPE
+
+def test_qk_norm_rope_hand_example():
+    """One Q head of 4 values [3, 4, 0, 0], gamma 1, eps 0: rms = 2.5, normalized [1.2, 1.6, 0, 0].
+    Rope half 2 with (c, s) = (0.6, 0.8) for pair (0, 2) and (0, 1) for pair (1, 3):
+    (1.2, 0) -> (0.72, 0.96) and (1.6, 0) -> (0, 1.6).  The K head [0, 0, 0, 2] normalizes to
+    [0, 0, 0, 2] (rms 1), then (0, 0) -> (0, 0) and (0, 2) -> (-2, 0).  V head untouched."""
+    y = np.array([[3.0, 4.0, 0.0, 0.0, 0.0, 0.0, 0.0, 2.0, 7.0, -1.0, 0.5, 9.0]])
+    out = oracle.qk_norm_rope(y, 1, 1, 4, 2, np.ones(4), np.ones(4), 0.0,
+                              np.array([[0.6, 0.0]]), np.array([[0.8, 1.0]]))
+    want = [0.72, 0.0, 0.96, 1.6, 0.0, -2.0, 0.0, 0.0, 7.0, -1.0, 0.5, 9.0]
+    assert np.allclose(out[0], want, rtol=0, atol=1e-15), out
+
+
+def test_qk_norm_rope_invariants():
+    g = np.random.default_rng(61)
+    nb, nq, nkv, hd, rh = 3, 4, 2, 64, 16
+    row = (nq + 2 * nkv) * hd
+    y = g.standard_normal((nb, row))
+    th = g.uniform(-3, 3, (nb, rh))
+    c, s = np.cos(th), np.sin(th)
+    qg, kg = g.uniform(0.5, 1.5, hd), g.uniform(0.5, 1.5, hd)
+    out = oracle.qk_norm_rope(y, nq, nkv, hd, rh, qg, kg, 1e-6, c, s)
+    # V heads untouched, bit for bit
+    assert np.array_equal(out[:, (nq + nkv) * hd:], y[:, (nq + nkv) * hd:])
+    # the rotation back (c, -s) gives the normalized heads: mean of (v / gamma)^2 ~ 1
+    back = oracle.qk_norm_rope(out, nq, nkv, hd, rh, None, None, 0.0, c, -s)
+    for h in range(nq + nkv):
+        v = back[:, h * hd:(h + 1) * hd] / (qg if h < nq else kg)
+        ms = np.mean(v * v, axis=1)
+        raw = y[:, h * hd:(h + 1) * hd]
+        want = np.mean(raw * raw, axis=1) / (np.mean(raw * raw, axis=1) + 1e-6)
+        assert np.allclose(ms, want, rtol=1e-12, atol=0)
+    # each rotated pair keeps its length; values past 2 rh are only normalized
+    q0 = oracle.qk_norm_rope(y, nq, nkv, hd, rh, qg, kg, 1e-6, np.ones((nb, rh)), np.zeros((nb, rh)))
+    for h in range(nq + nkv):
+        a0, b0 = q0[:, h * hd:h * hd + rh], q0[:, h * hd + rh:h * hd + 2 * rh]
+        a1, b1 = out[:, h * hd:h * hd + rh], out[:, h * hd + rh:h * hd + 2 * rh]
+        assert np.allclose(a0 * a0 + b0 * b0, a1 * a1 + b1 * b1, rtol=1e-12, atol=1e-15)
+        assert np.array_equal(q0[:, h * hd + 2 * rh:(h + 1) * hd], out[:, h * hd + 2 * rh:(h + 1) * hd])
+    # a quarter turn (c, s) = (0, 1) maps (a, b) -> (-b, a) exactly
+    qt = oracle.qk_norm_rope(y, nq, nkv, hd, rh, qg, kg, 1e-6, np.zeros((nb, rh)), np.ones((nb, rh)))
+    for h in range(nq + nkv):
+        assert np.array_equal(qt[:, h * hd:h * hd + rh], -q0[:, h * hd + rh:h * hd + 2 * rh])
+        assert np.array_equal(qt[:, h * hd + rh:h * hd + 2 * rh], q0[:, h * hd:h * hd + rh])
+
+
+def test_nrm_bias_with_zero_weights_is_the_bias():
+    g = np.random.default_rng(63)
+    N, K = 9, 64
+    W = np.frombuffer((f16_bytes(0.5) + bytes([0x88] * 16)) * (N * K // 32), dtype=np.uint8)
+    bias = g.standard_normal(N)
+    y, A = oracle.qgemv_nrm_bias(Q4_0, W, N, K, g.standard_normal((2, K)), np.ones(K), 1e-5, bias)
+    assert np.array_equal(y, np.stack([bias, bias])) and np.all(A == 0)
