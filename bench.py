@@ -204,6 +204,44 @@ def make_qkv(warm, nb):
                  cpu, cfg, flops=2 * nb * w.N * w.K)
 
 
+def make_qkv_attn(warm, nb, n_q_heads=12, n_kv_heads=2, head_dim=128, theta=1e6):
+    """The attention-side chain of the QKV workload: norm + Q8_0 QKV GEMV + bias (one launch),
+    then the per-head QK RMSNorm + RoPE in place (a second launch) at positions 1000 + r."""
+    import torch
+    import dequant_gemv_q4_amd as q
+    from dequant_gemv_q4_amd import device as D
+    import workloads as wl
+
+    w = wl.qkv_q8(nb=nb)
+    a = w.arrays
+    g = wl.rng(2, 7)
+    rh = head_dim // 2
+    Wp = D.pack(q.Q8_0, a["W"], w.N, w.K)
+    R = _copies(Wp.numel(), warm)
+    sets = _rotated(Wp, R)
+    x, gamma = D.to_device(a["x"]), D.to_device(a["gamma"])
+    bias = D.to_device(wl.normal_f32(g, (w.N,)))
+    qg, kg = D.to_device(wl.gamma_f32(g, head_dim)), D.to_device(wl.gamma_f32(g, head_dim))
+    ang = (1000 + np.arange(nb))[:, None] / theta ** (2.0 * np.arange(rh)[None, :] / head_dim)
+    cs, sn = D.to_device(np.cos(ang).astype(np.float32)), D.to_device(np.sin(ang).astype(np.float32))
+    y = torch.empty((nb, w.N), dtype=torch.float32, device="cuda")
+
+    def gemv(i):
+        q.qgemv_nrm_bias(q.Q8_0, sets[i % R], w.N, w.K, x, gamma, w.params["eps"], bias, nb, y)
+
+    def step(i):
+        gemv(i)
+        q.qgemv_qk_norm_rope(y, nb, n_q_heads, n_kv_heads, head_dim, rh, qg, kg, 1e-6, cs, sn)
+
+    alg = a["W"].nbytes + nb * w.K * 4 + w.K * 4 + w.N * 4 + nb * w.N * 4
+    name = f"qkv_attn_q8_0_{w.N}x{w.K}_nb{nb}"
+    cfg = {"workload": name, "nb": nb, "format": "q8_0", "N": w.N, "K": w.K, "bias": True,
+           "qk_norm_rope": {"q_heads": n_q_heads, "kv_heads": n_kv_heads, "head_dim": head_dim},
+           "launches_per_step": 2, "weight_copies": R, "cold": not warm}
+    return Bench(name, a["W"].nbytes, alg, f"qgemv_nrm_bias (q8_0, {w.N}x{w.K}, nb={nb})", step,
+                 gemv, lambda: 0, cfg, flops=2 * nb * w.N * w.K)
+
+
 def make_moe(warm):
     import torch
     import dequant_gemv_q4_amd as q
@@ -517,6 +555,8 @@ def main():
         extras["moe_q4k_nb16"] = run_extra("moe", lambda: make_moe(False), es, ew, torch)
         extras["qkv_q8_nb16"] = run_extra("qkv nb=16", lambda: make_qkv(False, 16), es, ew, torch)
         extras["decode_mlp"] = run_extra("decode mlp", lambda: make_decode_mlp(False), es, ew, torch)
+        extras["qkv_attn_nb1"] = run_extra("qkv + bias + qk norm + rope",
+                                           lambda: make_qkv_attn(False, 1), es, ew, torch)
         extras["lm_head_nb1"] = run_extra("lm_head", lambda: make_lm_head(False, 1), es, ew, torch)
         w = run_extra("gemv warm", lambda: make_gemv(True, 1), es, ew, torch)
         w["label"] = "cache-assisted: one weight copy reused, served in part by the 256 MB MALL"

@@ -5,7 +5,8 @@ The functions exported here are the C entry points under the same names (see ``_
 ``device`` holds torch-side plumbing (device buffers for packed weights and workspaces).
 """
 from ._binding import (  # noqa: F401
-    LIB_PATH, OP_ARGMAX, OP_GEMV, OP_GUS_NRM, OP_MOE, OP_NRM, OP_RES, Q4_0, Q4_K, Q8_0, QgemvError,
+    ACT_GELU_TANH, ACT_SILU, LIB_PATH, OP_ARGMAX, OP_GEMV, OP_GUS_NRM, OP_MOE, OP_NRM, OP_NRM_BIAS,
+    OP_RES, Q4_0, Q4_K, Q8_0, QgemvError, qgemv_gus_act_nrm, qgemv_nrm_bias, qgemv_qk_norm_rope,
     header_functions, lib, qgemv, qgemv_argmax, qgemv_argmax_noalloc, qgemv_gus_nrm, qgemv_layout_version, qgemv_moe,
     qgemv_moe_error, qgemv_nrm, qgemv_pack, qgemv_packed_bytes, qgemv_res, qgemv_status_str,
     qgemv_workspace_bytes,

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_PKG, "libqgemv.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "qgemv.h")
 
 Q4_0, Q8_0, Q4_K = 2, 8, 12
-OP_GEMV, OP_NRM, OP_GUS_NRM, OP_RES, OP_ARGMAX, OP_MOE = range(6)
+OP_GEMV, OP_NRM, OP_GUS_NRM, OP_RES, OP_ARGMAX, OP_MOE, OP_NRM_BIAS = range(7)
+ACT_SILU, ACT_GELU_TANH = 0, 1
 STATUS = {0: "QG_OK", 1: "QG_ERR_NULL", 2: "QG_ERR_FORMAT", 3: "QG_ERR_SHAPE", 4: "QG_ERR_ALIGN",
           5: "QG_ERR_WORKSPACE", 6: "QG_ERR_LAUNCH", 7: "QG_ERR_ALIAS"}
 
@@ -37,6 +38,11 @@ _SIGS = {
     "qgemv": (_i32, [_i32, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _sz, _vp]),
     "qgemv_nrm": (_i32, [_i32, _vp, _i64, _i64, _vp, _vp, _f32, _i32, _vp, _vp, _sz, _vp]),
     "qgemv_gus_nrm": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _vp, _f32, _i32, _vp, _vp, _sz, _vp]),
+    "qgemv_nrm_bias": (_i32, [_i32, _vp, _i64, _i64, _vp, _vp, _f32, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "qgemv_gus_act_nrm": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _vp, _f32, _i32, _i32, _vp, _vp,
+                                 _sz, _vp]),
+    "qgemv_qk_norm_rope": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _f32, _vp, _vp,
+                                  _vp]),
     "qgemv_res": (_i32, [_i32, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "qgemv_argmax": (_i32, [_i32, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "qgemv_argmax_noalloc": (_i32, [_i32, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp]),
@@ -137,6 +143,29 @@ def qgemv_gus_nrm(fmt, Wg, Wu, N, K, x, gamma, eps, nb, h, ws=None, ws_bytes=Non
                                                 nb, _p(h), _p(ws),
                                                 _nbytes(ws) if ws_bytes is None else ws_bytes,
                                                 _stream(stream)))
+
+
+def qgemv_nrm_bias(fmt, W, N, K, x, gamma, eps, bias, nb, y, ws=None, ws_bytes=None, stream=None):
+    _check("qgemv_nrm_bias", lib().qgemv_nrm_bias(fmt, _p(W), N, K, _p(x), _p(gamma), eps, _p(bias),
+                                                  nb, _p(y), _p(ws),
+                                                  _nbytes(ws) if ws_bytes is None else ws_bytes,
+                                                  _stream(stream)))
+
+
+def qgemv_gus_act_nrm(fmt, Wg, Wu, N, K, x, gamma, eps, act, nb, h, ws=None, ws_bytes=None,
+                      stream=None):
+    _check("qgemv_gus_act_nrm", lib().qgemv_gus_act_nrm(fmt, _p(Wg), _p(Wu), N, K, _p(x),
+                                                        _p(gamma), eps, act, nb, _p(h), _p(ws),
+                                                        _nbytes(ws) if ws_bytes is None
+                                                        else ws_bytes, _stream(stream)))
+
+
+def qgemv_qk_norm_rope(qkv, nb, n_q_heads, n_kv_heads, head_dim, rope_half, q_gamma, k_gamma, eps,
+                       rope_cos, rope_sin, stream=None):
+    _check("qgemv_qk_norm_rope", lib().qgemv_qk_norm_rope(_p(qkv), nb, n_q_heads, n_kv_heads,
+                                                          head_dim, rope_half, _p(q_gamma),
+                                                          _p(k_gamma), eps, _p(rope_cos),
+                                                          _p(rope_sin), _stream(stream)))
 
 
 def qgemv_res(fmt, W, N, K, x, res, nb, y, ws=None, ws_bytes=None, stream=None):

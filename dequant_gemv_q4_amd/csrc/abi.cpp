@@ -381,6 +381,7 @@ int64_t qgemv_workspace_bytes(int op, int fmt, int64_t N, int64_t K, int nb, int
     case QG_OP_NRM:
     case QG_OP_GUS_NRM:
     case QG_OP_RES:
+    case QG_OP_NRM_BIAS:
         return 0;
     case QG_OP_ARGMAX:
         return ws_argmax_bytes(nb);
@@ -431,12 +432,49 @@ int qgemv_nrm(int fmt, const void *W, int64_t N, int64_t K, const float *x, cons
     return run_gemv(fmt, E_STORE, true, a, stream);
 }
 
+int qgemv_nrm_bias(int fmt, const void *W, int64_t N, int64_t K, const float *x,
+                   const float *gamma, float eps, const float *bias, int nb, float *y, void *ws,
+                   size_t ws_bytes, void *stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    Layout L;
+    int st = check_common(fmt, W, N, K, x, nb, y, &L);
+    if (st != QG_OK)
+        return st;
+    if (!gamma || !bias)
+        return QG_ERR_NULL;
+    if (!al(gamma, 16) || !al(bias, 4))
+        return QG_ERR_ALIGN;
+    const int64_t yb = (int64_t)nb * N * 4;
+    if (overlap(y, yb, gamma, K * 4) || overlap(y, yb, bias, N * 4))
+        return QG_ERR_ALIAS;
+    if (!(eps >= 0.0f))
+        return QG_ERR_SHAPE;
+    GemvArgs a = gemv_args(L, W, N, K, x, nb, y);
+    a.gamma = gamma;
+    a.eps = eps;
+    a.res = bias;
+    a.res_rstride = 0;
+    return run_gemv(fmt, E_RES, true, a, stream);
+}
+
 int qgemv_gus_nrm(int fmt, const void *Wg, const void *Wu, int64_t N, int64_t K, const float *x,
                   const float *gamma, float eps, int nb, float *h, void *ws, size_t ws_bytes,
                   void *stream)
 {
+    return qgemv_gus_act_nrm(fmt, Wg, Wu, N, K, x, gamma, eps, QG_ACT_SILU, nb, h, ws, ws_bytes,
+                             stream);
+}
+
+int qgemv_gus_act_nrm(int fmt, const void *Wg, const void *Wu, int64_t N, int64_t K,
+                      const float *x, const float *gamma, float eps, int act, int nb, float *h,
+                      void *ws, size_t ws_bytes, void *stream)
+{
     (void)ws;
     (void)ws_bytes;
+    if (act != QG_ACT_SILU && act != QG_ACT_GELU_TANH)
+        return QG_ERR_SHAPE;
     Layout L;
     int st = check_common(fmt, Wg, N, K, x, nb, h, &L);
     if (st != QG_OK)
@@ -455,6 +493,7 @@ int qgemv_gus_nrm(int fmt, const void *Wg, const void *Wu, int64_t N, int64_t K,
     a.sc1 = a.qs1 + L.sc_off;
     a.gamma = gamma;
     a.eps = eps;
+    a.act = act;
     return run_gemv(fmt, E_GUS, true, a, stream);
 }
 
@@ -476,6 +515,7 @@ int qgemv_res(int fmt, const void *W, int64_t N, int64_t K, const float *x, cons
         return QG_ERR_ALIAS;
     GemvArgs a = gemv_args(L, W, N, K, x, nb, y);
     a.res = res;
+    a.res_rstride = N;
     return run_gemv(fmt, E_RES, false, a, stream);
 }
 
@@ -585,6 +625,30 @@ int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t 
     a.topk = topk;
     a.pool_max = mp.pool_max;
     return launch_status(launch_moe(fmt, mp.cpl, mp.pd, a, mp.grid, mp.lds, stream));
+}
+
+int qgemv_qk_norm_rope(float *qkv, int nb, int n_q_heads, int n_kv_heads, int head_dim,
+                       int rope_half, const float *q_gamma, const float *k_gamma, float eps,
+                       const float *rope_cos, const float *rope_sin, void *stream)
+{
+    if (!qkv || (rope_half > 0 && (!rope_cos || !rope_sin)))
+        return QG_ERR_NULL;
+    if (nb < 1 || nb > QG_MAX_NB || n_q_heads < 1 || n_kv_heads < 0 || head_dim < 2 ||
+        head_dim > QG_HEAD_DIM_MAX || head_dim % 2 || rope_half < 0 || 2 * rope_half > head_dim ||
+        !(eps >= 0.0f) || (int64_t)(n_q_heads + 2 * (int64_t)n_kv_heads) * head_dim > 0x7fffffffLL)
+        return QG_ERR_SHAPE;
+    if (!al(qkv, 4) || (q_gamma && !al(q_gamma, 4)) || (k_gamma && !al(k_gamma, 4)) ||
+        (rope_cos && !al(rope_cos, 4)) || (rope_sin && !al(rope_sin, 4)))
+        return QG_ERR_ALIGN;
+    const int64_t row = (int64_t)(n_q_heads + 2 * n_kv_heads) * head_dim;
+    const int64_t yb = (int64_t)nb * row * 4, tb = (int64_t)nb * rope_half * 4;
+    if ((q_gamma && overlap(qkv, yb, q_gamma, (int64_t)head_dim * 4)) ||
+        (k_gamma && overlap(qkv, yb, k_gamma, (int64_t)head_dim * 4)) ||
+        (rope_half > 0 && (overlap(qkv, yb, rope_cos, tb) || overlap(qkv, yb, rope_sin, tb))))
+        return QG_ERR_ALIAS;
+    return launch_status(launch_qk_norm_rope(qkv, row, nb, n_q_heads, n_kv_heads, head_dim,
+                                             rope_half, q_gamma, k_gamma, eps, rope_cos,
+                                             rope_sin, stream));
 }
 
 int qgemv_moe_error(const void *ws, int64_t n_exp, int64_t N, int64_t K, int fmt, int *flag,

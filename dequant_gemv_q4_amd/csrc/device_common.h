@@ -378,6 +378,20 @@ __device__ __forceinline__ float group_sum(float v, int lpr)
     return v;
 }
 
+// act(g) u of the gated product: silu(g) = g / (1 + e^-g) ("honeycrisp mod.rs",
+// fused_norm_swiglu_down), or the tanh form of GELU, 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3)))
+// (the GeluTanh variant of the gate/up + norm pipeline, "honeycrisp mod.rs",
+// pipe_q8_large4_gus_nrm_gelu).  act is uniform across the launch.
+__device__ __forceinline__ float gated(float g, float u, int act)
+{
+    if (act == A_GELU_TANH) {
+        const float k0 = 0.7978845608028654f;   // sqrt(2 / pi)
+        const float t = tanhf(k0 * fmaf(0.044715f * g, g * g, g));
+        return 0.5f * g * (1.0f + t) * u;
+    }
+    return g / (1.0f + expf(-g)) * u;
+}
+
 // Order-preserving key: larger value -> larger key; equal values -> the lower index wins.
 __device__ __forceinline__ unsigned long long argmax_key(float v, int64_t n)
 {

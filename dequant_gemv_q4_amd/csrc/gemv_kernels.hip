@@ -93,10 +93,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a)
                     if constexpr (EPI == E_STORE) {
                         a.y[o] = acc[0][u][r];
                     } else if constexpr (EPI == E_RES) {
-                        a.y[o] = acc[0][u][r] + a.res[o];
+                        a.y[o] = acc[0][u][r] + a.res[(int64_t)r * a.res_rstride + n];
                     } else if constexpr (EPI == E_GUS) {
-                        const float g = acc[0][u][r], up = acc[MATS - 1][u][r];
-                        a.y[o] = g / (1.0f + expf(-g)) * up;
+                        a.y[o] = gated(acc[0][u][r], acc[MATS - 1][u][r], a.act);
                     } else {
                         const float v = acc[0][u][r];
                         a.y[o] = v;
@@ -157,7 +156,89 @@ __global__ __launch_bounds__(256) void k_pack(const uint8_t *src, int64_t nblock
     }
 }
 
+// ------------------------------------------------------------------------------------ QK norm + RoPE
+
+// Attention-side epilogue of a fused QKV GEMV ("honeycrisp mod.rs", pipe_qk_norm_rope: one group
+// per head, the Q heads then the K heads, with q_norm / k_norm weights, rope_half and eps; the
+// cos / sin tables hold one row of rope_half values per position).  In place on y[r] =
+// [Q heads | K heads | V heads] of head_dim values each: every Q and K head is RMS-normalized
+// over its head_dim values and scaled by its gamma (skipped when that gamma is NULL), then the
+// first 2 rope_half values are rotated in pairs (j, j + rope_half) by the angle whose cosine and
+// sine are cos[r][j], sin[r][j]; V heads are left as they are.  One wave per (row, head); a
+// lane holds elements lane + 64 i; the pair partner comes through the wave's own LDS row.
+__global__ __launch_bounds__(256) void k_qk_norm_rope(float *y, int64_t row_stride, int nb,
+                                                      int nq, int nkv, int hd, int rh,
+                                                      const float *qg, const float *kg, float eps,
+                                                      const float *cs, const float *sn)
+{
+    __shared__ float buf[4][QG_HEAD_DIM_MAX];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int heads = nq + nkv;
+    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+    if (item >= (int64_t)nb * heads)
+        return;                                    // no workgroup barrier below: waves may leave
+    const int r = (int)(item / heads), h = (int)(item % heads);
+    float *yh = y + (int64_t)r * row_stride + (int64_t)h * hd;
+    const float *gam = h < nq ? qg : kg;
+    constexpr int NI = QG_HEAD_DIM_MAX / 64;
+    float v[NI];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < hd ? yh[e] : 0.f;
+        ss = fmaf(v[i], v[i], ss);
+    }
+    if (gam) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            ss += __shfl_xor(ss, off);
+        const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int e = lane + 64 * i;
+            if (e < hd)
+                v[i] = v[i] * inv * gam[e];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int e = lane + 64 * i;
+        if (e < hd)
+            buf[wave][e] = v[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const float *cr = cs + (int64_t)r * rh, *sr = sn + (int64_t)r * rh;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int e = lane + 64 * i;
+        if (e < hd) {
+            float out = v[i];
+            if (e < rh) {
+                out = v[i] * cr[e] - buf[wave][e + rh] * sr[e];
+            } else if (e < 2 * rh) {
+                const int j = e - rh;
+                out = v[i] * cr[j] + buf[wave][j] * sr[j];
+            }
+            yh[e] = out;
+        }
+    }
+}
+
 // ------------------------------------------------------------------------------------ launchers
+
+int launch_qk_norm_rope(float *y, int64_t row_stride, int nb, int nq, int nkv, int hd, int rh,
+                        const float *qg, const float *kg, float eps, const float *cs,
+                        const float *sn, void *stream)
+{
+    const int64_t items = (int64_t)nb * (nq + nkv);
+    hipLaunchKernelGGL(k_qk_norm_rope, dim3((unsigned)((items + 3) / 4)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), y, row_stride, nb, nq, nkv, hd, rh, qg,
+                       kg, eps, cs, sn);
+    return (int)hipGetLastError();
+}
 
 int launch_pack(int fmt, const void *src, int64_t N, int64_t K, void *dst, void *stream)
 {
@@ -208,7 +289,8 @@ static int launch_gemv_fmt(int epi, bool nrm, const GemvArgs &a, int grid, size_
         return nrm ? launch_gemv_nb<FMT, E_STORE, true>(a, grid, lds, s)
                    : launch_gemv_nb<FMT, E_STORE, false>(a, grid, lds, s);
     case E_RES:
-        return launch_gemv_nb<FMT, E_RES, false>(a, grid, lds, s);
+        return nrm ? launch_gemv_nb<FMT, E_RES, true>(a, grid, lds, s)
+                   : launch_gemv_nb<FMT, E_RES, false>(a, grid, lds, s);
     case E_GUS:
         return launch_gemv_nb<FMT, E_GUS, true>(a, grid, lds, s);
     case E_ARGMAX:

@@ -338,9 +338,9 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
         const bool ok = b < a.nb && nn < a.N;
         float out;
         if constexpr (EPI == E_GUS) {
-            out = v[0] / (1.0f + expf(-v[0])) * v[MATS - 1];
+            out = gated(v[0], v[MATS - 1], a.act);
         } else if constexpr (EPI == E_RES) {
-            out = v[0] + (ok ? a.res[(int64_t)b * a.N + nn] : 0.f);
+            out = v[0] + (ok ? a.res[(int64_t)b * a.res_rstride + nn] : 0.f);
         } else {
             out = v[0];
         }
@@ -466,7 +466,9 @@ static const void *mfma_fn_fmt(int epi, bool nrm, int kc, bool sv, int tpw)
     case E_STORE:
         return nrm ? mfma_fn_ns<FMT, E_STORE, true>(kc, sv, tpw)
                    : mfma_fn_ns<FMT, E_STORE, false>(kc, sv, tpw);
-    case E_RES: return mfma_fn_ns<FMT, E_RES, false>(kc, sv, tpw);
+    case E_RES:
+        return nrm ? mfma_fn_ns<FMT, E_RES, true>(kc, sv, tpw)
+                   : mfma_fn_ns<FMT, E_RES, false>(kc, sv, tpw);
     case E_GUS: return mfma_fn_ns<FMT, E_GUS, true>(kc, sv, tpw);
     case E_ARGMAX: return mfma_fn_ns<FMT, E_ARGMAX, false>(kc, sv, tpw);
     default: return nullptr;

@@ -10,8 +10,11 @@ namespace qg {
 
 enum Fmt { FQ4_0 = 2, FQ8_0 = 8, FQ4_K = 12 };
 
-// Epilogue kinds of the vector GEMV kernel.
+// Epilogue kinds of the GEMV kernels: store; add a residual row or a bias (E_RES); gated product
+// act(g) u of two matrices (E_GUS); store and argmax keys (E_ARGMAX).
 enum Epi { E_STORE = 0, E_RES = 1, E_GUS = 2, E_ARGMAX = 3 };
+// Activations of the gated product.
+enum Act { A_SILU = 0, A_GELU_TANH = 1 };
 
 // Argmax: partial keys are kept per workgroup (and batch row), so its launches have at most this
 // many workgroups.
@@ -117,13 +120,15 @@ struct GemvArgs {
     const uint8_t *qs1, *sc1;   // matrix 1 (the up matrix of the gated product)
     const float *x;             // [nb][K]
     const float *gamma;         // [K] (norm prologue)
-    const float *res;           // [nb][N] (residual epilogue)
+    const float *res;           // residual [nb][N] (res_rstride N) or bias [N] (res_rstride 0)
     float *y;                   // [nb][N]
     int32_t *idx;               // [nb] (argmax)
     unsigned long long *keys;   // argmax: partial key per workgroup and batch row (workspace)
     int64_t N, K;
     int64_t qs_row, sc_row;
     float eps;
+    int64_t res_rstride;        // elements between the batch rows of res (0: one row for all)
+    int act;                    // gated product: 0 silu(g) u, 1 gelu_tanh(g) u
     int nb;
     int lpr_log2;               // log2 of lanes cooperating on one row
     int kt;                     // K elements per LDS tile
@@ -171,6 +176,11 @@ bool plan_mfma(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb, MfmaPla
 int launch_mfma(int fmt, int epi, bool nrm, const MfmaPlan &p, const GemvArgs &a, void *stream);
 int launch_argmax_fold(const unsigned long long *part, int n_part, int nb, int32_t *idx,
                        void *stream);
+// Per-head QK RMSNorm + RoPE in place on a QKV output (gemv_kernels.hip).
+#define QG_HEAD_DIM_MAX 256
+int launch_qk_norm_rope(float *y, int64_t row_stride, int nb, int nq, int nkv, int hd, int rh,
+                        const float *qg, const float *kg, float eps, const float *cs,
+                        const float *sn, void *stream);
 // Device address of this device's copy of the library's fixed scratch array (the argmax partial
 // keys of the no-allocation entry point) and its size; looked up once per device.  0 = ok.
 int noalloc_scratch(void **ptr, size_t *bytes);

@@ -657,7 +657,7 @@ void k_stream(GemvArgs a)
     auto load_res = [&](int gl) -> float {
         if constexpr (EPI == E_RES) {
             const int64_t g = gclamp(gl), nr = (g < 0 ? 0 : g) * R + my_u;
-            return a.res[(int64_t)my_r * a.N + (nr < a.N ? nr : a.N - 1)];
+            return a.res[(int64_t)my_r * a.res_rstride + (nr < a.N ? nr : a.N - 1)];
         } else {
             return 0.f;
         }
@@ -749,8 +749,7 @@ void k_stream(GemvArgs a)
         if constexpr (EPI == E_RES) {
             out = v[0] + res;
         } else if constexpr (EPI == E_GUS) {
-            const float gt = v[0], up = v[MATS - 1];
-            out = gt / (1.0f + expf(-gt)) * up;
+            out = gated(v[0], v[MATS - 1], a.act);
         } else {
             out = v[0];
         }
@@ -1392,7 +1391,9 @@ static StreamFn stream_fn_fmt(int epi, bool nrm, int ks, int nb, int pd)
     case E_STORE:
         return nrm ? stream_fn_ks<FMT, E_STORE, true>(ks, nb, pd)
                    : stream_fn_ks<FMT, E_STORE, false>(ks, nb, pd);
-    case E_RES: return stream_fn_ks<FMT, E_RES, false>(ks, nb, pd);
+    case E_RES:
+        return nrm ? stream_fn_ks<FMT, E_RES, true>(ks, nb, pd)
+                   : stream_fn_ks<FMT, E_RES, false>(ks, nb, pd);
     case E_GUS: return stream_fn_ks<FMT, E_GUS, true>(ks, nb, pd);
     case E_ARGMAX: return stream_fn_ks<FMT, E_ARGMAX, false>(ks, nb, pd);
     default: return {nullptr, 0};

@@ -63,7 +63,10 @@ enum {
 
 /* Operation ids for qgemv_workspace_bytes. */
 enum { QG_OP_GEMV = 0, QG_OP_NRM = 1, QG_OP_GUS_NRM = 2, QG_OP_RES = 3, QG_OP_ARGMAX = 4,
-       QG_OP_MOE = 5 };
+       QG_OP_MOE = 5, QG_OP_NRM_BIAS = 6 };
+
+/* Activations of the gated product (qgemv_gus_act_nrm). */
+enum { QG_ACT_SILU = 0, QG_ACT_GELU_TANH = 1 };
 
 /* Limits checked by every entry point. */
 #define QG_MAX_NB 16
@@ -105,6 +108,34 @@ int qgemv_nrm(int fmt, const void *W, int64_t N, int64_t K, const float *x, cons
 int qgemv_gus_nrm(int fmt, const void *Wg, const void *Wu, int64_t N, int64_t K, const float *x,
                   const float *gamma, float eps, int nb, float *h, void *ws, size_t ws_bytes,
                   void *stream);
+
+/* y = W rmsnorm(x) + bias: qgemv_nrm with bias[n] added to every batch row at the output
+ * ("honeycrisp mod.rs", pipe_q8_nrm_mb64_bias: "add bias[row] at output"; the Qwen2-style
+ * attention bias of the fused QKV).  bias is f32 [N], 4-B aligned, not overlapping y. */
+int qgemv_nrm_bias(int fmt, const void *W, int64_t N, int64_t K, const float *x,
+                   const float *gamma, float eps, const float *bias, int nb, float *y, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/* qgemv_gus_nrm with a choice of activation: h = act(g) * u, act = QG_ACT_SILU (g / (1 + e^-g))
+ * or QG_ACT_GELU_TANH (0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))), the GeluTanh variant of
+ * "honeycrisp mod.rs", pipe_q8_large4_gus_nrm_gelu).  Any other act is QG_ERR_SHAPE. */
+int qgemv_gus_act_nrm(int fmt, const void *Wg, const void *Wu, int64_t N, int64_t K,
+                      const float *x, const float *gamma, float eps, int act, int nb, float *h,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* Per-head QK RMSNorm + RoPE, in place on the output of a fused QKV GEMV ("honeycrisp mod.rs",
+ * pipe_qk_norm_rope and its launch: one group per head, Q heads then K heads).  qkv is f32
+ * [nb][(n_q_heads + 2 n_kv_heads) head_dim]: the Q heads, then the K heads, then the V heads.
+ * Each Q (K) head h: v = v * q_gamma / sqrt(mean(v^2) + eps) over its head_dim values
+ * (k_gamma for K heads; a NULL gamma skips that normalization), then for j < rope_half the pair
+ * (v[j], v[j + rope_half]) becomes (v[j] c - v[j + rope_half] s, v[j + rope_half] c + v[j] s)
+ * with c = rope_cos[r][j], s = rope_sin[r][j] (the caller's tables, one row of rope_half values
+ * per batch row: the position's row of the [max_seq][rope_half] tables); values from
+ * 2 rope_half on are not rotated.  V heads are not touched.  Limits: head_dim even, <= 256;
+ * 0 <= rope_half <= head_dim / 2; nb in [1, 16]. */
+int qgemv_qk_norm_rope(float *qkv, int nb, int n_q_heads, int n_kv_heads, int head_dim,
+                       int rope_half, const float *q_gamma, const float *k_gamma, float eps,
+                       const float *rope_cos, const float *rope_sin, void *stream);
 
 /* y[r][n] = sum_k W[n][k] x[r][k] + res[r][n].  ("honeycrisp mod.rs", fused matmul + residual in
  * forward_decode_fused_layers.)  res is f32 [nb][N]; y may equal res (in place), no other
