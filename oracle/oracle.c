@@ -33,8 +33,11 @@
 int orc_threads(void);
 
 #define ORC_Q4_0 2
+#define ORC_Q5_0 6
 #define ORC_Q8_0 8
 #define ORC_Q4_K 12
+#define ORC_Q5_K 13
+#define ORC_Q6_K 14
 
 /* ---------------------------------------------------------------------------
  * IEEE 754 binary16 -> double, exact for every bit pattern (little-endian
@@ -63,8 +66,11 @@ int64_t orc_block_bytes(int fmt)
 {
     switch (fmt) {
     case ORC_Q4_0: return 18;   /* [ILayer] gemv_q1_k_lcpp_src: Q4_0 is 18 B per 32 weights */
+    case ORC_Q5_0: return 22;   /* [ILayer] gemv_q5_0n_k_lcpp_src: f16 d, 4 B qh, 16 B nibbles */
     case ORC_Q8_0: return 34;   /* [ILayer] gemv_q8_0n_k_lcpp_src: f16 d + 32 x i8 */
     case ORC_Q4_K: return 144;  /* f16 d, f16 dmin, 12 B packed 6-bit pairs, 128 B nibbles */
+    case ORC_Q5_K: return 176;  /* [ILayer] gemv_q5k_k_lcpp_src: Q4_K's fields + 32 B qh */
+    case ORC_Q6_K: return 210;  /* [ILayer] gemv_q6k_k_lcpp_src: 128 ql, 64 qh, 16 i8 scales, d */
     default: return -1;
     }
 }
@@ -73,8 +79,11 @@ int64_t orc_block_weights(int fmt)
 {
     switch (fmt) {
     case ORC_Q4_0: return 32;
+    case ORC_Q5_0: return 32;
     case ORC_Q8_0: return 32;
     case ORC_Q4_K: return 256;  /* [Honey] quant_matmul: Q4_K when k % 256 == 0 */
+    case ORC_Q5_K: return 256;
+    case ORC_Q6_K: return 256;
     default: return -1;
     }
 }
@@ -146,6 +155,80 @@ static void dq_q4_k(const uint8_t *b, double *w)
     }
 }
 
+/* Q5_0: w = d ((nib | bit << 4) - 16).  [ILayer] gemv_q5_0n_k_lcpp_src (and
+ * q5_0_to_q8_0n: q8 = (nib | bit << 4) - 16).  Field order d, qh, qs as the
+ * page's padded layout lists them.  Bit order (a reading): element j takes its
+ * nibble as Q4_0 does (low nibble of byte j for j < 16, high nibble of byte
+ * j - 16 otherwise) and its fifth bit from bit j of the little-endian qh word. */
+static void dq_q5_0(const uint8_t *b, double *w)
+{
+    double d = orc_f16(rd16(b));
+    uint32_t qh = (uint32_t)b[2] | ((uint32_t)b[3] << 8) | ((uint32_t)b[4] << 16) |
+                  ((uint32_t)b[5] << 24);
+    const uint8_t *qs = b + 6;
+    for (int j = 0; j < 16; ++j) {
+        int lo = (qs[j] & 15) | (int)(((qh >> j) & 1u) << 4);
+        int hi = (qs[j] >> 4) | (int)(((qh >> (j + 16)) & 1u) << 4);
+        w[j] = d * (double)(lo - 16);
+        w[j + 16] = d * (double)(hi - 16);
+    }
+}
+
+/* Q5_K super-block of 256: w = d sc_j q - dmin m_j with q = nib | bit << 4.
+ * [ILayer] gemv_q5k_k_lcpp_src: Q4_K's d, dmin and 12-byte 6-bit pack, then
+ * 32 qh bytes, then 128 nibble bytes; sub-block s takes bit s of qh[l].  The
+ * nibble order and l (the element's place within its sub-block of 32) follow
+ * the Q4_K reading. */
+static void dq_q5_k(const uint8_t *b, double *w)
+{
+    double d = orc_f16(rd16(b));
+    double dmin = orc_f16(rd16(b + 2));
+    const uint8_t *s = b + 4;
+    const uint8_t *qh = b + 16;
+    const uint8_t *qs = b + 48;
+    for (int c = 0; c < 4; ++c) {
+        int sc0, m0, sc1, m1;
+        orc_q4k_scale_min(s, 2 * c, &sc0, &m0);
+        orc_q4k_scale_min(s, 2 * c + 1, &sc1, &m1);
+        for (int l = 0; l < 32; ++l) {
+            int lo = (qs[32 * c + l] & 15) | (((qh[l] >> (2 * c)) & 1) << 4);
+            int hi = (qs[32 * c + l] >> 4) | (((qh[l] >> (2 * c + 1)) & 1) << 4);
+            w[64 * c + l] = d * (double)sc0 * (double)lo - dmin * (double)m0;
+            w[64 * c + 32 + l] = d * (double)sc1 * (double)hi - dmin * (double)m1;
+        }
+    }
+}
+
+/* Q6_K super-block of 256: 128 ql bytes (low 4 bits), 64 qh bytes (high 2
+ * bits), 16 signed 8-bit scales (one per 16 weights), f16 d ([ILayer]
+ * gemv_q6k_k_lcpp_src gives these fields in this order).  w = d sc (q - 32)
+ * with q = low | high << 4 in 0..63.  Which bits of which bytes form element
+ * e (a reading; the page gives field sizes only): in each half n of 128
+ * elements, for l < 32, byte ql[64n + l] holds element 128n + l (low nibble)
+ * and 128n + 64 + l (high nibble), byte ql[64n + 32 + l] holds 128n + 32 + l
+ * and 128n + 96 + l, and qh[32n + l] holds their high bits in bit pairs 0-1,
+ * 2-3, 4-5, 6-7 for elements 128n + l, + 32, + 64, + 96; element 128n + i
+ * takes scale 8n + i / 16. */
+static void dq_q6_k(const uint8_t *b, double *w)
+{
+    const uint8_t *ql = b, *qh = b + 128;
+    const int8_t *sc = (const int8_t *)(b + 192);
+    double d = orc_f16(rd16(b + 208));
+    for (int n = 0; n < 2; ++n) {
+        for (int l = 0; l < 32; ++l) {
+            int q1 = (ql[64 * n + l] & 15) | (((qh[32 * n + l] >> 0) & 3) << 4);
+            int q2 = (ql[64 * n + 32 + l] & 15) | (((qh[32 * n + l] >> 2) & 3) << 4);
+            int q3 = (ql[64 * n + l] >> 4) | (((qh[32 * n + l] >> 4) & 3) << 4);
+            int q4 = (ql[64 * n + 32 + l] >> 4) | (((qh[32 * n + l] >> 6) & 3) << 4);
+            int e = 128 * n + l;
+            w[e] = d * (double)sc[8 * n + e % 128 / 16] * (double)(q1 - 32);
+            w[e + 32] = d * (double)sc[8 * n + (e + 32) % 128 / 16] * (double)(q2 - 32);
+            w[e + 64] = d * (double)sc[8 * n + (e + 64) % 128 / 16] * (double)(q3 - 32);
+            w[e + 96] = d * (double)sc[8 * n + (e + 96) % 128 / 16] * (double)(q4 - 32);
+        }
+    }
+}
+
 /* Dequantize one row of K weights (K a multiple of the block size) from its
  * GGUF-native bytes.  A row is K/bs consecutive blocks ([Honey]
  * transpose_q8_blocks: [n_rows, n_blocks, block] is the native order). */
@@ -157,9 +240,14 @@ int orc_dequant_row(int fmt, const uint8_t *row, int64_t K, double *w)
     for (int64_t b = 0; b < K / bw; ++b) {
         const uint8_t *blk = row + b * bb;
         double *out = w + b * bw;
-        if (fmt == ORC_Q4_0) dq_q4_0(blk, out);
-        else if (fmt == ORC_Q8_0) dq_q8_0(blk, out);
-        else dq_q4_k(blk, out);
+        switch (fmt) {
+        case ORC_Q4_0: dq_q4_0(blk, out); break;
+        case ORC_Q5_0: dq_q5_0(blk, out); break;
+        case ORC_Q8_0: dq_q8_0(blk, out); break;
+        case ORC_Q4_K: dq_q4_k(blk, out); break;
+        case ORC_Q5_K: dq_q5_k(blk, out); break;
+        default: dq_q6_k(blk, out); break;
+        }
     }
     return 0;
 }

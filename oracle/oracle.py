@@ -20,7 +20,7 @@ import subprocess
 
 import numpy as np
 
-Q4_0, Q8_0, Q4_K = 2, 8, 12
+Q4_0, Q5_0, Q8_0, Q4_K, Q5_K, Q6_K = 2, 6, 8, 12, 13, 14
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")

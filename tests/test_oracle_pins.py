@@ -651,3 +651,152 @@ def test_nrm_bias_with_zero_weights_is_the_bias():
     bias = g.standard_normal(N)
     y, A = oracle.qgemv_nrm_bias(Q4_0, W, N, K, g.standard_normal((2, K)), np.ones(K), 1e-5, bias)
     assert np.array_equal(y, np.stack([bias, bias])) and np.all(A == 0)
+
+
+# ----------------------------------------------------------------------------- Q5_0, Q5_K, Q6_K
+
+Q5_0, Q5_K, Q6_K = oracle.Q5_0, oracle.Q5_K, oracle.Q6_K
+
+
+def test_q5_0_hand_block():
+    """d = 0.25; element j (j < 16) has nibble j % 16 and fifth bit 1 for odd j; element j + 16
+    has nibble 15 - j and fifth bit 1 for j < 8 (qh = 0x00FFAAAA little-endian):
+    w = 0.25 (q - 16) with q listed by hand below."""
+    qs = bytes((j & 15) | ((15 - j) << 4) for j in range(16))
+    qh = (0x00FFAAAA).to_bytes(4, "little")
+    blk = np.frombuffer(f16_bytes(0.25) + qh + qs, dtype=np.uint8)
+    q = [j | (16 if j % 2 else 0) for j in range(16)] + [(15 - j) | (16 if j < 8 else 0) for j in range(16)]
+    # spelled out: elements 0..15 -> 0,17,2,19,4,21,6,23,8,25,10,27,12,29,14,31
+    assert q[:16] == [0, 17, 2, 19, 4, 21, 6, 23, 8, 25, 10, 27, 12, 29, 14, 31]
+    assert q[16:] == [31, 30, 29, 28, 27, 26, 25, 24, 7, 6, 5, 4, 3, 2, 1, 0]
+    w = oracle.dequant(Q5_0, blk, 32)[0]
+    assert np.array_equal(w, 0.25 * (np.array(q, dtype=np.float64) - 16))
+
+
+def test_q5_0_upcast_to_q8_0_is_exact():
+    """'Crate inferencelayer' docs, q5_0_to_q8_0n: d8 = d5, q8 = (nib | bit << 4) - 16 is a
+    lossless re-encoding."""
+    g = np.random.default_rng(71)
+    N, K = 6, 128
+    import workloads as wl
+    W5 = wl.q5_0_matrix(g, N, K).reshape(N, -1, 22)
+    W8 = np.empty(W5.shape[:2] + (34,), np.uint8)
+    W8[..., :2] = W5[..., :2]
+    qh = W5[..., 2:6].copy().view("<u4")[..., 0]
+    for j in range(16):
+        lo = (W5[..., 6 + j] & 15) | (((qh >> j) & 1) << 4).astype(np.uint8)
+        hi = (W5[..., 6 + j] >> 4) | (((qh >> (j + 16)) & 1) << 4).astype(np.uint8)
+        W8[..., 2 + j] = (lo.astype(np.int16) - 16).astype(np.int8).view(np.uint8)
+        W8[..., 18 + j] = (hi.astype(np.int16) - 16).astype(np.int8).view(np.uint8)
+    W5, W8 = W5.reshape(N, -1), W8.reshape(N, -1)
+    assert np.array_equal(oracle.dequant(Q5_0, W5, K), oracle.dequant(Q8_0, W8, K))
+    x = g.standard_normal((2, K))
+    assert np.array_equal(oracle.gemv(Q5_0, W5, N, K, x)[0], oracle.gemv(Q8_0, W8, N, K, x)[0])
+
+
+def _q5k_from_q4k(b4: np.ndarray, qh: bytes) -> np.ndarray:
+    b4 = b4.reshape(-1)
+    return np.frombuffer(b4[:16].tobytes() + qh + b4[16:].tobytes(), dtype=np.uint8)
+
+
+def test_q5_k_without_fifth_bits_is_q4_k_and_each_bit_adds_16_d_sc():
+    """'Crate inferencelayer' docs, gemv_q5k_k_lcpp_src: Q4_K plus the fifth-bit plane, sub-block
+    s taking bit s of qh[l].  With qh = 0 the weights equal Q4_K's on the same fields; setting
+    only bit s of qh[l] raises exactly element (sub-block s, place l) by 16 d sc_s."""
+    import workloads as wl
+    g = np.random.default_rng(73)
+    b4 = wl.q4_k_matrix(g, 1, 256)
+    w4 = oracle.dequant(Q4_K, b4, 256)[0]
+    assert np.array_equal(oracle.dequant(Q5_K, _q5k_from_q4k(b4, bytes(32)), 256)[0], w4)
+    d = float(b4.reshape(-1)[0:2].view("<f2")[0])
+    scales = b4.reshape(-1)[4:16].tobytes()
+    for s_ in range(8):
+        sc, _ = oracle.q4k_scale_min(scales, s_)
+        for l in (0, 5, 31):
+            qh = bytearray(32)
+            qh[l] = 1 << s_
+            w5 = oracle.dequant(Q5_K, _q5k_from_q4k(b4, bytes(qh)), 256)[0]
+            e = 64 * (s_ // 2) + 32 * (s_ % 2) + l
+            diff = w5 - w4
+            assert diff[e] == 16 * d * sc and np.count_nonzero(diff) == (1 if sc else 0), (s_, l)
+
+
+def _q6k_block(ql, qh, sc, d):
+    return np.frombuffer(bytes(ql) + bytes(qh) + np.asarray(sc, np.int8).tobytes() + f16_bytes(d),
+                         dtype=np.uint8)
+
+
+def test_q6_k_zero_point_and_one_hot_sweep():
+    """q = 32 everywhere (every low nibble 0, every high pair 2 = 0b10) gives w = 0.  Then each
+    element on its own: its low nibble set to v and its high pair to 3 gives q = 48 + v, so only
+    that element moves, to d sc (16 + v), with the scale of its sixteen."""
+    ql0 = [0] * 128
+    qh0 = [0xAA] * 64                       # every 2-bit field = 2
+    sc = [((i * 37) % 255) - 127 for i in range(16)]
+    d = 0.0078125
+    assert np.all(oracle.dequant(Q6_K, _q6k_block(ql0, qh0, sc, d), 256)[0] == 0.0)
+    for e in range(256):
+        n, i = divmod(e, 128)
+        quarter, l = divmod(i, 32)              # element 128 n + 32 quarter + l
+        byte = 64 * n + l + (32 if quarter in (1, 3) else 0)
+        shift = 4 if quarter >= 2 else 0
+        v = (e * 7) % 16
+        ql = list(ql0)
+        ql[byte] |= v << shift
+        qh = list(qh0)
+        qh[32 * n + l] |= 3 << (2 * quarter)
+        w = oracle.dequant(Q6_K, _q6k_block(ql, qh, sc, d), 256)[0]
+        want = d * sc[8 * n + i // 16] * (16 + v)
+        assert w[e] == want and np.count_nonzero(w) == (1 if want else 0), e
+
+
+def test_k_quant_brute_force_second_forms():
+    """K = 256 and 512, small-integer x, power-of-two d and dmin: the oracle equals, exactly, the
+    sub-block forms worked in integers here: Q5_K sum_j (d sc_j sum q x - dmin m_j sum x) and
+    Q6_K sum_j d sc_j sum (q - 32) x."""
+    import workloads as wl
+    g = np.random.default_rng(79)
+    for K in (256, 512):
+        for fmt in (Q5_K, Q6_K):
+            N = 8
+            W = wl.matrix(fmt, g, N, K).reshape(N, -1, wl.BLOCK_BYTES[fmt]).copy()
+            e = g.integers(2, 8, size=W.shape[:2])
+            doff = 0 if fmt == Q5_K else 208
+            W[..., doff:doff + 2] = (2.0 ** -e).astype("<f2")[..., None].view(np.uint8)
+            if fmt == Q5_K:
+                W[..., 2:4] = (2.0 ** -(e + 1)).astype("<f2")[..., None].view(np.uint8)
+            W = W.reshape(N, -1)
+            x = g.integers(-5, 6, size=(2, K))
+            y, _ = oracle.gemv(fmt, W, N, K, x.astype(np.float64))
+            blk = W.reshape(N, -1, wl.BLOCK_BYTES[fmt])
+            for r in range(2):
+                for n in range(N):
+                    tot = 0.0
+                    for b in range(K // 256):
+                        B = blk[n, b]
+                        xs = x[r, 256 * b:256 * b + 256]
+                        if fmt == Q5_K:
+                            d = float(B[0:2].view("<f2")[0]); dm = float(B[2:4].view("<f2")[0])
+                            for c in range(4):
+                                for part in (0, 1):
+                                    s_ = 2 * c + part
+                                    sc, m = oracle.q4k_scale_min(B[4:16].tobytes(), s_)
+                                    qx = sx = 0
+                                    for l in range(32):
+                                        nib = (int(B[48 + 32 * c + l]) >> (4 * part)) & 15
+                                        q5 = nib | (((int(B[16 + l]) >> s_) & 1) << 4)
+                                        qx += q5 * int(xs[64 * c + 32 * part + l])
+                                        sx += int(xs[64 * c + 32 * part + l])
+                                    tot += d * sc * qx - dm * m * sx
+                        else:
+                            d = float(B[208:210].view("<f2")[0])
+                            scs = B[192:208].view(np.int8)
+                            for hh in range(2):
+                                for l in range(32):
+                                    for qq in range(4):
+                                        src = 64 * hh + l + (32 if qq in (1, 3) else 0)
+                                        nib = (int(B[src]) >> (4 if qq >= 2 else 0)) & 15
+                                        hi = (int(B[128 + 32 * hh + l]) >> (2 * qq)) & 3
+                                        el = 128 * hh + 32 * qq + l
+                                        tot += d * int(scs[8 * hh + (32 * qq + l) // 16]) * ((nib | hi << 4) - 32) * int(xs[el])
+                    assert y[r, n] == tot, (fmt, K, r, n)

@@ -23,10 +23,10 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-Q4_0, Q8_0, Q4_K = 2, 8, 12
-FMT_NAME = {Q4_0: "q4_0", Q8_0: "q8_0", Q4_K: "q4_k"}
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144}
-BLOCK_WEIGHTS = {Q4_0: 32, Q8_0: 32, Q4_K: 256}
+Q4_0, Q5_0, Q8_0, Q4_K, Q5_K, Q6_K = 2, 6, 8, 12, 13, 14
+FMT_NAME = {Q4_0: "q4_0", Q5_0: "q5_0", Q8_0: "q8_0", Q4_K: "q4_k", Q5_K: "q5_k", Q6_K: "q6_k"}
+BLOCK_BYTES = {Q4_0: 18, Q5_0: 22, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
+BLOCK_WEIGHTS = {Q4_0: 32, Q5_0: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
 
 T_X, T_GAMMA, T_W, T_UP, T_DOWN, T_ROUTER, T_EXPERTS = 0, 1, 2, 3, 4, 5, 6
 
@@ -81,8 +81,42 @@ def q4_k_matrix(g: np.random.Generator, N: int, K: int, d_range=Q4_K_D) -> np.nd
     return blk.reshape(N, nbk * 144)
 
 
+def q5_0_matrix(g: np.random.Generator, N: int, K: int, d_range=Q4_0_D) -> np.ndarray:
+    """uint8 [N, K/32*22]: d ~ U[d_range] as f16, then 4 bytes of fifth bits and 16 nibble bytes,
+    all uniform (so q = nib | bit << 4 ~ U{0..31})."""
+    nbk = K // 32
+    blk = np.empty((N, nbk, 22), dtype=np.uint8)
+    blk[..., 0:2] = _f16_bytes(g.uniform(*d_range, size=(N, nbk)))
+    blk[..., 2:22] = g.integers(0, 256, size=(N, nbk, 20), dtype=np.uint8)
+    return blk.reshape(N, nbk * 22)
+
+
+def q5_k_matrix(g: np.random.Generator, N: int, K: int, d_range=Q4_K_D) -> np.ndarray:
+    """uint8 [N, K/256*176]: d, dmin ~ U[d_range] as f16; scale, fifth-bit and nibble bytes
+    uniform."""
+    nbk = K // 256
+    blk = np.empty((N, nbk, 176), dtype=np.uint8)
+    blk[..., 0:2] = _f16_bytes(g.uniform(*d_range, size=(N, nbk)))
+    blk[..., 2:4] = _f16_bytes(g.uniform(*d_range, size=(N, nbk)))
+    blk[..., 4:176] = g.integers(0, 256, size=(N, nbk, 172), dtype=np.uint8)
+    return blk.reshape(N, nbk * 176)
+
+
+def q6_k_matrix(g: np.random.Generator, N: int, K: int, d_range=Q4_K_D) -> np.ndarray:
+    """uint8 [N, K/256*210]: ql and qh bytes uniform (q ~ U{0..63}), 16 scales ~ U{-127..127}
+    as signed bytes, d ~ U[d_range] as f16 (last)."""
+    nbk = K // 256
+    blk = np.empty((N, nbk, 210), dtype=np.uint8)
+    blk[..., 0:192] = g.integers(0, 256, size=(N, nbk, 192), dtype=np.uint8)
+    sc = g.integers(-127, 128, size=(N, nbk, 16), dtype=np.int16).astype(np.int8)
+    blk[..., 192:208] = sc.view(np.uint8)
+    blk[..., 208:210] = _f16_bytes(g.uniform(*d_range, size=(N, nbk)))
+    return blk.reshape(N, nbk * 210)
+
+
 def matrix(fmt: int, g: np.random.Generator, N: int, K: int) -> np.ndarray:
-    return {Q4_0: q4_0_matrix, Q8_0: q8_0_matrix, Q4_K: q4_k_matrix}[fmt](g, N, K)
+    return {Q4_0: q4_0_matrix, Q5_0: q5_0_matrix, Q8_0: q8_0_matrix, Q4_K: q4_k_matrix,
+            Q5_K: q5_k_matrix, Q6_K: q6_k_matrix}[fmt](g, N, K)
 
 
 def normal_f32(g: np.random.Generator, shape) -> np.ndarray:
