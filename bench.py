@@ -143,36 +143,41 @@ def make_lm_head(warm, nb):
                  step, cpu, cfg, flops=2 * nb * w.N * w.K)
 
 
-def make_gemv(warm, nb, rows=65536, hidden=2048):
-    """Plain Q4_0 GEMV, by default on the lm_head-sized matrix (65536 x 2048): the nb=1 gate
-    shape; --rows / --hidden pick other sizes."""
+def make_gemv(warm, nb, rows=65536, hidden=2048, fmt=None):
+    """Plain GEMV, by default Q4_0 on the lm_head-sized matrix (65536 x 2048): the nb=1 gate
+    shape; --rows / --hidden pick other sizes, fmt another block format (same seeded recipe:
+    the lm_head workload's x, the format's own generator for W)."""
     import torch
     import dequant_gemv_q4_amd as q
     from dequant_gemv_q4_amd import device as D
     import workloads as wl
 
+    fmt = q.Q4_0 if fmt is None else fmt
     w = wl.lm_head(nb=nb, vocab=rows, hidden=hidden)
     a = w.arrays
-    Wp = D.pack(q.Q4_0, a["W"], w.N, w.K)
+    if fmt != q.Q4_0:
+        a = dict(a, W=wl.matrix(fmt, wl.rng(3, wl.T_W), w.N, w.K))
+    Wp = D.pack(fmt, a["W"], w.N, w.K)
     R = _copies(Wp.numel(), warm)
     sets = _rotated(Wp, R)
     x = D.to_device(a["x"])
     y = torch.empty((nb, w.N), dtype=torch.float32, device="cuda")
 
     def step(i):
-        q.qgemv(q.Q4_0, sets[i % R], w.N, w.K, x, nb, y)
+        q.qgemv(fmt, sets[i % R], w.N, w.K, x, nb, y)
 
     def cpu():
         import oracle
-        oracle.qgemv(q.Q4_0, a["W"], w.N, w.K, a["x"])
+        oracle.qgemv(fmt, a["W"], w.N, w.K, a["x"])
         return a["W"].nbytes
 
+    fname = wl.FMT_NAME[fmt]
     alg = a["W"].nbytes + nb * w.K * 4 + nb * w.N * 4
-    name = f"q4_0_gemv_{w.N}x{w.K}_nb{nb}"
-    cfg = {"workload": name, "nb": nb, "format": "q4_0", "N": w.N, "K": w.K,
+    name = f"{fname}_gemv_{w.N}x{w.K}_nb{nb}"
+    cfg = {"workload": name, "nb": nb, "format": fname, "N": w.N, "K": w.K,
            "launches_per_step": 1, "weight_copies": R, "cold": not warm}
-    return Bench(name, a["W"].nbytes, alg, f"qgemv (q4_0, {w.N}x{w.K}, nb={nb})", step, step, cpu,
-                 cfg, flops=2 * nb * w.N * w.K)
+    return Bench(name, a["W"].nbytes, alg, f"qgemv ({fname}, {w.N}x{w.K}, nb={nb})", step, step,
+                 cpu, cfg, flops=2 * nb * w.N * w.K)
 
 
 def make_qkv(warm, nb):
@@ -558,6 +563,11 @@ def main():
         extras["qkv_attn_nb1"] = run_extra("qkv + bias + qk norm + rope",
                                            lambda: make_qkv_attn(False, 1), es, ew, torch)
         extras["lm_head_nb1"] = run_extra("lm_head", lambda: make_lm_head(False, 1), es, ew, torch)
+        import dequant_gemv_q4_amd as qq
+        for f, nm in ((qq.Q8_0, "q8_0"), (qq.Q4_K, "q4_k"), (qq.Q5_0, "q5_0"), (qq.Q5_K, "q5_k"),
+                      (qq.Q6_K, "q6_k")):
+            extras[f"{nm}_gemv_nb1"] = run_extra(f"{nm} gemv", lambda f=f: make_gemv(False, 1, fmt=f),
+                                                 es, ew, torch)
         w = run_extra("gemv warm", lambda: make_gemv(True, 1), es, ew, torch)
         w["label"] = "cache-assisted: one weight copy reused, served in part by the 256 MB MALL"
         extras["gemv_nb1_warm"] = w

@@ -15,7 +15,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqgemv.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "qgemv.h")
 
-Q4_0, Q8_0, Q4_K = 2, 8, 12
+Q4_0, Q5_0, Q8_0, Q4_K, Q5_K, Q6_K = 2, 6, 8, 12, 13, 14
 OP_GEMV, OP_NRM, OP_GUS_NRM, OP_RES, OP_ARGMAX, OP_MOE, OP_NRM_BIAS = range(7)
 ACT_SILU, ACT_GELU_TANH = 0, 1
 STATUS = {0: "QG_OK", 1: "QG_ERR_NULL", 2: "QG_ERR_FORMAT", 3: "QG_ERR_SHAPE", 4: "QG_ERR_ALIGN",

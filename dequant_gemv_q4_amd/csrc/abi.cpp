@@ -30,22 +30,35 @@ namespace qg {
 
 static int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
 
-bool fmt_valid(int fmt) { return fmt == FQ4_0 || fmt == FQ8_0 || fmt == FQ4_K; }
+bool fmt_valid(int fmt)
+{
+    return fmt == FQ4_0 || fmt == FQ5_0 || fmt == FQ8_0 || fmt == FQ4_K || fmt == FQ5_K ||
+           fmt == FQ6_K;
+}
 
+// Packed layout: the quant plane (nibbles, or Q8_0 bytes), the scale plane (f16 d per 32, or the
+// 16-byte Q4_K / Q5_K header, or the 16 signed Q6_K scales per 256), then for the high-bit
+// formats a plane of the fifth (sixth) bits re-laid per 32 weights, and for Q6_K a plane of its
+// f16 d per 256.  Each plane starts 256-B aligned; the bytes per weight equal GGUF's.
 bool layout(int fmt, int64_t N, int64_t K, Layout *L)
 {
     if (!fmt_valid(fmt) || N < 1 || K < 1)
         return false;
-    const int bw = fmt == FQ4_K ? 256 : 32;
-    const int bb = fmt == FQ4_0 ? 18 : fmt == FQ8_0 ? 34 : 144;
+    const int bw = fmt_super(fmt) ? 256 : 32;
+    const int bb = fmt == FQ4_0 ? 18 : fmt == FQ5_0 ? 22 : fmt == FQ8_0 ? 34 : fmt == FQ4_K ? 144
+                 : fmt == FQ5_K ? 176 : 210;
     if (K % bw != 0 || K > QG_MAX_K)
         return false;
     L->block_w = bw;
     L->block_b = bb;
     L->qs_row = fmt == FQ8_0 ? K : K / 2;
     L->sc_row = K / 16;
+    L->hb_row = fmt == FQ6_K ? K / 4 : fmt_hbits(fmt) ? K / 8 : 0;
+    L->d_row = fmt == FQ6_K ? K / 128 : 0;
     L->sc_off = round256(N * L->qs_row);
-    L->total = L->sc_off + round256(N * L->sc_row);
+    L->hb_off = L->sc_off + round256(N * L->sc_row);
+    L->d_off = L->hb_off + round256(N * L->hb_row);
+    L->total = L->d_off + round256(N * L->d_row);
     L->gguf_row = K / bw * bb;
     return true;
 }
@@ -196,6 +209,8 @@ static bool plan_moe(int fmt, int64_t n_exp, int64_t N, int64_t K, int nb, int t
 {
     if (n_exp < 1 || n_exp > QG_MOE_EXPERTS_MAX)   // the per-expert counts live in LDS
         return false;
+    if (fmt_hbits(fmt))                            // the expert kernel takes Q4_0, Q8_0, Q4_K
+        return false;
     const int64_t C = (fmt == FQ8_0 ? K : K / 2) / 16;
     p->cpl = C <= 64 ? 1 : C <= 128 ? 2 : C <= 256 ? 4 : 0;
     if (!p->cpl)
@@ -272,6 +287,10 @@ static GemvArgs gemv_args(const Layout &L, const void *W, int64_t N, int64_t K, 
     memset(&a, 0, sizeof(a));
     a.qs0 = static_cast<const uint8_t *>(W);
     a.sc0 = a.qs0 + L.sc_off;
+    a.hb0 = a.qs0 + L.hb_off;
+    a.dd0 = a.qs0 + L.d_off;
+    a.hb_row = L.hb_row;
+    a.d_row = L.d_row;
     a.x = x;
     a.y = y;
     a.N = N;
@@ -291,7 +310,8 @@ static int run_gemv(int fmt, int epi, bool nrm, GemvArgs a, void *stream)
     StreamPlan sp;
     MfmaPlan mp;
     // the streaming and matrix kernels address each plane with 32-bit buffer offsets
-    const bool small = a.N * a.qs_row < QG_BUF_MAX && a.N * a.sc_row < QG_BUF_MAX;
+    const bool small = a.N * a.qs_row < QG_BUF_MAX && a.N * a.sc_row < QG_BUF_MAX &&
+                       a.N * a.hb_row < QG_BUF_MAX && a.N * a.d_row < QG_BUF_MAX;
     if (small && a.nb >= QG_MFMA_MIN_NB && plan_mfma(fmt, epi, nrm, a.N, a.K, a.nb, &mp) &&
         mp.grid <= QG_ARGMAX_MAX_GRID) {
         grid = mp.grid;
@@ -310,7 +330,8 @@ static int run_gemv(int fmt, int epi, bool nrm, GemvArgs a, void *stream)
         a.rows_per_step = p.rows_per_step;
         a.n_steps = p.n_steps;
         grid = p.grid;
-        herr = launch_gemv(fmt, epi, nrm, a, p.grid, p.lds, stream);
+        herr = fmt_hbits(fmt) ? launch_gemv_x(fmt, epi, nrm, a, p.grid, p.lds, stream)
+                              : launch_gemv(fmt, epi, nrm, a, p.grid, p.lds, stream);
     }
     if (herr == 0 && epi == E_ARGMAX)
         herr = launch_argmax_fold(a.keys, grid, a.nb, a.idx, stream);
@@ -336,7 +357,7 @@ const char *qgemv_status_str(int status)
     switch (status) {
     case QG_OK: return "ok";
     case QG_ERR_NULL: return "a required pointer is NULL";
-    case QG_ERR_FORMAT: return "unknown format (expected Q4_0=2, Q8_0=8 or Q4_K=12)";
+    case QG_ERR_FORMAT: return "unknown or unsupported format (Q4_0=2, Q5_0=6, Q8_0=8, Q4_K=12, Q5_K=13, Q6_K=14; experts: Q4_0, Q8_0, Q4_K)";
     case QG_ERR_SHAPE: return "bad shape (N, K, nb, topk or n_exp out of range, or K not a multiple of the block)";
     case QG_ERR_ALIGN: return "misaligned pointer (W needs 256 B, x and gamma 16 B, other arrays 4 B)";
     case QG_ERR_WORKSPACE: return "workspace missing or smaller than qgemv_workspace_bytes()";
@@ -491,6 +512,8 @@ int qgemv_gus_act_nrm(int fmt, const void *Wg, const void *Wu, int64_t N, int64_
     GemvArgs a = gemv_args(L, Wg, N, K, x, nb, h);
     a.qs1 = static_cast<const uint8_t *>(Wu);
     a.sc1 = a.qs1 + L.sc_off;
+    a.hb1 = a.qs1 + L.hb_off;
+    a.dd1 = a.qs1 + L.d_off;
     a.gamma = gamma;
     a.eps = eps;
     a.act = act;
@@ -581,6 +604,8 @@ int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t 
     int st = check_common(fmt, W_experts, N, K, x, nb, y, &L);
     if (st != QG_OK)
         return st;
+    if (fmt_hbits(fmt))
+        return QG_ERR_FORMAT;
     if (!ids || !wts)
         return QG_ERR_NULL;
     if (!ws)

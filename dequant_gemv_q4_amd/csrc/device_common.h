@@ -41,10 +41,17 @@ template <int FMT> struct Fc {
 template <int FMT>
 __device__ __forceinline__ int chunk_elem(int i, int j)
 {
-    if constexpr (FMT == FQ4_0) {
+    if constexpr (FMT == FQ4_0 || FMT == FQ5_0) {
         return 32 * i + 4 * j;             // one 32-weight block per chunk
     } else if constexpr (FMT == FQ8_0) {
         return 16 * i + 4 * j;             // half a block per chunk
+    } else if constexpr (FMT == FQ6_K) {
+        // Q6_K: chunk i is ql bytes 16t..16t+15 of super-block s (t = i % 8, n = t / 4,
+        // u = t % 4); its low nibbles are elements 128n + 16u + 0..15, its high nibbles
+        // elements 128n + 64 + 16u + 0..15.
+        const int s = i >> 3, t = i & 7, n = t >> 2, u = t & 3;
+        const int base = 256 * s + 128 * n + 16 * u;
+        return j < 4 ? base + 4 * j : base + 64 + 4 * (j - 4);
     } else {
         // Q4_K: chunk i is bytes 16q..16q+15 of super-block s's nibbles (q = i % 8).  Its low
         // nibbles are elements 64c + 16h + 0..15 (sub-block 2c), its high nibbles elements
@@ -84,7 +91,7 @@ __device__ void stage_tile(const float *const *xrow, const float *gamma, const f
     for (int f = threadIdx.x; f < NB * ct; f += blockDim.x) {
         const int r = f / ct, i = f % ct;
         const float4 *xc = X4 + (size_t)r * XF4 * ct + i;
-        if constexpr (FMT == FQ4_0) {
+        if constexpr (FMT == FQ4_0 || FMT == FQ5_0) {
             // dot order: for each dword k, its low nibbles (elements 4k..4k+3) then its high
             // nibbles (elements 16+4k..16+4k+3)
             float s = 0.f;
@@ -151,7 +158,12 @@ __device__ void row_inv_rms(const float *const *xrow, int64_t K, float eps, floa
 // ------------------------------------------------------------------------------------ compute
 
 struct MatPtr {
-    const uint8_t *qs, *sc;
+    const uint8_t *qs, *sc, *hb, *dd;   // quant, scale, high-bit and (Q6_K) d planes
+};
+
+// Row strides of the four planes.
+struct RowBytes {
+    int64_t qs, sc, hb, d;
 };
 
 // Scale terms of one chunk of one row: Q4_0/Q8_0 use a (the block scale); Q4_K uses
@@ -164,7 +176,16 @@ template <int FMT>
 __device__ __forceinline__ ChunkScale chunk_scale(const uint4 &s, int q /* chunk in super-block */)
 {
     ChunkScale cs;
-    if constexpr (FMT == FQ4_K) {
+    if constexpr (FMT == FQ6_K) {
+        // s.x, s.y: the eight signed scales of the chunk's half of the super-block (bytes 8n..8n+7,
+        // n = q / 4); the chunk (u = q % 4) takes scale u (low nibbles) and u + 4 (high);
+        // s.z: the super-block's f16 d
+        const float d = h2f(s.z & 0xffffu);
+        const int u = q & 3;
+        cs.a = d * (float)(int8_t)((s.x >> (8 * u)) & 0xffu);
+        cs.a2 = d * (float)(int8_t)((s.y >> (8 * u)) & 0xffu);
+        cs.b = cs.b2 = 0.f;
+    } else if constexpr (fmt_min(FMT)) {
         const float d = h2f(s.x & 0xffffu), dmin = h2f(s.x >> 16);
         const int c = q >> 1;
         const int jA = 2 * c, jB = 2 * c + 1;
@@ -202,11 +223,35 @@ __device__ __forceinline__ float k_center(float a, float b)
 }
 
 // Decode the 16-byte chunk into the per-element factors the dot multiplies, exact in f32 and in
-// dot order: Q4_0 the signed q - 8, Q8_0 the signed byte, Q4_K the nibble (its -dmin m term is
-// applied to the chunk's x sums).  The Q4_0 and Q8_0 dots then hold no offset to cancel.
+// dot order: Q4_0 the signed q - 8, Q5_0 q - 16, Q8_0 the signed byte, Q6_K q - 32, Q4_K and Q5_K
+// the unsigned q (centred per sub-block in chunk_dot).  h: the chunk's high-bit words (the
+// layout k_pack writes: low nibble of byte 4k + m at bit 8m + k, high nibble at 8m + 4 + k; Q6_K
+// two bits each, at 8m + 2k of h.x (low) and h.y (high)).
 template <int FMT>
-__device__ __forceinline__ void decode_chunk(const uint4 &q, float *w)
+__device__ __forceinline__ void decode_chunk(const uint4 &q, const uint2 &h, float *w)
 {
+    if constexpr (fmt_hbits(FMT)) {
+        const float off = FMT == FQ5_0 ? 16.0f : FMT == FQ6_K ? 32.0f : 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t v = ucomp(q, k);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint32_t lo = (v >> (8 * m)) & 15u, hi = (v >> (8 * m + 4)) & 15u;
+                uint32_t bl, bh;
+                if constexpr (FMT == FQ6_K) {
+                    bl = (h.x >> (8 * m + 2 * k)) & 3u;
+                    bh = (h.y >> (8 * m + 2 * k)) & 3u;
+                } else {
+                    bl = (h.x >> (8 * m + k)) & 1u;
+                    bh = (h.x >> (8 * m + 4 + k)) & 1u;
+                }
+                w[8 * k + m] = (float)(lo | (bl << 4)) - off;
+                w[8 * k + 4 + m] = (float)(hi | (bh << 4)) - off;
+            }
+        }
+        return;
+    }
     if constexpr (FMT == FQ8_0) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -235,7 +280,7 @@ template <int FMT>
 __device__ __forceinline__ float chunk_dot(const float *w, const float4 *xv, const float *Sv,
                                            const ChunkScale &cs, float acc)
 {
-    if constexpr (FMT == FQ4_0) {
+    if constexpr (FMT == FQ4_0 || FMT == FQ5_0) {
         float dot = 0.f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -259,6 +304,20 @@ __device__ __forceinline__ float chunk_dot(const float *w, const float4 *xv, con
             dot = fmaf(w[4 * k + 3], xv[k].w, dot);
         }
         return fmaf(cs.a, dot, acc);
+    } else if constexpr (FMT == FQ6_K) {
+        float da = 0.f, db = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            da = fmaf(w[8 * k + 0], xv[k].x, da);
+            da = fmaf(w[8 * k + 1], xv[k].y, da);
+            da = fmaf(w[8 * k + 2], xv[k].z, da);
+            da = fmaf(w[8 * k + 3], xv[k].w, da);
+            db = fmaf(w[8 * k + 4], xv[4 + k].x, db);
+            db = fmaf(w[8 * k + 5], xv[4 + k].y, db);
+            db = fmaf(w[8 * k + 6], xv[4 + k].z, db);
+            db = fmaf(w[8 * k + 7], xv[4 + k].w, db);
+        }
+        return fmaf(cs.a2, db, fmaf(cs.a, da, acc));
     } else {
         // centred sub-blocks (k_center): dots over n - c, then the (a c - b) sum x terms
         const float cA = k_center(cs.a, cs.b), cB = k_center(cs.a2, cs.b2);
@@ -283,25 +342,35 @@ __device__ __forceinline__ float chunk_dot(const float *w, const float4 *xv, con
 }
 
 template <int FMT>
-__device__ __forceinline__ void load_chunk(const MatPtr &m, int64_t qs_row, int64_t sc_row,
-                                           int64_t n, int64_t ci, uint4 &q, uint4 &s)
+__device__ __forceinline__ void load_chunk(const MatPtr &m, const RowBytes &rb, int64_t n,
+                                           int64_t ci, uint4 &q, uint4 &s, uint2 &h)
 {
-    q = *reinterpret_cast<const uint4 *>(m.qs + n * qs_row + ci * 16);
-    if constexpr (FMT == FQ4_0) {
-        s = make_uint4(*reinterpret_cast<const uint16_t *>(m.sc + n * sc_row + ci * 2), 0u, 0u, 0u);
+    q = *reinterpret_cast<const uint4 *>(m.qs + n * rb.qs + ci * 16);
+    h = make_uint2(0u, 0u);
+    if constexpr (FMT == FQ4_0 || FMT == FQ5_0) {
+        s = make_uint4(*reinterpret_cast<const uint16_t *>(m.sc + n * rb.sc + ci * 2), 0u, 0u, 0u);
     } else if constexpr (FMT == FQ8_0) {
-        s = make_uint4(*reinterpret_cast<const uint16_t *>(m.sc + n * sc_row + (ci >> 1) * 2), 0u,
+        s = make_uint4(*reinterpret_cast<const uint16_t *>(m.sc + n * rb.sc + (ci >> 1) * 2), 0u,
                        0u, 0u);
+    } else if constexpr (FMT == FQ6_K) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(m.sc + n * rb.sc + (ci >> 3) * 16 +
+                                                         ((ci & 7) >> 2) * 8);
+        s = make_uint4(w.x, w.y,
+                       *reinterpret_cast<const uint16_t *>(m.dd + n * rb.d + (ci >> 3) * 2), 0u);
     } else {
-        s = *reinterpret_cast<const uint4 *>(m.sc + n * sc_row + (ci >> 3) * 16);
+        s = *reinterpret_cast<const uint4 *>(m.sc + n * rb.sc + (ci >> 3) * 16);
     }
+    if constexpr (FMT == FQ6_K)
+        h = *reinterpret_cast<const uint2 *>(m.hb + n * rb.hb + ci * 8);
+    else if constexpr (fmt_hbits(FMT))
+        h.x = *reinterpret_cast<const uint32_t *>(m.hb + n * rb.hb + ci * 4);
 }
 
 // One K tile of one wave step: rows row0 + u*G + slot (u < U) of each of MATS matrices against
 // the NB staged x rows.  Lane lir of its LPR-lane group takes chunks lir, lir + lpr, ...
 template <int FMT, int NB, int U, int MATS>
-__device__ __forceinline__ void tile_compute(const MatPtr (&mat)[MATS], int64_t qs_row,
-                                             int64_t sc_row, int64_t row0, int64_t N, int G,
+__device__ __forceinline__ void tile_compute(const MatPtr (&mat)[MATS], const RowBytes &rb,
+                                             int64_t row0, int64_t N, int G,
                                              int slot, int lir, int lpr, int t, int ct,
                                              const float4 *X4, const float *S,
                                              float (&acc)[MATS][U][NB])
@@ -310,16 +379,18 @@ __device__ __forceinline__ void tile_compute(const MatPtr (&mat)[MATS], int64_t 
     for (int i = lir; i < ct; i += lpr) {
         const int64_t ci = (int64_t)t * ct + i;
         uint4 q[MATS][U], s[MATS][U];
+        uint2 h[MATS][U];
 #pragma unroll
         for (int m = 0; m < MATS; ++m)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t n = row0 + (int64_t)u * G + slot;
                 if (n < N) {
-                    load_chunk<FMT>(mat[m], qs_row, sc_row, n, ci, q[m][u], s[m][u]);
+                    load_chunk<FMT>(mat[m], rb, n, ci, q[m][u], s[m][u], h[m][u]);
                 } else {
                     q[m][u] = make_uint4(0u, 0u, 0u, 0u);
                     s[m][u] = make_uint4(0u, 0u, 0u, 0u);
+                    h[m][u] = make_uint2(0u, 0u);
                 }
             }
         const int qpos = (int)(ci & 7);
@@ -337,7 +408,7 @@ __device__ __forceinline__ void tile_compute(const MatPtr (&mat)[MATS], int64_t 
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     float w[CE];
-                    decode_chunk<FMT>(q[m][u], w);
+                    decode_chunk<FMT>(q[m][u], h[m][u], w);
                     const ChunkScale cs = chunk_scale<FMT>(s[m][u], qpos);
                     acc[m][u][0] = chunk_dot<FMT>(w, xv, Sv, cs, acc[m][u][0]);
                 }
@@ -348,7 +419,7 @@ __device__ __forceinline__ void tile_compute(const MatPtr (&mat)[MATS], int64_t 
             for (int m = 0; m < MATS; ++m)
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    decode_chunk<FMT>(q[m][u], w[m][u]);
+                    decode_chunk<FMT>(q[m][u], h[m][u], w[m][u]);
                     cs[m][u] = chunk_scale<FMT>(s[m][u], qpos);
                 }
 #pragma unroll

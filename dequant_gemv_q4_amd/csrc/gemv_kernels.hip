@@ -15,144 +15,118 @@
 // silu(gate) * up (fused_norm_swiglu_down), matmul + residual (forward_decode_fused_layers).
 #include <hip/hip_runtime.h>
 
-#include "device_common.h"
+#include "gemv_impl.h"
 
 namespace qg {
-
-// ------------------------------------------------------------------------------------ GEMV kernel
-
-template <int FMT, int NB, int EPI, bool NRM>
-__global__ __launch_bounds__(256) void k_gemv(GemvArgs a)
-{
-    constexpr int MATS = EPI == E_GUS ? 2 : 1;
-    constexpr int U = rows_in_flight(NB, MATS);
-    constexpr int XF4 = Fc<FMT>::XF4, CE = Fc<FMT>::CE;
-    extern __shared__ float4 lds4[];
-    __shared__ float s_inv[NB];
-    __shared__ float s_red[NB * 4];
-    __shared__ unsigned long long s_key[NB * 4];
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int lpr = 1 << a.lpr_log2, G = 64 >> a.lpr_log2;
-    const int slot = lane >> a.lpr_log2, lir = lane & (lpr - 1);
-    const int ct = a.kt / CE;
-    float4 *X4 = lds4;
-    float *S = reinterpret_cast<float *>(lds4 + (size_t)NB * XF4 * ct);
-
-    const float *xrow[NB];
-#pragma unroll
-    for (int r = 0; r < NB; ++r)
-        xrow[r] = a.x + (int64_t)r * a.K;
-    if constexpr (NRM)
-        row_inv_rms<NB>(xrow, a.K, a.eps, s_inv, s_red);
-
-    MatPtr mat[MATS];
-    mat[0] = MatPtr{a.qs0, a.sc0};
-    if constexpr (MATS == 2)
-        mat[MATS - 1] = MatPtr{a.qs1, a.sc1};
-
-    unsigned long long best[NB];
-#pragma unroll
-    for (int r = 0; r < NB; ++r)
-        best[r] = 0ull;
-
-    for (int64_t st = blockIdx.x; st < a.n_steps; st += gridDim.x) {
-        const int64_t row0 = st * a.rows_per_step + (int64_t)wave * U * G;
-        float acc[MATS][U][NB];
-#pragma unroll
-        for (int m = 0; m < MATS; ++m)
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int r = 0; r < NB; ++r)
-                    acc[m][u][r] = 0.f;
-        for (int t = 0; t < a.n_kt; ++t) {
-            if (a.n_kt > 1 || st == (int64_t)blockIdx.x) {
-                __syncthreads();
-                stage_tile<FMT, NB, NRM>(xrow, a.gamma, s_inv, t, a.kt, X4, S);
-            }
-            tile_compute<FMT, NB, U, MATS>(mat, a.qs_row, a.sc_row, row0, a.N, G, slot, lir, lpr,
-                                           t, ct, X4, S, acc);
-        }
-#pragma unroll
-        for (int m = 0; m < MATS; ++m)
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int r = 0; r < NB; ++r)
-                    acc[m][u][r] = group_sum(acc[m][u][r], lpr);
-        if (lir == 0) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t n = row0 + (int64_t)u * G + slot;
-                if (n >= a.N)
-                    continue;
-#pragma unroll
-                for (int r = 0; r < NB; ++r) {
-                    const int64_t o = (int64_t)r * a.N + n;
-                    if constexpr (EPI == E_STORE) {
-                        a.y[o] = acc[0][u][r];
-                    } else if constexpr (EPI == E_RES) {
-                        a.y[o] = acc[0][u][r] + a.res[(int64_t)r * a.res_rstride + n];
-                    } else if constexpr (EPI == E_GUS) {
-                        a.y[o] = gated(acc[0][u][r], acc[MATS - 1][u][r], a.act);
-                    } else {
-                        const float v = acc[0][u][r];
-                        a.y[o] = v;
-                        const unsigned long long k = argmax_key(v, n);
-                        best[r] = k > best[r] ? k : best[r];
-                    }
-                }
-            }
-        }
-    }
-
-    if constexpr (EPI == E_ARGMAX) {
-        // workgroup max per row as this workgroup's partial key
-#pragma unroll
-        for (int r = 0; r < NB; ++r) {
-            unsigned long long k = best[r];
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                const unsigned long long o = shfl_xor_u64(k, off);
-                k = o > k ? o : k;
-            }
-            if (lane == 0)
-                s_key[r * 4 + wave] = k;
-        }
-        __syncthreads();
-        if (threadIdx.x < NB) {
-            const int r = threadIdx.x;
-            unsigned long long k = s_key[r * 4];
-            for (int w = 1; w < 4; ++w)
-                k = s_key[r * 4 + w] > k ? s_key[r * 4 + w] : k;
-            a.keys[(int64_t)blockIdx.x * NB + r] = k;   // folded by k_argmax_fold
-        }
-    }
-}
 
 // ------------------------------------------------------------------------------------ pack
 
 // GGUF-native blocks (row-major, K/bw blocks per row) -> planes.  Block number blk (= row * nblk +
-// block) moves its quant bytes to qs + blk * QB and its scale bytes to sc + blk * SB: for Q4_0
-// (QB, SB) = (16, 2), Q8_0 (32, 2), Q4_K (128, 16) -- the Q4_K scale bytes are d, dmin and the 12
-// packed (scale, min) bytes, unchanged.
+// block) moves its quant bytes to qs + blk * QB and its scale bytes to sc + blk * SB: Q4_0 and
+// Q5_0 (16, 2), Q8_0 (32, 2), Q4_K and Q5_K (128, 16: d, dmin and the 12 packed (scale, min)
+// bytes, unchanged), Q6_K (128, 16: the 16 signed scales; its d goes to dd + blk * 2).  The high
+// bits of Q5_0 / Q5_K / Q6_K go to hb + blk * HB, re-laid per 32 weights (q5_bits, q6_bits) so
+// that the kernels insert them into the nibble bytes with one shift and one and-or per dword.
+//
+// Fifth bits of one 16-byte nibble chunk, 4 bytes: the bit of the low nibble of chunk byte
+// 4k + m at bit 8m + k, the bit of its high nibble at bit 8m + 4 + k (k, m < 4).
+__device__ __forceinline__ uint32_t q5_bits(const uint8_t (&lo)[16], const uint8_t (&hi)[16])
+{
+    uint32_t w = 0;
+    for (int k = 0; k < 4; ++k)
+        for (int m = 0; m < 4; ++m) {
+            w |= (uint32_t)(lo[4 * k + m] & 1) << (8 * m + k);
+            w |= (uint32_t)(hi[4 * k + m] & 1) << (8 * m + 4 + k);
+        }
+    return w;
+}
+
+// Q6_K: the two high bits of the low (high) nibble of chunk byte 4k + m at bits 8m + 2k, +1 of
+// the first (second) word.
+__device__ __forceinline__ uint32_t q6_bits(const uint8_t (&two)[16])
+{
+    uint32_t w = 0;
+    for (int k = 0; k < 4; ++k)
+        for (int m = 0; m < 4; ++m)
+            w |= (uint32_t)(two[4 * k + m] & 3) << (8 * m + 2 * k);
+    return w;
+}
+
 template <int FMT>
 __global__ __launch_bounds__(256) void k_pack(const uint8_t *src, int64_t nblocks, uint8_t *qs,
-                                              uint8_t *sc)
+                                              uint8_t *sc, uint8_t *hb, uint8_t *dd)
 {
-    constexpr int BB = FMT == FQ4_0 ? 18 : FMT == FQ8_0 ? 34 : 144;
-    constexpr int SB = FMT == FQ4_K ? 16 : 2;
-    constexpr int QB = BB - SB;
+    constexpr int BB = FMT == FQ4_0 ? 18 : FMT == FQ5_0 ? 22 : FMT == FQ8_0 ? 34
+                     : FMT == FQ4_K ? 144 : FMT == FQ5_K ? 176 : 210;
     for (int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; blk < nblocks;
          blk += (int64_t)gridDim.x * blockDim.x) {
         const uint8_t *b = src + blk * BB;
-        uint8_t *dq = qs + blk * QB;
-        uint8_t *ds = sc + blk * SB;
-        for (int k = 0; k < SB; ++k)
-            ds[k] = b[k];
-        for (int k = 0; k < QB; ++k)
-            dq[k] = b[SB + k];
+        if constexpr (FMT == FQ4_0 || FMT == FQ8_0 || FMT == FQ4_K) {
+            constexpr int SB = FMT == FQ4_K ? 16 : 2;
+            constexpr int QB = BB - SB;
+            for (int k = 0; k < SB; ++k)
+                sc[blk * SB + k] = b[k];
+            for (int k = 0; k < QB; ++k)
+                qs[blk * QB + k] = b[SB + k];
+        } else if constexpr (FMT == FQ5_0) {
+            // d (2), qh (4, little-endian: bit j for element j), nibbles (16)
+            sc[blk * 2] = b[0];
+            sc[blk * 2 + 1] = b[1];
+            const uint32_t qh = (uint32_t)b[2] | ((uint32_t)b[3] << 8) | ((uint32_t)b[4] << 16) |
+                                ((uint32_t)b[5] << 24);
+            uint8_t lo[16], hi[16];
+            for (int i = 0; i < 16; ++i) {
+                qs[blk * 16 + i] = b[6 + i];
+                lo[i] = (uint8_t)((qh >> i) & 1u);          // element i: low nibble of byte i
+                hi[i] = (uint8_t)((qh >> (16 + i)) & 1u);   // element 16 + i: its high nibble
+            }
+            const uint32_t w = q5_bits(lo, hi);
+            for (int k = 0; k < 4; ++k)
+                hb[blk * 4 + k] = (uint8_t)(w >> (8 * k));
+        } else if constexpr (FMT == FQ5_K) {
+            // d, dmin, 12 scale bytes (16), qh (32), nibbles (128); chunk q = bytes 16q..16q+15 of
+            // the nibbles: byte 32c + 16h + i (c = q / 2, h = q % 2) takes bits 2c (low nibble)
+            // and 2c + 1 (high nibble) of qh[16h + i]
+            for (int k = 0; k < 16; ++k)
+                sc[blk * 16 + k] = b[k];
+            for (int k = 0; k < 128; ++k)
+                qs[blk * 128 + k] = b[48 + k];
+            for (int q = 0; q < 8; ++q) {
+                const int c = q >> 1, h = q & 1;
+                uint8_t lo[16], hi[16];
+                for (int i = 0; i < 16; ++i) {
+                    lo[i] = (uint8_t)((b[16 + 16 * h + i] >> (2 * c)) & 1);
+                    hi[i] = (uint8_t)((b[16 + 16 * h + i] >> (2 * c + 1)) & 1);
+                }
+                const uint32_t w = q5_bits(lo, hi);
+                for (int k = 0; k < 4; ++k)
+                    hb[blk * 32 + 4 * q + k] = (uint8_t)(w >> (8 * k));
+            }
+        } else {
+            // Q6_K: ql (128), qh (64), 16 signed scales, d.  Chunk t = ql bytes 16t..16t+15
+            // (n = t / 4, u = t % 4); its byte i pairs with qh[32n + 16 (u % 2) + i], whose bits
+            // 0-1 / 4-5 (u < 2) or 2-3 / 6-7 (u >= 2) are the low / high nibble's high bits
+            for (int k = 0; k < 128; ++k)
+                qs[blk * 128 + k] = b[k];
+            for (int k = 0; k < 16; ++k)
+                sc[blk * 16 + k] = b[192 + k];
+            dd[blk * 2] = b[208];
+            dd[blk * 2 + 1] = b[209];
+            for (int t = 0; t < 8; ++t) {
+                const int n = t >> 2, u = t & 3, sh = u >= 2 ? 2 : 0;
+                uint8_t lo[16], hi[16];
+                for (int i = 0; i < 16; ++i) {
+                    const uint8_t h = b[128 + 32 * n + 16 * (u & 1) + i];
+                    lo[i] = (uint8_t)((h >> sh) & 3);
+                    hi[i] = (uint8_t)((h >> (sh + 4)) & 3);
+                }
+                const uint32_t wa = q6_bits(lo), wb = q6_bits(hi);
+                for (int k = 0; k < 4; ++k) {
+                    hb[blk * 64 + 8 * t + k] = (uint8_t)(wa >> (8 * k));
+                    hb[blk * 64 + 8 * t + 4 + k] = (uint8_t)(wb >> (8 * k));
+                }
+            }
+        }
     }
 }
 
@@ -247,57 +221,23 @@ int launch_pack(int fmt, const void *src, int64_t N, int64_t K, void *dst, void 
         return (int)hipErrorInvalidValue;
     const int64_t nblocks = N * (K / L.block_w);
     uint8_t *qs = static_cast<uint8_t *>(dst);
-    uint8_t *sc = qs + L.sc_off;
+    uint8_t *sc = qs + L.sc_off, *hb = qs + L.hb_off, *dd = qs + L.d_off;
     const int64_t want = (nblocks + 255) / 256;
     const int grid = (int)(want < 65536 ? want : 65536);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint8_t *in = static_cast<const uint8_t *>(src);
-    if (fmt == FQ4_0)
-        hipLaunchKernelGGL(k_pack<FQ4_0>, dim3(grid), dim3(256), 0, s, in, nblocks, qs, sc);
-    else if (fmt == FQ8_0)
-        hipLaunchKernelGGL(k_pack<FQ8_0>, dim3(grid), dim3(256), 0, s, in, nblocks, qs, sc);
-    else
-        hipLaunchKernelGGL(k_pack<FQ4_K>, dim3(grid), dim3(256), 0, s, in, nblocks, qs, sc);
-    return (int)hipGetLastError();
-}
-
-template <int FMT, int EPI, bool NRM>
-static int launch_gemv_nb(const GemvArgs &a, int grid, size_t lds, hipStream_t s)
-{
-#define QG_NB_CASE(NBV)                                                                     \
-    case NBV:                                                                               \
-        hipLaunchKernelGGL((k_gemv<FMT, NBV, EPI, NRM>), dim3(grid), dim3(256), lds, s, a); \
-        break;
-    switch (a.nb) {
-        QG_NB_CASE(1) QG_NB_CASE(2) QG_NB_CASE(3) QG_NB_CASE(4)
-        QG_NB_CASE(5) QG_NB_CASE(6) QG_NB_CASE(7) QG_NB_CASE(8)
-        QG_NB_CASE(9) QG_NB_CASE(10) QG_NB_CASE(11) QG_NB_CASE(12)
-        QG_NB_CASE(13) QG_NB_CASE(14) QG_NB_CASE(15) QG_NB_CASE(16)
-    default:
-        return (int)hipErrorInvalidValue;
+#define QG_PACK(F)                                                                                \
+    hipLaunchKernelGGL(k_pack<F>, dim3(grid), dim3(256), 0, s, in, nblocks, qs, sc, hb, dd)
+    switch (fmt) {
+    case FQ4_0: QG_PACK(FQ4_0); break;
+    case FQ5_0: QG_PACK(FQ5_0); break;
+    case FQ8_0: QG_PACK(FQ8_0); break;
+    case FQ4_K: QG_PACK(FQ4_K); break;
+    case FQ5_K: QG_PACK(FQ5_K); break;
+    default: QG_PACK(FQ6_K); break;
     }
-#undef QG_NB_CASE
+#undef QG_PACK
     return (int)hipGetLastError();
-}
-
-template <int FMT>
-static int launch_gemv_fmt(int epi, bool nrm, const GemvArgs &a, int grid, size_t lds,
-                           hipStream_t s)
-{
-    switch (epi) {
-    case E_STORE:
-        return nrm ? launch_gemv_nb<FMT, E_STORE, true>(a, grid, lds, s)
-                   : launch_gemv_nb<FMT, E_STORE, false>(a, grid, lds, s);
-    case E_RES:
-        return nrm ? launch_gemv_nb<FMT, E_RES, true>(a, grid, lds, s)
-                   : launch_gemv_nb<FMT, E_RES, false>(a, grid, lds, s);
-    case E_GUS:
-        return launch_gemv_nb<FMT, E_GUS, true>(a, grid, lds, s);
-    case E_ARGMAX:
-        return launch_gemv_nb<FMT, E_ARGMAX, false>(a, grid, lds, s);
-    default:
-        return (int)hipErrorInvalidValue;
-    }
 }
 
 int launch_gemv(int fmt, int epi, bool nrm, const GemvArgs &a, int grid, size_t lds_bytes,

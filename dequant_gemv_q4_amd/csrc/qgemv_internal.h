@@ -8,7 +8,19 @@
 
 namespace qg {
 
-enum Fmt { FQ4_0 = 2, FQ8_0 = 8, FQ4_K = 12 };
+enum Fmt { FQ4_0 = 2, FQ5_0 = 6, FQ8_0 = 8, FQ4_K = 12, FQ5_K = 13, FQ6_K = 14 };
+
+// Format classes.  Super-block formats hold 256 weights per block; high-bit formats carry a plane
+// of fifth (Q5) or fifth-and-sixth (Q6_K) bits beside the nibbles; min formats have the
+// d sc q - dmin m form; the Q4 formats hold their high-nibble weights x16 in the f16 pairs.
+__host__ __device__ constexpr bool fmt_super(int f) { return f == FQ4_K || f == FQ5_K || f == FQ6_K; }
+__host__ __device__ constexpr bool fmt_hbits(int f) { return f == FQ5_0 || f == FQ5_K || f == FQ6_K; }
+__host__ __device__ constexpr bool fmt_min(int f) { return f == FQ4_K || f == FQ5_K; }
+__host__ __device__ constexpr bool fmt_q4(int f) { return f == FQ4_0 || f == FQ4_K; }
+// 32-bit words of high bits per 16-byte chunk of nibbles (32 weights).
+__host__ __device__ constexpr int fmt_hwords(int f) { return f == FQ6_K ? 2 : fmt_hbits(f) ? 1 : 0; }
+// Formats whose chunk carries two sub-block scales (a low-nibble and a high-nibble sub-block).
+__host__ __device__ constexpr bool fmt_two_sub(int f) { return fmt_super(f); }
 
 // Epilogue kinds of the GEMV kernels: store; add a residual row or a bias (E_RES); gated product
 // act(g) u of two matrices (E_GUS); store and argmax keys (E_ARGMAX).
@@ -50,9 +62,13 @@ __host__ __device__ constexpr int moe_threads(int fmt, int cpl, int pd)
 // plane of scale bytes (row n at n * sc_row), each starting 256-B aligned.  Same bytes per weight
 // as the GGUF blocks.
 struct Layout {
-    int64_t qs_row;     // quant bytes per row: Q4_0 / Q4_K K/2, Q8_0 K
+    int64_t qs_row;     // quant bytes per row: Q8_0 K, every other format K/2 (the nibbles)
     int64_t sc_row;     // scale bytes per row: K/16 for every format
     int64_t sc_off;     // byte offset of the scale plane (qs plane rounded up to 256 B)
+    int64_t hb_row;     // high-bit bytes per row: Q5_0 / Q5_K K/8, Q6_K K/4, others 0
+    int64_t hb_off;     // byte offset of the high-bit plane (after the scale plane)
+    int64_t d_row;      // Q6_K: bytes of the super-block d values per row (K/128), others 0
+    int64_t d_off;      // byte offset of that plane
     int64_t total;      // packed bytes
     int64_t gguf_row;   // GGUF bytes per row
     int block_w;        // weights per GGUF block
@@ -68,8 +84,8 @@ struct FmtFacts {
 __host__ __device__ constexpr FmtFacts fmt_facts(int fmt)
 {
     return fmt == FQ8_0 ? FmtFacts{4, 16, 1, 32}
-         : fmt == FQ4_K ? FmtFacts{8, 32, 2, 256}
-                        : FmtFacts{8, 32, 1, 32};
+         : fmt_super(fmt) ? FmtFacts{8, 32, 2, 256}
+                          : FmtFacts{8, 32, 1, 32};
 }
 
 // Rows a wave keeps in flight per step of the vector kernel, by row-batch size and matrix count.
@@ -118,6 +134,8 @@ bool layout(int fmt, int64_t N, int64_t K, Layout *out);
 struct GemvArgs {
     const uint8_t *qs0, *sc0;   // matrix 0 (the only matrix, or the gate)
     const uint8_t *qs1, *sc1;   // matrix 1 (the up matrix of the gated product)
+    const uint8_t *hb0, *hb1;   // high-bit planes of the two matrices (high-bit formats)
+    const uint8_t *dd0, *dd1;   // Q6_K: planes of the super-block d values
     const float *x;             // [nb][K]
     const float *gamma;         // [K] (norm prologue)
     const float *res;           // residual [nb][N] (res_rstride N) or bias [N] (res_rstride 0)
@@ -125,7 +143,7 @@ struct GemvArgs {
     int32_t *idx;               // [nb] (argmax)
     unsigned long long *keys;   // argmax: partial key per workgroup and batch row (workspace)
     int64_t N, K;
-    int64_t qs_row, sc_row;
+    int64_t qs_row, sc_row, hb_row, d_row;
     float eps;
     int64_t res_rstride;        // elements between the batch rows of res (0: one row for all)
     int act;                    // gated product: 0 silu(g) u, 1 gelu_tanh(g) u
@@ -157,8 +175,15 @@ struct MoeArgs {
 int launch_pack(int fmt, const void *src, int64_t N, int64_t K, void *dst, void *stream);
 int launch_gemv(int fmt, int epi, bool nrm, const GemvArgs &a, int grid, size_t lds_bytes,
                 void *stream);
+// The same for the high-bit formats (gemv_kernels_x.hip).
+int launch_gemv_x(int fmt, int epi, bool nrm, const GemvArgs &a, int grid, size_t lds_bytes,
+                  void *stream);
 int launch_stream(int fmt, int epi, bool nrm, int cpl, int pd, const GemvArgs &a, int grid,
                   size_t lds_bytes, void *stream);
+// The streaming kernel variant (function and threads per workgroup) of a high-bit format
+// (stream_kernels_x.hip); *fn = nullptr if there is none.
+void stream_fn_x(int fmt, int epi, bool nrm, int ks, int nb, int pd, const void **fn,
+                 int *threads);
 // Routed experts: the expert kernel (x rows per set 4 / cpl, pd groups in flight per wave), then
 // the combine.
 int launch_moe(int fmt, int cpl, int pd, const MoeArgs &a, int grid, size_t lds_bytes,

@@ -9,11 +9,19 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  - Formats (GGUF type ids): QG_Q4_0 = 2, QG_Q8_0 = 8, QG_Q4_K = 12.
+ *  - Formats (GGUF type ids): QG_Q4_0 = 2, QG_Q5_0 = 6, QG_Q8_0 = 8, QG_Q4_K = 12,
+ *    QG_Q5_K = 13, QG_Q6_K = 14 ("Crate inferencelayer" docs, the gemv_*_lcpp_src family).
  *      Q4_0: 32 weights in 18 B (f16 d, 16 B nibbles), w = (q - 8) * d.
+ *      Q5_0: 32 weights in 22 B (f16 d, 4 B of fifth bits, 16 B nibbles), w = d * (q - 16),
+ *            q = nib | bit << 4 (element j: bit j).
  *      Q8_0: 32 weights in 34 B (f16 d, 32 x i8),     w = d * q.
  *      Q4_K: 256 weights in 144 B (f16 d, f16 dmin, 12 B of eight packed 6-bit (scale, min)
  *            pairs, 128 B nibbles), w = d * sc_j * q - dmin * m_j.
+ *      Q5_K: 256 weights in 176 B (Q4_K's d, dmin, 12 B pack, then 32 B of fifth bits, 128 B
+ *            nibbles; sub-block s takes bit s of qh[l]), w = d * sc_j * q - dmin * m_j.
+ *      Q6_K: 256 weights in 210 B (128 B low nibbles, 64 B high bit pairs, 16 signed scales,
+ *            f16 d), w = d * sc * (q - 32) with one scale per 16 weights.
+ *    Routed experts (qgemv_moe) take Q4_0, Q8_0 and Q4_K.
  *  - W arguments of the compute entry points are in the PACKED device layout written by
  *    qgemv_pack (same bytes per weight as GGUF, split into planes so every hot load is an
  *    aligned 16-byte load).  Rows are in output order; K is the reduction length.  A W buffer
@@ -46,12 +54,12 @@
 extern "C" {
 #endif
 
-enum { QG_Q4_0 = 2, QG_Q8_0 = 8, QG_Q4_K = 12 };
+enum { QG_Q4_0 = 2, QG_Q5_0 = 6, QG_Q8_0 = 8, QG_Q4_K = 12, QG_Q5_K = 13, QG_Q6_K = 14 };
 
 enum {
     QG_OK = 0,
     QG_ERR_NULL = 1,       /* a required pointer is NULL */
-    QG_ERR_FORMAT = 2,     /* unknown format id */
+    QG_ERR_FORMAT = 2,     /* unknown format id, or a format the entry point does not take */
     QG_ERR_SHAPE = 3,      /* N < 1, nb outside [1, 16], K not a positive multiple of the block,
                               topk outside [1, 8], n_exp < 1, or a size beyond the limits */
     QG_ERR_ALIGN = 4,      /* W or a workspace not 256-B aligned, x or gamma not 16-B aligned, or
@@ -74,7 +82,9 @@ enum { QG_ACT_SILU = 0, QG_ACT_GELU_TANH = 1 };
 #define QG_MAX_K 65536
 
 /* Bytes of the packed device layout of an N x K matrix, or -1 if (fmt, N, K) is invalid.
- * Equal to the GGUF byte count rounded up to 256 B per plane.  Host-only, no HIP call. */
+ * Equal to the GGUF byte count rounded up to 256 B per plane (two planes: quants and scales; the
+ * Q5 formats add a plane of fifth bits, Q6_K one of high bit pairs and one of its d values).
+ * Host-only, no HIP call. */
 int64_t qgemv_packed_bytes(int fmt, int64_t N, int64_t K);
 
 /* Re-lay GGUF-native blocks (w_gguf: N rows of K/bs consecutive blocks, the native row order of
