@@ -282,6 +282,43 @@ def make_moe(warm):
                  step, step, cpu, cfg, flops=2 * nb * topk * w.N * w.K)
 
 
+def make_gemm(warm, M=512, N=8192, K=2048, fmt=None):
+    """Wide row batch (a prefill chunk of M rows): qgemm on an N x K matrix (default the decode
+    MLP's Q4_0 gate matrix, 8192 x 2048, with a 512-row chunk).  Compute-bound at these M: the
+    roofline is the f16 MFMA peak (2.5 PFLOP/s dense) over 2 M N K flops."""
+    import torch
+    import dequant_gemv_q4_amd as q
+    from dequant_gemv_q4_amd import device as D
+    import workloads as wl
+
+    fmt = q.Q4_0 if fmt is None else fmt
+    g = wl.rng(5, wl.T_W)
+    W = wl.matrix(fmt, g, N, K)
+    x = wl.normal_f32(wl.rng(5, wl.T_X), (M, K))
+    Wp = D.pack(fmt, W, N, K)
+    R = _copies(Wp.numel(), warm)
+    sets = _rotated(Wp, R)
+    xd = D.to_device(x)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(q.qgemm_workspace_bytes(fmt, N, K, M), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        q.qgemm(fmt, sets[i % R], N, K, xd, M, y, ws)
+
+    def cpu():
+        import oracle
+        oracle.gemv(fmt, W, N, K, x)
+        return W.nbytes
+
+    fname = wl.FMT_NAME[fmt]
+    name = f"{fname}_gemm_{N}x{K}_m{M}"
+    alg = W.nbytes + M * K * 4 + M * N * 4
+    cfg = {"workload": name, "M": M, "format": fname, "N": N, "K": K, "launches_per_step": 2,
+           "weight_copies": R, "cold": not warm}
+    return Bench(name, W.nbytes, alg, f"qgemm ({fname}, {N}x{K}, M={M})", step, step, cpu, cfg,
+                 flops=2 * M * N * K)
+
+
 def make_read(warm, nbytes=75497472, shape=(256, 1024)):
     """The attainable read rate: the plain 16-byte-load read kernel (libqgbw.so) over the same
     number of bytes as the gate's weights, rotated over >= 1 GiB like the GEMV, at one launch
@@ -455,6 +492,12 @@ def summary(b, ms_step, ms_eager, ms_dom):
            "config": b.config}
     if b.flops:
         out["tflops"] = round(b.flops / (ms_step * 1e-3) / 1e12, 3)
+        if "M" in b.config:    # wide row batch: bound by the matrix cores, not by HBM
+            out["roofline"].update({
+                "bound": "mfma", "achieved": round(b.flops / (ms_dom * 1e-3) / 1e12, 2),
+                "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(b.flops / (ms_dom * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                "hbm_gbps": round(achieved, 2)})
     return out
 
 
@@ -477,7 +520,7 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gemv",
-                    choices=["gemv", "decode_mlp", "lm_head", "qkv", "moe", "read", "copy"])
+                    choices=["gemv", "decode_mlp", "lm_head", "qkv", "moe", "gemm", "read", "copy"])
     ap.add_argument("--nb", type=int, default=None)
     ap.add_argument("--rows", type=int, default=65536, help="gemv workload: output rows")
     ap.add_argument("--hidden", type=int, default=2048, help="gemv workload: reduction length")
@@ -512,6 +555,8 @@ def main():
         b = make_gemv(args.warm, args.nb or 1, args.rows, args.hidden)
     elif wl_name == "qkv":
         b = make_qkv(args.warm, args.nb or 16)
+    elif wl_name == "gemm":
+        b = make_gemm(args.warm, args.nb or 512)
     elif wl_name == "read":
         b = make_read(args.warm)
         args.no_cpu = True
@@ -568,6 +613,9 @@ def main():
                       (qq.Q6_K, "q6_k")):
             extras[f"{nm}_gemv_nb1"] = run_extra(f"{nm} gemv", lambda f=f: make_gemv(False, 1, fmt=f),
                                                  es, ew, torch)
+        for M in (64, 512, 2048):
+            extras[f"gemm_q4_0_m{M}"] = run_extra(f"gemm M={M}", lambda M=M: make_gemm(False, M),
+                                                  min(es, 50), 5, torch)
         w = run_extra("gemv warm", lambda: make_gemv(True, 1), es, ew, torch)
         w["label"] = "cache-assisted: one weight copy reused, served in part by the 256 MB MALL"
         extras["gemv_nb1_warm"] = w

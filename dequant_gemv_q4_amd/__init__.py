@@ -6,7 +6,7 @@ The functions exported here are the C entry points under the same names (see ``_
 """
 from ._binding import (  # noqa: F401
     ACT_GELU_TANH, ACT_SILU, LIB_PATH, OP_ARGMAX, OP_GEMV, OP_GUS_NRM, OP_MOE, OP_NRM, OP_NRM_BIAS,
-    OP_RES, Q4_0, Q4_K, Q5_0, Q5_K, Q6_K, Q8_0, QgemvError, qgemv_gus_act_nrm, qgemv_nrm_bias, qgemv_qk_norm_rope,
+    OP_RES, Q4_0, Q4_K, Q5_0, Q5_K, Q6_K, Q8_0, QgemvError, qgemm, qgemm_workspace_bytes, qgemv_gus_act_nrm, qgemv_nrm_bias, qgemv_qk_norm_rope,
     header_functions, lib, qgemv, qgemv_argmax, qgemv_argmax_noalloc, qgemv_gus_nrm, qgemv_layout_version, qgemv_moe,
     qgemv_moe_error, qgemv_nrm, qgemv_pack, qgemv_packed_bytes, qgemv_res, qgemv_status_str,
     qgemv_workspace_bytes,

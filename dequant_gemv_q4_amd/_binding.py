@@ -47,6 +47,8 @@ _SIGS = {
     "qgemv_argmax": (_i32, [_i32, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "qgemv_argmax_noalloc": (_i32, [_i32, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp]),
     "qgemv_moe": (_i32, [_i32, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "qgemm_workspace_bytes": (_i64, [_i32, _i64, _i64, _i64]),
+    "qgemm": (_i32, [_i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
     "qgemv_moe_error": (_i32, [_vp, _i64, _i64, _i64, _i32, ctypes.POINTER(ctypes.c_int), _vp]),
     "qgemv_status_str": (ctypes.c_char_p, [_i32]),
     "qgemv_layout_version": (_i32, []),
@@ -73,7 +75,7 @@ def header_functions() -> list[str]:
     """Names of the functions include/qgemv.h declares."""
     txt = open(HEADER_PATH).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(qgemv[A-Za-z0-9_]*)\s*\(", txt, re.M)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(qgem[mv][A-Za-z0-9_]*)\s*\(", txt, re.M)
 
 
 def _p(a):
@@ -191,6 +193,15 @@ def qgemv_moe(fmt, W_experts, n_exp, N, K, x, nb, ids, wts, topk, y, ws, ws_byte
                                         _p(wts), topk, _p(y), _p(ws),
                                         _nbytes(ws) if ws_bytes is None else ws_bytes,
                                         _stream(stream)))
+
+
+def qgemm_workspace_bytes(fmt: int, N: int, K: int, M: int) -> int:
+    return lib().qgemm_workspace_bytes(fmt, N, K, M)
+
+
+def qgemm(fmt, W, N, K, x, M, y, ws, ws_bytes=None, stream=None):
+    _check("qgemm", lib().qgemm(fmt, _p(W), N, K, _p(x), M, _p(y), _p(ws),
+                                _nbytes(ws) if ws_bytes is None else ws_bytes, _stream(stream)))
 
 
 def qgemv_moe_error(ws, n_exp, N, K, fmt, stream=None) -> int:

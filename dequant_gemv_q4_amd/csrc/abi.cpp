@@ -676,6 +676,62 @@ int qgemv_qk_norm_rope(float *qkv, int nb, int n_q_heads, int n_kv_heads, int he
                                              rope_sin, stream));
 }
 
+static int64_t gemm_m_tiles(int64_t M) { return (M + QG_GEMM_BM - 1) / QG_GEMM_BM; }
+static int64_t gemm_n_tiles(int64_t N) { return (N + QG_GEMM_BN - 1) / QG_GEMM_BN; }
+
+int64_t qgemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M)
+{
+    Layout L;
+    if ((fmt != QG_Q4_0 && fmt != QG_Q8_0) || M < 1 || M > QG_GEMM_MAX_M || !layout(fmt, N, K, &L))
+        return -1;
+    const int64_t Mp = gemm_m_tiles(M) * QG_GEMM_BM;
+    return round256(Mp * K * 2) + round256(Mp * 4);
+}
+
+int qgemm(int fmt, const void *W, int64_t N, int64_t K, const float *x, int64_t M, float *y,
+          void *ws, size_t ws_bytes, void *stream)
+{
+    if (!fmt_valid(fmt))
+        return QG_ERR_FORMAT;
+    if (fmt != QG_Q4_0 && fmt != QG_Q8_0)
+        return QG_ERR_FORMAT;
+    if (!W || !x || !y)
+        return QG_ERR_NULL;
+    Layout L;
+    if (M < 1 || M > QG_GEMM_MAX_M || N < 1 || N > 0x7fffffffLL || !layout(fmt, N, K, &L) ||
+        N * L.qs_row >= QG_BUF_MAX || N * L.sc_row >= QG_BUF_MAX ||
+        gemm_n_tiles(N) * gemm_m_tiles(M) > 0x7fffffffLL - 8)
+        return QG_ERR_SHAPE;
+    if (!ws)
+        return QG_ERR_WORKSPACE;
+    if (!al(W, 256) || !al(x, 4) || !al(y, 4) || !al(ws, 256))
+        return QG_ERR_ALIGN;
+    const int64_t need = qgemm_workspace_bytes(fmt, N, K, M);
+    if ((int64_t)ws_bytes < need)
+        return QG_ERR_WORKSPACE;
+    const int64_t yb = M * N * 4, xb = M * K * 4, wsb = (int64_t)ws_bytes;
+    if (overlap(y, yb, x, xb) || overlap(y, yb, W, L.total) || overlap(y, yb, ws, wsb) ||
+        overlap(ws, wsb, x, xb) || overlap(ws, wsb, W, L.total))
+        return QG_ERR_ALIAS;
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.qs = static_cast<const uint8_t *>(W);
+    a.sc = a.qs + L.sc_off;
+    const int64_t Mp = gemm_m_tiles(M) * QG_GEMM_BM;
+    uint8_t *w8 = static_cast<uint8_t *>(ws);
+    a.xh = reinterpret_cast<_Float16 *>(w8);
+    a.rs = reinterpret_cast<float *>(w8 + round256(Mp * K * 2));
+    a.y = y;
+    a.N = N;
+    a.K = K;
+    a.M = M;
+    a.qs_row = L.qs_row;
+    a.sc_row = L.sc_row;
+    a.n_tiles = (int)gemm_n_tiles(N);
+    a.m_tiles = (int)gemm_m_tiles(M);
+    return launch_status(launch_gemm(fmt, a, x, stream));
+}
+
 int qgemv_moe_error(const void *ws, int64_t n_exp, int64_t N, int64_t K, int fmt, int *flag,
                     void *stream)
 {

@@ -23,105 +23,12 @@
 // the step's four blocks (Q4_0) or two blocks (Q8_0).
 #include <hip/hip_runtime.h>
 
-#include "device_common.h"
+#include "mfma_common.h"
 
 #include <mutex>
 #include <vector>
 
 namespace qg {
-
-typedef _Float16 mh2 __attribute__((ext_vector_type(2)));
-typedef _Float16 mh8 __attribute__((ext_vector_type(8)));
-typedef float mf4 __attribute__((ext_vector_type(4)));
-
-constexpr int MF_WAVES = 16;             // waves per workgroup: one per batch row in the prologue
-constexpr int MF_THREADS = 64 * MF_WAVES;
-constexpr int MF_KMAX = 4096;            // longest row the staged x fits (x2 K classes)
-
-__device__ __forceinline__ uint32_t mf_and_or(uint32_t v, uint32_t m, uint32_t c)
-{
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(m), "v"(c));
-    return r;
-}
-
-__device__ __forceinline__ uint32_t mf_hadd(uint32_t a, uint32_t b)
-{
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(mh2, a) + __builtin_bit_cast(mh2, b));
-}
-
-struct MfConst {
-    uint32_t m_lo, m_hi, c, off_lo, off_hi;
-};
-
-template <int FMT>
-__device__ __forceinline__ MfConst mf_const()
-{
-    MfConst k;
-    k.m_lo = FMT == FQ8_0 ? 0x00FF00FFu : 0x000F000Fu;
-    k.m_hi = 0x00F000F0u;
-    k.c = 0x64006400u;
-    k.off_lo = FMT == FQ8_0 ? 0xE480E480u : 0xE408E408u;   // -1152 (Q8_0) / -1032 (n - 8)
-    k.off_hi = 0xE480E480u;                                // -1152: 16 n - 128
-    asm volatile("" : "+v"(k.m_lo), "+v"(k.m_hi), "+v"(k.c), "+v"(k.off_lo), "+v"(k.off_hi));
-    return k;
-}
-
-// B operand (eight exact f16 weights) of one block from the lane's dword(s).
-template <int FMT>
-__device__ __forceinline__ mh8 mf_bop(uint32_t q0, uint32_t q1, const MfConst &k)
-{
-    uint32_t w[4];
-    if constexpr (FMT == FQ8_0) {
-        const uint32_t u0 = q0 ^ 0x80808080u, u1 = q1 ^ 0x80808080u;
-        w[0] = mf_hadd(mf_and_or(u0, k.m_lo, k.c), k.off_lo);          // bytes 0, 2 (half 0)
-        w[1] = mf_hadd(mf_and_or(u0 >> 8, k.m_lo, k.c), k.off_lo);     // bytes 1, 3
-        w[2] = mf_hadd(mf_and_or(u1, k.m_lo, k.c), k.off_lo);          // bytes 0, 2 (half 1)
-        w[3] = mf_hadd(mf_and_or(u1 >> 8, k.m_lo, k.c), k.off_lo);     // bytes 1, 3
-    } else {
-        const uint32_t t = q0 >> 8;
-        w[0] = mf_hadd(mf_and_or(q0, k.m_lo, k.c), k.off_lo);   // low nibbles of bytes 0, 2
-        w[1] = mf_hadd(mf_and_or(q0, k.m_hi, k.c), k.off_hi);   // high nibbles of bytes 0, 2 (x16)
-        w[2] = mf_hadd(mf_and_or(t, k.m_lo, k.c), k.off_lo);    // low nibbles of bytes 1, 3
-        w[3] = mf_hadd(mf_and_or(t, k.m_hi, k.c), k.off_hi);    // high nibbles of bytes 1, 3 (x16)
-    }
-    struct W4 {
-        uint32_t v[4];
-    } p = {{w[0], w[1], w[2], w[3]}};
-    return __builtin_bit_cast(mh8, p);
-}
-
-// Position (dword j of the block, half h of the lane's eight) of block element eb (0..31), and
-// whether it carries the 1/16 of a high nibble.
-template <int FMT>
-__device__ __forceinline__ void mf_slot(int eb, int &j, int &h, bool &hi)
-{
-    const int second = eb >= 16, e = eb & 15, t = e & 3;
-    j = e >> 2;
-    if constexpr (FMT == FQ8_0) {
-        // halves: [b0, b2, b1, b3] of half 0, then of half 1
-        h = 4 * second + (t == 0 ? 0 : t == 2 ? 1 : t == 1 ? 2 : 3);
-        hi = false;
-    } else {
-        // halves: [lo b0, lo b2, hi b0, hi b2, lo b1, lo b3, hi b1, hi b3]
-        h = (t & 1) * 4 + second * 2 + (t >> 1);
-        hi = second;
-    }
-}
-
-// 4 x 4 transpose of dwords across the four 16-lane rows: register r of lane row c holds dword
-// c of row r's chunk afterwards.
-__device__ __forceinline__ void mf_xpose(uint32_t (&v)[4])
-{
-    auto s0 = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
-    auto s1 = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
-    auto t0 = __builtin_amdgcn_permlane16_swap(s0[0], s1[0], false, false);
-    auto t1 = __builtin_amdgcn_permlane16_swap(s0[1], s1[1], false, false);
-    v[0] = t0[0];
-    v[1] = t0[1];
-    v[2] = t1[0];
-    v[3] = t1[1];
-}
 
 template <int OFF>
 __device__ __forceinline__ float mf_xor(float v)

@@ -171,6 +171,22 @@ struct MoeArgs {
     int pool_max;               // most row groups one workgroup's range may hold
 };
 
+// Tile of the wide row-batch GEMM: rows of x and rows of W per workgroup.
+#define QG_GEMM_BM 128
+#define QG_GEMM_BN 64
+// Arguments of the wide row-batch GEMM (gemm_kernels.hip).
+struct GemmArgs {
+    const uint8_t *qs, *sc;     // packed W (Q4_0 / Q8_0)
+    _Float16 *xh;               // workspace: x as f16 in operand order, [m_tiles * BM][K]
+    float *rs;                  // workspace: factor undoing each x row's scale, [m_tiles * BM]
+    float *y;                   // [M][N]
+    int64_t N, K, M;
+    int64_t qs_row, sc_row;
+    int n_tiles, m_tiles;       // tiles of W (QG_GEMM_BN rows) and of x (QG_GEMM_BM rows)
+};
+// x preparation then the GEMM, both on `stream`.
+int launch_gemm(int fmt, const GemmArgs &a, const float *x, void *stream);
+
 // Launch helpers (gemv_kernels.hip).  Return a hipError_t value (0 = success).
 int launch_pack(int fmt, const void *src, int64_t N, int64_t K, void *dst, void *stream);
 int launch_gemv(int fmt, int epi, bool nrm, const GemvArgs &a, int grid, size_t lds_bytes,

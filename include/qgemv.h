@@ -181,6 +181,19 @@ int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t 
               int nb, const int32_t *ids, const float *wts, int topk, float *y, void *ws,
               size_t ws_bytes, void *stream);
 
+/* Wide row batch (prefill chunks): y[m][n] = sum_k W[n][k] x[m][k] for M rows of x at once, so
+ * every weight streams once for the whole chunk ("Module gpu", module prefill; "Crate
+ * inferencelayer", gemm_q1_src / gemm_q4_src: tiles sharing one weight stream, one 32-weight
+ * block per inner step).  Formats Q4_0 and Q8_0 (others: QG_ERR_FORMAT).  x f32 [M][K], y f32
+ * [M][N], 4-B aligned; 1 <= M <= QG_GEMM_MAX_M.  ws: at least qgemm_workspace_bytes(fmt, N, K, M)
+ * bytes, 256-B aligned, written before it is read (x converted to f16 once per call); two
+ * launches on `stream`.  The same arithmetic as the row-batch GEMV: exact weights, x rounded to
+ * f16 after a power-of-two scaling of each row, f32 accumulation. */
+#define QG_GEMM_MAX_M (1 << 20)
+int64_t qgemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M);
+int qgemm(int fmt, const void *W, int64_t N, int64_t K, const float *x, int64_t M, float *y,
+          void *ws, size_t ws_bytes, void *stream);
+
 /* Reads and clears the bad-expert-id flag qgemv_moe leaves in its workspace (*flag = 1 if any id
  * of an earlier call on this workspace was out of range; any other nonzero value means a launch
  * broke the kernel's own sizing contract, a library bug).  Unlike every other entry point this
