@@ -38,6 +38,21 @@ int orc_threads(void);
 #define ORC_Q4_K 12
 #define ORC_Q5_K 13
 #define ORC_Q6_K 14
+#define ORC_IQ4_NL 20
+#define ORC_IQ4_XS 23
+#define ORC_Q1_0 40
+#define ORC_AQ4 41
+
+/* The 16-entry codebook of the IQ4 formats.  The pages say the codebook is a
+ * 16-entry nonlinear table of signed values applied in the shader ([ILayer]
+ * gemv_iq4_nl_k_lcpp_src) but print none of its values, so it is an input:
+ * orc_set_codebook installs the table the next decodes use. */
+static int8_t orc_cb[16];
+
+void orc_set_codebook(const int8_t *cb)
+{
+    memcpy(orc_cb, cb, 16);
+}
 
 /* ---------------------------------------------------------------------------
  * IEEE 754 binary16 -> double, exact for every bit pattern (little-endian
@@ -71,6 +86,10 @@ int64_t orc_block_bytes(int fmt)
     case ORC_Q4_K: return 144;  /* f16 d, f16 dmin, 12 B packed 6-bit pairs, 128 B nibbles */
     case ORC_Q5_K: return 176;  /* [ILayer] gemv_q5k_k_lcpp_src: Q4_K's fields + 32 B qh */
     case ORC_Q6_K: return 210;  /* [ILayer] gemv_q6k_k_lcpp_src: 128 ql, 64 qh, 16 i8 scales, d */
+    case ORC_IQ4_NL: return 18; /* [ILayer] iq4_nl_pad_blocks: IQ4_NL blocks are 18 bytes */
+    case ORC_IQ4_XS: return 136;/* [ILayer] gemv_iq4_xs_k_lcpp_src: 136-byte superblocks */
+    case ORC_Q1_0: return 18;   /* [ILayer] gemv_q1_k_lcpp_src: 4.5 B per 32 weights, 128 per scale */
+    case ORC_AQ4: return 20;    /* [Gpu] struct Q: affine Q4, f16 scale and bias per 32 (a reading) */
     default: return -1;
     }
 }
@@ -84,6 +103,10 @@ int64_t orc_block_weights(int fmt)
     case ORC_Q4_K: return 256;  /* [Honey] quant_matmul: Q4_K when k % 256 == 0 */
     case ORC_Q5_K: return 256;
     case ORC_Q6_K: return 256;
+    case ORC_IQ4_NL: return 32;
+    case ORC_IQ4_XS: return 256;
+    case ORC_Q1_0: return 128;
+    case ORC_AQ4: return 32;
     default: return -1;
     }
 }
@@ -229,6 +252,70 @@ static void dq_q6_k(const uint8_t *b, double *w)
     }
 }
 
+/* IQ4_NL: 32 weights, f16 d + 16 bytes of codebook indices; w = d cb[idx].
+ * [ILayer] gemv_iq4_nl_k_lcpp_src (the 16-entry nonlinear codebook applied in
+ * the shader), iq4_nl_pad_blocks (18-byte blocks: f16 d then the 16 index
+ * bytes).  Index order (a reading): as Q4_0, element j in the low nibble of
+ * byte j, element j + 16 in its high nibble. */
+static void dq_iq4_nl(const uint8_t *b, double *w)
+{
+    double d = orc_f16(rd16(b));
+    for (int j = 0; j < 16; ++j) {
+        w[j] = d * (double)orc_cb[b[2 + j] & 15];
+        w[j + 16] = d * (double)orc_cb[b[2 + j] >> 4];
+    }
+}
+
+/* IQ4_XS: 256 weights, f16 d, packed 6-bit sub-scales biased by -32, then 8
+ * sub-blocks of 32 codebook indices ([ILayer] gemv_iq4_xs_k_lcpp_src).  The
+ * 6-bit packing (a reading): a 16-bit word of high 2-bit pairs (sub-block s at
+ * bits 2s, 2s+1), then 4 bytes of low nibbles (sub-block s at bits 4s..4s+3 of
+ * the little-endian word); sub-block s's weights are d (ls - 32) cb[idx] with
+ * its 16 index bytes holding elements 32s + j (low nibble) and 32s + 16 + j
+ * (high nibble). */
+static void dq_iq4_xs(const uint8_t *b, double *w)
+{
+    double d = orc_f16(rd16(b));
+    uint32_t sh = rd16(b + 2);
+    uint32_t sl = (uint32_t)b[4] | ((uint32_t)b[5] << 8) | ((uint32_t)b[6] << 16) |
+                  ((uint32_t)b[7] << 24);
+    const uint8_t *qs = b + 8;
+    for (int s = 0; s < 8; ++s) {
+        int ls = (int)((sl >> (4 * s)) & 15u) | (int)(((sh >> (2 * s)) & 3u) << 4);
+        double dl = d * (double)(ls - 32);
+        for (int j = 0; j < 16; ++j) {
+            w[32 * s + j] = dl * (double)orc_cb[qs[16 * s + j] & 15];
+            w[32 * s + 16 + j] = dl * (double)orc_cb[qs[16 * s + j] >> 4];
+        }
+    }
+}
+
+/* Q1_0: 128 weights, f16 d then 16 bytes of sign bits; bit i of the
+ * little-endian bit stream (bit i % 8 of byte i / 8) is element i's sign,
+ * 1 -> +d, 0 -> -d.  [ILayer] gemv_q1_k_lcpp_src ("bit i is x-element i's
+ * sign, 1 -> +1, 0 -> -1", one f16 scale per 128 weights, 4.5 bytes per 32);
+ * the field order (d first) is a reading, as for the other block types. */
+static void dq_q1_0(const uint8_t *b, double *w)
+{
+    double d = orc_f16(rd16(b));
+    for (int i = 0; i < 128; ++i)
+        w[i] = ((b[2 + i / 8] >> (i % 8)) & 1) ? d : -d;
+}
+
+/* Affine Q4 (AQ4): 32 weights, f16 scale s, f16 bias c, 16 nibble bytes;
+ * w = s q + c.  [Gpu] struct Q ("affine-Q4 projection") and struct HalfSet
+ * (x as even / odd halves plus per-32 group sums: the sums multiply the bias).
+ * Nibble order (a reading matching the even / odd split): element 2i is the
+ * low nibble of byte i, element 2i + 1 its high nibble. */
+static void dq_aq4(const uint8_t *b, double *w)
+{
+    double sc = orc_f16(rd16(b)), c = orc_f16(rd16(b + 2));
+    for (int i = 0; i < 16; ++i) {
+        w[2 * i] = sc * (double)(b[4 + i] & 15) + c;
+        w[2 * i + 1] = sc * (double)(b[4 + i] >> 4) + c;
+    }
+}
+
 /* Dequantize one row of K weights (K a multiple of the block size) from its
  * GGUF-native bytes.  A row is K/bs consecutive blocks ([Honey]
  * transpose_q8_blocks: [n_rows, n_blocks, block] is the native order). */
@@ -246,7 +333,11 @@ int orc_dequant_row(int fmt, const uint8_t *row, int64_t K, double *w)
         case ORC_Q8_0: dq_q8_0(blk, out); break;
         case ORC_Q4_K: dq_q4_k(blk, out); break;
         case ORC_Q5_K: dq_q5_k(blk, out); break;
-        default: dq_q6_k(blk, out); break;
+        case ORC_Q6_K: dq_q6_k(blk, out); break;
+        case ORC_IQ4_NL: dq_iq4_nl(blk, out); break;
+        case ORC_IQ4_XS: dq_iq4_xs(blk, out); break;
+        case ORC_Q1_0: dq_q1_0(blk, out); break;
+        default: dq_aq4(blk, out); break;
         }
     }
     return 0;

@@ -21,6 +21,7 @@ import subprocess
 import numpy as np
 
 Q4_0, Q5_0, Q8_0, Q4_K, Q5_K, Q6_K = 2, 6, 8, 12, 13, 14
+IQ4_NL, IQ4_XS, Q1_0, AQ4 = 20, 23, 40, 41
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -66,6 +67,7 @@ def _load():
         lib.orc_swiglu.argtypes = [_dp, _dp, ctypes.c_int64, _dp]
         lib.orc_argmax.argtypes = [_dp, ctypes.c_int64, ctypes.c_int64, _i64p]
         lib.orc_gelu_tanh_gate.argtypes = [_dp, _dp, ctypes.c_int64, _dp]
+        lib.orc_set_codebook.argtypes = [ctypes.POINTER(ctypes.c_int8)]
         lib.orc_qk_norm_rope.argtypes = [_dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_int64, _dp, _dp,
                                          ctypes.c_double, _dp, _dp]
@@ -82,6 +84,12 @@ def _c(a, dtype):
 
 def _ptr(a, ctype):
     return a.ctypes.data_as(ctype)
+
+
+def set_codebook(cb) -> None:
+    """Install the 16-entry signed codebook the IQ4 decodes use (an input: the pages print none)."""
+    c = _c(np.asarray(cb).reshape(16), np.int8)
+    _load().orc_set_codebook(c.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)))
 
 
 def threads() -> int:

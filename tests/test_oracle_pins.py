@@ -800,3 +800,105 @@ def test_k_quant_brute_force_second_forms():
                                         el = 128 * hh + 32 * qq + l
                                         tot += d * int(scs[8 * hh + (32 * qq + l) // 16]) * ((nib | hi << 4) - 32) * int(xs[el])
                     assert y[r, n] == tot, (fmt, K, r, n)
+
+
+# ----------------------------------------------------------------------------- IQ4, Q1, affine Q4
+
+IQ4_NL, IQ4_XS, Q1_0, AQ4 = oracle.IQ4_NL, oracle.IQ4_XS, oracle.Q1_0, oracle.AQ4
+LINEAR_CB = np.arange(16) - 8          # codebook of Q4_0's own values
+
+
+def test_iq4_nl_with_the_linear_codebook_is_q4_0():
+    """Codebook i - 8 turns IQ4_NL into Q4_0 on the same 18 bytes (d, then index bytes in Q4_0's
+    order): the dequantized rows must agree exactly; a second codebook is applied per index."""
+    import workloads as wl
+    g = np.random.default_rng(81)
+    W = wl.q4_0_matrix(g, 5, 128)
+    oracle.set_codebook(LINEAR_CB)
+    assert np.array_equal(oracle.dequant(IQ4_NL, W, 128), oracle.dequant(Q4_0, W, 128))
+    cb = wl.iq4_codebook()
+    oracle.set_codebook(cb)
+    blk = np.frombuffer(f16_bytes(0.5) + bytes((j & 15) | ((15 - j) << 4) for j in range(16)),
+                        np.uint8)
+    w = oracle.dequant(IQ4_NL, blk, 32)[0]
+    want = [0.5 * int(cb[j]) for j in range(16)] + [0.5 * int(cb[15 - j]) for j in range(16)]
+    assert np.array_equal(w, want)
+
+
+def test_iq4_xs_sub_scales():
+    """With every sub-scale 33 (ls - 32 = 1) and the linear codebook, an IQ4_XS super-block is
+    eight Q4_0 blocks with the same d.  Then each sub-block s and each ls in 0..63 on its own:
+    only sub-block s changes, by the factor ls - 32."""
+    import workloads as wl
+    g = np.random.default_rng(83)
+    oracle.set_codebook(LINEAR_CB)
+    d = 0.0625
+    qs = g.integers(0, 256, 128, dtype=np.uint8)
+
+    def blk(ls):
+        sh = sum(((v >> 4) & 3) << (2 * s) for s, v in enumerate(ls))
+        sl = sum((v & 15) << (4 * s) for s, v in enumerate(ls))
+        return np.frombuffer(f16_bytes(d) + int(sh).to_bytes(2, "little") + int(sl).to_bytes(4, "little")
+                             + qs.tobytes(), np.uint8)
+
+    base = oracle.dequant(IQ4_XS, blk([33] * 8), 256)[0]
+    q4 = np.concatenate([np.frombuffer(f16_bytes(d) + qs[16 * s:16 * s + 16].tobytes(), np.uint8)
+                         for s in range(8)])
+    assert np.array_equal(base, oracle.dequant(Q4_0, q4, 256)[0])
+    for s in range(8):
+        for v in (0, 1, 31, 32, 47, 63):
+            ls = [33] * 8
+            ls[s] = v
+            w = oracle.dequant(IQ4_XS, blk(ls), 256)[0]
+            want = base.copy()
+            want[32 * s:32 * s + 32] *= (v - 32)
+            assert np.array_equal(w, want), (s, v)
+
+
+def test_q1_0_signs_and_brute_force():
+    """Bit i of the sign bytes is element i: 1 -> +d, 0 -> -d; and with small-integer x the
+    oracle equals d (2 sum_{bit=1} x - sum x) exactly."""
+    d = 0.25
+    bits = bytes([0b10110001] + [0] * 14 + [0xFF])
+    w = oracle.dequant(Q1_0, np.frombuffer(f16_bytes(d) + bits, np.uint8), 128)[0]
+    want = np.full(128, -d)
+    for i in (0, 4, 5, 7):
+        want[i] = d
+    want[120:128] = d
+    assert np.array_equal(w, want)
+    g = np.random.default_rng(87)
+    N, K = 9, 256
+    W = np.concatenate([np.frombuffer(f16_bytes(2.0 ** -int(g.integers(1, 6))) +
+                                      g.integers(0, 256, 16, dtype=np.uint8).tobytes(), np.uint8)
+                        for _ in range(N * K // 128)]).reshape(N, -1)
+    x = g.integers(-9, 10, size=(2, K))
+    y, _ = oracle.gemv(Q1_0, W, N, K, x.astype(np.float64))
+    for r in range(2):
+        for n in range(N):
+            tot = 0.0
+            for b in range(K // 128):
+                B = W[n, 18 * b:18 * b + 18]
+                dd = float(B[0:2].view("<f2")[0])
+                on = sum(int(x[r, 128 * b + i]) for i in range(128) if (B[2 + i // 8] >> (i % 8)) & 1)
+                tot += dd * (2 * on - int(x[r, 128 * b:128 * b + 128].sum()))
+            assert y[r, n] == tot
+
+
+def test_aq4_even_odd_order_and_q4_0_equivalence():
+    """Element 2i is the low nibble of byte i, 2i + 1 its high nibble; w = s q + c.  With c = -8 s
+    an AQ4 block equals the Q4_0 block holding the same 32 nibbles in Q4_0's order."""
+    g = np.random.default_rng(89)
+    for _ in range(10):
+        nib = g.integers(0, 16, 32)
+        s = 2.0 ** -int(g.integers(2, 8))
+        aq = np.frombuffer(f16_bytes(s) + f16_bytes(-8 * s) +
+                           bytes(int(nib[2 * i]) | (int(nib[2 * i + 1]) << 4) for i in range(16)),
+                           np.uint8)
+        q4 = np.frombuffer(f16_bytes(s) + bytes(int(nib[j]) | (int(nib[j + 16]) << 4) for j in range(16)),
+                           np.uint8)
+        assert np.array_equal(oracle.dequant(AQ4, aq, 32)[0], oracle.dequant(Q4_0, q4, 32)[0])
+    # a hand block: s = 0.5, c = 0.25, bytes 0x21 0x43 ...: elements 1, 2, 3, 4, ...
+    blk = np.frombuffer(f16_bytes(0.5) + f16_bytes(0.25) +
+                        bytes(((2 * i + 1) & 15) | (((2 * i + 2) & 15) << 4) for i in range(16)), np.uint8)
+    w = oracle.dequant(AQ4, blk, 32)[0]
+    assert np.array_equal(w, [0.5 * ((e + 1) & 15) + 0.25 for e in range(32)])

@@ -24,9 +24,13 @@ from dataclasses import dataclass, field
 import numpy as np
 
 Q4_0, Q5_0, Q8_0, Q4_K, Q5_K, Q6_K = 2, 6, 8, 12, 13, 14
-FMT_NAME = {Q4_0: "q4_0", Q5_0: "q5_0", Q8_0: "q8_0", Q4_K: "q4_k", Q5_K: "q5_k", Q6_K: "q6_k"}
-BLOCK_BYTES = {Q4_0: 18, Q5_0: 22, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
-BLOCK_WEIGHTS = {Q4_0: 32, Q5_0: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+IQ4_NL, IQ4_XS, Q1_0, AQ4 = 20, 23, 40, 41
+FMT_NAME = {Q4_0: "q4_0", Q5_0: "q5_0", Q8_0: "q8_0", Q4_K: "q4_k", Q5_K: "q5_k", Q6_K: "q6_k",
+            IQ4_NL: "iq4_nl", IQ4_XS: "iq4_xs", Q1_0: "q1_0", AQ4: "aq4"}
+BLOCK_BYTES = {Q4_0: 18, Q5_0: 22, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210,
+               IQ4_NL: 18, IQ4_XS: 136, Q1_0: 18, AQ4: 20}
+BLOCK_WEIGHTS = {Q4_0: 32, Q5_0: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256,
+                 IQ4_NL: 32, IQ4_XS: 256, Q1_0: 128, AQ4: 32}
 
 T_X, T_GAMMA, T_W, T_UP, T_DOWN, T_ROUTER, T_EXPERTS = 0, 1, 2, 3, 4, 5, 6
 
@@ -114,9 +118,57 @@ def q6_k_matrix(g: np.random.Generator, N: int, K: int, d_range=Q4_K_D) -> np.nd
     return blk.reshape(N, nbk * 210)
 
 
+def iq4_codebook() -> np.ndarray:
+    """A 16-entry signed, monotone, nonlinear codebook for the IQ4 formats (int8).  The pages
+    give no values for the codebook, so the synthetic workloads use this one: 127 t |t|^0.6 at
+    16 evenly spaced t in [-1, 1], rounded."""
+    t = (np.arange(16) - 7.5) / 7.5
+    return np.round(127 * t * np.abs(t) ** 0.6).astype(np.int8)
+
+
+def iq4_nl_matrix(g: np.random.Generator, N: int, K: int, d_range=(0.0005, 0.002)) -> np.ndarray:
+    """uint8 [N, K/32*18]: d ~ U[d_range] as f16, index bytes uniform."""
+    nbk = K // 32
+    blk = np.empty((N, nbk, 18), dtype=np.uint8)
+    blk[..., 0:2] = _f16_bytes(g.uniform(*d_range, size=(N, nbk)))
+    blk[..., 2:18] = g.integers(0, 256, size=(N, nbk, 16), dtype=np.uint8)
+    return blk.reshape(N, nbk * 18)
+
+
+def iq4_xs_matrix(g: np.random.Generator, N: int, K: int, d_range=(2e-5, 1e-4)) -> np.ndarray:
+    """uint8 [N, K/256*136]: d ~ U[d_range] as f16; sub-scale and index bytes uniform."""
+    nbk = K // 256
+    blk = np.empty((N, nbk, 136), dtype=np.uint8)
+    blk[..., 0:2] = _f16_bytes(g.uniform(*d_range, size=(N, nbk)))
+    blk[..., 2:136] = g.integers(0, 256, size=(N, nbk, 134), dtype=np.uint8)
+    return blk.reshape(N, nbk * 136)
+
+
+def q1_0_matrix(g: np.random.Generator, N: int, K: int, d_range=(0.01, 0.05)) -> np.ndarray:
+    """uint8 [N, K/128*18]: d ~ U[d_range] as f16, sign bytes uniform."""
+    nbk = K // 128
+    blk = np.empty((N, nbk, 18), dtype=np.uint8)
+    blk[..., 0:2] = _f16_bytes(g.uniform(*d_range, size=(N, nbk)))
+    blk[..., 2:18] = g.integers(0, 256, size=(N, nbk, 16), dtype=np.uint8)
+    return blk.reshape(N, nbk * 18)
+
+
+def aq4_matrix(g: np.random.Generator, N: int, K: int, d_range=Q4_0_D) -> np.ndarray:
+    """uint8 [N, K/32*20]: scale s ~ U[d_range], bias c = -s U[6, 9] (weights spread about 0 as
+    Q4_0's do), both f16; nibble bytes uniform."""
+    nbk = K // 32
+    blk = np.empty((N, nbk, 20), dtype=np.uint8)
+    sc = g.uniform(*d_range, size=(N, nbk))
+    blk[..., 0:2] = _f16_bytes(sc)
+    blk[..., 2:4] = _f16_bytes(-sc * g.uniform(6.0, 9.0, size=(N, nbk)))
+    blk[..., 4:20] = g.integers(0, 256, size=(N, nbk, 16), dtype=np.uint8)
+    return blk.reshape(N, nbk * 20)
+
+
 def matrix(fmt: int, g: np.random.Generator, N: int, K: int) -> np.ndarray:
     return {Q4_0: q4_0_matrix, Q5_0: q5_0_matrix, Q8_0: q8_0_matrix, Q4_K: q4_k_matrix,
-            Q5_K: q5_k_matrix, Q6_K: q6_k_matrix}[fmt](g, N, K)
+            Q5_K: q5_k_matrix, Q6_K: q6_k_matrix, IQ4_NL: iq4_nl_matrix, IQ4_XS: iq4_xs_matrix,
+            Q1_0: q1_0_matrix, AQ4: aq4_matrix}[fmt](g, N, K)
 
 
 def normal_f32(g: np.random.Generator, shape) -> np.ndarray:
