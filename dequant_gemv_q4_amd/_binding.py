@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libqgemv.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "qgemv.h")
 
 Q4_0, Q5_0, Q8_0, Q4_K, Q5_K, Q6_K = 2, 6, 8, 12, 13, 14
+IQ4_NL, IQ4_XS, Q1_0, AQ4 = 20, 23, 40, 41
 OP_GEMV, OP_NRM, OP_GUS_NRM, OP_RES, OP_ARGMAX, OP_MOE, OP_NRM_BIAS = range(7)
 ACT_SILU, ACT_GELU_TANH = 0, 1
 STATUS = {0: "QG_OK", 1: "QG_ERR_NULL", 2: "QG_ERR_FORMAT", 3: "QG_ERR_SHAPE", 4: "QG_ERR_ALIGN",
@@ -34,6 +35,7 @@ _vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctyp
 _SIGS = {
     "qgemv_packed_bytes": (_i64, [_i32, _i64, _i64]),
     "qgemv_pack": (_i32, [_i32, _vp, _i64, _i64, _vp, _vp]),
+    "qgemv_pack_codebook": (_i32, [_i32, _vp, _i64, _i64, _vp, _vp, _vp]),
     "qgemv_workspace_bytes": (_i64, [_i32, _i32, _i64, _i64, _i32, _i64, _i32]),
     "qgemv": (_i32, [_i32, _vp, _i64, _i64, _vp, _i32, _vp, _vp, _sz, _vp]),
     "qgemv_nrm": (_i32, [_i32, _vp, _i64, _i64, _vp, _vp, _f32, _i32, _vp, _vp, _sz, _vp]),
@@ -127,6 +129,20 @@ def qgemv_workspace_bytes(op: int, fmt: int, N: int, K: int, nb: int, n_exp: int
 
 def qgemv_pack(fmt, w_gguf, N, K, w_packed, stream=None):
     _check("qgemv_pack", lib().qgemv_pack(fmt, _p(w_gguf), N, K, _p(w_packed), _stream(stream)))
+
+
+def qgemv_pack_codebook(fmt, w_gguf, N, K, codebook, w_packed, stream=None):
+    """codebook: 16 signed bytes on the host (any sequence of ints in [-128, 127]), or None."""
+    cb = None
+    if codebook is not None:
+        vals = [int(v) for v in codebook]
+        if len(vals) != 16:
+            raise ValueError("the codebook has 16 entries")
+        cb = (ctypes.c_int8 * 16)(*vals)
+    _check("qgemv_pack_codebook",
+           lib().qgemv_pack_codebook(fmt, _p(w_gguf), N, K,
+                                     None if cb is None else ctypes.addressof(cb), _p(w_packed),
+                                     _stream(stream)))
 
 
 def qgemv(fmt, W, N, K, x, nb, y, ws=None, ws_bytes=None, stream=None):

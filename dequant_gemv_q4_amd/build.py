@@ -22,6 +22,7 @@ LIB = os.path.join(PKG, "libqgemv.so")
 BW_LIB = os.path.join(PKG, "libqgbw.so")       # the benchmark's bandwidth reference (bw_read.hip)
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["gemv_kernels.hip", "gemv_kernels_x.hip", "stream_kernels.hip", "stream_kernels_x.hip",
+           "stream_kernels_g.hip",
            "mfma_kernels.hip", "gemm_kernels.hip", "abi.cpp"]
 ARCH = "gfx950"
 

@@ -33,7 +33,7 @@ static int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
 bool fmt_valid(int fmt)
 {
     return fmt == FQ4_0 || fmt == FQ5_0 || fmt == FQ8_0 || fmt == FQ4_K || fmt == FQ5_K ||
-           fmt == FQ6_K;
+           fmt == FQ6_K || fmt_generic(fmt);
 }
 
 // Packed layout: the quant plane (nibbles, or Q8_0 bytes), the scale plane (f16 d per 32, or the
@@ -44,21 +44,25 @@ bool layout(int fmt, int64_t N, int64_t K, Layout *L)
 {
     if (!fmt_valid(fmt) || N < 1 || K < 1)
         return false;
-    const int bw = fmt_super(fmt) ? 256 : 32;
+    const int bw = (fmt_super(fmt) || fmt == FIQ4_XS) ? 256 : fmt == FQ1_0 ? 128 : 32;
     const int bb = fmt == FQ4_0 ? 18 : fmt == FQ5_0 ? 22 : fmt == FQ8_0 ? 34 : fmt == FQ4_K ? 144
-                 : fmt == FQ5_K ? 176 : 210;
+                 : fmt == FQ5_K ? 176 : fmt == FQ6_K ? 210 : fmt == FIQ4_NL ? 18
+                 : fmt == FIQ4_XS ? 136 : fmt == FQ1_0 ? 18 : 20;
     if (K % bw != 0 || K > QG_MAX_K)
         return false;
     L->block_w = bw;
     L->block_b = bb;
-    L->qs_row = fmt == FQ8_0 ? K : K / 2;
-    L->sc_row = K / 16;
+    L->qs_row = fmt == FQ8_0 ? K : fmt == FQ1_0 ? K / 8 : K / 2;
+    // scale bytes per row: f16 d per 32 (K/16), IQ4_XS's 8-byte header per 256 (K/32), Q1_0's
+    // f16 d per 128 (K/64), the affine format's f16 scale and bias per 32 (K/8)
+    L->sc_row = fmt == FIQ4_XS ? K / 32 : fmt == FQ1_0 ? K / 64 : fmt == FAQ4 ? K / 8 : K / 16;
     L->hb_row = fmt == FQ6_K ? K / 4 : fmt_hbits(fmt) ? K / 8 : 0;
     L->d_row = fmt == FQ6_K ? K / 128 : 0;
     L->sc_off = round256(N * L->qs_row);
     L->hb_off = L->sc_off + round256(N * L->sc_row);
     L->d_off = L->hb_off + round256(N * L->hb_row);
-    L->total = L->d_off + round256(N * L->d_row);
+    L->cb_off = L->d_off + round256(N * L->d_row);
+    L->total = L->cb_off + (fmt_codebook(fmt) ? 256 : 0);
     L->gguf_row = K / bw * bb;
     return true;
 }
@@ -115,7 +119,7 @@ static int stream_cpl(int fmt, int64_t K, int nb)
 {
     if (nb > 4)
         return 0;
-    const int64_t C = (fmt == FQ8_0 ? K : K / 2) / 16;
+    const int64_t C = fmt == FQ8_0 ? K / 16 : K / 32;   // lane chunks per row
     return C <= 64 ? 1 : C <= 128 ? 2 : C <= 256 ? 4 : 0;
 }
 
@@ -209,7 +213,7 @@ static bool plan_moe(int fmt, int64_t n_exp, int64_t N, int64_t K, int nb, int t
 {
     if (n_exp < 1 || n_exp > QG_MOE_EXPERTS_MAX)   // the per-expert counts live in LDS
         return false;
-    if (fmt_hbits(fmt))                            // the expert kernel takes Q4_0, Q8_0, Q4_K
+    if (fmt_hbits(fmt) || fmt_generic(fmt))         // the expert kernel takes Q4_0, Q8_0, Q4_K
         return false;
     const int64_t C = (fmt == FQ8_0 ? K : K / 2) / 16;
     p->cpl = C <= 64 ? 1 : C <= 128 ? 2 : C <= 256 ? 4 : 0;
@@ -291,6 +295,7 @@ static GemvArgs gemv_args(const Layout &L, const void *W, int64_t N, int64_t K, 
     a.dd0 = a.qs0 + L.d_off;
     a.hb_row = L.hb_row;
     a.d_row = L.d_row;
+    a.cb0 = reinterpret_cast<const int8_t *>(a.qs0 + L.cb_off);
     a.x = x;
     a.y = y;
     a.N = N;
@@ -330,8 +335,9 @@ static int run_gemv(int fmt, int epi, bool nrm, GemvArgs a, void *stream)
         a.rows_per_step = p.rows_per_step;
         a.n_steps = p.n_steps;
         grid = p.grid;
-        herr = fmt_hbits(fmt) ? launch_gemv_x(fmt, epi, nrm, a, p.grid, p.lds, stream)
-                              : launch_gemv(fmt, epi, nrm, a, p.grid, p.lds, stream);
+        herr = (fmt_hbits(fmt) || fmt_generic(fmt))
+                   ? launch_gemv_x(fmt, epi, nrm, a, p.grid, p.lds, stream)
+                   : launch_gemv(fmt, epi, nrm, a, p.grid, p.lds, stream);
     }
     if (herr == 0 && epi == E_ARGMAX)
         herr = launch_argmax_fold(a.keys, grid, a.nb, a.idx, stream);
@@ -377,9 +383,15 @@ int64_t qgemv_packed_bytes(int fmt, int64_t N, int64_t K)
 
 int qgemv_pack(int fmt, const void *w_gguf, int64_t N, int64_t K, void *w_packed, void *stream)
 {
+    return qgemv_pack_codebook(fmt, w_gguf, N, K, nullptr, w_packed, stream);
+}
+
+int qgemv_pack_codebook(int fmt, const void *w_gguf, int64_t N, int64_t K, const int8_t *codebook,
+                        void *w_packed, void *stream)
+{
     if (!fmt_valid(fmt))
         return QG_ERR_FORMAT;
-    if (!w_gguf || !w_packed)
+    if (!w_gguf || !w_packed || (fmt_codebook(fmt) && !codebook))
         return QG_ERR_NULL;
     Layout L;
     if (!layout(fmt, N, K, &L))
@@ -388,7 +400,7 @@ int qgemv_pack(int fmt, const void *w_gguf, int64_t N, int64_t K, void *w_packed
         return QG_ERR_ALIGN;
     if (overlap(w_gguf, N * L.gguf_row, w_packed, L.total))
         return QG_ERR_ALIAS;
-    return launch_status(launch_pack(fmt, w_gguf, N, K, w_packed, stream));
+    return launch_status(launch_pack(fmt, w_gguf, N, K, codebook, w_packed, stream));
 }
 
 int64_t qgemv_workspace_bytes(int op, int fmt, int64_t N, int64_t K, int nb, int64_t n_exp,
@@ -514,6 +526,7 @@ int qgemv_gus_act_nrm(int fmt, const void *Wg, const void *Wu, int64_t N, int64_
     a.sc1 = a.qs1 + L.sc_off;
     a.hb1 = a.qs1 + L.hb_off;
     a.dd1 = a.qs1 + L.d_off;
+    a.cb1 = reinterpret_cast<const int8_t *>(a.qs1 + L.cb_off);
     a.gamma = gamma;
     a.eps = eps;
     a.act = act;
@@ -604,7 +617,7 @@ int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t 
     int st = check_common(fmt, W_experts, N, K, x, nb, y, &L);
     if (st != QG_OK)
         return st;
-    if (fmt_hbits(fmt))
+    if (fmt_hbits(fmt) || fmt_generic(fmt))
         return QG_ERR_FORMAT;
     if (!ids || !wts)
         return QG_ERR_NULL;

@@ -41,8 +41,8 @@ template <int FMT> struct Fc {
 template <int FMT>
 __device__ __forceinline__ int chunk_elem(int i, int j)
 {
-    if constexpr (FMT == FQ4_0 || FMT == FQ5_0) {
-        return 32 * i + 4 * j;             // one 32-weight block per chunk
+    if constexpr (FMT == FQ4_0 || FMT == FQ5_0 || fmt_generic(FMT)) {
+        return 32 * i + 4 * j;             // 32 consecutive weights per chunk
     } else if constexpr (FMT == FQ8_0) {
         return 16 * i + 4 * j;             // half a block per chunk
     } else if constexpr (FMT == FQ6_K) {
@@ -91,9 +91,9 @@ __device__ void stage_tile(const float *const *xrow, const float *gamma, const f
     for (int f = threadIdx.x; f < NB * ct; f += blockDim.x) {
         const int r = f / ct, i = f % ct;
         const float4 *xc = X4 + (size_t)r * XF4 * ct + i;
-        if constexpr (FMT == FQ4_0 || FMT == FQ5_0) {
+        if constexpr (FMT == FQ4_0 || FMT == FQ5_0 || fmt_generic(FMT)) {
             // dot order: for each dword k, its low nibbles (elements 4k..4k+3) then its high
-            // nibbles (elements 16+4k..16+4k+3)
+            // nibbles (elements 16+4k..16+4k+3) (the affine format's sum: any fixed order)
             float s = 0.f;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -159,7 +159,22 @@ __device__ void row_inv_rms(const float *const *xrow, int64_t K, float eps, floa
 
 struct MatPtr {
     const uint8_t *qs, *sc, *hb, *dd;   // quant, scale, high-bit and (Q6_K) d planes
+    uint4 cbt;                          // IQ4 formats: the 16 signed codebook bytes
 };
+
+// Codebook lookup of four 4-bit indices (one per byte of idx, bits 4-7 clear) in the 16-entry
+// byte table T (entry e = byte e % 4 of T[e / 4]): v_perm_b32 picks bytes out of eight, so
+// entries 0-7 and 8-15 are looked up separately and a third permute takes, per byte, the one
+// that bit 3 of the index names (selector i, or i + 4 for the second lookup).  The first two
+// permutes see the index with bit 3 still set and return a constant for it, which the third
+// drops.
+__device__ __forceinline__ uint32_t cb_lookup(const uint4 &T, uint32_t idx)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(T.y, T.x, idx);
+    const uint32_t hi = __builtin_amdgcn_perm(T.w, T.z, idx & 0x07070707u);
+    const uint32_t sel = ((idx >> 1) & 0x04040404u) | 0x03020100u;
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
 
 // Row strides of the four planes.
 struct RowBytes {
@@ -176,7 +191,18 @@ template <int FMT>
 __device__ __forceinline__ ChunkScale chunk_scale(const uint4 &s, int q /* chunk in super-block */)
 {
     ChunkScale cs;
-    if constexpr (FMT == FQ6_K) {
+    if constexpr (FMT == FIQ4_XS) {
+        // s.x: f16 d, then the 16-bit word of high scale bits (sub-block q at bits 2q, 2q + 1);
+        // s.y: the low 4-bit scale of sub-block q at bits 4q..4q+3; scale d (ls - 32)
+        const uint32_t ls = ((s.y >> (4 * q)) & 15u) | (((s.x >> (16 + 2 * q)) & 3u) << 4);
+        cs.a = h2f(s.x & 0xffffu) * (float)((int)ls - 32);
+        cs.b = cs.a2 = cs.b2 = 0.f;
+    } else if constexpr (FMT == FAQ4) {
+        // f16 scale s and f16 bias c: w = s q + c, held as a q - b with b = -c
+        cs.a = h2f(s.x & 0xffffu);
+        cs.b = -h2f(s.x >> 16);
+        cs.a2 = cs.b2 = 0.f;
+    } else if constexpr (FMT == FQ6_K) {
         // s.x, s.y: the eight signed scales of the chunk's half of the super-block (bytes 8n..8n+7,
         // n = q / 4); the chunk (u = q % 4) takes scale u (low nibbles) and u + 4 (high);
         // s.z: the super-block's f16 d
@@ -222,14 +248,58 @@ __device__ __forceinline__ float k_center(float a, float b)
     return fminf(fmaxf(rintf(b * __builtin_amdgcn_rcpf(a)), 0.f), 63.f);
 }
 
+// The affine format's centre: w = s q + c = s (q - c') + (s c' + c) with c' the point of
+// {0, ..., 15} nearest t = -c / s.  Every weight has |q - t| >= |c' - t| (c' is the nearest of
+// the values q takes), so |s c' + c| = |s| |c' - t| <= |w| and |s (q - c')| <= 2 |w| for every
+// weight of the block: the dot over q - c' and the term (s c' + c) sum x round relative to
+// sum |w x|.  s = 0 (t infinite or NaN) gives 0 or 15, exact there (every w is c).
+__device__ __forceinline__ float aq_center(float a, float b)
+{
+    return fminf(fmaxf(rintf(b * __builtin_amdgcn_rcpf(a)), 0.f), 15.f);
+}
+
 // Decode the 16-byte chunk into the per-element factors the dot multiplies, exact in f32 and in
 // dot order: Q4_0 the signed q - 8, Q5_0 q - 16, Q8_0 the signed byte, Q6_K q - 32, Q4_K and Q5_K
 // the unsigned q (centred per sub-block in chunk_dot).  h: the chunk's high-bit words (the
 // layout k_pack writes: low nibble of byte 4k + m at bit 8m + k, high nibble at 8m + 4 + k; Q6_K
 // two bits each, at 8m + 2k of h.x (low) and h.y (high)).
 template <int FMT>
-__device__ __forceinline__ void decode_chunk(const uint4 &q, const uint2 &h, float *w)
+__device__ __forceinline__ void decode_chunk(const uint4 &q, const uint2 &h, const uint4 &cbt,
+                                             float *w)
 {
+    if constexpr (fmt_codebook(FMT)) {
+        // codebook entries in Q4_0's nibble order: w[8k + m] element 4k + m (low nibble of byte
+        // 4k + m), w[8k + 4 + m] element 16 + 4k + m (its high nibble)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t v = ucomp(q, k);
+            const uint32_t lo = cb_lookup(cbt, v & 0x0f0f0f0fu);
+            const uint32_t hi = cb_lookup(cbt, (v >> 4) & 0x0f0f0f0fu);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                w[8 * k + m] = (float)(int8_t)((lo >> (8 * m)) & 0xffu);
+                w[8 * k + 4 + m] = (float)(int8_t)((hi >> (8 * m)) & 0xffu);
+            }
+        }
+        return;
+    }
+    if constexpr (FMT == FQ1_0) {
+        // natural order: w[e] = +1 if bit e of the chunk's word is set, else -1
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+            w[e] = ((q.x >> e) & 1u) ? 1.0f : -1.0f;
+        return;
+    }
+    if constexpr (FMT == FAQ4) {
+        // natural order: element 2i the low nibble of byte i, 2i + 1 its high nibble
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t b = (ucomp(q, i >> 2) >> (8 * (i & 3))) & 0xffu;
+            w[2 * i] = (float)(b & 15u);
+            w[2 * i + 1] = (float)(b >> 4);
+        }
+        return;
+    }
     if constexpr (fmt_hbits(FMT)) {
         const float off = FMT == FQ5_0 ? 16.0f : FMT == FQ6_K ? 32.0f : 0.0f;
 #pragma unroll
@@ -280,7 +350,23 @@ template <int FMT>
 __device__ __forceinline__ float chunk_dot(const float *w, const float4 *xv, const float *Sv,
                                            const ChunkScale &cs, float acc)
 {
-    if constexpr (FMT == FQ4_0 || FMT == FQ5_0) {
+    if constexpr (FMT == FQ1_0 || FMT == FAQ4) {
+        // natural order; the affine format centred (aq_center), its (s c' + c) term times the
+        // chunk's x sum
+        const float c = FMT == FAQ4 ? aq_center(cs.a, cs.b) : 0.f;
+        float dot = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            dot = fmaf(w[4 * j + 0] - c, xv[j].x, dot);
+            dot = fmaf(w[4 * j + 1] - c, xv[j].y, dot);
+            dot = fmaf(w[4 * j + 2] - c, xv[j].z, dot);
+            dot = fmaf(w[4 * j + 3] - c, xv[j].w, dot);
+        }
+        acc = fmaf(cs.a, dot, acc);
+        if constexpr (FMT == FAQ4)
+            acc = fmaf(fmaf(cs.a, c, -cs.b), Sv[0], acc);
+        return acc;
+    } else if constexpr (FMT == FQ4_0 || FMT == FQ5_0 || fmt_codebook(FMT)) {
         float dot = 0.f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -345,9 +431,20 @@ template <int FMT>
 __device__ __forceinline__ void load_chunk(const MatPtr &m, const RowBytes &rb, int64_t n,
                                            int64_t ci, uint4 &q, uint4 &s, uint2 &h)
 {
-    q = *reinterpret_cast<const uint4 *>(m.qs + n * rb.qs + ci * 16);
+    if constexpr (FMT == FQ1_0)
+        q = make_uint4(*reinterpret_cast<const uint32_t *>(m.qs + n * rb.qs + ci * 4), 0u, 0u, 0u);
+    else
+        q = *reinterpret_cast<const uint4 *>(m.qs + n * rb.qs + ci * 16);
     h = make_uint2(0u, 0u);
-    if constexpr (FMT == FQ4_0 || FMT == FQ5_0) {
+    if constexpr (FMT == FIQ4_XS) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(m.sc + n * rb.sc + (ci >> 3) * 8);
+        s = make_uint4(w.x, w.y, 0u, 0u);
+    } else if constexpr (FMT == FQ1_0) {
+        s = make_uint4(*reinterpret_cast<const uint16_t *>(m.sc + n * rb.sc + (ci >> 2) * 2), 0u,
+                       0u, 0u);
+    } else if constexpr (FMT == FAQ4) {
+        s = make_uint4(*reinterpret_cast<const uint32_t *>(m.sc + n * rb.sc + ci * 4), 0u, 0u, 0u);
+    } else if constexpr (FMT == FQ4_0 || FMT == FQ5_0 || FMT == FIQ4_NL) {
         s = make_uint4(*reinterpret_cast<const uint16_t *>(m.sc + n * rb.sc + ci * 2), 0u, 0u, 0u);
     } else if constexpr (FMT == FQ8_0) {
         s = make_uint4(*reinterpret_cast<const uint16_t *>(m.sc + n * rb.sc + (ci >> 1) * 2), 0u,
@@ -408,7 +505,7 @@ __device__ __forceinline__ void tile_compute(const MatPtr (&mat)[MATS], const Ro
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     float w[CE];
-                    decode_chunk<FMT>(q[m][u], h[m][u], w);
+                    decode_chunk<FMT>(q[m][u], h[m][u], mat[m].cbt, w);
                     const ChunkScale cs = chunk_scale<FMT>(s[m][u], qpos);
                     acc[m][u][0] = chunk_dot<FMT>(w, xv, Sv, cs, acc[m][u][0]);
                 }
@@ -419,7 +516,7 @@ __device__ __forceinline__ void tile_compute(const MatPtr (&mat)[MATS], const Ro
             for (int m = 0; m < MATS; ++m)
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    decode_chunk<FMT>(q[m][u], h[m][u], w[m][u]);
+                    decode_chunk<FMT>(q[m][u], h[m][u], mat[m].cbt, w[m][u]);
                     cs[m][u] = chunk_scale<FMT>(s[m][u], qpos);
                 }
 #pragma unroll

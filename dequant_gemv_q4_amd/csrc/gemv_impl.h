@@ -37,9 +37,14 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a)
         row_inv_rms<NB>(xrow, a.K, a.eps, s_inv, s_red);
 
     MatPtr mat[MATS];
-    mat[0] = MatPtr{a.qs0, a.sc0, a.hb0, a.dd0};
+    mat[0] = MatPtr{a.qs0, a.sc0, a.hb0, a.dd0, make_uint4(0u, 0u, 0u, 0u)};
     if constexpr (MATS == 2)
-        mat[MATS - 1] = MatPtr{a.qs1, a.sc1, a.hb1, a.dd1};
+        mat[MATS - 1] = MatPtr{a.qs1, a.sc1, a.hb1, a.dd1, make_uint4(0u, 0u, 0u, 0u)};
+    if constexpr (fmt_codebook(FMT)) {
+        mat[0].cbt = *reinterpret_cast<const uint4 *>(a.cb0);
+        if constexpr (MATS == 2)
+            mat[MATS - 1].cbt = *reinterpret_cast<const uint4 *>(a.cb1);
+    }
     const RowBytes rb{a.qs_row, a.sc_row, a.hb_row, a.d_row};
 
     unsigned long long best[NB];

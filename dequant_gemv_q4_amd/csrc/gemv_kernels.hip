@@ -22,9 +22,11 @@ namespace qg {
 // ------------------------------------------------------------------------------------ pack
 
 // GGUF-native blocks (row-major, K/bw blocks per row) -> planes.  Block number blk (= row * nblk +
-// block) moves its quant bytes to qs + blk * QB and its scale bytes to sc + blk * SB: Q4_0 and
-// Q5_0 (16, 2), Q8_0 (32, 2), Q4_K and Q5_K (128, 16: d, dmin and the 12 packed (scale, min)
-// bytes, unchanged), Q6_K (128, 16: the 16 signed scales; its d goes to dd + blk * 2).  The high
+// block) moves its quant bytes to qs + blk * QB and its scale bytes to sc + blk * SB: Q4_0,
+// Q5_0, IQ4_NL and Q1_0 (16, 2), Q8_0 (32, 2), the affine Q4 (16, 4: scale and bias), IQ4_XS
+// (128, 8: d and the packed sub-scales), Q4_K and Q5_K (128, 16: d, dmin and the 12 packed
+// (scale, min) bytes, unchanged), Q6_K (128, 16: the 16 signed scales; its d goes to
+// dd + blk * 2).  The IQ4 formats' 16-byte codebook (cb) is written once, after every plane.  The high
 // bits of Q5_0 / Q5_K / Q6_K go to hb + blk * HB, re-laid per 32 weights (q5_bits, q6_bits) so
 // that the kernels insert them into the nibble bytes with one shift and one and-or per dword.
 //
@@ -54,15 +56,19 @@ __device__ __forceinline__ uint32_t q6_bits(const uint8_t (&two)[16])
 
 template <int FMT>
 __global__ __launch_bounds__(256) void k_pack(const uint8_t *src, int64_t nblocks, uint8_t *qs,
-                                              uint8_t *sc, uint8_t *hb, uint8_t *dd)
+                                              uint8_t *sc, uint8_t *hb, uint8_t *dd, uint4 cbv,
+                                              uint8_t *cb)
 {
     constexpr int BB = FMT == FQ4_0 ? 18 : FMT == FQ5_0 ? 22 : FMT == FQ8_0 ? 34
-                     : FMT == FQ4_K ? 144 : FMT == FQ5_K ? 176 : 210;
+                     : FMT == FQ4_K ? 144 : FMT == FQ5_K ? 176 : FMT == FQ6_K ? 210
+                     : FMT == FIQ4_NL ? 18 : FMT == FIQ4_XS ? 136 : FMT == FQ1_0 ? 18 : 20;
+    if (fmt_codebook(FMT) && blockIdx.x == 0 && threadIdx.x == 0)
+        *reinterpret_cast<uint4 *>(cb) = cbv;
     for (int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; blk < nblocks;
          blk += (int64_t)gridDim.x * blockDim.x) {
         const uint8_t *b = src + blk * BB;
-        if constexpr (FMT == FQ4_0 || FMT == FQ8_0 || FMT == FQ4_K) {
-            constexpr int SB = FMT == FQ4_K ? 16 : 2;
+        if constexpr (FMT == FQ4_0 || FMT == FQ8_0 || FMT == FQ4_K || fmt_generic(FMT)) {
+            constexpr int SB = FMT == FQ4_K ? 16 : FMT == FIQ4_XS ? 8 : FMT == FAQ4 ? 4 : 2;
             constexpr int QB = BB - SB;
             for (int k = 0; k < SB; ++k)
                 sc[blk * SB + k] = b[k];
@@ -214,27 +220,38 @@ int launch_qk_norm_rope(float *y, int64_t row_stride, int nb, int nq, int nkv, i
     return (int)hipGetLastError();
 }
 
-int launch_pack(int fmt, const void *src, int64_t N, int64_t K, void *dst, void *stream)
+int launch_pack(int fmt, const void *src, int64_t N, int64_t K, const int8_t *codebook, void *dst,
+                void *stream)
 {
     Layout L;
     if (!layout(fmt, N, K, &L))
         return (int)hipErrorInvalidValue;
     const int64_t nblocks = N * (K / L.block_w);
     uint8_t *qs = static_cast<uint8_t *>(dst);
-    uint8_t *sc = qs + L.sc_off, *hb = qs + L.hb_off, *dd = qs + L.d_off;
+    uint8_t *sc = qs + L.sc_off, *hb = qs + L.hb_off, *dd = qs + L.d_off, *cb = qs + L.cb_off;
+    // the codebook travels by value (a kernel argument): the host table is read before return
+    uint32_t cw[4] = {0u, 0u, 0u, 0u};
+    if (fmt_codebook(fmt))
+        for (int e = 0; e < 16; ++e)
+            cw[e / 4] |= (uint32_t)(uint8_t)codebook[e] << (8 * (e % 4));
+    const uint4 cbv = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     const int64_t want = (nblocks + 255) / 256;
     const int grid = (int)(want < 65536 ? want : 65536);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint8_t *in = static_cast<const uint8_t *>(src);
 #define QG_PACK(F)                                                                                \
-    hipLaunchKernelGGL(k_pack<F>, dim3(grid), dim3(256), 0, s, in, nblocks, qs, sc, hb, dd)
+    hipLaunchKernelGGL(k_pack<F>, dim3(grid), dim3(256), 0, s, in, nblocks, qs, sc, hb, dd, cbv, cb)
     switch (fmt) {
     case FQ4_0: QG_PACK(FQ4_0); break;
     case FQ5_0: QG_PACK(FQ5_0); break;
     case FQ8_0: QG_PACK(FQ8_0); break;
     case FQ4_K: QG_PACK(FQ4_K); break;
     case FQ5_K: QG_PACK(FQ5_K); break;
-    default: QG_PACK(FQ6_K); break;
+    case FQ6_K: QG_PACK(FQ6_K); break;
+    case FIQ4_NL: QG_PACK(FIQ4_NL); break;
+    case FIQ4_XS: QG_PACK(FIQ4_XS); break;
+    case FQ1_0: QG_PACK(FQ1_0); break;
+    default: QG_PACK(FAQ4); break;
     }
 #undef QG_PACK
     return (int)hipGetLastError();

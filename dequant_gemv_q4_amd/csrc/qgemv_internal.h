@@ -8,7 +8,19 @@
 
 namespace qg {
 
-enum Fmt { FQ4_0 = 2, FQ5_0 = 6, FQ8_0 = 8, FQ4_K = 12, FQ5_K = 13, FQ6_K = 14 };
+enum Fmt { FQ4_0 = 2, FQ5_0 = 6, FQ8_0 = 8, FQ4_K = 12, FQ5_K = 13, FQ6_K = 14, FIQ4_NL = 20,
+           FIQ4_XS = 23, FQ1_0 = 40, FAQ4 = 41 };
+
+// Formats the K-tiled kernel serves with a per-element decode (codebook, sign and affine
+// formats): fewer bytes per weight, where the byte ratio is the speed ratio.
+__host__ __device__ constexpr bool fmt_generic(int f)
+{
+    return f == FIQ4_NL || f == FIQ4_XS || f == FQ1_0 || f == FAQ4;
+}
+// Formats whose weights come from a 16-entry codebook stored with the packed matrix.
+__host__ __device__ constexpr bool fmt_codebook(int f) { return f == FIQ4_NL || f == FIQ4_XS; }
+// Quant bytes of the chunk (32 weights; Q8_0 16) one lane takes: Q1_0's 32 sign bits are 4 bytes.
+__host__ __device__ constexpr int fmt_chunk_bytes(int f) { return f == FQ1_0 ? 4 : 16; }
 
 // Format classes.  Super-block formats hold 256 weights per block; high-bit formats carry a plane
 // of fifth (Q5) or fifth-and-sixth (Q6_K) bits beside the nibbles; min formats have the
@@ -16,7 +28,7 @@ enum Fmt { FQ4_0 = 2, FQ5_0 = 6, FQ8_0 = 8, FQ4_K = 12, FQ5_K = 13, FQ6_K = 14 }
 __host__ __device__ constexpr bool fmt_super(int f) { return f == FQ4_K || f == FQ5_K || f == FQ6_K; }
 __host__ __device__ constexpr bool fmt_hbits(int f) { return f == FQ5_0 || f == FQ5_K || f == FQ6_K; }
 __host__ __device__ constexpr bool fmt_min(int f) { return f == FQ4_K || f == FQ5_K; }
-__host__ __device__ constexpr bool fmt_q4(int f) { return f == FQ4_0 || f == FQ4_K; }
+__host__ __device__ constexpr bool fmt_q4(int f) { return f == FQ4_0 || f == FQ4_K || f == FAQ4; }
 // 32-bit words of high bits per 16-byte chunk of nibbles (32 weights).
 __host__ __device__ constexpr int fmt_hwords(int f) { return f == FQ6_K ? 2 : fmt_hbits(f) ? 1 : 0; }
 // Formats whose chunk carries two sub-block scales (a low-nibble and a high-nibble sub-block).
@@ -62,21 +74,22 @@ __host__ __device__ constexpr int moe_threads(int fmt, int cpl, int pd)
 // plane of scale bytes (row n at n * sc_row), each starting 256-B aligned.  Same bytes per weight
 // as the GGUF blocks.
 struct Layout {
-    int64_t qs_row;     // quant bytes per row: Q8_0 K, every other format K/2 (the nibbles)
-    int64_t sc_row;     // scale bytes per row: K/16 for every format
+    int64_t qs_row;     // quant bytes per row: Q8_0 K, Q1_0 K/8 (sign bits), others K/2 (nibbles)
+    int64_t sc_row;     // scale bytes per row: K/16, IQ4_XS K/32, Q1_0 K/64, affine Q4 K/8
     int64_t sc_off;     // byte offset of the scale plane (qs plane rounded up to 256 B)
     int64_t hb_row;     // high-bit bytes per row: Q5_0 / Q5_K K/8, Q6_K K/4, others 0
     int64_t hb_off;     // byte offset of the high-bit plane (after the scale plane)
     int64_t d_row;      // Q6_K: bytes of the super-block d values per row (K/128), others 0
     int64_t d_off;      // byte offset of that plane
+    int64_t cb_off;     // IQ4 formats: byte offset of the 16-byte codebook (after every plane)
     int64_t total;      // packed bytes
     int64_t gguf_row;   // GGUF bytes per row
     int block_w;        // weights per GGUF block
     int block_b;        // bytes per GGUF block
 };
 
-// Facts of the 16-byte quant chunk one lane processes: x float4s it multiplies (xf4), x elements
-// (ce), block sums it needs (ns), and the K granularity a tile must keep (tile_align).
+// Facts of the quant chunk one lane processes (16 bytes; Q1_0 4): x float4s it multiplies (xf4),
+// x elements (ce), block sums it needs (ns), and the K granularity a tile must keep (tile_align).
 struct FmtFacts {
     int xf4, ce, ns, tile_align;
 };
@@ -84,6 +97,8 @@ struct FmtFacts {
 __host__ __device__ constexpr FmtFacts fmt_facts(int fmt)
 {
     return fmt == FQ8_0 ? FmtFacts{4, 16, 1, 32}
+         : fmt == FQ1_0 ? FmtFacts{8, 32, 1, 128}
+         : fmt == FIQ4_XS ? FmtFacts{8, 32, 1, 256}
          : fmt_super(fmt) ? FmtFacts{8, 32, 2, 256}
                           : FmtFacts{8, 32, 1, 32};
 }
@@ -136,6 +151,7 @@ struct GemvArgs {
     const uint8_t *qs1, *sc1;   // matrix 1 (the up matrix of the gated product)
     const uint8_t *hb0, *hb1;   // high-bit planes of the two matrices (high-bit formats)
     const uint8_t *dd0, *dd1;   // Q6_K: planes of the super-block d values
+    const int8_t *cb0, *cb1;    // IQ4 formats: the 16-entry codebooks of the two matrices
     const float *x;             // [nb][K]
     const float *gamma;         // [K] (norm prologue)
     const float *res;           // residual [nb][N] (res_rstride N) or bias [N] (res_rstride 0)
@@ -188,7 +204,8 @@ struct GemmArgs {
 int launch_gemm(int fmt, const GemmArgs &a, const float *x, void *stream);
 
 // Launch helpers (gemv_kernels.hip).  Return a hipError_t value (0 = success).
-int launch_pack(int fmt, const void *src, int64_t N, int64_t K, void *dst, void *stream);
+int launch_pack(int fmt, const void *src, int64_t N, int64_t K, const int8_t *codebook, void *dst,
+                void *stream);
 int launch_gemv(int fmt, int epi, bool nrm, const GemvArgs &a, int grid, size_t lds_bytes,
                 void *stream);
 // The same for the high-bit formats (gemv_kernels_x.hip).
@@ -199,6 +216,9 @@ int launch_stream(int fmt, int epi, bool nrm, int cpl, int pd, const GemvArgs &a
 // The streaming kernel variant (function and threads per workgroup) of a high-bit format
 // (stream_kernels_x.hip); *fn = nullptr if there is none.
 void stream_fn_x(int fmt, int epi, bool nrm, int ks, int nb, int pd, const void **fn,
+                 int *threads);
+// The same for the codebook, sign and affine formats (stream_kernels_g.hip).
+void stream_fn_g(int fmt, int epi, bool nrm, int ks, int nb, int pd, const void **fn,
                  int *threads);
 // Routed experts: the expert kernel (x rows per set 4 / cpl, pd groups in flight per wave), then
 // the combine.

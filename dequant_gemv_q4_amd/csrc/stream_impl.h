@@ -98,11 +98,11 @@ struct SP {
     // batch of 2..4 on one matrix with one wave per row holds its x pairs in about 120 VGPRs,
     // so three waves fit (more waves to hide the longer decode of several batch rows); rows
     // split over several waves are short, and fewer, smaller workgroups start sooner there
-    // (the super-block and high-bit formats hold more per chunk: two waves per SIMD)
+    // (the super-block, high-bit and codebook formats hold more per chunk: two waves per SIMD)
     static constexpr int WPE = (NB == 1 && CPL == 1 && !fmt_super(FMT) && !fmt_hbits(FMT))
                                    ? QG_WPE_NB1
                              : (NB > 1 && KS == 1 && MATS == 1 && !fmt_super(FMT) &&
-                                !fmt_hbits(FMT)) ? 3 : 2;
+                                !fmt_hbits(FMT) && !fmt_codebook(FMT)) ? 3 : 2;
     static constexpr int ITEMS = R * NB;
     static constexpr int IP = pow2_ceil(ITEMS);
     // GEMV family: one workgroup fills a CU (WPE waves on each of its 4 SIMDs)
@@ -127,6 +127,14 @@ struct ScaleT<FQ5_K> {
 template <>
 struct ScaleT<FQ6_K> {
     using T = uint4;
+};
+template <>
+struct ScaleT<FIQ4_XS> {   // f16 d and the 16-bit word of high scale bits; the low 4-bit scales
+    using T = uint2;
+};
+template <>
+struct ScaleT<FAQ4> {      // f16 scale and f16 bias
+    using T = uint32_t;
 };
 
 // Loads of one row group: for each matrix, row and chunk slot, 16 bytes of quants, the scale and
@@ -197,9 +205,12 @@ __device__ __forceinline__ LaneOff<CPL> lane_offsets(int lane, int C)
         const int c = lane + 64 * i;
         o.ok[i] = c < C;
         const uint32_t cx = (uint32_t)(c < C ? c : C - 1);
-        o.q[i] = cx * 16u;
-        o.s[i] = (FMT == FQ4_0 || FMT == FQ5_0) ? cx * 2u
+        o.q[i] = cx * (uint32_t)fmt_chunk_bytes(FMT);
+        o.s[i] = (FMT == FQ4_0 || FMT == FQ5_0 || FMT == FIQ4_NL) ? cx * 2u
                : FMT == FQ8_0 ? (cx >> 1) * 2u
+               : FMT == FQ1_0 ? (cx >> 2) * 2u
+               : FMT == FAQ4 ? cx * 4u
+               : FMT == FIQ4_XS ? (cx >> 3) * 8u
                : FMT == FQ6_K ? (cx >> 3) * 16u + ((cx & 7u) >> 2) * 8u
                               : (cx >> 3) * 16u;
         o.h[i] = cx * 4u * (uint32_t)(fmt_hwords(FMT) > 0 ? fmt_hwords(FMT) : 1);
@@ -233,9 +244,15 @@ __device__ __forceinline__ void load_group(GroupBuf<FMT, CPL, MATS, R> &b, const
             for (int i = 0; i < CPL; ++i) {
                 const uint32_t roq = in ? n * qs_row : mat[m].q_end;
                 const uint32_t ros = in ? n * sc_row : mat[m].s_end;
-                const auto v = __builtin_amdgcn_raw_buffer_load_b128(mat[m].q,
-                                                                     (int)(lo.q[i] + roq), 0, QG_WCPOL_STREAM);
-                b.q[m][u][i] = make_uint4(v[0], v[1], v[2], v[3]);
+                if constexpr (FMT == FQ1_0) {
+                    b.q[m][u][i] = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(
+                                                  mat[m].q, (int)(lo.q[i] + roq), 0, QG_WCPOL_STREAM),
+                                              0u, 0u, 0u);
+                } else {
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+                        mat[m].q, (int)(lo.q[i] + roq), 0, QG_WCPOL_STREAM);
+                    b.q[m][u][i] = make_uint4(v[0], v[1], v[2], v[3]);
+                }
                 // raw scale bytes: the lane mask is applied where they are used, so that no
                 // instruction touches a load's result before its group is decoded
                 if constexpr (SCW) {
@@ -244,6 +261,13 @@ __device__ __forceinline__ void load_group(GroupBuf<FMT, CPL, MATS, R> &b, const
                     const auto w = __builtin_amdgcn_raw_buffer_load_b128(
                         mat[m].s, (int)(lo.s[i] + ros), 0, QG_WCPOL_STREAM);
                     b.s[m][u][i] = make_uint4(w[0], w[1], w[2], w[3]);
+                } else if constexpr (FMT == FIQ4_XS) {
+                    const auto w = __builtin_amdgcn_raw_buffer_load_b64(
+                        mat[m].s, (int)(lo.s[i] + ros), 0, QG_WCPOL_STREAM);
+                    b.s[m][u][i] = make_uint2(w[0], w[1]);
+                } else if constexpr (FMT == FAQ4) {
+                    b.s[m][u][i] = __builtin_amdgcn_raw_buffer_load_b32(
+                        mat[m].s, (int)(lo.s[i] + ros), 0, QG_WCPOL_STREAM);
                 } else if constexpr (FMT == FQ6_K) {
                     const auto w = __builtin_amdgcn_raw_buffer_load_b64(
                         mat[m].s, (int)(lo.s[i] + ros), 0, QG_WCPOL_STREAM);
@@ -279,6 +303,10 @@ template <int FMT>
 __device__ __forceinline__ ChunkScale scale_of(uint16_t s, int) { ChunkScale cs; cs.a = (float)__builtin_bit_cast(_Float16, s); cs.b = cs.a2 = cs.b2 = 0.f; return cs; }
 template <int FMT>
 __device__ __forceinline__ ChunkScale scale_of(const uint4 &s, int qpos) { return chunk_scale<FMT>(s, qpos); }
+template <int FMT>
+__device__ __forceinline__ ChunkScale scale_of(const uint2 &s, int qpos) { return chunk_scale<FMT>(make_uint4(s.x, s.y, 0u, 0u), qpos); }
+template <int FMT>
+__device__ __forceinline__ ChunkScale scale_of(uint32_t s, int qpos) { return chunk_scale<FMT>(make_uint4(s, 0u, 0u, 0u), qpos); }
 
 // Workgroup-shared x.  A few loader waves each load float4s base + stride * i of the NB rows
 // (and of gamma) and write them to LDS (natural [row][K] order).  With NRM the stored value is
@@ -382,25 +410,29 @@ __device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t m, uint32_t c)
 // pairs added to remove the offsets (low nibble / byte, high nibble held x16).
 struct WConst {
     uint32_t m_lo, m_hi, c, off_lo, off_hi, m_nb, m_hb;
+    uint4 cb[2];   // IQ4 formats: the codebooks of the (up to two) matrices, each byte + 128
 };
 
 template <int FMT>
 __device__ __forceinline__ WConst w_const()
 {
     WConst k;
-    // byte formats (Q8_0 and the high-bit formats, whose nibbles and high bits are first joined
-    // into bytes) take bytes 0 / 2 of a dword; the Q4 formats take nibbles
-    k.m_lo = (FMT == FQ8_0 || fmt_hbits(FMT)) ? 0x00FF00FFu : 0x000F000Fu;
+    // byte formats (Q8_0, the high-bit formats, whose nibbles and high bits are first joined into
+    // bytes, and the codebook formats, whose looked-up entries are bytes) take bytes 0 / 2 of a
+    // dword; the Q4 formats take nibbles; Q1_0 takes the sign bits of a pair (its c: 1.0, 1.0)
+    k.m_lo = (FMT == FQ8_0 || fmt_hbits(FMT) || fmt_codebook(FMT)) ? 0x00FF00FFu
+           : FMT == FQ1_0 ? 0x80008000u : 0x000F000Fu;
     k.m_hi = 0x00F000F0u;
-    k.c = 0x64006400u;
+    k.c = FMT == FQ1_0 ? 0x3C003C00u : 0x64006400u;
     // Q4_0: -1032 (1024 + n -> n - 8), -1152 (1024 + 16 n -> 16 (n - 8)); Q8_0: -1152
     // (1024 + q + 128 -> q); Q5_0: -1040 (1024 + q -> q - 16); Q6_K: -1056 (1024 + q -> q - 32);
     // Q4_K / Q5_K: set per sub-block from its centre (see compute_group_h)
-    k.off_lo = FMT == FQ4_0 ? 0xE408E408u : FMT == FQ8_0 ? 0xE480E480u
+    k.off_lo = FMT == FQ4_0 ? 0xE408E408u : (FMT == FQ8_0 || fmt_codebook(FMT)) ? 0xE480E480u
              : FMT == FQ5_0 ? 0xE410E410u : FMT == FQ6_K ? 0xE420E420u : 0xE400E400u;
     k.off_hi = FMT == FQ4_0 ? 0xE480E480u : fmt_hbits(FMT) ? k.off_lo : 0xE400E400u;
     k.m_nb = 0x0F0F0F0Fu;                                  // the nibbles of four bytes
     k.m_hb = FMT == FQ6_K ? 0x30303030u : 0x10101010u;     // their high bits' places
+    k.cb[0] = k.cb[1] = make_uint4(0u, 0u, 0u, 0u);
     asm volatile("" : "+v"(k.m_lo), "+v"(k.m_hi), "+v"(k.c), "+v"(k.off_lo), "+v"(k.off_hi),
                  "+v"(k.m_nb), "+v"(k.m_hb));
     return k;
@@ -463,6 +495,30 @@ __device__ __forceinline__ void w_pairs_hb(uint32_t q, uint32_t h0, uint32_t h1,
     w[3] = h2_add(and_or(hi >> 8, k.m_lo, k.c), k.off_hi);
 }
 
+// Codebook formats: the pairs of dword q of a chunk in Q4_0's pair order (low-nibble entries of
+// bytes 0, 2; high-nibble entries of bytes 0, 2; low 1, 3; high 1, 3).  T holds every entry
+// + 128 as an unsigned byte, so a looked-up byte becomes its pair half as Q8_0's bytes do
+// (mantissa of 1024, then -1152): exact signed entries.
+__device__ __forceinline__ void w_pairs_cb(uint32_t q, const WConst &k, const uint4 &T, uint32_t *w)
+{
+    const uint32_t lo = cb_lookup(T, q & 0x0F0F0F0Fu);
+    const uint32_t hi = cb_lookup(T, (q >> 4) & 0x0F0F0F0Fu);
+    w[0] = h2_add(and_or(lo, k.m_lo, k.c), k.off_lo);
+    w[1] = h2_add(and_or(hi, k.m_lo, k.c), k.off_lo);
+    w[2] = h2_add(and_or(lo >> 8, k.m_lo, k.c), k.off_lo);
+    w[3] = h2_add(and_or(hi >> 8, k.m_lo, k.c), k.off_lo);
+}
+
+// Q1_0: pair p (p < 16) of the chunk's 32 sign bits is (element p, element p + 16) as f16 +-1:
+// the inverted bits p and p + 16 shifted to bits 15 and 31 (the f16 sign bits) over 1.0, 1.0.
+__device__ __forceinline__ void w_pairs_q1(uint32_t q, const WConst &k, uint32_t *w)
+{
+    const uint32_t v = ~q;
+#pragma unroll
+    for (int p = 0; p < 16; ++p)
+        w[p] = and_or(v << (15 - p), k.m_lo, k.c);
+}
+
 // Dot chains of one chunk for one batch row: d[0] (two-sub-block formats: low-nibble chain d[0],
 // high d[1]).
 template <int FMT>
@@ -502,7 +558,41 @@ __device__ __forceinline__ void chunk_chains(const uint32_t (&w)[FMT == FQ8_0 ? 
 template <int FMT>
 __device__ __forceinline__ void x_pairs(const float4 *xv, float sc, uint32_t *p, float *z)
 {
-    if constexpr (FMT == FQ8_0) {
+    if constexpr (FMT == FQ1_0) {
+        // pair p: elements p and p + 16
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[4 * i + 0] = pack_h2(xv[i].x * sc, xv[4 + i].x * sc);
+            p[4 * i + 1] = pack_h2(xv[i].y * sc, xv[4 + i].y * sc);
+            p[4 * i + 2] = pack_h2(xv[i].z * sc, xv[4 + i].z * sc);
+            p[4 * i + 3] = pack_h2(xv[i].w * sc, xv[4 + i].w * sc);
+        }
+        z[0] = 0.f;
+    } else if constexpr (FMT == FAQ4) {
+        // dword k holds elements 8k..8k+7, element 2i in the low nibble of byte i: pairs
+        // (8k, 8k+4), (8k+1, 8k+5) / 16, (8k+2, 8k+6), (8k+3, 8k+7) / 16, the high-nibble pairs
+        // carrying 1/16 as the Q4 formats' do; z[0] the sum of the rounded, scaled x
+        const float sh = sc * 0.0625f;
+        float sa = 0.f, sb = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float4 a = xv[2 * k], b = xv[2 * k + 1];
+            p[4 * k + 0] = pack_h2(a.x * sc, b.x * sc);
+            p[4 * k + 1] = pack_h2(a.y * sh, b.y * sh);
+            p[4 * k + 2] = pack_h2(a.z * sc, b.z * sc);
+            p[4 * k + 3] = pack_h2(a.w * sh, b.w * sh);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const qg_h2 h = __builtin_bit_cast(qg_h2, p[4 * k + j]);
+                if (j & 1) {
+                    sb += (float)h.x; sb += (float)h.y;
+                } else {
+                    sa += (float)h.x; sa += (float)h.y;
+                }
+            }
+        }
+        z[0] = fmaf(sb, 16.0f, sa);
+    } else if constexpr (FMT == FQ8_0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             p[2 * i + 0] = pack_h2(xv[i].x * sc, xv[i].z * sc);
@@ -630,6 +720,13 @@ __device__ __forceinline__ void compute_group_h(const GroupBuf<FMT, CPL, MATS, R
                 kk.off_hi = h2_splat(-1024.0f - (fmt_q4(FMT) ? 16.0f : 1.0f) * cB);
                 resA = fmaf(cs.a, cA, -cs.b);
                 resB = fmaf(cs.a2, cB, -cs.b2);
+            } else if constexpr (FMT == FAQ4) {
+                // centred block (aq_center): pairs q - c' (high nibbles 16 (q - c')), and
+                // (s c' + c) times the chunk's x sum
+                const float cA = aq_center(cs.a, cs.b);
+                kk.off_lo = h2_splat(-1024.0f - cA);
+                kk.off_hi = h2_splat(-1024.0f - 16.0f * cA);
+                resA = fmaf(cs.a, cA, -cs.b);
             }
             if constexpr (fmt_hbits(FMT)) {
                 const uint32_t h0 = b.h[m][u][i][0];
@@ -638,6 +735,13 @@ __device__ __forceinline__ void compute_group_h(const GroupBuf<FMT, CPL, MATS, R
                 w_pairs_hb<FMT, 1>(q.y, h0, h1, kk, w + 4);
                 w_pairs_hb<FMT, 2>(q.z, h0, h1, kk, w + 8);
                 w_pairs_hb<FMT, 3>(q.w, h0, h1, kk, w + 12);
+            } else if constexpr (fmt_codebook(FMT)) {
+                w_pairs_cb(q.x, kk, kk.cb[m], w + 0);
+                w_pairs_cb(q.y, kk, kk.cb[m], w + 4);
+                w_pairs_cb(q.z, kk, kk.cb[m], w + 8);
+                w_pairs_cb(q.w, kk, kk.cb[m], w + 12);
+            } else if constexpr (FMT == FQ1_0) {
+                w_pairs_q1(q.x, kk, w);
             } else {
                 w_pairs<FMT>(q.x, kk, w + 0 * (NP / 4));
                 w_pairs<FMT>(q.y, kk, w + 1 * (NP / 4));
@@ -657,6 +761,9 @@ __device__ __forceinline__ void compute_group_h(const GroupBuf<FMT, CPL, MATS, R
                 } else if constexpr (FMT == FQ6_K) {
                     a = fmaf(cs.a, d[0], a);
                     a = fmaf(cs.a2, d[1], a);
+                } else if constexpr (FMT == FAQ4) {
+                    a = fmaf(cs.a, d[0], a);
+                    a = fmaf(resA, xh.z[r][i][0], a);
                 } else {
                     a = fmaf(cs.a, d[0], a);
                 }
@@ -707,7 +814,7 @@ void k_stream(GemvArgs a)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ks = wave % KS, team = wave / KS;
-    const int C = (int)(a.qs_row / 16);
+    const int C = (int)(a.qs_row / fmt_chunk_bytes(FMT));
     const int K4 = (int)(a.K / 4);
     float4 *X4 = lds4;                                              // x (norm: x * gamma)
     float *SS = reinterpret_cast<float *>(lds4 + (size_t)NB * K4);  // norm: float4 squares
@@ -727,12 +834,14 @@ void k_stream(GemvArgs a)
     const RowB rw{(uint32_t)a.qs_row, srow, (uint32_t)a.hb_row, (uint32_t)a.d_row};
     // one-load scales (see load_group): this lane's block scale of row u of a group is half
     // ssh[u] / 16 of the dword that lane sbp[u] / 4 loaded
-    constexpr bool SCW = KS == 1 && MATS == 1 && R == 2 && (FMT == FQ4_0 || FMT == FQ8_0);
+    constexpr bool SCW = KS == 1 && MATS == 1 && R == 2 &&
+                         (FMT == FQ4_0 || FMT == FQ8_0 || FMT == FIQ4_NL || FMT == FQ1_0);
     uint32_t sbp[R], ssh[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
         const uint32_t cx = (uint32_t)(lane < C ? lane : C - 1);
-        const uint32_t byte = u * srow + 2u * (FMT == FQ8_0 ? cx >> 1 : cx);
+        const uint32_t byte =
+            u * srow + 2u * (FMT == FQ8_0 ? cx >> 1 : FMT == FQ1_0 ? cx >> 2 : cx);
         sbp[u] = byte & ~3u;
         ssh[u] = (byte & 2u) * 8u;
     }
@@ -839,7 +948,17 @@ void k_stream(GemvArgs a)
         __builtin_amdgcn_s_sleep(1);
     asm volatile("" ::: "memory");
     XH<FMT, NB> xh;
-    const WConst wk = w_const<FMT>();
+    WConst wk = w_const<FMT>();
+    if constexpr (fmt_codebook(FMT)) {
+        const uint4 t0 = *reinterpret_cast<const uint4 *>(a.cb0);
+        wk.cb[0] = make_uint4(t0.x ^ 0x80808080u, t0.y ^ 0x80808080u, t0.z ^ 0x80808080u,
+                              t0.w ^ 0x80808080u);
+        if constexpr (MATS == 2) {
+            const uint4 t1 = *reinterpret_cast<const uint4 *>(a.cb1);
+            wk.cb[1] = make_uint4(t1.x ^ 0x80808080u, t1.y ^ 0x80808080u, t1.z ^ 0x80808080u,
+                                  t1.w ^ 0x80808080u);
+        }
+    }
     float un[NB];   // factor undoing the scale of this lane's x chunk, per batch row
     xh_from_lds<FMT, NB>(xh, un, X4, K4, C, cme);
     // the row factor this lane's reported item takes: 1 / rms of its batch row with the norm,

@@ -428,10 +428,13 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float *part, const in
 
 static StreamFn stream_fn(int fmt, int epi, bool nrm, int ks, int nb, int pd)
 {
-    if (fmt_hbits(fmt)) {
+    if (fmt_hbits(fmt) || fmt_generic(fmt)) {
         const void *fn = nullptr;
         int threads = 0;
-        stream_fn_x(fmt, epi, nrm, ks, nb, pd, &fn, &threads);
+        if (fmt_hbits(fmt))
+            stream_fn_x(fmt, epi, nrm, ks, nb, pd, &fn, &threads);
+        else
+            stream_fn_g(fmt, epi, nrm, ks, nb, pd, &fn, &threads);
         return {fn, threads};
     }
     return fmt == FQ4_0 ? stream_fn_fmt<FQ4_0>(epi, nrm, ks, nb, pd)

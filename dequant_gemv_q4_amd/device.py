@@ -19,14 +19,20 @@ def to_device(a, device="cuda") -> torch.Tensor:
     return torch.from_numpy(a).to(device)
 
 
-def pack(fmt: int, w_gguf, N: int, K: int, device="cuda", stream=None) -> torch.Tensor:
-    """GGUF-native blocks (numpy uint8 [N, row_bytes] or a device tensor) -> packed device buffer."""
+def pack(fmt: int, w_gguf, N: int, K: int, device="cuda", stream=None,
+         codebook=None) -> torch.Tensor:
+    """GGUF-native blocks (numpy uint8 [N, row_bytes] or a device tensor) -> packed device buffer.
+
+    codebook: the 16 signed entries of the IQ4 formats (host values), None for the others."""
     src = w_gguf if isinstance(w_gguf, torch.Tensor) else to_device(w_gguf, device)
     nbytes = B.qgemv_packed_bytes(fmt, N, K)
     if nbytes < 0:
         raise ValueError(f"invalid format/shape for packing: fmt={fmt} N={N} K={K}")
     out = torch.empty(nbytes, dtype=torch.uint8, device=src.device)
-    B.qgemv_pack(fmt, src, N, K, out, stream=stream)
+    if codebook is None:
+        B.qgemv_pack(fmt, src, N, K, out, stream=stream)
+    else:
+        B.qgemv_pack_codebook(fmt, src, N, K, codebook, out, stream=stream)
     return out
 
 

@@ -9,8 +9,10 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  - Formats (GGUF type ids): QG_Q4_0 = 2, QG_Q5_0 = 6, QG_Q8_0 = 8, QG_Q4_K = 12,
- *    QG_Q5_K = 13, QG_Q6_K = 14 ("Crate inferencelayer" docs, the gemv_*_lcpp_src family).
+ *  - Formats (GGUF type ids where GGUF has one): QG_Q4_0 = 2, QG_Q5_0 = 6, QG_Q8_0 = 8,
+ *    QG_Q4_K = 12, QG_Q5_K = 13, QG_Q6_K = 14, QG_IQ4_NL = 20, QG_IQ4_XS = 23, and two ids of
+ *    this library's own, QG_Q1_0 = 40 and QG_AQ4 = 41 ("Crate inferencelayer" docs, the
+ *    gemv_*_lcpp_src family; the affine Q4 of "Module gpu").
  *      Q4_0: 32 weights in 18 B (f16 d, 16 B nibbles), w = (q - 8) * d.
  *      Q5_0: 32 weights in 22 B (f16 d, 4 B of fifth bits, 16 B nibbles), w = d * (q - 16),
  *            q = nib | bit << 4 (element j: bit j).
@@ -21,7 +23,21 @@
  *            nibbles; sub-block s takes bit s of qh[l]), w = d * sc_j * q - dmin * m_j.
  *      Q6_K: 256 weights in 210 B (128 B low nibbles, 64 B high bit pairs, 16 signed scales,
  *            f16 d), w = d * sc * (q - 32) with one scale per 16 weights.
- *    Routed experts (qgemv_moe) take Q4_0, Q8_0 and Q4_K.
+ *      IQ4_NL: 32 weights in 18 B (f16 d, 16 B of 4-bit indices in Q4_0's nibble order),
+ *            w = d * cb[q] with cb a 16-entry table of signed bytes (gemv_iq4_nl_k_lcpp_src).
+ *      IQ4_XS: 256 weights in 136 B (f16 d, a 16-bit word of high scale bits (sub-block s at
+ *            bits 2s, 2s+1), 4 B of low 4-bit scales (sub-block s at bits 4s..4s+3), 128 B of
+ *            indices, 16 B per 32-weight sub-block), w = d * (ls - 32) * cb[q]
+ *            (gemv_iq4_xs_k_lcpp_src).
+ *      Q1_0: 128 weights in 18 B (f16 d, 16 B of sign bits: bit i % 8 of byte i / 8 for
+ *            element i), w = +d for a set bit, -d for a clear one (gemv_q1_k_lcpp_src).
+ *      AQ4:  32 weights in 20 B (f16 scale s, f16 bias c, 16 B nibbles: element 2i the low
+ *            nibble of byte i, 2i + 1 its high nibble), w = s * q + c ("Module gpu", struct Q).
+ *    The field orders and bit orders of IQ4_NL, IQ4_XS, Q1_0 and AQ4 are this library's reading
+ *    of pages that name the formats without printing their layout.  The IQ4 formats' codebook
+ *    is an input (qgemv_pack_codebook), stored inside the packed matrix.
+ *    Routed experts (qgemv_moe) take Q4_0, Q8_0 and Q4_K; the row-batch GEMM (qgemm) Q4_0 and
+ *    Q8_0.
  *  - W arguments of the compute entry points are in the PACKED device layout written by
  *    qgemv_pack (same bytes per weight as GGUF, split into planes so every hot load is an
  *    aligned 16-byte load).  Rows are in output order; K is the reduction length.  A W buffer
@@ -54,7 +70,8 @@
 extern "C" {
 #endif
 
-enum { QG_Q4_0 = 2, QG_Q5_0 = 6, QG_Q8_0 = 8, QG_Q4_K = 12, QG_Q5_K = 13, QG_Q6_K = 14 };
+enum { QG_Q4_0 = 2, QG_Q5_0 = 6, QG_Q8_0 = 8, QG_Q4_K = 12, QG_Q5_K = 13, QG_Q6_K = 14,
+       QG_IQ4_NL = 20, QG_IQ4_XS = 23, QG_Q1_0 = 40, QG_AQ4 = 41 };
 
 enum {
     QG_OK = 0,
@@ -83,7 +100,8 @@ enum { QG_ACT_SILU = 0, QG_ACT_GELU_TANH = 1 };
 
 /* Bytes of the packed device layout of an N x K matrix, or -1 if (fmt, N, K) is invalid.
  * Equal to the GGUF byte count rounded up to 256 B per plane (two planes: quants and scales; the
- * Q5 formats add a plane of fifth bits, Q6_K one of high bit pairs and one of its d values).
+ * Q5 formats add a plane of fifth bits, Q6_K one of high bit pairs and one of its d values, the
+ * IQ4 formats 256 B that hold the 16-byte codebook).
  * Host-only, no HIP call. */
 int64_t qgemv_packed_bytes(int fmt, int64_t N, int64_t K);
 
@@ -92,8 +110,18 @@ int64_t qgemv_packed_bytes(int fmt, int64_t N, int64_t K);
  * qgemv_packed_bytes bytes, 256-B aligned).  A pure byte move, done once per matrix; the
  * analogue of the pad/re-layout passes of "Crate inferencelayer" (q8_0_pad_blocks,
  * q6k_pad_blocks).  Both pointers are device pointers and must not overlap.  For Q4_K expert
- * stacks pass N = n_exp * rows. */
+ * stacks pass N = n_exp * rows.  The IQ4 formats need their codebook: qgemv_pack returns
+ * QG_ERR_NULL for them; use qgemv_pack_codebook. */
 int qgemv_pack(int fmt, const void *w_gguf, int64_t N, int64_t K, void *w_packed, void *stream);
+
+/* qgemv_pack with the 16-entry codebook of the IQ4 formats ("Crate inferencelayer",
+ * gemv_iq4_nl_k_lcpp_src: a nonlinear table of signed values applied as the weights are read).
+ * codebook is a HOST pointer to 16 signed bytes (entry q = codebook[q]), copied before the call
+ * returns and stored inside w_packed, so every later call on that matrix uses it.  Required
+ * (QG_ERR_NULL if NULL) for QG_IQ4_NL and QG_IQ4_XS; ignored, and may be NULL, for the other
+ * formats. */
+int qgemv_pack_codebook(int fmt, const void *w_gguf, int64_t N, int64_t K, const int8_t *codebook,
+                        void *w_packed, void *stream);
 
 /* Workspace bytes an operation needs for these sizes (0 if none), or -1 on invalid sizes.
  * n_exp and topk are read only for QG_OP_MOE.  Host-only. */

@@ -29,7 +29,8 @@ def test_every_header_function_is_exported(lib):
 
 def test_packed_bytes_equal_gguf_bytes():
     for fmt, bw, bb in ((q.Q4_0, 32, 18), (q.Q8_0, 32, 34), (q.Q4_K, 256, 144), (q.Q5_0, 32, 22),
-                        (q.Q5_K, 256, 176), (q.Q6_K, 256, 210)):
+                        (q.Q5_K, 256, 176), (q.Q6_K, 256, 210), (q.IQ4_NL, 32, 18),
+                        (q.IQ4_XS, 256, 136), (q.Q1_0, 128, 18), (q.AQ4, 32, 20)):
         for N, K in ((1024, 1024), (65536, 2048), (2048, 8192), (16, 256)):
             gguf = N * K // bw * bb
             got = q.qgemv_packed_bytes(fmt, N, K)
@@ -42,6 +43,9 @@ def test_packed_bytes_rejects_bad_shapes():
     assert q.qgemv_packed_bytes(q.Q4_K, 16, 512 + 32) == -1  # K not a multiple of 256
     assert q.qgemv_packed_bytes(q.Q4_0, 0, 64) == -1
     assert q.qgemv_packed_bytes(7, 16, 64) == -1
+    assert q.qgemv_packed_bytes(q.IQ4_XS, 16, 512 + 32) == -1
+    assert q.qgemv_packed_bytes(q.Q1_0, 16, 64) == -1        # K not a multiple of 128
+    assert q.qgemv_packed_bytes(q.AQ4, 16, 48) == -1
 
 
 def test_workspace_sizes():
@@ -106,6 +110,18 @@ def test_other_entry_points_validate(lib):
     assert lib.qgemv_pack(3, A256, 64, 64, A256 + (1 << 20), None) == 2
     assert lib.qgemv_pack(q.Q4_0, A256, 64, 64, A256 + (1 << 20) + 128, None) == 4
     assert lib.qgemv_pack(q.Q4_0, A256, 64, 64, A256, None) == 7
+    # the codebook formats need their codebook; the others ignore it
+    for fmt in (q.IQ4_NL, q.IQ4_XS):
+        assert lib.qgemv_pack(fmt, A256, 64, 256, A256 + (1 << 20), None) == 1
+        assert lib.qgemv_pack_codebook(fmt, A256, 64, 256, None, A256 + (1 << 20), None) == 1
+    cb = (ctypes.c_int8 * 16)(*range(-8, 8))
+    assert lib.qgemv_pack_codebook(q.IQ4_NL, A256, 64, 256, ctypes.addressof(cb),
+                                   A256 + (1 << 20) + 128, None) == 4
+    # routed experts take Q4_0, Q8_0 and Q4_K only
+    ws = A256 + (1 << 26)
+    for fmt in (q.IQ4_NL, q.IQ4_XS, q.Q1_0, q.AQ4, q.Q5_0, q.Q6_K):
+        assert lib.qgemv_moe(fmt, A256, 4, 64, 256, X16, 2, Y16 + 8192, Y16 + 16384, 2, Y16, ws,
+                             1 << 20, None) == 2
 
 
 def test_status_strings():
