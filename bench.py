@@ -157,7 +157,8 @@ def make_gemv(warm, nb, rows=65536, hidden=2048, fmt=None):
     a = w.arrays
     if fmt != q.Q4_0:
         a = dict(a, W=wl.matrix(fmt, wl.rng(3, wl.T_W), w.N, w.K))
-    Wp = D.pack(fmt, a["W"], w.N, w.K)
+    cb = wl.iq4_codebook() if fmt in (q.IQ4_NL, q.IQ4_XS) else None
+    Wp = D.pack(fmt, a["W"], w.N, w.K, codebook=cb)
     R = _copies(Wp.numel(), warm)
     sets = _rotated(Wp, R)
     x = D.to_device(a["x"])
@@ -168,6 +169,8 @@ def make_gemv(warm, nb, rows=65536, hidden=2048, fmt=None):
 
     def cpu():
         import oracle
+        if cb is not None:
+            oracle.set_codebook(cb)
         oracle.qgemv(fmt, a["W"], w.N, w.K, a["x"])
         return a["W"].nbytes
 
@@ -610,7 +613,8 @@ def main():
         extras["lm_head_nb1"] = run_extra("lm_head", lambda: make_lm_head(False, 1), es, ew, torch)
         import dequant_gemv_q4_amd as qq
         for f, nm in ((qq.Q8_0, "q8_0"), (qq.Q4_K, "q4_k"), (qq.Q5_0, "q5_0"), (qq.Q5_K, "q5_k"),
-                      (qq.Q6_K, "q6_k")):
+                      (qq.Q6_K, "q6_k"), (qq.IQ4_NL, "iq4_nl"), (qq.IQ4_XS, "iq4_xs"),
+                      (qq.Q1_0, "q1_0"), (qq.AQ4, "aq4")):
             extras[f"{nm}_gemv_nb1"] = run_extra(f"{nm} gemv", lambda f=f: make_gemv(False, 1, fmt=f),
                                                  es, ew, torch)
         for M in (64, 512, 2048):
