@@ -7,6 +7,9 @@
 
 #include <string.h>
 
+#include <mutex>
+#include <unordered_map>
+
 #include "../../include/qgemv.h"
 #include "qgemv_internal.h"
 
@@ -137,7 +140,7 @@ static bool plan_stream(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb
     if (!cpl)
         return false;
     const int mats = epi == E_GUS ? 2 : 1;
-    const int R = stream_rows(nb, 1, mats);
+    const int R = stream_rows_fmt(fmt, nb, 1, mats);
     const int64_t groups = (N + R - 1) / R;
     const int64_t items = (int64_t)R * nb;            // results per row group
     // tiles of up to QG_TILE_GROUPS groups, smaller when that leaves CUs without a tile
@@ -306,29 +309,103 @@ static GemvArgs gemv_args(const Layout &L, const void *W, int64_t N, int64_t K, 
     return a;
 }
 
-// Launch one member of the GEMV family: the streaming kernel when the shape allows it (a whole
-// wave per row), else the tiled kernel (any nb, any K).  An argmax launch is followed by the
-// one-workgroup fold of its per-workgroup partial keys.
+// The launch plan of one GEMV-family call: which kernel takes it and that kernel's plan.
+struct GemvPlan {
+    int kind;   // 0: matrix cores, 1: streaming, 2: K-tiled
+    MfmaPlan mp;
+    StreamPlan sp;
+    Plan p;
+};
+
+// Choose the kernel: the matrix-core kernel from QG_MFMA_MIN_NB batch rows when it takes the
+// shape, else the streaming kernel when the shape allows it (a whole wave per row), else the
+// tiled kernel (any nb, any K).  false: no kernel takes the shape.
+static bool plan_call(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb, GemvPlan *g)
+{
+    Layout L;
+    if (!layout(fmt, N, K, &L))
+        return false;
+    // the streaming and matrix kernels address each plane with 32-bit buffer offsets
+    const bool small = N * L.qs_row < QG_BUF_MAX && N * L.sc_row < QG_BUF_MAX &&
+                       N * L.hb_row < QG_BUF_MAX && N * L.d_row < QG_BUF_MAX;
+    if (small && nb >= QG_MFMA_MIN_NB && plan_mfma(fmt, epi, nrm, N, K, nb, &g->mp) &&
+        g->mp.grid <= QG_ARGMAX_MAX_GRID) {
+        g->kind = 0;
+        return true;
+    }
+    if (small && plan_stream(fmt, epi, nrm, N, K, nb, &g->sp)) {
+        g->kind = 1;
+        return true;
+    }
+    g->kind = 2;
+    return plan_gemv(fmt, N, K, nb, epi == E_GUS ? 2 : 1, &g->p);
+}
+
+// Plans are a function of (device, format, op, N, K, nb) alone, so they are kept: after the first
+// call of a shape, an eager call queries nothing from the device.
+struct PlanKey {
+    int dev, fmt, epi, nrm, nb;
+    int64_t N, K;
+    bool operator==(const PlanKey &o) const
+    {
+        return dev == o.dev && fmt == o.fmt && epi == o.epi && nrm == o.nrm && nb == o.nb &&
+               N == o.N && K == o.K;
+    }
+};
+struct PlanKeyHash {
+    size_t operator()(const PlanKey &k) const
+    {
+        uint64_t h = 1469598103934665603ull;
+        const int64_t v[7] = {k.dev, k.fmt, k.epi, k.nrm, k.nb, k.N, k.K};
+        for (int64_t x : v)
+            h = (h ^ (uint64_t)x) * 1099511628211ull;
+        return (size_t)h;
+    }
+};
+
+static bool cached_plan(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb, GemvPlan *g)
+{
+    static std::mutex mu;
+    static std::unordered_map<PlanKey, GemvPlan, PlanKeyHash> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return false;
+    const PlanKey key{dev, fmt, epi, nrm ? 1 : 0, nb, N, K};
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        auto it = cache.find(key);
+        if (it != cache.end()) {
+            *g = it->second;
+            return true;
+        }
+    }
+    if (!plan_call(fmt, epi, nrm, N, K, nb, g))
+        return false;
+    std::lock_guard<std::mutex> lk(mu);
+    if (cache.size() < 4096)   // a bound on the memory a stream of odd shapes can take
+        cache.emplace(key, *g);
+    return true;
+}
+
+// Launch one member of the GEMV family on the kernel its plan names.  An argmax launch is
+// followed by the one-workgroup fold of its per-workgroup partial keys.
 static int run_gemv(int fmt, int epi, bool nrm, GemvArgs a, void *stream)
 {
     int grid = 0, herr = 0;
-    StreamPlan sp;
-    MfmaPlan mp;
-    // the streaming and matrix kernels address each plane with 32-bit buffer offsets
-    const bool small = a.N * a.qs_row < QG_BUF_MAX && a.N * a.sc_row < QG_BUF_MAX &&
-                       a.N * a.hb_row < QG_BUF_MAX && a.N * a.d_row < QG_BUF_MAX;
-    if (small && a.nb >= QG_MFMA_MIN_NB && plan_mfma(fmt, epi, nrm, a.N, a.K, a.nb, &mp) &&
-        mp.grid <= QG_ARGMAX_MAX_GRID) {
+    GemvPlan g;
+    if (!cached_plan(fmt, epi, nrm, a.N, a.K, a.nb, &g))
+        return QG_ERR_SHAPE;
+    if (g.kind == 0) {
+        const MfmaPlan &mp = g.mp;
         grid = mp.grid;
         herr = launch_mfma(fmt, epi, nrm, mp, a, stream);
-    } else if (small && plan_stream(fmt, epi, nrm, a.N, a.K, a.nb, &sp)) {
+    } else if (g.kind == 1) {
+        const StreamPlan &sp = g.sp;
         grid = sp.grid;
         a.tg_log2 = sp.tg_log2;
         herr = launch_stream(fmt, epi, nrm, sp.cpl, sp.pd, a, sp.grid, sp.lds, stream);
     } else {
-        Plan p;
-        if (!plan_gemv(fmt, a.N, a.K, a.nb, epi == E_GUS ? 2 : 1, &p))
-            return QG_ERR_SHAPE;
+        const Plan &p = g.p;
         a.lpr_log2 = p.lpr_log2;
         a.kt = p.kt;
         a.n_kt = p.n_kt;

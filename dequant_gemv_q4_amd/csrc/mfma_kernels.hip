@@ -51,7 +51,8 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
     constexpr int BPS = FMT == FQ8_0 ? 2 : 4;   // blocks per step
     constexpr int MF_XR = 8 * KC;                // float4s of x a lane stages
     constexpr int KS = MF_WAVES / TPW;           // waves per tile
-    constexpr int PD = TPW >= 8 && MATS == 1 ? 4 : 2;   // steps in flight per wave
+    constexpr int PD = TPW >= 8 && MATS == 1 ? 4 : 2;   // steps in flight per wave (8: slower)
+    constexpr int SG = PD < 4 ? PD : 4;          // steps whose scales one load brings (SV)
     extern __shared__ float4 mf_lds[];
     __shared__ float s_rs[16];
     __shared__ unsigned long long s_best[16];
@@ -94,16 +95,21 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
     const int my_t = wave / KS, slice = wave % KS;
     const int nst = S > slice ? (S - 1 - slice) / KS + 1 : 0;   // this wave's steps per tile
 
-    // one step's loads: the lane's 16-byte chunk of its row and the step's block scales
+    // one step's loads: the lane's 16-byte chunk of its row and the step's block scales.  SV: the
+    // first step of a round of PD steps also loads the round's scales, lane (i, c) those of step
+    // k + c % PD of row i (one load instruction per round instead of one per step, each touching
+    // 16 scale lines); a step takes its scales from lane i + 16 (k % PD)
     struct StepBuf {
         uint32_t q[MATS][4];
         uint16_t s[MATS][BPS];        // per-block scale loads
-        uint32_t sw[MATS][BPS / 2];   // SV: the step's scales as loaded (two f16 per dword)
+        uint32_t sw[MATS][BPS / 2];   // SV: scales of step k + c % PD as loaded (two f16 a dword)
     };
-    auto load_step = [&](StepBuf &sb, int64_t n, int k) {
+    auto load_step = [&](StepBuf &sb, int64_t n, int k, bool round_first) {
         const int kk = k < nst ? k : nst - 1;              // past the wave's steps: its last
         const int st = slice + KS * (kk > 0 ? kk : 0);      // (a wave with none: a clamped chunk)
         const int ch = 4 * st + lc < C ? 4 * st + lc : C - 1;
+        const int ks = k + lc % SG < nst ? k + lc % SG : nst - 1;
+        const int sst = slice + KS * (ks > 0 ? ks : 0);     // the step whose scales this lane loads
 #pragma unroll
         for (int m = 0; m < MATS; ++m) {
             const auto v = __builtin_amdgcn_raw_buffer_load_b128(
@@ -112,7 +118,9 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
             if constexpr (SV) {
                 // raw dwords: halves are split where they are used, so that no instruction
                 // touches the load's result before its step is computed
-                const int so = (int)((uint32_t)n * (uint32_t)a.sc_row + 2u * BPS * (uint32_t)st);
+                if (!round_first)   // known at compile time where the loop is unrolled
+                    continue;
+                const int so = (int)((uint32_t)n * (uint32_t)a.sc_row + 2u * BPS * (uint32_t)sst);
                 if constexpr (BPS == 4) {
                     const auto w = __builtin_amdgcn_raw_buffer_load_b64(rsc[m], so, 0, QG_WCPOL);
                     sb.sw[m][0] = w[0];
@@ -136,14 +144,16 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
         const int64_t r = t * 16 + ir;
         return r < a.N ? r : a.N - 1;
     };
-    // the first group's first PD steps go out before x is converted
+    // the first group's first PD steps go out once this wave's x has arrived
     StepBuf sbuf[PD];
     const int64_t grp0 = blockIdx.x;
+    auto issue_first = [&]() {
 #pragma unroll
-    for (int p = 0; p < PD; ++p) {
-        load_step(sbuf[p], tile_row(grp0), p);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+        for (int p = 0; p < PD; ++p) {
+            load_step(sbuf[p], tile_row(grp0), p, p % SG == 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
     if constexpr (NRM) {
         if (tid < K4)
             G4[tid] = gone;
@@ -193,6 +203,11 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
         const float sc = inv * ldexpf(1.0f, sk), sh = sc * 0.0625f;
         if (lane == 0)
             s_rs[wave] = ldexpf(1.0f, -sk);
+        // the first weight loads go out once this wave's x has arrived (x requests first in the
+        // memory queues), before its conversion
+        __builtin_amdgcn_sched_barrier(0);
+        issue_first();
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < MF_XR; ++i) {
             const int f = lane + 64 * i;
@@ -214,7 +229,8 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
 
     const MfConst kc = mf_const<FMT>();
     // one step: transpose, B operands, one MFMA per block, scaled accumulation
-    auto compute = [&](const StepBuf &sb, int k, float (&acc)[MATS][4]) {
+    auto compute = [&](const StepBuf &sb, const uint32_t (&scl)[MATS][BPS / 2], int k,
+                       float (&acc)[MATS][4]) {
         const int st = slice + KS * k;
 #pragma unroll
         for (int m = 0; m < MATS; ++m) {
@@ -223,12 +239,14 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
 #pragma unroll
             for (int b = 0; b < BPS; ++b) {
                 const int blk = BPS * st + b;
-                const uint16_t sbits = SV ? (uint16_t)(sb.sw[m][b >> 1] >> (16 * (b & 1)))
-                                          : sb.s[m][b];
-                const float d = blk < KB ? (float)__builtin_bit_cast(_Float16, sbits) : 0.f;
+                // SV: K is a whole number of steps, so every block of a step exists
+                const float d =
+                    SV ? (float)__builtin_bit_cast(
+                             _Float16, (uint16_t)(scl[m][b >> 1] >> (16 * (b & 1))))
+                       : blk < KB ? (float)__builtin_bit_cast(_Float16, sb.s[m][b]) : 0.f;
                 const mh8 bop = FMT == FQ8_0 ? mf_bop<FMT>(q[2 * b], q[2 * b + 1], kc)
                                              : mf_bop<FMT>(q[b], 0u, kc);
-                const int blc = blk < KB ? blk : KB - 1;
+                const int blc = SV || blk < KB ? blk : KB - 1;
                 const mh8 aop = *reinterpret_cast<const mh8 *>(
                     XA + ((size_t)(blc * 4 + lc) * 16 + ir) * 16);
                 const mf4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -267,25 +285,30 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
         if (grp != grp0) {
 #pragma unroll
             for (int p = 0; p < PD; ++p)
-                load_step(sbuf[p], n, p);
+                load_step(sbuf[p], n, p, p % SG == 0);
         }
         // rounds of PD steps (the loop has one exit, at the end of a round); a step past the
         // wave's own is skipped, its buffer re-loaded with the wave's last step
         for (int k = 0; k < nst; k += PD) {
+            uint32_t scl[PD][MATS][BPS / 2];
 #pragma unroll
             for (int p = 0; p < PD; ++p) {
-                float t[MATS][4];
+                // at the first step of a scale group, its steps' scales: step p + j's from lane
+                // ir + 16 j of the group's first buffer (before that buffer is loaded again)
+                if (p % SG == 0)
 #pragma unroll
-                for (int m = 0; m < MATS; ++m)
-                    t[m][0] = t[m][1] = t[m][2] = t[m][3] = 0.f;
+                    for (int j = 0; j < SG; ++j)
+#pragma unroll
+                        for (int m = 0; m < MATS; ++m)
+#pragma unroll
+                            for (int d = 0; d < BPS / 2; ++d)
+                                scl[p + j][m][d] =
+                                    SV ? (uint32_t)__builtin_amdgcn_ds_bpermute(
+                                             (ir + 16 * j) << 2, (int)sbuf[p].sw[m][d])
+                                       : 0u;
                 if (k + p < nst)
-                    compute(sbuf[p], k + p, t);
-#pragma unroll
-                for (int m = 0; m < MATS; ++m)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[m][r] += t[m][r];
-                load_step(sbuf[p], n, k + p + PD);
+                    compute(sbuf[p], scl[p], k + p, acc);
+                load_step(sbuf[p], n, k + p + PD, p % SG == 0);
             }
         }
         const int64_t tile = grp * TPW + my_t;

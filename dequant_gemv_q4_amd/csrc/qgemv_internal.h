@@ -135,6 +135,13 @@ __host__ __device__ constexpr int stream_rows(int nb, int cpl, int mats)
                           ? (mats == 1 ? QG_R_NB1 : (QG_R_NB1 + 1) / 2) / cpl : 1)
                    : (cpl == 1 ? 2 : 1);
 }
+// Rows per group of the GEMV streaming kernel for a format: Q1_0's lane chunks are 4 bytes, so its
+// groups take four times the rows (the same bytes per group as the 16-byte formats; the per-group
+// reduction and epilogue are spread over four times the weights).
+__host__ __device__ constexpr int stream_rows_fmt(int fmt, int nb, int cpl, int mats)
+{
+    return stream_rows(nb, cpl, mats) * (fmt == FQ1_0 ? 4 : 1);
+}
 
 // LDS bytes of one staged x tile of nb rows and kt elements (float4 region, then block sums).
 __host__ __device__ constexpr size_t lds_tile_bytes(int fmt, int nb, int kt)

@@ -92,7 +92,7 @@ constexpr int pow2_ceil(int v) { return v <= 1 ? 1 : 2 * pow2_ceil((v + 1) / 2);
 // Compile-time shape of the streaming kernels.  KS: waves that share one row.
 template <int FMT, int NB, int CPL, int MATS, int KS = 1>
 struct SP {
-    static constexpr int R = stream_rows(NB, CPL, MATS);
+    static constexpr int R = stream_rows_fmt(FMT, NB, CPL, MATS);
     static constexpr int XF4 = Fc<FMT>::XF4, CE = Fc<FMT>::CE, NS = Fc<FMT>::NS;
     // waves per SIMD the register budget must allow (at most 512 / WPE VGPRs per lane): a row
     // batch of 2..4 on one matrix with one wave per row holds its x pairs in about 120 VGPRs,
@@ -432,6 +432,13 @@ __device__ __forceinline__ WConst w_const()
     k.off_hi = FMT == FQ4_0 ? 0xE480E480u : fmt_hbits(FMT) ? k.off_lo : 0xE400E400u;
     k.m_nb = 0x0F0F0F0Fu;                                  // the nibbles of four bytes
     k.m_hb = FMT == FQ6_K ? 0x30303030u : 0x10101010u;     // their high bits' places
+    if constexpr (fmt_codebook(FMT)) {
+        // codebook lookups (cb_pairs): bit 2 of each byte, the identity byte selectors, and the
+        // high byte of f16 1024 + u in every byte
+        k.m_hi = 0x04040404u;
+        k.c = 0x03020100u;
+        k.m_nb = 0x64646464u;
+    }
     k.cb[0] = k.cb[1] = make_uint4(0u, 0u, 0u, 0u);
     asm volatile("" : "+v"(k.m_lo), "+v"(k.m_hi), "+v"(k.c), "+v"(k.off_lo), "+v"(k.off_hi),
                  "+v"(k.m_nb), "+v"(k.m_hb));
@@ -497,16 +504,25 @@ __device__ __forceinline__ void w_pairs_hb(uint32_t q, uint32_t h0, uint32_t h1,
 
 // Codebook formats: the pairs of dword q of a chunk in Q4_0's pair order (low-nibble entries of
 // bytes 0, 2; high-nibble entries of bytes 0, 2; low 1, 3; high 1, 3).  T holds every entry
-// + 128 as an unsigned byte, so a looked-up byte becomes its pair half as Q8_0's bytes do
-// (mantissa of 1024, then -1152): exact signed entries.
+// + 128 as an unsigned byte; four indices are looked up as in cb_lookup (entries 0-7 and 8-15 by
+// one permute each, with bit 3 of the index dropped, then a per-byte choice by bit 3, taken from
+// q itself), and two permutes then place bytes 0, 2 and 1, 3 of the result under the byte 0x64:
+// f16 1024 + entry + 128, from which the exact signed entry is one packed add away (-1152).
+__device__ __forceinline__ void cb_pairs(uint32_t idx7, uint32_t b3, const WConst &k,
+                                         const uint4 &T, uint32_t &w02, uint32_t &w13)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(T.y, T.x, idx7);
+    const uint32_t hi = __builtin_amdgcn_perm(T.w, T.z, idx7);
+    const uint32_t r = __builtin_amdgcn_perm(hi, lo, and_or(b3, k.m_hi, k.c));
+    w02 = h2_add(__builtin_amdgcn_perm(k.m_nb, r, 0x04020400u), k.off_lo);
+    w13 = h2_add(__builtin_amdgcn_perm(k.m_nb, r, 0x04030401u), k.off_lo);
+}
+
 __device__ __forceinline__ void w_pairs_cb(uint32_t q, const WConst &k, const uint4 &T, uint32_t *w)
 {
-    const uint32_t lo = cb_lookup(T, q & 0x0F0F0F0Fu);
-    const uint32_t hi = cb_lookup(T, (q >> 4) & 0x0F0F0F0Fu);
-    w[0] = h2_add(and_or(lo, k.m_lo, k.c), k.off_lo);
-    w[1] = h2_add(and_or(hi, k.m_lo, k.c), k.off_lo);
-    w[2] = h2_add(and_or(lo >> 8, k.m_lo, k.c), k.off_lo);
-    w[3] = h2_add(and_or(hi >> 8, k.m_lo, k.c), k.off_lo);
+    // bit 3 of each low nibble moved to bit 2 of its byte (q >> 1), of each high nibble (q >> 5)
+    cb_pairs(q & 0x07070707u, q >> 1, k, T, w[0], w[2]);
+    cb_pairs((q >> 4) & 0x07070707u, q >> 5, k, T, w[1], w[3]);
 }
 
 // Q1_0: pair p (p < 16) of the chunk's 32 sign bits is (element p, element p + 16) as f16 +-1:
@@ -834,8 +850,9 @@ void k_stream(GemvArgs a)
     const RowB rw{(uint32_t)a.qs_row, srow, (uint32_t)a.hb_row, (uint32_t)a.d_row};
     // one-load scales (see load_group): this lane's block scale of row u of a group is half
     // ssh[u] / 16 of the dword that lane sbp[u] / 4 loaded
-    constexpr bool SCW = KS == 1 && MATS == 1 && R == 2 &&
-                         (FMT == FQ4_0 || FMT == FQ8_0 || FMT == FIQ4_NL || FMT == FQ1_0);
+    constexpr bool SCW = KS == 1 && MATS == 1 &&
+                         (((FMT == FQ4_0 || FMT == FQ8_0 || FMT == FIQ4_NL) && R == 2) ||
+                          (FMT == FQ1_0 && R == 8));
     uint32_t sbp[R], ssh[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
