@@ -6,7 +6,8 @@
 // B[8 (l / 16) + 0..7][l % 16], and D[4 (l / 16) + 0..3][l % 16].  A k position may be any block
 // element as long as A and B agree, so the eight halves a lane holds for one block are the eight
 // elements of one dword of quant bytes (Q4_0: bytes 4j..4j+3, their low and high nibbles; Q8_0:
-// bytes 4j..4j+3 of both 16-byte halves of the block), and x is laid out to match (mf_slot).
+// bytes 4j..4j+3 of both 16-byte halves of the block; Q4_K: the low (or high) nibbles of bytes
+// 4j..4j+3 of the sub-block's two 16-byte chunks), and x is laid out to match (mf_slot).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -83,7 +84,7 @@ __device__ __forceinline__ void mf_slot(int eb, int &j, int &h, bool &hi)
 {
     const int second = eb >= 16, e = eb & 15, t = e & 3;
     j = e >> 2;
-    if constexpr (FMT == FQ8_0) {
+    if constexpr (FMT == FQ8_0 || FMT == FQ4_K) {
         // halves: [b0, b2, b1, b3] of half 0, then of half 1
         h = 4 * second + (t == 0 ? 0 : t == 2 ? 1 : t == 1 ? 2 : 3);
         hi = false;
@@ -92,6 +93,32 @@ __device__ __forceinline__ void mf_slot(int eb, int &j, int &h, bool &hi)
         h = (t & 1) * 4 + second * 2 + (t >> 1);
         hi = second;
     }
+}
+
+// Q4_K B operand of one 32-weight sub-block: the low nibbles of dwords q0 and q1 (the sub-block's
+// two 16-byte chunks; a high-nibble sub-block passes q >> 4) as the exact centred weights n - c,
+// with off the f16 pair -(1024 + c) (mf_splat_off).  Halves: [b0, b2, b1, b3] of q0, then of q1.
+__device__ __forceinline__ mh8 mf_bop_k(uint32_t q0, uint32_t q1, uint32_t off, const MfConst &k)
+{
+    struct W4 {
+        uint32_t v[4];
+    } p = {{mf_hadd(mf_and_or(q0, k.m_lo, k.c), off), mf_hadd(mf_and_or(q0 >> 8, k.m_lo, k.c), off),
+            mf_hadd(mf_and_or(q1, k.m_lo, k.c), off), mf_hadd(mf_and_or(q1 >> 8, k.m_lo, k.c), off)}};
+    return __builtin_bit_cast(mh8, p);
+}
+
+// The f16 pair -(1024 + c), c an integer in [0, 63] (exact).
+__device__ __forceinline__ uint32_t mf_splat_off(float c)
+{
+    const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)(-1024.0f - c));
+    return h | (h << 16);
+}
+
+// All-ones B operand (sums of the A operand's k values).
+__device__ __forceinline__ mh8 kc_ones()
+{
+    const _Float16 o = (_Float16)1.0f;
+    return mh8{o, o, o, o, o, o, o, o};
 }
 
 // 4 x 4 transpose of dwords across the four 16-lane rows: register r of lane row c holds dword
@@ -114,7 +141,7 @@ __device__ __forceinline__ void mf_xpose(uint32_t (&v)[4])
 template <int FMT>
 __device__ __forceinline__ int mf_elem(int j, int h, bool &hi)
 {
-    if constexpr (FMT == FQ8_0) {
+    if constexpr (FMT == FQ8_0 || FMT == FQ4_K) {
         // halves: [b0, b2, b1, b3] of half 0, then of half 1
         const int second = h >> 2, t4 = h & 3;
         const int t = t4 == 0 ? 0 : t4 == 1 ? 2 : t4 == 2 ? 1 : 3;

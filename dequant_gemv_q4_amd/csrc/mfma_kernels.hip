@@ -21,6 +21,14 @@
 // step s; a 4 x 4 transpose of dwords across the four 16-lane rows (v_permlane32_swap, then
 // v_permlane16_swap) leaves in lane (i, j) dword j of each of the four chunks: the B operands of
 // the step's four blocks (Q4_0) or two blocks (Q8_0).
+//
+// Q4_K ("Crate inferencelayer" docs, gemv_q4_k_lcpp_src; w = d sc q - dmin m per 32-weight
+// sub-block): a step is half a super-block, four 16-byte chunks; chunks 2p and 2p + 1 hold one
+// sub-block in their low nibbles and the next in their high nibbles, so each sub-block is one
+// 32-k product over the low (or high) nibbles of dword j of the two chunks.  Its weights are
+// centred as on the vector path (k_center: B = q - c, exact) and the term (a c - b) sum x comes
+// from a second product of the same x with all-ones weights; the x sums are those of the f16 x
+// the products use.
 #include <hip/hip_runtime.h>
 
 #include "mfma_common.h"
@@ -48,7 +56,8 @@ template <int FMT, int EPI, bool NRM, int KC, int TPW, bool SV>
 __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
 {
     constexpr int MATS = EPI == E_GUS ? 2 : 1;
-    constexpr int BPS = FMT == FQ8_0 ? 2 : 4;   // blocks per step
+    constexpr int BPS = FMT == FQ8_0 ? 2 : 4;   // blocks (Q4_K: 32-weight sub-blocks) per step
+    constexpr int SW = FMT == FQ4_K ? 4 : BPS / 2;   // scale dwords of a step (Q4_K: its header)
     constexpr int MF_XR = 8 * KC;                // float4s of x a lane stages
     constexpr int KS = MF_WAVES / TPW;           // waves per tile
     constexpr int PD = TPW >= 8 && MATS == 1 ? 4 : 2;   // steps in flight per wave (8: slower)
@@ -102,7 +111,8 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
     struct StepBuf {
         uint32_t q[MATS][4];
         uint16_t s[MATS][BPS];        // per-block scale loads
-        uint32_t sw[MATS][BPS / 2];   // SV: scales of step k + c % PD as loaded (two f16 a dword)
+        uint32_t sw[MATS][SW];        // SV: scales of step k + c % PD as loaded (two f16 a dword;
+                                      // Q4_K: the 16-byte header of the step's super-block)
     };
     auto load_step = [&](StepBuf &sb, int64_t n, int k, bool round_first) {
         const int kk = k < nst ? k : nst - 1;              // past the wave's steps: its last
@@ -120,6 +130,16 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
                 // touches the load's result before its step is computed
                 if (!round_first)   // known at compile time where the loop is unrolled
                     continue;
+                if constexpr (FMT == FQ4_K) {
+                    // two steps per super-block
+                    const int so = (int)((uint32_t)n * (uint32_t)a.sc_row + 16u * (uint32_t)(sst >> 1));
+                    const auto w = __builtin_amdgcn_raw_buffer_load_b128(rsc[m], so, 0, QG_WCPOL);
+                    sb.sw[m][0] = w[0];
+                    sb.sw[m][1] = w[1];
+                    sb.sw[m][2] = w[2];
+                    sb.sw[m][3] = w[3];
+                    continue;
+                }
                 const int so = (int)((uint32_t)n * (uint32_t)a.sc_row + 2u * BPS * (uint32_t)sst);
                 if constexpr (BPS == 4) {
                     const auto w = __builtin_amdgcn_raw_buffer_load_b64(rsc[m], so, 0, QG_WCPOL);
@@ -229,13 +249,45 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
 
     const MfConst kc = mf_const<FMT>();
     // one step: transpose, B operands, one MFMA per block, scaled accumulation
-    auto compute = [&](const StepBuf &sb, const uint32_t (&scl)[MATS][BPS / 2], int k,
+    auto compute = [&](const StepBuf &sb, const uint32_t (&scl)[MATS][SW], int k,
                        float (&acc)[MATS][4]) {
         const int st = slice + KS * k;
 #pragma unroll
         for (int m = 0; m < MATS; ++m) {
             uint32_t q[4] = {sb.q[m][0], sb.q[m][1], sb.q[m][2], sb.q[m][3]};
             mf_xpose(q);
+            if constexpr (FMT == FQ4_K) {
+                // the step is half h of super-block st / 2: its chunks 4h + b (b < 4).  Chunk pair
+                // (4h + 2p, 4h + 2p + 1) holds sub-block 4h + 2p in its low nibbles (the pair's
+                // 32 weights, lane (i, j) dword j of each) and 4h + 2p + 1 in its high nibbles.
+                // Centred weights (k_center): B = q - c exact; the offset term (a c - b) sum x
+                // comes from a second product with all-ones weights (sum of the same f16 x)
+                const uint4 hdr = make_uint4(scl[m][0], scl[m][1], scl[m][2], scl[m][3]);
+                const int half = st & 1;
+#pragma unroll
+                for (int p2 = 0; p2 < 2; ++p2) {
+                    const ChunkScale cs = chunk_scale<FQ4_K>(hdr, 4 * half + 2 * p2);
+                    const uint32_t q0 = q[2 * p2], q1 = q[2 * p2 + 1];
+#pragma unroll
+                    for (int hi = 0; hi < 2; ++hi) {
+                        const float a_ = hi ? cs.a2 : cs.a, b_ = hi ? cs.b2 : cs.b;
+                        const float c = k_center(a_, b_);
+                        const mh8 bop = mf_bop_k(hi ? q0 >> 4 : q0, hi ? q1 >> 4 : q1,
+                                                 mf_splat_off(c), kc);
+                        const int blk = 8 * (st >> 1) + 4 * half + 2 * p2 + hi;
+                        const mh8 aop = *reinterpret_cast<const mh8 *>(
+                            XA + ((size_t)(blk * 4 + lc) * 16 + ir) * 16);
+                        const mf4 zero = {0.f, 0.f, 0.f, 0.f};
+                        const mf4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, zero, 0, 0, 0);
+                        const mf4 Sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, kc_ones(), zero, 0, 0, 0);
+                        const float res = fmaf(a_, c, -b_);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[m][r] = fmaf(res, Sx[r], fmaf(a_, D[r], acc[m][r]));
+                    }
+                }
+                continue;
+            }
 #pragma unroll
             for (int b = 0; b < BPS; ++b) {
                 const int blk = BPS * st + b;
@@ -290,7 +342,7 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
         // rounds of PD steps (the loop has one exit, at the end of a round); a step past the
         // wave's own is skipped, its buffer re-loaded with the wave's last step
         for (int k = 0; k < nst; k += PD) {
-            uint32_t scl[PD][MATS][BPS / 2];
+            uint32_t scl[PD][MATS][SW];
 #pragma unroll
             for (int p = 0; p < PD; ++p) {
                 // at the first step of a scale group, its steps' scales: step p + j's from lane
@@ -301,7 +353,7 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
 #pragma unroll
                         for (int m = 0; m < MATS; ++m)
 #pragma unroll
-                            for (int d = 0; d < BPS / 2; ++d)
+                            for (int d = 0; d < SW; ++d)
                                 scl[p + j][m][d] =
                                     SV ? (uint32_t)__builtin_amdgcn_ds_bpermute(
                                              (ir + 16 * j) << 2, (int)sbuf[p].sw[m][d])
@@ -374,7 +426,11 @@ static const void *mfma_fn_tpw(int tpw)
 template <int FMT, int EPI, bool NRM, int KC>
 static const void *mfma_fn_sv(bool sv, int tpw)
 {
-    return sv ? mfma_fn_tpw<FMT, EPI, NRM, KC, true>(tpw) : mfma_fn_tpw<FMT, EPI, NRM, KC, false>(tpw);
+    if constexpr (FMT == FQ4_K)   // a whole number of super-blocks: always whole steps
+        return sv ? mfma_fn_tpw<FMT, EPI, NRM, KC, true>(tpw) : nullptr;
+    else
+        return sv ? mfma_fn_tpw<FMT, EPI, NRM, KC, true>(tpw)
+                  : mfma_fn_tpw<FMT, EPI, NRM, KC, false>(tpw);
 }
 
 template <int FMT, int EPI, bool NRM>
@@ -408,7 +464,8 @@ static const void *mfma_fn_fmt(int epi, bool nrm, int kc, bool sv, int tpw)
 static const void *mfma_fn(int fmt, int epi, bool nrm, int kc, bool sv, int tpw)
 {
     return fmt == FQ4_0 ? mfma_fn_fmt<FQ4_0>(epi, nrm, kc, sv, tpw)
-         : fmt == FQ8_0 ? mfma_fn_fmt<FQ8_0>(epi, nrm, kc, sv, tpw) : nullptr;
+         : fmt == FQ8_0 ? mfma_fn_fmt<FQ8_0>(epi, nrm, kc, sv, tpw)
+         : fmt == FQ4_K ? mfma_fn_fmt<FQ4_K>(epi, nrm, kc, sv, tpw) : nullptr;
 }
 
 // Plan of the row-batch kernel: K class (1: K <= 2048, 2: K <= 4096), tiles per group (16 / waves
@@ -416,12 +473,12 @@ static const void *mfma_fn(int fmt, int epi, bool nrm, int kc, bool sv, int tpw)
 // for the staged x, LDS).
 bool plan_mfma(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb, MfmaPlan *p)
 {
-    if (fmt != FQ4_0 && fmt != FQ8_0)
+    if (fmt != FQ4_0 && fmt != FQ8_0 && fmt != FQ4_K)
         return false;
     if (nb < 1 || nb > 16 || K > MF_KMAX || N < 1)
         return false;
     p->kc = K <= 2048 ? 1 : 2;
-    p->sv = fmt == FQ4_0 ? K % 128 == 0 : K % 64 == 0;
+    p->sv = fmt == FQ4_0 ? K % 128 == 0 : fmt == FQ8_0 ? K % 64 == 0 : true;
     const int mats = epi == E_GUS ? 2 : 1;
     p->lds = (size_t)(K / 32) * 1024 + (size_t)MF_WAVES * mats * 4 * 64 * 4;
     // one workgroup per CU; enough tiles per group that the groups fill the CUs once, at most
