@@ -45,7 +45,8 @@
  *    after each plane (whole dwords of the scale plane), never past it.
  *  - Every pointer of a compute call is a DEVICE pointer (HIP device memory).  The caller owns
  *    all memory; the library never allocates or frees and carries no data from one call to the
- *    next (on the host it caches per-device occupancy queries, which only shape launches).
+ *    next (on the host it caches per-device occupancy queries and launch plans, which only shape
+ *    launches).
  *  - x is f32 [nb][K], outputs f32 [nb][N], all row-major and contiguous.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every call only
  *    enqueues work on that stream and returns; nothing synchronizes the host.
