@@ -38,6 +38,7 @@ __device__ __forceinline__ uint32_t mf_hadd(uint32_t a, uint32_t b)
 
 struct MfConst {
     uint32_t m_lo, m_hi, c, off_lo, off_hi;
+    uint32_t m_b, m_nb, m_sel, c_id, c64;   // byte mask, nibble mask, codebook lookup constants
 };
 
 template <int FMT>
@@ -49,7 +50,16 @@ __device__ __forceinline__ MfConst mf_const()
     k.c = 0x64006400u;
     k.off_lo = FMT == FQ8_0 ? 0xE480E480u : 0xE408E408u;   // -1152 (Q8_0) / -1032 (n - 8)
     k.off_hi = 0xE480E480u;                                // -1152: 16 n - 128
+    k.m_b = 0x00FF00FFu;
+    k.m_nb = 0x0F0F0F0Fu;
+    k.m_sel = 0x04040404u;
+    k.c_id = 0x03020100u;
+    k.c64 = 0x64646464u;
     asm volatile("" : "+v"(k.m_lo), "+v"(k.m_hi), "+v"(k.c), "+v"(k.off_lo), "+v"(k.off_hi));
+    if constexpr (FMT == FQ5_0 || FMT == FQ5_K)
+        asm volatile("" : "+v"(k.m_b), "+v"(k.m_nb));
+    if constexpr (fmt_codebook(FMT))
+        asm volatile("" : "+v"(k.m_sel), "+v"(k.c_id), "+v"(k.c64));
     return k;
 }
 
@@ -82,16 +92,27 @@ __device__ __forceinline__ mh8 mf_bop(uint32_t q0, uint32_t q1, const MfConst &k
 template <int FMT>
 __device__ __forceinline__ void mf_slot(int eb, int &j, int &h, bool &hi)
 {
+    if constexpr (FMT == FAQ4) {
+        // dword j holds elements 8j..8j+7, element 8j + 2m + u in nibble u of byte m; halves:
+        // [lo b0, lo b2, hi b0, hi b2, lo b1, lo b3, hi b1, hi b3] (high nibbles held x16)
+        const int r = eb & 7, m = r >> 1, u = r & 1;
+        j = eb >> 3;
+        h = (m & 1) * 4 + u * 2 + (m >> 1);
+        hi = u != 0;
+        return;
+    }
     const int second = eb >= 16, e = eb & 15, t = e & 3;
     j = e >> 2;
-    if constexpr (FMT == FQ8_0 || FMT == FQ4_K) {
-        // halves: [b0, b2, b1, b3] of half 0, then of half 1
-        h = 4 * second + (t == 0 ? 0 : t == 2 ? 1 : t == 1 ? 2 : 3);
-        hi = false;
-    } else {
+    if constexpr (FMT == FQ4_0) {
         // halves: [lo b0, lo b2, hi b0, hi b2, lo b1, lo b3, hi b1, hi b3]
         h = (t & 1) * 4 + second * 2 + (t >> 1);
         hi = second;
+    } else {
+        // byte-like formats (Q8_0; nibbles joined with high bits, codebook entries, K-quant
+        // sub-blocks over two chunks): halves [b0, b2, b1, b3] of the first 16 elements'
+        // dword, then of the second 16's
+        h = 4 * second + (t == 0 ? 0 : t == 2 ? 1 : t == 1 ? 2 : 3);
+        hi = false;
     }
 }
 
@@ -107,7 +128,7 @@ __device__ __forceinline__ mh8 mf_bop_k(uint32_t q0, uint32_t q1, uint32_t off, 
     return __builtin_bit_cast(mh8, p);
 }
 
-// The f16 pair -(1024 + c), c an integer in [0, 63] (exact).
+// The f16 pair -(1024 + c), c an integer in [0, 1023] (exact).
 __device__ __forceinline__ uint32_t mf_splat_off(float c)
 {
     const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)(-1024.0f - c));
@@ -119,6 +140,76 @@ __device__ __forceinline__ mh8 kc_ones()
 {
     const _Float16 o = (_Float16)1.0f;
     return mh8{o, o, o, o, o, o, o, o};
+}
+
+// The affine format's sum operand: 1 at low-nibble positions, 16 at high-nibble ones (whose x
+// the A operand holds / 16), so the product is the plain sum of the block's x.
+__device__ __forceinline__ mh8 mf_ones_q4()
+{
+    const _Float16 o = (_Float16)1.0f, s = (_Float16)16.0f;
+    return mh8{o, o, s, s, o, o, s, s};
+}
+
+// B operand of four weight bytes per half: bytes 0, 2 and 1, 3 of u0, then of u1, each in the
+// mantissa of 1024.0 and moved by the f16 pair off (exact).
+__device__ __forceinline__ mh8 mf_bop_bytes(uint32_t u0, uint32_t u1, uint32_t off, const MfConst &k)
+{
+    struct W4 {
+        uint32_t v[4];
+    } p = {{mf_hadd(mf_and_or(u0, k.m_b, k.c), off), mf_hadd(mf_and_or(u0 >> 8, k.m_b, k.c), off),
+            mf_hadd(mf_and_or(u1, k.m_b, k.c), off), mf_hadd(mf_and_or(u1 >> 8, k.m_b, k.c), off)}};
+    return __builtin_bit_cast(mh8, p);
+}
+
+// Q5 formats: dword j of a chunk's nibbles joined with their fifth bits (h: the chunk's high-bit
+// word as packed, the bit of the low nibble of byte 4k + m at bit 8m + k, of the high nibble at
+// 8m + 4 + k) into four bytes: the low nibbles (mf_join5_lo) or the high ones (mf_join5_hi).
+__device__ __forceinline__ uint32_t mf_join5_lo(uint32_t q, uint32_t h, int j)
+{
+    return mf_and_or(q, 0x0F0F0F0Fu, (h << (4 - j)) & 0x10101010u);
+}
+__device__ __forceinline__ uint32_t mf_join5_hi(uint32_t q, uint32_t h, int j)
+{
+    return mf_and_or(q >> 4, 0x0F0F0F0Fu, (h >> j) & 0x10101010u);
+}
+
+// IQ4 formats: the codebook entries of four indices (bits 0-2 in idx7, bit 3 at bit 2 of each
+// byte of b3) from the table T (entries + 128), as the two f16 pairs (bytes 0, 2) and (1, 3),
+// exact signed entries: entries 0-7 and 8-15 by one permute each, a third picks per byte, two
+// more place the bytes under 0x64 (f16 1024 + u), one packed add each removes 1152.
+__device__ __forceinline__ void mf_cb_pairs(uint32_t idx7, uint32_t b3, const uint4 &T,
+                                            const MfConst &k, uint32_t &w02, uint32_t &w13)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(T.y, T.x, idx7);
+    const uint32_t hi = __builtin_amdgcn_perm(T.w, T.z, idx7);
+    const uint32_t r = __builtin_amdgcn_perm(hi, lo, mf_and_or(b3, k.m_sel, k.c_id));
+    w02 = mf_hadd(__builtin_amdgcn_perm(k.c64, r, 0x04020400u), 0xE480E480u);
+    w13 = mf_hadd(__builtin_amdgcn_perm(k.c64, r, 0x04030401u), 0xE480E480u);
+}
+
+// B operand of an IQ4 block from dword j of its chunk: entries of the low nibbles (elements
+// 4j..4j+3), then of the high nibbles (16 + 4j..): the byte-like half order.
+__device__ __forceinline__ mh8 mf_bop_cb(uint32_t q, const uint4 &T, const MfConst &k)
+{
+    struct W4 {
+        uint32_t v[4];
+    } p;
+    mf_cb_pairs(q & 0x07070707u, q >> 1, T, k, p.v[0], p.v[1]);
+    mf_cb_pairs((q >> 4) & 0x07070707u, q >> 5, T, k, p.v[2], p.v[3]);
+    return __builtin_bit_cast(mh8, p);
+}
+
+// Affine Q4 B operand of dword j (elements 8j..8j+7): Q4_0's pair order with the centring offsets
+// off_lo = -(1024 + c), off_hi = -(1024 + 16 c): exact q - c and 16 (q - c).
+__device__ __forceinline__ mh8 mf_bop_aq(uint32_t q, uint32_t off_lo, uint32_t off_hi,
+                                         const MfConst &k)
+{
+    const uint32_t t = q >> 8;
+    struct W4 {
+        uint32_t v[4];
+    } p = {{mf_hadd(mf_and_or(q, k.m_lo, k.c), off_lo), mf_hadd(mf_and_or(q, k.m_hi, k.c), off_hi),
+            mf_hadd(mf_and_or(t, k.m_lo, k.c), off_lo), mf_hadd(mf_and_or(t, k.m_hi, k.c), off_hi)}};
+    return __builtin_bit_cast(mh8, p);
 }
 
 // 4 x 4 transpose of dwords across the four 16-lane rows: register r of lane row c holds dword
@@ -141,7 +232,8 @@ __device__ __forceinline__ void mf_xpose(uint32_t (&v)[4])
 template <int FMT>
 __device__ __forceinline__ int mf_elem(int j, int h, bool &hi)
 {
-    if constexpr (FMT == FQ8_0 || FMT == FQ4_K) {
+    static_assert(FMT != FAQ4, "the affine layout has no inverse here");
+    if constexpr (FMT != FQ4_0) {
         // halves: [b0, b2, b1, b3] of half 0, then of half 1
         const int second = h >> 2, t4 = h & 3;
         const int t = t4 == 0 ? 0 : t4 == 1 ? 2 : t4 == 2 ? 1 : 3;

@@ -56,12 +56,19 @@ template <int FMT, int EPI, bool NRM, int KC, int TPW, bool SV>
 __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
 {
     constexpr int MATS = EPI == E_GUS ? 2 : 1;
-    constexpr int BPS = FMT == FQ8_0 ? 2 : 4;   // blocks (Q4_K: 32-weight sub-blocks) per step
-    constexpr int SW = FMT == FQ4_K ? 4 : BPS / 2;   // scale dwords of a step (Q4_K: its header)
+    constexpr int BPS = FMT == FQ8_0 ? 2 : 4;   // blocks (K-quants: 32-weight sub-blocks) per step
+    // scale dwords of a step: the f16 d of its blocks (two a dword), the K-quants' 16-byte
+    // header, IQ4_XS's 8-byte header, the affine format's (s, c) per block
+    constexpr int SW = fmt_min(FMT) || FMT == FAQ4 ? 4 : FMT == FQ8_0 ? 1 : 2;
+    // high-bit dwords of a step (Q5_0, Q5_K: one per chunk)
+    constexpr int HW = FMT == FQ5_0 || FMT == FQ5_K ? 4 : 0;
+    constexpr int AW = SW + HW;                  // dwords a step takes from its round's loads
     constexpr int MF_XR = 8 * KC;                // float4s of x a lane stages
     constexpr int KS = MF_WAVES / TPW;           // waves per tile
     constexpr int PD = TPW >= 8 && MATS == 1 ? 4 : 2;   // steps in flight per wave (8: slower)
-    constexpr int SG = PD < 4 ? PD : 4;          // steps whose scales one load brings (SV)
+    // steps whose scales one load brings (SV); the gated product holds two matrices' loads and
+    // keeps one step per load (registers)
+    constexpr int SG = MATS == 2 ? 1 : PD < 4 ? PD : 4;
     extern __shared__ float4 mf_lds[];
     __shared__ float s_rs[16];
     __shared__ unsigned long long s_best[16];
@@ -93,12 +100,26 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
 
     const int ir = lane & 15, lc = lane >> 4;
     const uint32_t qbytes = (uint32_t)(a.N * a.qs_row), sbytes = (uint32_t)(a.N * a.sc_row);
-    __amdgpu_buffer_rsrc_t rq[MATS], rsc[MATS];
+    const uint32_t hbytes = (uint32_t)(a.N * a.hb_row);
+    __amdgpu_buffer_rsrc_t rq[MATS], rsc[MATS], rhb[MATS];
     rq[0] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.qs0), (short)0, (int)qbytes, 0x00020000);
     rsc[0] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.sc0), (short)0, (int)sbytes, 0x00020000);
+    rhb[0] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(HW ? a.hb0 : a.qs0), (short)0, (int)(HW ? hbytes : 0u), 0x00020000);
     if constexpr (MATS == 2) {
         rq[1] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.qs1), (short)0, (int)qbytes, 0x00020000);
         rsc[1] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.sc1), (short)0, (int)sbytes, 0x00020000);
+        rhb[1] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(HW ? a.hb1 : a.qs1), (short)0, (int)(HW ? hbytes : 0u), 0x00020000);
+    }
+    // IQ4 formats: each matrix's codebook, every entry + 128 as an unsigned byte
+    uint4 cbt[MATS];
+#pragma unroll
+    for (int m = 0; m < MATS; ++m) {
+        cbt[m] = make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (fmt_codebook(FMT)) {
+            const uint4 t = *reinterpret_cast<const uint4 *>(m == 0 ? a.cb0 : a.cb1);
+            cbt[m] = make_uint4(t.x ^ 0x80808080u, t.y ^ 0x80808080u, t.z ^ 0x80808080u,
+                                t.w ^ 0x80808080u);
+        }
     }
     const int64_t NT = (a.N + 15) / 16, G = (NT + TPW - 1) / TPW;
     const int my_t = wave / KS, slice = wave % KS;
@@ -111,8 +132,7 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
     struct StepBuf {
         uint32_t q[MATS][4];
         uint16_t s[MATS][BPS];        // per-block scale loads
-        uint32_t sw[MATS][SW];        // SV: scales of step k + c % PD as loaded (two f16 a dword;
-                                      // Q4_K: the 16-byte header of the step's super-block)
+        uint32_t sw[MATS][AW];        // SV: scales (then high bits) of step k + c % SG as loaded
     };
     auto load_step = [&](StepBuf &sb, int64_t n, int k, bool round_first) {
         const int kk = k < nst ? k : nst - 1;              // past the wave's steps: its last
@@ -130,9 +150,20 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
                 // touches the load's result before its step is computed
                 if (!round_first)   // known at compile time where the loop is unrolled
                     continue;
-                if constexpr (FMT == FQ4_K) {
-                    // two steps per super-block
-                    const int so = (int)((uint32_t)n * (uint32_t)a.sc_row + 16u * (uint32_t)(sst >> 1));
+                if constexpr (HW == 4) {
+                    // the high-bit words of the step's four chunks
+                    const int ho = (int)((uint32_t)n * (uint32_t)a.hb_row + 16u * (uint32_t)sst);
+                    const auto w = __builtin_amdgcn_raw_buffer_load_b128(rhb[m], ho, 0, QG_WCPOL);
+                    sb.sw[m][SW + 0] = w[0];
+                    sb.sw[m][SW + 1] = w[1];
+                    sb.sw[m][SW + 2] = w[2];
+                    sb.sw[m][SW + 3] = w[3];
+                }
+                if constexpr (SW == 4) {
+                    // K-quants: the header of super-block sst / 2 (two steps each); the affine
+                    // format: (s, c) of the step's four blocks
+                    const uint32_t off = fmt_min(FMT) ? 16u * (uint32_t)(sst >> 1) : 16u * (uint32_t)sst;
+                    const int so = (int)((uint32_t)n * (uint32_t)a.sc_row + off);
                     const auto w = __builtin_amdgcn_raw_buffer_load_b128(rsc[m], so, 0, QG_WCPOL);
                     sb.sw[m][0] = w[0];
                     sb.sw[m][1] = w[1];
@@ -140,7 +171,9 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
                     sb.sw[m][3] = w[3];
                     continue;
                 }
-                const int so = (int)((uint32_t)n * (uint32_t)a.sc_row + 2u * BPS * (uint32_t)sst);
+                // f16 d per block (IQ4_XS: the 8-byte header of super-block sst / 2)
+                const uint32_t off = FMT == FIQ4_XS ? 8u * (uint32_t)(sst >> 1) : 2u * BPS * (uint32_t)sst;
+                const int so = (int)((uint32_t)n * (uint32_t)a.sc_row + off);
                 if constexpr (BPS == 4) {
                     const auto w = __builtin_amdgcn_raw_buffer_load_b64(rsc[m], so, 0, QG_WCPOL);
                     sb.sw[m][0] = w[0];
@@ -249,14 +282,66 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
 
     const MfConst kc = mf_const<FMT>();
     // one step: transpose, B operands, one MFMA per block, scaled accumulation
-    auto compute = [&](const StepBuf &sb, const uint32_t (&scl)[MATS][SW], int k,
+    auto compute = [&](const StepBuf &sb, const uint32_t (&scl)[MATS][AW], int k,
                        float (&acc)[MATS][4]) {
         const int st = slice + KS * k;
+        const mf4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < MATS; ++m) {
             uint32_t q[4] = {sb.q[m][0], sb.q[m][1], sb.q[m][2], sb.q[m][3]};
             mf_xpose(q);
-            if constexpr (FMT == FQ4_K) {
+            if constexpr (FMT == FQ5_0 || fmt_codebook(FMT) || FMT == FAQ4) {
+                // one 32-weight block per chunk: lane (i, j) holds dword j of block b's chunk
+#pragma unroll
+                for (int b = 0; b < BPS; ++b) {
+                    const int blk = BPS * st + b;
+                    const mh8 aop = *reinterpret_cast<const mh8 *>(
+                        XA + ((size_t)(blk * 4 + lc) * 16 + ir) * 16);
+                    if constexpr (FMT == FAQ4) {
+                        // centred (aq_center): pairs q - c (high nibbles 16 (q - c)), and
+                        // (s c + bias) times the block's x sum (a product with weights 1 / 16)
+                        const uint32_t sc2 = scl[m][b];
+                        const float s_ = (float)__builtin_bit_cast(_Float16, (uint16_t)(sc2 & 0xffffu));
+                        const float nb_ = -(float)__builtin_bit_cast(_Float16, (uint16_t)(sc2 >> 16));
+                        const float c = aq_center(s_, nb_);
+                        const mh8 bop = mf_bop_aq(q[b], mf_splat_off(c), mf_splat_off(16.0f * c), kc);
+                        const mf4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, zero, 0, 0, 0);
+                        const mf4 Sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, mf_ones_q4(), zero, 0, 0, 0);
+                        const float res = fmaf(s_, c, -nb_);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[m][r] = fmaf(res, Sx[r], fmaf(s_, D[r], acc[m][r]));
+                        continue;
+                    }
+                    mh8 bop;
+                    if constexpr (FMT == FQ5_0) {
+                        const uint32_t h = scl[m][SW + b];
+                        bop = mf_bop_bytes(mf_join5_lo(q[b], h, lc), mf_join5_hi(q[b], h, lc),
+                                           0xE410E410u, kc);   // -1040: 1024 + q -> q - 16
+                    } else {
+                        bop = mf_bop_cb(q[b], cbt[m], kc);
+                    }
+                    float d;
+                    if constexpr (FMT == FIQ4_XS) {
+                        // header: f16 d, the high scale bits (sub-block s at bits 2s, 2s + 1 of
+                        // the next 16), then the low 4-bit scales (s at bits 4s..4s+3)
+                        const int sbk = 4 * (st & 1) + b;
+                        const uint32_t ls = ((scl[m][1] >> (4 * sbk)) & 15u) |
+                                            (((scl[m][0] >> (16 + 2 * sbk)) & 3u) << 4);
+                        d = (float)__builtin_bit_cast(_Float16, (uint16_t)(scl[m][0] & 0xffffu)) *
+                            (float)((int)ls - 32);
+                    } else {
+                        d = (float)__builtin_bit_cast(_Float16,
+                                                       (uint16_t)(scl[m][b >> 1] >> (16 * (b & 1))));
+                    }
+                    const mf4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, zero, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[m][r] = fmaf(d, D[r], acc[m][r]);
+                }
+                continue;
+            }
+            if constexpr (fmt_min(FMT)) {
                 // the step is half h of super-block st / 2: its chunks 4h + b (b < 4).  Chunk pair
                 // (4h + 2p, 4h + 2p + 1) holds sub-block 4h + 2p in its low nibbles (the pair's
                 // 32 weights, lane (i, j) dword j of each) and 4h + 2p + 1 in its high nibbles.
@@ -272,12 +357,20 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
                     for (int hi = 0; hi < 2; ++hi) {
                         const float a_ = hi ? cs.a2 : cs.a, b_ = hi ? cs.b2 : cs.b;
                         const float c = k_center(a_, b_);
-                        const mh8 bop = mf_bop_k(hi ? q0 >> 4 : q0, hi ? q1 >> 4 : q1,
-                                                 mf_splat_off(c), kc);
+                        mh8 bop;
+                        if constexpr (FMT == FQ5_K) {
+                            // nibbles joined with their fifth bits into bytes (0..31)
+                            const uint32_t h0 = scl[m][SW + 2 * p2], h1 = scl[m][SW + 2 * p2 + 1];
+                            bop = hi ? mf_bop_bytes(mf_join5_hi(q0, h0, lc), mf_join5_hi(q1, h1, lc),
+                                                    mf_splat_off(c), kc)
+                                     : mf_bop_bytes(mf_join5_lo(q0, h0, lc), mf_join5_lo(q1, h1, lc),
+                                                    mf_splat_off(c), kc);
+                        } else {
+                            bop = mf_bop_k(hi ? q0 >> 4 : q0, hi ? q1 >> 4 : q1, mf_splat_off(c), kc);
+                        }
                         const int blk = 8 * (st >> 1) + 4 * half + 2 * p2 + hi;
                         const mh8 aop = *reinterpret_cast<const mh8 *>(
                             XA + ((size_t)(blk * 4 + lc) * 16 + ir) * 16);
-                        const mf4 zero = {0.f, 0.f, 0.f, 0.f};
                         const mf4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, zero, 0, 0, 0);
                         const mf4 Sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, kc_ones(), zero, 0, 0, 0);
                         const float res = fmaf(a_, c, -b_);
@@ -342,7 +435,7 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
         // rounds of PD steps (the loop has one exit, at the end of a round); a step past the
         // wave's own is skipped, its buffer re-loaded with the wave's last step
         for (int k = 0; k < nst; k += PD) {
-            uint32_t scl[PD][MATS][SW];
+            uint32_t scl[PD][MATS][AW];
 #pragma unroll
             for (int p = 0; p < PD; ++p) {
                 // at the first step of a scale group, its steps' scales: step p + j's from lane
@@ -353,11 +446,12 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
 #pragma unroll
                         for (int m = 0; m < MATS; ++m)
 #pragma unroll
-                            for (int d = 0; d < SW; ++d)
+                            for (int d = 0; d < AW; ++d)
                                 scl[p + j][m][d] =
-                                    SV ? (uint32_t)__builtin_amdgcn_ds_bpermute(
-                                             (ir + 16 * j) << 2, (int)sbuf[p].sw[m][d])
-                                       : 0u;
+                                    !SV ? 0u
+                                    : SG == 1 ? sbuf[p].sw[m][d]
+                                              : (uint32_t)__builtin_amdgcn_ds_bpermute(
+                                                    (ir + 16 * j) << 2, (int)sbuf[p].sw[m][d]);
                 if (k + p < nst)
                     compute(sbuf[p], scl[p], k + p, acc);
                 load_step(sbuf[p], n, k + p + PD, p % SG == 0);
@@ -426,7 +520,7 @@ static const void *mfma_fn_tpw(int tpw)
 template <int FMT, int EPI, bool NRM, int KC>
 static const void *mfma_fn_sv(bool sv, int tpw)
 {
-    if constexpr (FMT == FQ4_K)   // a whole number of super-blocks: always whole steps
+    if constexpr (FMT != FQ4_0 && FMT != FQ8_0)   // these take whole steps only (sv)
         return sv ? mfma_fn_tpw<FMT, EPI, NRM, KC, true>(tpw) : nullptr;
     else
         return sv ? mfma_fn_tpw<FMT, EPI, NRM, KC, true>(tpw)
@@ -463,9 +557,17 @@ static const void *mfma_fn_fmt(int epi, bool nrm, int kc, bool sv, int tpw)
 
 static const void *mfma_fn(int fmt, int epi, bool nrm, int kc, bool sv, int tpw)
 {
-    return fmt == FQ4_0 ? mfma_fn_fmt<FQ4_0>(epi, nrm, kc, sv, tpw)
-         : fmt == FQ8_0 ? mfma_fn_fmt<FQ8_0>(epi, nrm, kc, sv, tpw)
-         : fmt == FQ4_K ? mfma_fn_fmt<FQ4_K>(epi, nrm, kc, sv, tpw) : nullptr;
+    switch (fmt) {
+    case FQ4_0: return mfma_fn_fmt<FQ4_0>(epi, nrm, kc, sv, tpw);
+    case FQ8_0: return mfma_fn_fmt<FQ8_0>(epi, nrm, kc, sv, tpw);
+    case FQ4_K: return mfma_fn_fmt<FQ4_K>(epi, nrm, kc, sv, tpw);
+    case FQ5_K: return mfma_fn_fmt<FQ5_K>(epi, nrm, kc, sv, tpw);
+    case FQ5_0: return mfma_fn_fmt<FQ5_0>(epi, nrm, kc, sv, tpw);
+    case FIQ4_NL: return mfma_fn_fmt<FIQ4_NL>(epi, nrm, kc, sv, tpw);
+    case FIQ4_XS: return mfma_fn_fmt<FIQ4_XS>(epi, nrm, kc, sv, tpw);
+    case FAQ4: return mfma_fn_fmt<FAQ4>(epi, nrm, kc, sv, tpw);
+    default: return nullptr;
+    }
 }
 
 // Plan of the row-batch kernel: K class (1: K <= 2048, 2: K <= 4096), tiles per group (16 / waves
@@ -473,12 +575,16 @@ static const void *mfma_fn(int fmt, int epi, bool nrm, int kc, bool sv, int tpw)
 // for the staged x, LDS).
 bool plan_mfma(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb, MfmaPlan *p)
 {
-    if (fmt != FQ4_0 && fmt != FQ8_0 && fmt != FQ4_K)
-        return false;
+    if (fmt != FQ4_0 && fmt != FQ8_0 && fmt != FQ4_K && fmt != FQ5_K && fmt != FQ5_0 &&
+        fmt != FIQ4_NL && fmt != FIQ4_XS && fmt != FAQ4)
+        return false;   // Q6_K (16-weight sub-blocks) and Q1_0 take the other kernels
     if (nb < 1 || nb > 16 || K > MF_KMAX || N < 1)
         return false;
     p->kc = K <= 2048 ? 1 : 2;
-    p->sv = fmt == FQ4_0 ? K % 128 == 0 : fmt == FQ8_0 ? K % 64 == 0 : true;
+    // whole steps: 128 weights (Q8_0: 64) per step
+    p->sv = fmt == FQ8_0 ? K % 64 == 0 : K % 128 == 0;
+    if (fmt != FQ4_0 && fmt != FQ8_0 && !p->sv)
+        return false;   // the other formats take whole steps only
     const int mats = epi == E_GUS ? 2 : 1;
     p->lds = (size_t)(K / 32) * 1024 + (size_t)MF_WAVES * mats * 4 * 64 * 4;
     // one workgroup per CU; enough tiles per group that the groups fill the CUs once, at most

@@ -160,10 +160,12 @@ def test_fused_ops_high_bit_formats(fmt, N, K, nb):
         assert i == m or yr[b, m] - yr[b, i] <= tol[b, m] + tol[b, i]
 
 
-def test_q5_k_centred_cancellation():
+@pytest.mark.parametrize("nb", [2, 9])
+def test_q5_k_centred_cancellation(nb):
     """Q5_K sub-blocks whose weights mostly sit at one value (d sc q = dmin m for the common q,
-    same-sign x): the centred arithmetic keeps the error relative to sum |w x|."""
-    say("q5_k cancellation")
+    same-sign x): the centred arithmetic keeps the error relative to sum |w x| (streaming and
+    matrix-core kernels)."""
+    say(f"q5_k cancellation nb={nb}")
     N, K = 48, 512
     g = wl.rng(2400, 1)
     W = wl.q5_k_matrix(g, N, K).reshape(N, -1, 176).copy()
@@ -179,7 +181,7 @@ def test_q5_k_centred_cancellation():
     W = W.reshape(N, -1)
     for j in range(8):
         assert oracle.q4k_scale_min(W[0, 4:16].tobytes(), j) == (1, 20)
-    x = g.uniform(0.9, 1.0, size=(2, K)).astype(np.float32)
+    x = g.uniform(0.9, 1.0, size=(nb, K)).astype(np.float32)
     y = _gemv(q.Q5_K, W, N, K, x)
     yr, A = oracle.gemv(q.Q5_K, W, N, K, x)
     assert_within(y, yr, tol_gemv(A, yr), "q5_k cancellation")

@@ -208,10 +208,11 @@ def test_fused_ops_new_formats(fmt, N, K, nb):
         assert i == m or yr[b, m] - yr[b, i] <= tol[b, m] + tol[b, i]
 
 
-def test_gate_and_up_keep_their_own_codebooks():
+@pytest.mark.parametrize("nb", [2, 6])
+def test_gate_and_up_keep_their_own_codebooks(nb):
     """The gated product reads each matrix's codebook from its own packed buffer."""
-    say("gus two codebooks")
-    fmt, N, K, nb = q.IQ4_NL, 96, 2048, 2
+    say(f"gus two codebooks nb={nb}")
+    fmt, N, K = q.IQ4_NL, 96, 2048
     g = wl.rng(3500, 1)
     W, Wu = wl.matrix(fmt, g, N, K), wl.matrix(fmt, g, N, K)
     x = wl.normal_f32(g, (nb, K))
