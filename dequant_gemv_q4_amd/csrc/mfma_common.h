@@ -18,6 +18,7 @@ namespace qg {
 
 typedef _Float16 mh2 __attribute__((ext_vector_type(2)));
 typedef _Float16 mh8 __attribute__((ext_vector_type(8)));
+typedef _Float16 mh4 __attribute__((ext_vector_type(4)));
 typedef float mf4 __attribute__((ext_vector_type(4)));
 
 constexpr int MF_WAVES = 16;             // waves per workgroup: one per batch row in the prologue
@@ -39,6 +40,7 @@ __device__ __forceinline__ uint32_t mf_hadd(uint32_t a, uint32_t b)
 struct MfConst {
     uint32_t m_lo, m_hi, c, off_lo, off_hi;
     uint32_t m_b, m_nb, m_sel, c_id, c64;   // byte mask, nibble mask, codebook lookup constants
+    uint32_t c1;                            // f16 pair (1.0, 1.0): Q1_0's sign pairs
 };
 
 template <int FMT>
@@ -55,9 +57,12 @@ __device__ __forceinline__ MfConst mf_const()
     k.m_sel = 0x04040404u;
     k.c_id = 0x03020100u;
     k.c64 = 0x64646464u;
+    k.c1 = 0x3C003C00u;
     asm volatile("" : "+v"(k.m_lo), "+v"(k.m_hi), "+v"(k.c), "+v"(k.off_lo), "+v"(k.off_hi));
-    if constexpr (FMT == FQ5_0 || FMT == FQ5_K)
+    if constexpr (FMT == FQ5_0 || FMT == FQ5_K || FMT == FQ6_K)
         asm volatile("" : "+v"(k.m_b), "+v"(k.m_nb));
+    if constexpr (FMT == FQ1_0)
+        asm volatile("" : "+v"(k.c1));
     if constexpr (fmt_codebook(FMT))
         asm volatile("" : "+v"(k.m_sel), "+v"(k.c_id), "+v"(k.c64));
     return k;
@@ -99,6 +104,13 @@ __device__ __forceinline__ void mf_slot(int eb, int &j, int &h, bool &hi)
         j = eb >> 3;
         h = (m & 1) * 4 + u * 2 + (m >> 1);
         hi = u != 0;
+        return;
+    }
+    if constexpr (FMT == FQ1_0) {
+        // lane column j takes elements 4j + t and 4j + t + 16 as the pair t (halves 2t, 2t + 1)
+        j = (eb & 15) >> 2;
+        h = 2 * (eb & 3) + (eb >> 4);
+        hi = false;
         return;
     }
     const int second = eb >= 16, e = eb & 15, t = e & 3;
@@ -232,7 +244,7 @@ __device__ __forceinline__ void mf_xpose(uint32_t (&v)[4])
 template <int FMT>
 __device__ __forceinline__ int mf_elem(int j, int h, bool &hi)
 {
-    static_assert(FMT != FAQ4, "the affine layout has no inverse here");
+    static_assert(FMT != FAQ4 && FMT != FQ1_0 && FMT != FQ6_K, "no inverse layout here");
     if constexpr (FMT != FQ4_0) {
         // halves: [b0, b2, b1, b3] of half 0, then of half 1
         const int second = h >> 2, t4 = h & 3;

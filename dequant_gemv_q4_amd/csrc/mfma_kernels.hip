@@ -56,13 +56,18 @@ template <int FMT, int EPI, bool NRM, int KC, int TPW, bool SV>
 __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
 {
     constexpr int MATS = EPI == E_GUS ? 2 : 1;
-    constexpr int BPS = FMT == FQ8_0 ? 2 : 4;   // blocks (K-quants: 32-weight sub-blocks) per step
+    // blocks (K-quants: 32-weight sub-blocks; Q6_K: 16-weight ones) per step
+    constexpr int BPS = FMT == FQ8_0 ? 2 : FMT == FQ6_K ? 8 : 4;
+    // Q1_0: the step's four sign words come with its round (16 bytes of a row per step)
+    constexpr int QW = FMT == FQ1_0 ? 4 : 0;
     // scale dwords of a step: the f16 d of its blocks (two a dword), the K-quants' 16-byte
-    // header, IQ4_XS's 8-byte header, the affine format's (s, c) per block
-    constexpr int SW = fmt_min(FMT) || FMT == FAQ4 ? 4 : FMT == FQ8_0 ? 1 : 2;
-    // high-bit dwords of a step (Q5_0, Q5_K: one per chunk)
-    constexpr int HW = FMT == FQ5_0 || FMT == FQ5_K ? 4 : 0;
-    constexpr int AW = SW + HW;                  // dwords a step takes from its round's loads
+    // header, IQ4_XS's 8-byte header, the affine format's (s, c) per block, Q6_K's eight signed
+    // scales and its f16 d, Q1_0's one f16 d
+    constexpr int SW = fmt_min(FMT) || FMT == FAQ4 ? 4 : FMT == FQ6_K ? 3
+                     : FMT == FQ8_0 || FMT == FQ1_0 ? 1 : 2;
+    // high-bit dwords of a step (Q5_0, Q5_K: one per chunk; Q6_K: two per chunk)
+    constexpr int HW = FMT == FQ5_0 || FMT == FQ5_K ? 4 : FMT == FQ6_K ? 8 : 0;
+    constexpr int AW = QW + SW + HW;             // dwords a step takes from its round's loads
     constexpr int MF_XR = 8 * KC;                // float4s of x a lane stages
     constexpr int KS = MF_WAVES / TPW;           // waves per tile
     constexpr int PD = TPW >= 8 && MATS == 1 ? 4 : 2;   // steps in flight per wave (8: slower)
@@ -75,7 +80,8 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int C = (int)(a.qs_row / 16), S = (C + 3) / 4, KB = (int)(a.K / 32);
+    // C: 16-byte pieces of a row; S: steps of 128 weights (Q8_0: 64)
+    const int C = (int)(a.qs_row / 16), S = FMT == FQ1_0 ? C : (C + 3) / 4, KB = (int)(a.K / 32);
     const int K4 = (int)(a.K / 4);
     uint8_t *XA = reinterpret_cast<uint8_t *>(mf_lds);                   // [KB][4][16] x 16 B
     float *PART = reinterpret_cast<float *>(XA + (size_t)KB * 1024);    // [16][MATS][4][64]
@@ -101,14 +107,17 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
     const int ir = lane & 15, lc = lane >> 4;
     const uint32_t qbytes = (uint32_t)(a.N * a.qs_row), sbytes = (uint32_t)(a.N * a.sc_row);
     const uint32_t hbytes = (uint32_t)(a.N * a.hb_row);
-    __amdgpu_buffer_rsrc_t rq[MATS], rsc[MATS], rhb[MATS];
+    const uint32_t dbytes = (uint32_t)(a.N * a.d_row);
+    __amdgpu_buffer_rsrc_t rq[MATS], rsc[MATS], rhb[MATS], rdd[MATS];
     rq[0] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.qs0), (short)0, (int)qbytes, 0x00020000);
     rsc[0] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.sc0), (short)0, (int)sbytes, 0x00020000);
     rhb[0] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(HW ? a.hb0 : a.qs0), (short)0, (int)(HW ? hbytes : 0u), 0x00020000);
+    rdd[0] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(FMT == FQ6_K ? a.dd0 : a.qs0), (short)0, (int)(FMT == FQ6_K ? dbytes : 0u), 0x00020000);
     if constexpr (MATS == 2) {
         rq[1] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.qs1), (short)0, (int)qbytes, 0x00020000);
         rsc[1] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.sc1), (short)0, (int)sbytes, 0x00020000);
         rhb[1] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(HW ? a.hb1 : a.qs1), (short)0, (int)(HW ? hbytes : 0u), 0x00020000);
+        rdd[1] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(FMT == FQ6_K ? a.dd1 : a.qs1), (short)0, (int)(FMT == FQ6_K ? dbytes : 0u), 0x00020000);
     }
     // IQ4 formats: each matrix's codebook, every entry + 128 as an unsigned byte
     uint4 cbt[MATS];
@@ -142,14 +151,43 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
         const int sst = slice + KS * (ks > 0 ? ks : 0);     // the step whose scales this lane loads
 #pragma unroll
         for (int m = 0; m < MATS; ++m) {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(
-                rq[m], (int)((uint32_t)n * (uint32_t)a.qs_row + 16u * (uint32_t)ch), 0, QG_WCPOL);
-            sb.q[m][0] = v[0]; sb.q[m][1] = v[1]; sb.q[m][2] = v[2]; sb.q[m][3] = v[3];
+            if constexpr (QW == 0) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+                    rq[m], (int)((uint32_t)n * (uint32_t)a.qs_row + 16u * (uint32_t)ch), 0, QG_WCPOL);
+                sb.q[m][0] = v[0]; sb.q[m][1] = v[1]; sb.q[m][2] = v[2]; sb.q[m][3] = v[3];
+            } else {
+                sb.q[m][0] = sb.q[m][1] = sb.q[m][2] = sb.q[m][3] = 0u;
+            }
             if constexpr (SV) {
                 // raw dwords: halves are split where they are used, so that no instruction
                 // touches the load's result before its step is computed
                 if (!round_first)   // known at compile time where the loop is unrolled
                     continue;
+                if constexpr (FMT == FQ1_0) {
+                    // the step's 16 bytes of sign words and its f16 d
+                    const auto w = __builtin_amdgcn_raw_buffer_load_b128(
+                        rq[m], (int)((uint32_t)n * (uint32_t)a.qs_row + 16u * (uint32_t)sst), 0, QG_WCPOL);
+                    sb.sw[m][0] = w[0]; sb.sw[m][1] = w[1]; sb.sw[m][2] = w[2]; sb.sw[m][3] = w[3];
+                    sb.sw[m][4] = __builtin_amdgcn_raw_buffer_load_b16(
+                        rsc[m], (int)((uint32_t)n * (uint32_t)a.sc_row + 2u * (uint32_t)sst), 0, QG_WCPOL);
+                    continue;
+                }
+                if constexpr (FMT == FQ6_K) {
+                    // the eight signed scales of half sst % 2 of super-block sst / 2, its d, and
+                    // the step's four chunks' high-bit word pairs
+                    const auto w = __builtin_amdgcn_raw_buffer_load_b64(
+                        rsc[m], (int)((uint32_t)n * (uint32_t)a.sc_row + 8u * (uint32_t)sst), 0, QG_WCPOL);
+                    sb.sw[m][0] = w[0];
+                    sb.sw[m][1] = w[1];
+                    sb.sw[m][2] = __builtin_amdgcn_raw_buffer_load_b16(
+                        rdd[m], (int)((uint32_t)n * (uint32_t)a.d_row + 2u * (uint32_t)(sst >> 1)), 0, QG_WCPOL);
+                    const int ho = (int)((uint32_t)n * (uint32_t)a.hb_row + 32u * (uint32_t)sst);
+                    const auto h0 = __builtin_amdgcn_raw_buffer_load_b128(rhb[m], ho, 0, QG_WCPOL);
+                    const auto h1 = __builtin_amdgcn_raw_buffer_load_b128(rhb[m], ho + 16, 0, QG_WCPOL);
+                    sb.sw[m][3] = h0[0]; sb.sw[m][4] = h0[1]; sb.sw[m][5] = h0[2]; sb.sw[m][6] = h0[3];
+                    sb.sw[m][7] = h1[0]; sb.sw[m][8] = h1[1]; sb.sw[m][9] = h1[2]; sb.sw[m][10] = h1[3];
+                    continue;
+                }
                 if constexpr (HW == 4) {
                     // the high-bit words of the step's four chunks
                     const int ho = (int)((uint32_t)n * (uint32_t)a.hb_row + 16u * (uint32_t)sst);
@@ -268,12 +306,22 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
                 const float e[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const int el = 4 * f + t, blk = el >> 5;
-                    int j, h;
-                    bool hi;
-                    mf_slot<FMT>(el & 31, j, h, hi);
-                    const _Float16 hv = (_Float16)(e[t] * (hi ? sh : sc));
-                    *reinterpret_cast<_Float16 *>(XA + (((size_t)(blk * 4 + j) * 16 + bx) * 8 + h) * 2) = hv;
+                    const int el = 4 * f + t;
+                    if constexpr (FMT == FQ6_K) {
+                        // 16-k products: [16-element block][lane column c][row][4 halves],
+                        // halves (b0, b2, b1, b3) of dword c
+                        const int b16 = el >> 4, c = (el >> 2) & 3, tt = el & 3;
+                        const int h = tt == 0 ? 0 : tt == 2 ? 1 : tt == 1 ? 2 : 3;
+                        *reinterpret_cast<_Float16 *>(XA + (((size_t)(b16 * 4 + c) * 16 + bx) * 4 + h) * 2) =
+                            (_Float16)(e[t] * sc);
+                    } else {
+                        const int blk = el >> 5;
+                        int j, h;
+                        bool hi;
+                        mf_slot<FMT>(el & 31, j, h, hi);
+                        const _Float16 hv = (_Float16)(e[t] * (hi ? sh : sc));
+                        *reinterpret_cast<_Float16 *>(XA + (((size_t)(blk * 4 + j) * 16 + bx) * 8 + h) * 2) = hv;
+                    }
                 }
             }
         }
@@ -288,8 +336,67 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
         const mf4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < MATS; ++m) {
+            if constexpr (FMT == FQ1_0) {
+                // four 32-weight blocks of one scale: the products chain in the accumulator.
+                // Lane (i, c) takes elements 4c + t and 4c + t + 16 (t < 4) of each block as the
+                // pair t: the inverted sign bits shifted to the f16 sign bits over 1.0, 1.0
+                mf4 D = zero;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t w = ~scl[m][b];
+                    struct W4 {
+                        uint32_t v[4];
+                    } p;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        p.v[t] = mf_and_or(w << (15 - 4 * lc - t), 0x80008000u, kc.c1);
+                    const mh8 aop = *reinterpret_cast<const mh8 *>(
+                        XA + ((size_t)((4 * st + b) * 4 + lc) * 16 + ir) * 16);
+                    D = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, __builtin_bit_cast(mh8, p), D, 0, 0, 0);
+                }
+                const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(scl[m][4] & 0xffffu));
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[m][r] = fmaf(d, D[r], acc[m][r]);
+                continue;
+            }
             uint32_t q[4] = {sb.q[m][0], sb.q[m][1], sb.q[m][2], sb.q[m][3]};
             mf_xpose(q);
+            if constexpr (FMT == FQ6_K) {
+                // the step is half n of super-block st / 2: chunk u (< 4) holds the 16-weight
+                // sub-block u of the half in its low nibbles (scale u) and u + 4 in its high ones;
+                // lane (i, j) has dword j of each chunk: k = 4j..4j+3 of a 16-k product.  Six-bit
+                // values: nibble | two high bits << 4, then q - 32 exact
+                const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(scl[m][2] & 0xffffu));
+                const int rot = (2 * lc + 28) & 31;   // bits 8m + 2j, +1 -> 8m + 4, 8m + 5
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t h0 = scl[m][3 + 2 * u], h1 = scl[m][4 + 2 * u];
+                    const uint32_t lo = mf_and_or(q[u], 0x0F0F0F0Fu,
+                                                  __builtin_amdgcn_alignbit(h0, h0, rot) & 0x30303030u);
+                    const uint32_t hi = mf_and_or(q[u] >> 4, 0x0F0F0F0Fu,
+                                                  __builtin_amdgcn_alignbit(h1, h1, rot) & 0x30303030u);
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const uint32_t by = half ? hi : lo;
+                        struct W2 {
+                            uint32_t v[2];
+                        } p = {{mf_hadd(mf_and_or(by, kc.m_b, kc.c), 0xE420E420u),
+                                mf_hadd(mf_and_or(by >> 8, kc.m_b, kc.c), 0xE420E420u)}};
+                        const int b16 = 16 * (st >> 1) + 8 * (st & 1) + 4 * half + u;
+                        const mh4 aop = *reinterpret_cast<const mh4 *>(
+                            XA + ((size_t)(b16 * 4 + lc) * 16 + ir) * 8);
+                        const mf4 D = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                            aop, __builtin_bit_cast(mh4, p), zero, 0, 0, 0);
+                        const float sv = (float)(int8_t)((scl[m][half] >> (8 * u)) & 0xffu);
+                        const float a_ = d * sv;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[m][r] = fmaf(a_, D[r], acc[m][r]);
+                    }
+                }
+                continue;
+            }
             if constexpr (FMT == FQ5_0 || fmt_codebook(FMT) || FMT == FAQ4) {
                 // one 32-weight block per chunk: lane (i, j) holds dword j of block b's chunk
 #pragma unroll
@@ -566,6 +673,8 @@ static const void *mfma_fn(int fmt, int epi, bool nrm, int kc, bool sv, int tpw)
     case FIQ4_NL: return mfma_fn_fmt<FIQ4_NL>(epi, nrm, kc, sv, tpw);
     case FIQ4_XS: return mfma_fn_fmt<FIQ4_XS>(epi, nrm, kc, sv, tpw);
     case FAQ4: return mfma_fn_fmt<FAQ4>(epi, nrm, kc, sv, tpw);
+    case FQ6_K: return mfma_fn_fmt<FQ6_K>(epi, nrm, kc, sv, tpw);
+    case FQ1_0: return mfma_fn_fmt<FQ1_0>(epi, nrm, kc, sv, tpw);
     default: return nullptr;
     }
 }
@@ -575,9 +684,8 @@ static const void *mfma_fn(int fmt, int epi, bool nrm, int kc, bool sv, int tpw)
 // for the staged x, LDS).
 bool plan_mfma(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb, MfmaPlan *p)
 {
-    if (fmt != FQ4_0 && fmt != FQ8_0 && fmt != FQ4_K && fmt != FQ5_K && fmt != FQ5_0 &&
-        fmt != FIQ4_NL && fmt != FIQ4_XS && fmt != FAQ4)
-        return false;   // Q6_K (16-weight sub-blocks) and Q1_0 take the other kernels
+    if (!fmt_valid(fmt))
+        return false;
     if (nb < 1 || nb > 16 || K > MF_KMAX || N < 1)
         return false;
     p->kc = K <= 2048 ? 1 : 2;
