@@ -790,7 +790,7 @@ int qgemm(int fmt, const void *W, int64_t N, int64_t K, const float *x, int64_t 
     Layout L;
     if (M < 1 || M > QG_GEMM_MAX_M || N < 1 || N > 0x7fffffffLL || !layout(fmt, N, K, &L) ||
         N * L.qs_row >= QG_BUF_MAX || N * L.sc_row >= QG_BUF_MAX ||
-        gemm_n_tiles(N) * gemm_m_tiles(M) > 0x7fffffffLL - 8)
+        (gemm_n_tiles(N) + 7) * gemm_m_tiles(M) > 0x7fffffffLL)   // the grid
         return QG_ERR_SHAPE;
     if (!ws)
         return QG_ERR_WORKSPACE;

@@ -19,9 +19,9 @@
 //    Either way the weights stay exact; only x is rounded, by at most 2^-11 of itself;
 //  - x tiles come from LDS, double-buffered: the next step's x and weights are loaded while the
 //    current step computes;
-//  - the grid walks the tiles XCD by XCD (workgroup i runs on XCD i % 8): each XCD takes a
-//    contiguous range of tiles in N-major order, so the row tiles sharing a weight tile share that
-//    XCD's L2.
+//  - the grid walks the tiles XCD by XCD (workgroup i runs on XCD i % 8): each XCD owns a range of
+//    weight tiles and walks them row-tile-major, so the workgroups resident on an XCD share a few x
+//    row tiles and the XCD's weight tiles in its L2.
 #include <hip/hip_runtime.h>
 
 #include "mfma_common.h"
@@ -86,13 +86,17 @@ __global__ __launch_bounds__(GM_THREADS, 2) void k_gemm(GemmArgs a)
     const int wm = wave >> 1, wn = wave & 1;
     const int ir = lane & 15, lc = lane >> 4;
 
-    // tile of this workgroup: XCD-major walk (workgroup id i runs on XCD i % 8)
-    const int T = a.n_tiles * a.m_tiles, per = (T + 7) / 8;
+    // tile of this workgroup (workgroup id i runs on XCD i % 8): XCD x owns weight tiles
+    // [x NTX, (x + 1) NTX) and walks them row-tile-major, so the workgroups resident on an XCD at
+    // a time share a few x row tiles and all of the XCD's weight tiles, both held in its L2
+    // (x tile-major would sweep all of x through the L2 for every few weight tiles)
+    const int NTX = (a.n_tiles + 7) / 8;
     const int id = blockIdx.x, xcd = id & 7, k8 = id >> 3;
-    const int v = xcd * per + k8;
-    if (k8 >= per || v >= T)
+    const int n_base = xcd * NTX;
+    const int ntx = a.n_tiles - n_base < NTX ? a.n_tiles - n_base : NTX;
+    if (ntx <= 0 || k8 >= ntx * a.m_tiles)
         return;
-    const int n_tile = v / a.m_tiles, m_tile = v - n_tile * a.m_tiles;
+    const int m_tile = k8 / ntx, n_tile = n_base + k8 % ntx;
     const int64_t m0 = (int64_t)m_tile * GM_BM, n0 = (int64_t)n_tile * GM_BN;
 
     const int C = (int)(a.qs_row / 16), S = (C + 3) / 4, KB = (int)(a.K / 32);
@@ -289,8 +293,7 @@ int launch_gemm(int fmt, const GemmArgs &a0, const float *x, void *stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return (int)e;
-    const int T = a.n_tiles * a.m_tiles;
-    const int grid = 8 * ((T + 7) / 8);
+    const int grid = 8 * ((a.n_tiles + 7) / 8) * a.m_tiles;
     if (fmt == FQ4_0)
         hipLaunchKernelGGL(k_gemm<FQ4_0>, dim3(grid), dim3(GM_THREADS), 0, s, a);
     else
