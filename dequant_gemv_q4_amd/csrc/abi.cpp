@@ -769,13 +769,41 @@ int qgemv_qk_norm_rope(float *qkv, int nb, int n_q_heads, int n_kv_heads, int he
 static int64_t gemm_m_tiles(int64_t M) { return (M + QG_GEMM_BM - 1) / QG_GEMM_BM; }
 static int64_t gemm_n_tiles(int64_t N) { return (N + QG_GEMM_BN - 1) / QG_GEMM_BN; }
 
+// Tiles, K steps and K splits of a qgemm call.  The split depends on the shape alone (so the
+// workspace size does too): when the output tiles are fewer than the 256 compute units the K
+// steps are dealt out to several workgroups per tile, at least two steps each.
+struct GemmPlan {
+    int64_t m_tiles, n_tiles, steps, sps, splits;
+    int64_t xh_bytes, rs_bytes, part_bytes;
+};
+static GemmPlan gemm_plan(int64_t N, int64_t K, int64_t M)
+{
+    GemmPlan p;
+    p.m_tiles = gemm_m_tiles(M);
+    p.n_tiles = gemm_n_tiles(N);
+    p.steps = (K + QG_GEMM_KSTEP - 1) / QG_GEMM_KSTEP;
+    const int64_t tiles = p.m_tiles * p.n_tiles;
+    p.sps = p.steps;
+    if (tiles < 192 && p.steps >= 4) {
+        const int64_t want = (256 + tiles - 1) / tiles;
+        const int64_t sps = (p.steps + want - 1) / want;
+        p.sps = sps < 2 ? 2 : sps;
+    }
+    p.splits = (p.steps + p.sps - 1) / p.sps;
+    const int64_t Mp = p.m_tiles * QG_GEMM_BM;
+    p.xh_bytes = round256(Mp * p.steps * QG_GEMM_KSTEP * 2);
+    p.rs_bytes = round256(Mp * 4);
+    p.part_bytes = p.splits > 1 ? round256(p.splits * M * N * 4) : 0;
+    return p;
+}
+
 int64_t qgemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M)
 {
     Layout L;
     if ((fmt != QG_Q4_0 && fmt != QG_Q8_0) || M < 1 || M > QG_GEMM_MAX_M || !layout(fmt, N, K, &L))
         return -1;
-    const int64_t Mp = gemm_m_tiles(M) * QG_GEMM_BM;
-    return round256(Mp * K * 2) + round256(Mp * 4);
+    const GemmPlan p = gemm_plan(N, K, M);
+    return p.xh_bytes + p.rs_bytes + p.part_bytes;
 }
 
 int qgemm(int fmt, const void *W, int64_t N, int64_t K, const float *x, int64_t M, float *y,
@@ -792,6 +820,10 @@ int qgemm(int fmt, const void *W, int64_t N, int64_t K, const float *x, int64_t 
         N * L.qs_row >= QG_BUF_MAX || N * L.sc_row >= QG_BUF_MAX ||
         (gemm_n_tiles(N) + 7) * gemm_m_tiles(M) > 0x7fffffffLL)   // the grid
         return QG_ERR_SHAPE;
+    const GemmPlan p = gemm_plan(N, K, M);
+    if ((p.n_tiles + 7) * p.m_tiles * p.splits > 0x7fffffffLL ||
+        p.m_tiles * QG_GEMM_BM / 16 * p.steps * QG_GEMM_KSTEP / 32 > 0x7fffffffLL)
+        return QG_ERR_SHAPE;
     if (!ws)
         return QG_ERR_WORKSPACE;
     if (!al(W, 256) || !al(x, 4) || !al(y, 4) || !al(ws, 256))
@@ -807,18 +839,22 @@ int qgemm(int fmt, const void *W, int64_t N, int64_t K, const float *x, int64_t 
     memset(&a, 0, sizeof(a));
     a.qs = static_cast<const uint8_t *>(W);
     a.sc = a.qs + L.sc_off;
-    const int64_t Mp = gemm_m_tiles(M) * QG_GEMM_BM;
     uint8_t *w8 = static_cast<uint8_t *>(ws);
     a.xh = reinterpret_cast<_Float16 *>(w8);
-    a.rs = reinterpret_cast<float *>(w8 + round256(Mp * K * 2));
+    a.rs = reinterpret_cast<float *>(w8 + p.xh_bytes);
+    a.part = p.splits > 1 ? reinterpret_cast<float *>(w8 + p.xh_bytes + p.rs_bytes) : nullptr;
     a.y = y;
     a.N = N;
     a.K = K;
     a.M = M;
     a.qs_row = L.qs_row;
     a.sc_row = L.sc_row;
-    a.n_tiles = (int)gemm_n_tiles(N);
-    a.m_tiles = (int)gemm_m_tiles(M);
+    a.n_tiles = (int)p.n_tiles;
+    a.m_tiles = (int)p.m_tiles;
+    a.KBp = (int)(p.steps * QG_GEMM_KSTEP / 32);
+    a.steps = (int)p.steps;
+    a.sps = (int)p.sps;
+    a.splits = (int)p.splits;
     return launch_status(launch_gemm(fmt, a, x, stream));
 }
 

@@ -5,299 +5,443 @@
 // tokens goes through a layer at once so that each weight is streamed once for the whole chunk;
 // "Crate inferencelayer" docs, gemm_q1_src / gemm_q4_src: a classic blocked GEMM whose tiles share
 // one weight stream, one Q4 block (32 k) per inner step, the activation tile staged in shared
-// memory.  Here:
+// memory; gemm_q4_splitk_src / gemm_q4_splitk_reduce_src: K split over workgroups when the tiles
+// alone do not fill the device, the partial sums folded by a second pass.  Here:
 //  - x is first turned into f16 once per call (k_xprep): each row scaled by the power of two that
-//    puts its largest |x| in [2^14, 2^15), laid out per 32-k block in the order the A operand of
-//    v_mfma_f32_16x16x32_f16 takes it (mf_elem), the high-nibble positions of Q4_0 times 1/16;
-//  - a workgroup (4 waves, 2 x 2) owns a 128 x 128 tile of Y; a wave owns 64 x 64 (4 x 4 MFMA
-//    tiles).  Per step of 128 k (Q4_0: 4 blocks; Q8_0: 64 k, 2 blocks) the wave loads its 64
-//    weight rows' 16-byte chunks (one load per lane per 16 rows), transposes them across the
-//    lane rows (mf_xpose) and decodes exact f16 weights (mf_bop).  Q4_0: the block scale splits
-//    exactly into d_hi (8 significant bits) + d_lo, so d_hi (q - 8) and d_lo (q - 8) are exact
-//    f16 operands and two MFMAs per block accumulate the scaled product straight into the MFMA
-//    accumulators; Q8_0 (8-bit q): one MFMA per block gives D = A B and acc += d D on the VALU.
-//    Either way the weights stay exact; only x is rounded, by at most 2^-11 of itself;
-//  - x tiles come from LDS, double-buffered: the next step's x and weights are loaded while the
-//    current step computes;
+//    puts its largest |x| in [2^14, 2^15), the high-nibble positions of Q4_0 times 1/16, and laid
+//    out in 1 KB chunks (16 rows x one 32-k block) whose 64 16-byte pieces are the A operands of
+//    v_mfma_f32_16x16x32_f16 in lane order (mf_elem), zero past K and past M;
+//  - a workgroup (8 waves) owns a 128 x 128 tile of Y; wave w owns all 128 x rows against weight
+//    rows 16 w .. 16 w + 15 (8 x 1 MFMA tiles), so each weight is decoded once per workgroup and
+//    feeds 16 MFMAs per block (the decode is VALU work; eight x tiles per decoded weight tile keep
+//    it under the matrix-core time).  A step covers 128 k (4 blocks);
+//  - x chunks, weight chunks (16 rows x 64 bytes for Q4_0, x 128 bytes for Q8_0) and the block
+//    scales go from global memory straight into LDS (global_load_lds: no registers, no LDS store
+//    instructions), three stages deep: the loads of step s + 2 are issued while step s computes,
+//    so each load has two steps of matrix work to arrive in.  One barrier per step;
+//  - the kernel is persistent (one workgroup per compute unit, each walking a list of tiles): the
+//    load stream runs across tile boundaries, so the next tile's first loads overlap the current
+//    tile's last steps and its stores, and there is no per-wave launch ramp between tiles;
+//  - a wave reads the weight chunks it loaded itself from LDS, transposes them across the lane
+//    rows (mf_xpose) and decodes exact f16 weights (mf_bop).  Q4_0: the block scale
+//    splits exactly into d_hi (8 significant bits) + d_lo, so d_hi (q - 8) and d_lo (q - 8) are
+//    exact f16 operands and two MFMAs per block accumulate the scaled product straight into the
+//    MFMA accumulators; Q8_0 (8-bit q): one MFMA per block gives D = A B and acc += d D on the
+//    VALU.  Either way the weights stay exact; only x is rounded, by at most 2^-11 of itself;
 //  - the grid walks the tiles XCD by XCD (workgroup i runs on XCD i % 8): each XCD owns a range of
 //    weight tiles and walks them row-tile-major, so the workgroups resident on an XCD share a few x
-//    row tiles and the XCD's weight tiles in its L2.
+//    row tiles and the XCD's weight tiles in its L2;
+//  - when the tiles are too few for the device the K steps are split over several workgroups; each
+//    writes its partial tile to the workspace and k_gemm_fold adds the splits in a fixed order.
 #include <hip/hip_runtime.h>
 
 #include "mfma_common.h"
 
 namespace qg {
 
-constexpr int GM_THREADS = 256;
-constexpr int GM_WT = 2;                          // 16-row weight tiles per wave
-constexpr int GM_BM = 128, GM_BN = 32 * GM_WT;    // rows of x, rows of W per workgroup
-static_assert(GM_BM == QG_GEMM_BM && GM_BN == QG_GEMM_BN, "the host plans with these tiles");
+constexpr int GM_THREADS = 512;                   // 8 waves
+constexpr int GM_BM = 128, GM_BN = 128;           // rows of x, rows of W per workgroup
+constexpr int GM_BPS = 4;                         // 32-k blocks per step
+constexpr int GM_STAGES = 3;
+static_assert(GM_BM == QG_GEMM_BM && GM_BN == QG_GEMM_BN && GM_BPS * 32 == QG_GEMM_KSTEP,
+              "the host plans with these tiles");
 
-// x [M][K] f32 -> xh [Mp][K] f16 in the A-operand order of each 32-k block, and rs[r] = the factor
-// undoing row r's scale; rows M..Mp-1 are zero (rs 0).  One workgroup per row.
+// LDS stage of one step: x chunks [row group 0..7][block 0..3] (1 KB each), then weight chunks
+// [row group 0..7][half] (1 KB each: 16 rows x 4 chunks of 16 B), then the scales [row][block],
+// one dword each (a 2-byte copy to LDS fills its lane's dword, zero-extended).
 template <int FMT>
-__global__ __launch_bounds__(256) void k_xprep(const float *x, int64_t M, int64_t K,
-                                               _Float16 *xh, float *rs)
+struct GemmStage {
+    static constexpr int WH = FMT == FQ8_0 ? 2 : 1;            // weight wave-loads per row group
+    static constexpr int XB = GM_BM / 16 * GM_BPS * 1024;
+    static constexpr int WB = GM_BN / 16 * WH * 1024;
+    static constexpr int SB = GM_BN * GM_BPS * 4;
+    static constexpr int BYTES = XB + WB + SB;
+    static constexpr int XPW = GM_BM / 16 * GM_BPS / 8;         // x wave-loads per wave
+};
+
+// s_waitcnt with vmcnt(N), lgkmcnt(0), expcnt left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void gm_wait()
 {
-    __shared__ float s_mx[4];
-    const int64_t r = blockIdx.x;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const float *xr = x + (r < M ? r : 0) * K;
-    float mx = 0.f;
-    if (r < M)
-        for (int64_t e = t; e < K; e += 256)
-            mx = fmaxf(mx, fabsf(xr[e]));
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Global -> LDS copies (global_load_lds): lane l's 16 bytes land at LDS address M0 + 16 l, M0
+// being the wave's destination; a 4-byte copy lands at M0 + 4 l and a 2-byte copy writes lane
+// l's value zero-extended to the dword at M0 + 4 l.  Written as asm so that the compiler does not track them: it
+// would otherwise wait for every copy in flight before any LDS read; the kernel waits for each
+// stage with vmcnt itself.  One wait state between the M0 write and the copy.
+__device__ __forceinline__ void gm_dma16(const void *src, const void *lds_dst)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0));
+}
+__device__ __forceinline__ void gm_dma4(const void *src, const void *lds_dst)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(src), "{m0}"(m0));
+}
+__device__ __forceinline__ void gm_dma2(const void *src, const void *lds_dst)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+    asm volatile("s_nop 0\n\tglobal_load_lds_ushort %0, off" : : "v"(src), "{m0}"(m0));
+}
+
+// workgroup barrier that the compiler may not move memory accesses across (the LDS reads of a
+// stage must stay after the wait for its loads and before the loads that overwrite it)
+__device__ __forceinline__ void gm_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// x [M][K] f32 -> xh chunks [Mp / 16][KBp][64 lanes][8 halves] in the A-operand order of each
+// 32-k block, and rs[r] = the factor undoing row r's scale; rows past M and columns past K are
+// zero (rs 0 past M).  Workgroup (g, p): rows 16 g .. 16 g + 15, blocks [p bpw, (p + 1) bpw); each
+// finds the largest |x| of its 16 rows over the whole row (a wave per 4 rows) so that the row
+// scale does not depend on the split.  Lane (ir, j) of a block holds elements 4j..4j+3 and
+// 16+4j..16+4j+3 of row ir in both formats (mf_elem(j, h) = mf_elem(0, h) + 4 j).
+template <int FMT>
+__global__ __launch_bounds__(256) void k_xprep(const float *x, int64_t M, int64_t K, int KBp,
+                                               int bpw, _Float16 *xh, float *rs)
+{
+    __shared__ float s_sc[16];
+    const int g = blockIdx.x, p = blockIdx.y, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const bool vec = ((uintptr_t)x & 15) == 0;          // K % 32 == 0: every row is aligned too
+    for (int i = 0; i < 4; ++i) {
+        const int rl = 4 * wave + i;
+        const int64_t r = (int64_t)g * 16 + rl;
+        float mx = 0.f;
+        if (r < M) {
+            const float *xr = x + r * K;
+            if (vec) {
+#pragma unroll 8
+                for (int64_t e = 4 * lane; e < K; e += 256) {
+                    const float4 v = *reinterpret_cast<const float4 *>(xr + e);
+                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+                }
+            } else {
+                for (int64_t e = lane; e < K; e += 64)
+                    mx = fmaxf(mx, fabsf(xr[e]));
+            }
+        }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        mx = fmaxf(mx, __shfl_xor(mx, off));
-    if (lane == 0)
-        s_mx[wave] = mx;
+        for (int off = 32; off > 0; off >>= 1)
+            mx = fmaxf(mx, __shfl_xor(mx, off));
+        if (lane == 0) {
+            int e2 = 0;
+            frexpf(mx, &e2);                                   // max |x| = f 2^e2, f in [0.5, 1)
+            const int sk = 15 - e2 < 127 ? 15 - e2 : 127;      // 2^sk stays a finite f32
+            s_sc[rl] = r < M ? ldexpf(1.0f, sk) : 0.f;
+            if (p == 0)
+                rs[r] = r < M ? ldexpf(1.0f, -sk) : 0.f;
+        }
+    }
     __syncthreads();
-    mx = fmaxf(fmaxf(s_mx[0], s_mx[1]), fmaxf(s_mx[2], s_mx[3]));
-    int e2 = 0;
-    frexpf(mx, &e2);                                   // max |x| = f 2^e2, f in [0.5, 1)
-    const int sk = 15 - e2 < 127 ? 15 - e2 : 127;      // 2^sk stays a finite f32
-    const float sc = r < M ? ldexpf(1.0f, sk) : 0.f;
-    if (t == 0)
-        rs[r] = r < M ? ldexpf(1.0f, -sk) : 0.f;
-    _Float16 *dst = xh + r * K;
-    for (int64_t i = t; i < K; i += 256) {
-        const int64_t blk = i >> 5;
-        const int pos = (int)(i & 31), j = pos >> 3, h = pos & 7;
-        bool hi = false;
-        const int e = mf_elem<FMT>(j, h, hi);
-        const float v = r < M ? xr[blk * 32 + e] * sc * (hi ? 0.0625f : 1.0f) : 0.f;
-        dst[i] = (_Float16)v;
+    const int KB = (int)(K / 32);
+    const int b_end = (p + 1) * bpw < KBp ? (p + 1) * bpw : KBp;
+    _Float16 *dst = xh + (int64_t)g * KBp * 512;
+#pragma unroll 4
+    for (int u = p * bpw * 64 + t; u < b_end * 64; u += 256) {
+        const int blk = u >> 6, l = u & 63, ir = l & 15, j = l >> 4;
+        const int64_t r = (int64_t)g * 16 + ir;
+        const float sc = s_sc[ir];
+        float lo[4] = {0.f, 0.f, 0.f, 0.f}, hi4[4] = {0.f, 0.f, 0.f, 0.f};
+        if (r < M && blk < KB) {
+            const float *xb = x + r * K + (int64_t)blk * 32 + 4 * j;
+            if (vec) {
+                const float4 a = *reinterpret_cast<const float4 *>(xb);
+                const float4 b = *reinterpret_cast<const float4 *>(xb + 16);
+                lo[0] = a.x; lo[1] = a.y; lo[2] = a.z; lo[3] = a.w;
+                hi4[0] = b.x; hi4[1] = b.y; hi4[2] = b.z; hi4[3] = b.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lo[i] = xb[i];
+                    hi4[i] = xb[16 + i];
+                }
+            }
+        }
+        mh8 v;
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+            bool hi = false;
+            const int e = mf_elem<FMT>(0, h, hi);
+            const float xv = e >= 16 ? hi4[e - 16] : lo[e];
+            v[h] = (_Float16)(xv * sc * (hi ? 0.0625f : 1.0f));
+        }
+        *reinterpret_cast<mh8 *>(dst + (int64_t)u * 8) = v;
     }
 }
 
 template <int FMT>
-__global__ __launch_bounds__(GM_THREADS, 2) void k_gemm(GemmArgs a)
+__global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
 {
-    constexpr int BPS = FMT == FQ8_0 ? 2 : 4;          // blocks per step (4 chunks of 16 B)
-    constexpr int KSTEP = 32 * BPS;                     // k per step
-    constexpr int LROW = KSTEP + 8;                     // LDS row stride in halves (+16 B pad)
-    constexpr int XSEG = GM_BM * KSTEP / 8;             // 16-byte x segments per step
-    constexpr int XPT = XSEG / GM_THREADS;              // per thread
-    __shared__ __attribute__((aligned(16))) _Float16 xs[2][GM_BM * LROW];
+    using G = GemmStage<FMT>;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[GM_STAGES * G::BYTES];
+    __shared__ __attribute__((aligned(16))) float s_rs[3][GM_BM];   // row factors of 3 tiles
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
     const int ir = lane & 15, lc = lane >> 4;
 
-    // tile of this workgroup (workgroup id i runs on XCD i % 8): XCD x owns weight tiles
-    // [x NTX, (x + 1) NTX) and walks them row-tile-major, so the workgroups resident on an XCD at
-    // a time share a few x row tiles and all of the XCD's weight tiles, both held in its L2
-    // (x tile-major would sweep all of x through the L2 for every few weight tiles)
+    // tiles of this workgroup (workgroup id i runs on XCD i % 8): XCD x owns weight tiles
+    // [x NTX, (x + 1) NTX) and numbers its tiles k8 row-tile-major, then split by split; its
+    // workgroups take k8 = slot, slot + nslots, ..., so the ones resident at a time work on a
+    // window of consecutive k8 (a few x row tiles, all of the XCD's weight tiles) held in its L2
     const int NTX = (a.n_tiles + 7) / 8;
-    const int id = blockIdx.x, xcd = id & 7, k8 = id >> 3;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
     const int n_base = xcd * NTX;
     const int ntx = a.n_tiles - n_base < NTX ? a.n_tiles - n_base : NTX;
-    if (ntx <= 0 || k8 >= ntx * a.m_tiles)
+    const int ntiles = ntx > 0 ? ntx * a.m_tiles * a.splits : 0;
+    if (slot >= ntiles)
         return;
-    const int m_tile = k8 / ntx, n_tile = n_base + k8 % ntx;
-    const int64_t m0 = (int64_t)m_tile * GM_BM, n0 = (int64_t)n_tile * GM_BN;
-
-    const int C = (int)(a.qs_row / 16), S = (C + 3) / 4, KB = (int)(a.K / 32);
-    const uint32_t qbytes = (uint32_t)(a.N * a.qs_row), sbytes = (uint32_t)(a.N * a.sc_row);
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(a.qs), (short)0, (int)qbytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(a.sc), (short)0, (int)sbytes, 0x00020000);
-
-    // the four weight rows (one per 16-row tile) this lane loads; rows past N read row N - 1
-    uint32_t wrow[GM_WT];
-#pragma unroll
-    for (int wt = 0; wt < GM_WT; ++wt) {
-        const int64_t n = n0 + 16 * GM_WT * wn + 16 * wt + ir;
-        wrow[wt] = (uint32_t)(n < a.N ? n : a.N - 1);
-    }
-
-    struct Step {
-        uint32_t q[GM_WT][4];        // [weight tile][dword]
-        uint16_t d[GM_WT][BPS];      // [weight tile][block] scale bits
+    struct Tile {
+        int64_t m0, n0;
+        int s0, S, split;
     };
-    auto load_w = [&](Step &st, int s) {
-        const int sc = s < S ? s : S - 1;
-        const int ch = 4 * sc + lc < C ? 4 * sc + lc : C - 1;
-#pragma unroll
-        for (int wt = 0; wt < GM_WT; ++wt) {
-            const auto q = __builtin_amdgcn_raw_buffer_load_b128(
-                rq, (int)(wrow[wt] * (uint32_t)a.qs_row + 16u * (uint32_t)ch), 0, 0);
-            st.q[wt][0] = q[0]; st.q[wt][1] = q[1]; st.q[wt][2] = q[2]; st.q[wt][3] = q[3];
-#pragma unroll
-            for (int b = 0; b < BPS; ++b) {
-                const int blk = BPS * sc + b < KB ? BPS * sc + b : KB - 1;
-                st.d[wt][b] = __builtin_amdgcn_raw_buffer_load_b16(
-                    rsc, (int)(wrow[wt] * (uint32_t)a.sc_row + 2u * (uint32_t)blk), 0, 0);
-            }
-        }
-    };
-    // x of step s: segment g = tid + 256 u is row g / (KSTEP / 8), 16-byte column g % (KSTEP / 8);
-    // columns past K (the last step of a K that is not a multiple of the step) are zero.  Loads
-    // are unconditional (a clamped address, then a select) so the loop has no branches.
-    auto load_x = [&](uint4 (&xr)[XPT], int s) {
-#pragma unroll
-        for (int u = 0; u < XPT; ++u) {
-            const int g = tid + GM_THREADS * u;
-            const int row = g / (KSTEP / 8), col = g % (KSTEP / 8);
-            const int64_t k0 = (int64_t)s * KSTEP + 8 * col;
-            const bool in = k0 < a.K;
-            const uint4 val =
-                *reinterpret_cast<const uint4 *>(a.xh + (m0 + row) * a.K + (in ? k0 : 0));
-            xr[u] = in ? val : make_uint4(0u, 0u, 0u, 0u);
-        }
-    };
-    auto store_x = [&](const uint4 (&xr)[XPT], int buf) {
-#pragma unroll
-        for (int u = 0; u < XPT; ++u) {
-            const int g = tid + GM_THREADS * u;
-            const int row = g / (KSTEP / 8), col = g % (KSTEP / 8);
-            *reinterpret_cast<uint4 *>(&xs[buf][row * LROW + 8 * col]) = xr[u];
-        }
+    auto tile_of = [&](int k8) {
+        Tile t;
+        const int rest = k8 / ntx;
+        t.n0 = (int64_t)(n_base + k8 % ntx) * GM_BN;
+        t.m0 = (int64_t)(rest % a.m_tiles) * GM_BM;
+        t.split = rest / a.m_tiles;
+        t.s0 = t.split * a.sps;
+        t.S = a.steps - t.s0 < a.sps ? a.steps - t.s0 : a.sps;   // >= 1 (host plan)
+        return t;
     };
 
-    float acc[4][GM_WT][4];     // Q8_0: per-block scaled sums (VALU)
-    mf4 macc[4][GM_WT];         // Q4_0: sums kept in the MFMA accumulators
+    const int C = (int)(a.qs_row / 16), KB = (int)(a.K / 32);
+
+    // loads of step s of tile t into ring slot `ring`.  x: chunk c = XPW wave + u of the stage is
+    // row group c / 4, block c % 4.  Weights: row group `wave`, lane (ir, lc) -> row 16 wave + ir,
+    // chunk 4 h + lc of the step (rows past N read row N - 1, chunks past the row its last chunk).
+    // Scales: lane l -> row 16 wave + l / 4, block l % 4 of the step (dword 4 row + block of the
+    // scale area).  With a tile's first step, waves 0 and 1 also load its 128 row factors.
+    auto issue = [&](const Tile &t, int s_rel, int ring, int rs_slot) {
+        const int s = t.s0 + s_rel;
+        uint8_t *st = lds + ring * G::BYTES;
+        const _Float16 *xsrc = a.xh + (t.m0 / 16) * (int64_t)a.KBp * 512 + (int64_t)lane * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < GM_WT; ++j) {
-            acc[i][j][0] = acc[i][j][1] = acc[i][j][2] = acc[i][j][3] = 0.f;
-            macc[i][j] = mf4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < G::XPW; ++u) {
+            const int c = G::XPW * wave + u;
+            const _Float16 *src =
+                xsrc + ((int64_t)(c / GM_BPS) * a.KBp + (int64_t)s * GM_BPS + c % GM_BPS) * 512;
+            gm_dma16(src, st + c * 1024);
         }
+        const int64_t wr = t.n0 + 16 * wave + ir < a.N ? t.n0 + 16 * wave + ir : a.N - 1;
+        const uint8_t *wsrc = a.qs + wr * a.qs_row;
+#pragma unroll
+        for (int h = 0; h < G::WH; ++h) {
+            const int ch0 = (s * G::WH + h) * 4 + lc;
+            const int ch = ch0 < C ? ch0 : C - 1;
+            gm_dma16(wsrc + 16 * (int64_t)ch, st + G::XB + (wave * G::WH + h) * 1024);
+        }
+        const int64_t sr =
+            t.n0 + 16 * wave + (lane >> 2) < a.N ? t.n0 + 16 * wave + (lane >> 2) : a.N - 1;
+        const int b0 = s * GM_BPS + (lane & 3);
+        const int blk = b0 < KB ? b0 : KB - 1;
+        gm_dma2(a.sc + sr * a.sc_row + 2 * (int64_t)blk, st + G::XB + G::WB + wave * 256);
+        if (s_rel == 0 && wave < 2)
+            gm_dma4(a.rs + t.m0 + 64 * wave + lane, &s_rs[rs_slot][64 * wave]);
+    };
+
+    float acc[8][4];        // Q8_0: per-block scaled sums (VALU)
+    mf4 macc[8];            // Q4_0: sums kept in the MFMA accumulators
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            acc[i][0] = acc[i][1] = acc[i][2] = acc[i][3] = 0.f;
+            macc[i] = mf4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    zero_acc();
 
     const MfConst kc = mf_const<FMT>();
-    // one step from LDS buffer `buf` and the weights in st
-    auto compute = [&](Step &st, int s, int buf) {
+    auto compute = [&](const Tile &t, int s_rel, int ring) {
+        const int s = t.s0 + s_rel;
+        const uint8_t *st = lds + ring * G::BYTES;
+        // this wave's weights (row group `wave`, loaded by this wave); after the transpose q[h][b']
+        // is dword lc of chunk 4 h + b' of row ir
+        uint32_t q[G::WH][4];
 #pragma unroll
-        for (int wt = 0; wt < GM_WT; ++wt)
-            mf_xpose(st.q[wt]);
+        for (int h = 0; h < G::WH; ++h) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(st + G::XB + (wave * G::WH + h) * 1024 +
+                                                             16 * lane);
+            q[h][0] = v.x; q[h][1] = v.y; q[h][2] = v.z; q[h][3] = v.w;
+        }
+        const uint4 dsc = *reinterpret_cast<const uint4 *>(st + G::XB + G::WB + (16 * wave + ir) * 16);
 #pragma unroll
-        for (int b = 0; b < BPS; ++b) {
-            const int blk = BPS * s + b;
-            mh8 A[4];
+        for (int h = 0; h < G::WH; ++h)
+            mf_xpose(q[h]);
 #pragma unroll
-            for (int bt = 0; bt < 4; ++bt)
-                A[bt] = *reinterpret_cast<const mh8 *>(
-                    &xs[buf][(64 * wm + 16 * bt + ir) * LROW + 32 * b + 8 * lc]);
+        for (int b = 0; b < GM_BPS; ++b) {
+            const int blk = GM_BPS * s + b;
+            mh8 A[8];
+#pragma unroll
+            for (int bt = 0; bt < 8; ++bt)
+                A[bt] = *reinterpret_cast<const mh8 *>(st + (bt * GM_BPS + b) * 1024 + 16 * lane);
+            const uint32_t dw = b == 0 ? dsc.x : b == 1 ? dsc.y : b == 2 ? dsc.z : dsc.w;
             if constexpr (FMT == FQ4_0) {
                 // exact scaled weights: d = d_hi + d_lo with d_hi the top 8 significant bits of
                 // the f16 scale, d_lo the rest (3 bits); |q - 8| <= 8 needs at most 3 more bits,
                 // so d_hi (q - 8) and d_lo (q - 8) are exact f16 values (the high-nibble halves,
                 // held x16, too).  Two MFMAs per block accumulate them straight into the
-                // accumulators (no per-block scaling on the VALU): first the d_hi products of
-                // all 16 tiles, then the d_lo ones, so an accumulator's two updates are 16
-                // independent MFMAs apart.
-                mh8 Bh[GM_WT], Bl[GM_WT];
+                // accumulators: first the d_hi products of all 8 tiles, then the d_lo ones.
+                const mh8 B = mf_bop<FMT>(q[0][b], 0u, kc);
+                const uint16_t db = blk < KB ? (uint16_t)(dw & 0xFFFFu) : (uint16_t)0;
+                const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)(db & 0xFFF8u));
+                const _Float16 dl = __builtin_bit_cast(_Float16, db) - dh;
+                const mh8 Bh = B * dh, Bl = B * dl;
 #pragma unroll
-                for (int wt = 0; wt < GM_WT; ++wt) {
-                    const mh8 B = mf_bop<FMT>(st.q[wt][b], 0u, kc);
-                    const uint16_t db = blk < KB ? st.d[wt][b] : (uint16_t)0;
-                    const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)(db & 0xFFF8u));
-                    const _Float16 dl = __builtin_bit_cast(_Float16, db) - dh;
-                    Bh[wt] = B * dh;
-                    Bl[wt] = B * dl;
-                }
+                for (int bt = 0; bt < 8; ++bt)
+                    macc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt], Bh, macc[bt], 0, 0, 0);
 #pragma unroll
-                for (int wt = 0; wt < GM_WT; ++wt)
-#pragma unroll
-                    for (int bt = 0; bt < 4; ++bt)
-                        macc[bt][wt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt], Bh[wt], macc[bt][wt], 0, 0, 0);
-#pragma unroll
-                for (int wt = 0; wt < GM_WT; ++wt)
-#pragma unroll
-                    for (int bt = 0; bt < 4; ++bt)
-                        macc[bt][wt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt], Bl[wt], macc[bt][wt], 0, 0, 0);
-                continue;
-            }
-#pragma unroll
-            for (int wt = 0; wt < GM_WT; ++wt) {
-                const mh8 B = FMT == FQ8_0 ? mf_bop<FMT>(st.q[wt][2 * b], st.q[wt][2 * b + 1], kc)
-                                           : mf_bop<FMT>(st.q[wt][b], 0u, kc);
-                const float d = blk < KB ? (float)__builtin_bit_cast(_Float16, st.d[wt][b]) : 0.f;
+                for (int bt = 0; bt < 8; ++bt)
+                    macc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt], Bl, macc[bt], 0, 0, 0);
+            } else {
+                // block b = chunks 2 b, 2 b + 1 of the step
+                const int h = b >> 1, p = 2 * (b & 1);
+                const mh8 B = mf_bop<FMT>(q[h][p], q[h][p + 1], kc);
+                const uint16_t db = (uint16_t)(dw & 0xFFFFu);
+                const float d = blk < KB ? (float)__builtin_bit_cast(_Float16, db) : 0.f;
                 const mf4 zero = {0.f, 0.f, 0.f, 0.f};
-                mf4 D[4];
 #pragma unroll
-                for (int bt = 0; bt < 4; ++bt)
-                    D[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt], B, zero, 0, 0, 0);
+                for (int bt = 0; bt < 8; bt += 4) {
+                    mf4 D[4];
 #pragma unroll
-                for (int bt = 0; bt < 4; ++bt) {
-                    acc[bt][wt][0] = fmaf(d, D[bt][0], acc[bt][wt][0]);
-                    acc[bt][wt][1] = fmaf(d, D[bt][1], acc[bt][wt][1]);
-                    acc[bt][wt][2] = fmaf(d, D[bt][2], acc[bt][wt][2]);
-                    acc[bt][wt][3] = fmaf(d, D[bt][3], acc[bt][wt][3]);
+                    for (int i = 0; i < 4; ++i)
+                        D[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt + i], B, zero, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[bt + i][0] = fmaf(d, D[i][0], acc[bt + i][0]);
+                        acc[bt + i][1] = fmaf(d, D[i][1], acc[bt + i][1]);
+                        acc[bt + i][2] = fmaf(d, D[i][2], acc[bt + i][2]);
+                        acc[bt + i][3] = fmaf(d, D[i][3], acc[bt + i][3]);
+                    }
                 }
-                // one (block, weight tile) group at a time: its results are consumed before the
-                // next group's MFMAs issue, so few result registers are live
-                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
 
-    // steps in pairs, the two register sets taking turns (no copies between them); every step
-    // loads the next one's weights and x (a clamped step past the end reloads the last) and
-    // stores that x into the other LDS buffer after computing, then one barrier
-    Step s0, s1;
-    uint4 xr[XPT];
-    load_w(s0, 0);
-    load_x(xr, 0);
-    store_x(xr, 0);
-    __syncthreads();
-    for (int s = 0; s < S; s += 2) {
-        load_w(s1, s + 1);
-        load_x(xr, s + 1 < S ? s + 1 : s);
-        compute(s0, s, 0);
-        store_x(xr, 1);
-        __syncthreads();
-        if (s + 1 >= S)
-            break;
-        load_w(s0, s + 2);
-        load_x(xr, s + 2 < S ? s + 2 : s + 1);
-        compute(s1, s + 1, 1);
-        store_x(xr, 0);
-        __syncthreads();
-    }
-
-    // lane (ir, lc) holds D[4 lc + v][ir]: x row 16 bt + 4 lc + v, weight row 16 wt + ir
+    // lane (ir, lc) holds D[4 lc + v][ir]: x row 16 bt + 4 lc + v, weight row 16 wave + ir
+    auto epilogue = [&](const Tile &t, int rs_slot) {
+        const bool fold = a.splits > 1;
+        float *out = fold ? a.part + (int64_t)t.split * a.M * a.N : a.y;
+        const int64_t n = t.n0 + 16 * wave + ir;
 #pragma unroll
-    for (int bt = 0; bt < 4; ++bt)
+        for (int bt = 0; bt < 8; ++bt)
 #pragma unroll
-        for (int vv = 0; vv < 4; ++vv) {
-            const int64_t r = m0 + 64 * wm + 16 * bt + 4 * lc + vv;
-            if (r >= a.M)
-                continue;
-            const float f = a.rs[r];
-#pragma unroll
-            for (int wt = 0; wt < GM_WT; ++wt) {
-                const int64_t n = n0 + 16 * GM_WT * wn + 16 * wt + ir;
-                const float v = FMT == FQ4_0 ? macc[bt][wt][vv] : acc[bt][wt][vv];
-                if (n < a.N)
-                    a.y[r * a.N + n] = v * f;
+            for (int vv = 0; vv < 4; ++vv) {
+                const int rl = 16 * bt + 4 * lc + vv;
+                const int64_t r = t.m0 + rl;
+                if (r >= a.M || n >= a.N)
+                    continue;
+                const float f = fold ? 1.0f : s_rs[rs_slot][rl];
+                const float v = FMT == FQ4_0 ? macc[bt][vv] : acc[bt][vv];
+                out[r * a.N + n] = v * f;
             }
+    };
+
+    // One stream of (tile, step) pairs per workgroup; the loads run two steps ahead of the
+    // compute, across tile boundaries (the next tile's first loads overlap this tile's last steps
+    // and its stores).  Ring slot of stream position p: p % 3.
+    constexpr int LPS = G::XPW + G::WH + 1;   // loads per thread per step (+1 at a tile's start)
+    int ik8 = slot, is = 0, itn = 0, pi = 0;  // issue cursor: tile, step, tile ordinal, position
+    Tile ti = tile_of(ik8);
+    auto issue_next = [&]() {
+        if (ik8 >= ntiles)
+            return;
+        issue(ti, is, pi % GM_STAGES, itn % 3);
+        ++pi;
+        if (++is == ti.S) {
+            is = 0;
+            ++itn;
+            ik8 += nslots;
+            if (ik8 < ntiles)
+                ti = tile_of(ik8);
         }
+    };
+    issue_next();
+    issue_next();
+    int ck8 = slot, cs = 0, ctn = 0, pc = 0;  // compute cursor
+    Tile tc = tile_of(ck8);
+    while (true) {
+        // this thread's loads of position pc have landed (those of pc + 1 may still be in
+        // flight; the stores of a finished tile are waited for too), and after the barrier
+        // everyone's have; every wave is also done reading position pc - 1, whose ring slot the
+        // loads of pc + 2 overwrite
+        if (pi - pc >= 2)
+            gm_wait<LPS>();
+        else
+            gm_wait<0>();
+        gm_barrier();
+        issue_next();
+        compute(tc, cs, pc % GM_STAGES);
+        ++pc;
+        if (++cs == tc.S) {
+            epilogue(tc, ctn % 3);
+            zero_acc();
+            cs = 0;
+            ++ctn;
+            ck8 += nslots;
+            if (ck8 >= ntiles)
+                break;
+            tc = tile_of(ck8);
+        }
+    }
 }
 
-int launch_gemm(int fmt, const GemmArgs &a0, const float *x, void *stream)
+// y[r][n] = rs[r] (sum over the splits, in split order, of part[split][r][n])
+__global__ __launch_bounds__(256) void k_gemm_fold(const float *part, const float *rs, int splits,
+                                                   int64_t M, int64_t N, float *y)
+{
+    const int64_t total = M * N, stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
+        float v = 0.f;
+        for (int sp = 0; sp < splits; ++sp)
+            v += part[sp * total + i];
+        y[i] = v * rs[i / N];
+    }
+}
+
+int launch_gemm(int fmt, const GemmArgs &a, const float *x, void *stream)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const GemmArgs &a = a0;
-    const int64_t Mp = (int64_t)a.m_tiles * GM_BM;
+    // x preparation: 16-row groups, split along K into parts of at least 4 blocks (one piece per
+    // thread) until there are about 256 workgroups (each part re-reads its rows for the maximum)
+    const int groups = a.m_tiles * GM_BM / 16;
+    int parts = (256 + groups - 1) / groups;
+    parts = parts < a.KBp / 4 ? parts : a.KBp / 4;
+    parts = parts < 1 ? 1 : parts;
+    const int bpw = (a.KBp + parts - 1) / parts;
+    parts = (a.KBp + bpw - 1) / bpw;
     if (fmt == FQ4_0)
-        hipLaunchKernelGGL(k_xprep<FQ4_0>, dim3((unsigned)Mp), dim3(256), 0, s, x, a.M, a.K,
-                           a.xh, a.rs);
+        hipLaunchKernelGGL(k_xprep<FQ4_0>, dim3(groups, parts), dim3(256), 0, s, x, a.M, a.K,
+                           a.KBp, bpw, a.xh, a.rs);
     else
-        hipLaunchKernelGGL(k_xprep<FQ8_0>, dim3((unsigned)Mp), dim3(256), 0, s, x, a.M, a.K,
-                           a.xh, a.rs);
+        hipLaunchKernelGGL(k_xprep<FQ8_0>, dim3(groups, parts), dim3(256), 0, s, x, a.M, a.K,
+                           a.KBp, bpw, a.xh, a.rs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return (int)e;
-    const int grid = 8 * ((a.n_tiles + 7) / 8) * a.m_tiles;
+    // persistent: at most one workgroup per compute unit (the LDS ring takes most of a CU), 32 per
+    // XCD, each walking its XCD's tiles
+    const int per_xcd = ((a.n_tiles + 7) / 8) * a.m_tiles * a.splits;
+    const int grid = 8 * (per_xcd < 32 ? per_xcd : 32);
     if (fmt == FQ4_0)
         hipLaunchKernelGGL(k_gemm<FQ4_0>, dim3(grid), dim3(GM_THREADS), 0, s, a);
     else
         hipLaunchKernelGGL(k_gemm<FQ8_0>, dim3(grid), dim3(GM_THREADS), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess || a.splits == 1)
+        return (int)e;
+    const int64_t total = a.M * a.N;
+    const int64_t fg = (total + 255) / 256 < 2048 ? (total + 255) / 256 : 2048;
+    hipLaunchKernelGGL(k_gemm_fold, dim3((unsigned)fg), dim3(256), 0, s, a.part, a.rs, a.splits,
+                       a.M, a.N, a.y);
     return (int)hipGetLastError();
 }
 

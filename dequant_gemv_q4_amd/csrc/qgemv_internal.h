@@ -194,18 +194,22 @@ struct MoeArgs {
     int pool_max;               // most row groups one workgroup's range may hold
 };
 
-// Tile of the wide row-batch GEMM: rows of x and rows of W per workgroup.
+// Tile of the wide row-batch GEMM: rows of x and rows of W per workgroup, k per step.
 #define QG_GEMM_BM 128
-#define QG_GEMM_BN 64
+#define QG_GEMM_BN 128
+#define QG_GEMM_KSTEP 128
 // Arguments of the wide row-batch GEMM (gemm_kernels.hip).
 struct GemmArgs {
     const uint8_t *qs, *sc;     // packed W (Q4_0 / Q8_0)
-    _Float16 *xh;               // workspace: x as f16 in operand order, [m_tiles * BM][K]
+    _Float16 *xh;               // workspace: x as f16 in operand chunks, [m_tiles * BM / 16][KBp][512]
     float *rs;                  // workspace: factor undoing each x row's scale, [m_tiles * BM]
+    float *part;                // workspace: partial tiles of the K splits, [splits][M][N] (splits > 1)
     float *y;                   // [M][N]
     int64_t N, K, M;
     int64_t qs_row, sc_row;
     int n_tiles, m_tiles;       // tiles of W (QG_GEMM_BN rows) and of x (QG_GEMM_BM rows)
+    int KBp;                    // 32-k blocks of a padded x row: steps * QG_GEMM_KSTEP / 32
+    int steps, sps, splits;     // K steps, steps per split, splits (ceil(steps / sps))
 };
 // x preparation then the GEMM, both on `stream`.
 int launch_gemm(int fmt, const GemmArgs &a, const float *x, void *stream);

@@ -1,7 +1,8 @@
 """The wide row-batch GEMM (prefill chunks, M > 16 rows of x; "Module gpu", module prefill) on the
 GPU against the f64 oracle: Q4_0 and Q8_0, M in {17, 64, 512, 2048} and ragged sizes (partial
-128-row tiles of x and W, K not a multiple of the 128-k step), every output compared up to
-M = 512 and sampled rows and columns beyond; integer inputs bit for bit."""
+128-row tiles of x and W, K not a multiple of the 128-k step, K split over workgroups with a
+shorter last split), every output compared up to M = 512 and sampled rows and columns beyond;
+integer inputs bit for bit."""
 import numpy as np
 import pytest
 
@@ -32,7 +33,9 @@ def _gemm(fmt, Wp, N, K, x):
                                        (q.Q4_0, 512, 517, 2048), (q.Q8_0, 17, 129, 1536),
                                        (q.Q8_0, 64, 2048, 1536), (q.Q8_0, 512, 260, 2048),
                                        (q.Q4_0, 200, 130, 96), (q.Q8_0, 131, 77, 32),
-                                       (q.Q4_0, 1, 64, 4096), (q.Q4_0, 129, 257, 8192)])
+                                       (q.Q4_0, 1, 64, 4096), (q.Q4_0, 129, 257, 8192),
+                                       (q.Q4_0, 40, 200, 608), (q.Q8_0, 33, 150, 608),
+                                       (q.Q4_0, 100, 3000, 1024)])
 def test_qgemm_parity(fmt, M, N, K):
     say(f"qgemm fmt={fmt} M={M} N={N} K={K}")
     g = wl.rng(3000 + fmt, M + N + K)
