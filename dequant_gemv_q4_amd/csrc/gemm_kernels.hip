@@ -99,58 +99,51 @@ __device__ __forceinline__ void gm_barrier()
 
 // x [M][K] f32 -> xh chunks [Mp / 16][KBp][64 lanes][8 halves] in the A-operand order of each
 // 32-k block, and rs[r] = the factor undoing row r's scale; rows past M and columns past K are
-// zero (rs 0 past M).  Workgroup (g, p): rows 16 g .. 16 g + 15, blocks [p bpw, (p + 1) bpw); each
-// finds the largest |x| of its 16 rows over the whole row (a wave per 4 rows) so that the row
-// scale does not depend on the split.  Lane (ir, j) of a block holds elements 4j..4j+3 and
-// 16+4j..16+4j+3 of row ir in both formats (mf_elem(j, h) = mf_elem(0, h) + 4 j).
+// zero (rs 0 past M).  One wave per row: it finds the row's largest |x|, then writes the row's
+// pieces (lane l = (ir, j) of a chunk holds elements 4j..4j+3 and 16+4j..16+4j+3 of row ir in
+// both formats: mf_elem(j, h) = mf_elem(0, h) + 4 j).  The second pass re-reads the row from the
+// cache.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_xprep(const float *x, int64_t M, int64_t K, int KBp,
-                                               int bpw, _Float16 *xh, float *rs)
+                                               _Float16 *xh, float *rs)
 {
-    __shared__ float s_sc[16];
-    const int g = blockIdx.x, p = blockIdx.y, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const bool live = r < M;
     const bool vec = ((uintptr_t)x & 15) == 0;          // K % 32 == 0: every row is aligned too
-    for (int i = 0; i < 4; ++i) {
-        const int rl = 4 * wave + i;
-        const int64_t r = (int64_t)g * 16 + rl;
-        float mx = 0.f;
-        if (r < M) {
-            const float *xr = x + r * K;
-            if (vec) {
+    const float *xr = x + (live ? r : 0) * K;
+    float mx = 0.f;
+    if (live) {
+        if (vec) {
 #pragma unroll 8
-                for (int64_t e = 4 * lane; e < K; e += 256) {
-                    const float4 v = *reinterpret_cast<const float4 *>(xr + e);
-                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-                }
-            } else {
-                for (int64_t e = lane; e < K; e += 64)
-                    mx = fmaxf(mx, fabsf(xr[e]));
+            for (int64_t e = 4 * lane; e < K; e += 256) {
+                const float4 v = *reinterpret_cast<const float4 *>(xr + e);
+                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
             }
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-            mx = fmaxf(mx, __shfl_xor(mx, off));
-        if (lane == 0) {
-            int e2 = 0;
-            frexpf(mx, &e2);                                   // max |x| = f 2^e2, f in [0.5, 1)
-            const int sk = 15 - e2 < 127 ? 15 - e2 : 127;      // 2^sk stays a finite f32
-            s_sc[rl] = r < M ? ldexpf(1.0f, sk) : 0.f;
-            if (p == 0)
-                rs[r] = r < M ? ldexpf(1.0f, -sk) : 0.f;
+        } else {
+#pragma unroll 8
+            for (int64_t e = lane; e < K; e += 64)
+                mx = fmaxf(mx, fabsf(xr[e]));
         }
     }
-    __syncthreads();
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        mx = fmaxf(mx, __shfl_xor(mx, off));
+    int e2 = 0;
+    frexpf(mx, &e2);                                   // max |x| = f 2^e2, f in [0.5, 1)
+    const int sk = 15 - e2 < 127 ? 15 - e2 : 127;      // 2^sk stays a finite f32
+    const float sc = live ? ldexpf(1.0f, sk) : 0.f;
+    if (lane == 0)
+        rs[r] = live ? ldexpf(1.0f, -sk) : 0.f;
+    // piece q of the row: block q / 4, j = q % 4 -> chunk lane 16 j + (r % 16)
     const int KB = (int)(K / 32);
-    const int b_end = (p + 1) * bpw < KBp ? (p + 1) * bpw : KBp;
-    _Float16 *dst = xh + (int64_t)g * KBp * 512;
+    _Float16 *dst = xh + (r / 16) * (int64_t)KBp * 512 + (int64_t)(r % 16) * 8;
 #pragma unroll 4
-    for (int u = p * bpw * 64 + t; u < b_end * 64; u += 256) {
-        const int blk = u >> 6, l = u & 63, ir = l & 15, j = l >> 4;
-        const int64_t r = (int64_t)g * 16 + ir;
-        const float sc = s_sc[ir];
+    for (int q = lane; q < 4 * KBp; q += 64) {
+        const int blk = q >> 2, j = q & 3;
         float lo[4] = {0.f, 0.f, 0.f, 0.f}, hi4[4] = {0.f, 0.f, 0.f, 0.f};
-        if (r < M && blk < KB) {
-            const float *xb = x + r * K + (int64_t)blk * 32 + 4 * j;
+        if (live && blk < KB) {
+            const float *xb = xr + (int64_t)blk * 32 + 4 * j;
             if (vec) {
                 const float4 a = *reinterpret_cast<const float4 *>(xb);
                 const float4 b = *reinterpret_cast<const float4 *>(xb + 16);
@@ -172,7 +165,7 @@ __global__ __launch_bounds__(256) void k_xprep(const float *x, int64_t M, int64_
             const float xv = e >= 16 ? hi4[e - 16] : lo[e];
             v[h] = (_Float16)(xv * sc * (hi ? 0.0625f : 1.0f));
         }
-        *reinterpret_cast<mh8 *>(dst + (int64_t)u * 8) = v;
+        *reinterpret_cast<mh8 *>(dst + ((int64_t)blk * 64 + 16 * j) * 8) = v;
     }
 }
 
@@ -410,20 +403,14 @@ __global__ __launch_bounds__(256) void k_gemm_fold(const float *part, const floa
 int launch_gemm(int fmt, const GemmArgs &a, const float *x, void *stream)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // x preparation: 16-row groups, split along K into parts of at least 4 blocks (one piece per
-    // thread) until there are about 256 workgroups (each part re-reads its rows for the maximum)
-    const int groups = a.m_tiles * GM_BM / 16;
-    int parts = (256 + groups - 1) / groups;
-    parts = parts < a.KBp / 4 ? parts : a.KBp / 4;
-    parts = parts < 1 ? 1 : parts;
-    const int bpw = (a.KBp + parts - 1) / parts;
-    parts = (a.KBp + bpw - 1) / bpw;
+    // x preparation: one wave per row of the padded x
+    const unsigned groups = (unsigned)((int64_t)a.m_tiles * GM_BM / 4);
     if (fmt == FQ4_0)
-        hipLaunchKernelGGL(k_xprep<FQ4_0>, dim3(groups, parts), dim3(256), 0, s, x, a.M, a.K,
-                           a.KBp, bpw, a.xh, a.rs);
+        hipLaunchKernelGGL(k_xprep<FQ4_0>, dim3(groups), dim3(256), 0, s, x, a.M, a.K, a.KBp,
+                           a.xh, a.rs);
     else
-        hipLaunchKernelGGL(k_xprep<FQ8_0>, dim3(groups, parts), dim3(256), 0, s, x, a.M, a.K,
-                           a.KBp, bpw, a.xh, a.rs);
+        hipLaunchKernelGGL(k_xprep<FQ8_0>, dim3(groups), dim3(256), 0, s, x, a.M, a.K, a.KBp,
+                           a.xh, a.rs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return (int)e;
