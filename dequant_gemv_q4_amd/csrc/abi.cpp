@@ -767,20 +767,20 @@ int qgemv_qk_norm_rope(float *qkv, int nb, int n_q_heads, int n_kv_heads, int he
 }
 
 static int64_t gemm_m_tiles(int64_t M) { return (M + QG_GEMM_BM - 1) / QG_GEMM_BM; }
-static int64_t gemm_n_tiles(int64_t N) { return (N + QG_GEMM_BN - 1) / QG_GEMM_BN; }
-
-// Tiles, K steps and K splits of a qgemm call.  The split depends on the shape alone (so the
-// workspace size does too): when the output tiles are fewer than the 256 compute units the K
-// steps are dealt out to several workgroups per tile, at least two steps each.
+// Tiles, K steps and K splits of a qgemm call, from the shape alone (so the workspace size is
+// too).  Q4_0 takes 256-row weight tiles when those alone give the 256 compute units a tile each,
+// else 128-row ones; when the output tiles are still fewer than the compute units the K steps are
+// dealt out to several workgroups per tile, at least two steps each.
 struct GemmPlan {
-    int64_t m_tiles, n_tiles, steps, sps, splits;
+    int64_t m_tiles, n_tiles, bn, steps, sps, splits;
     int64_t xh_bytes, rs_bytes, part_bytes;
 };
-static GemmPlan gemm_plan(int64_t N, int64_t K, int64_t M)
+static GemmPlan gemm_plan(int fmt, int64_t N, int64_t K, int64_t M)
 {
     GemmPlan p;
     p.m_tiles = gemm_m_tiles(M);
-    p.n_tiles = gemm_n_tiles(N);
+    p.bn = fmt == QG_Q4_0 && p.m_tiles * ((N + 255) / 256) >= 256 ? 256 : 128;
+    p.n_tiles = (N + p.bn - 1) / p.bn;
     p.steps = (K + QG_GEMM_KSTEP - 1) / QG_GEMM_KSTEP;
     const int64_t tiles = p.m_tiles * p.n_tiles;
     p.sps = p.steps;
@@ -802,7 +802,7 @@ int64_t qgemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M)
     Layout L;
     if ((fmt != QG_Q4_0 && fmt != QG_Q8_0) || M < 1 || M > QG_GEMM_MAX_M || !layout(fmt, N, K, &L))
         return -1;
-    const GemmPlan p = gemm_plan(N, K, M);
+    const GemmPlan p = gemm_plan(fmt, N, K, M);
     return p.xh_bytes + p.rs_bytes + p.part_bytes;
 }
 
@@ -818,9 +818,9 @@ int qgemm(int fmt, const void *W, int64_t N, int64_t K, const float *x, int64_t 
     Layout L;
     if (M < 1 || M > QG_GEMM_MAX_M || N < 1 || N > 0x7fffffffLL || !layout(fmt, N, K, &L) ||
         N * L.qs_row >= QG_BUF_MAX || N * L.sc_row >= QG_BUF_MAX ||
-        (gemm_n_tiles(N) + 7) * gemm_m_tiles(M) > 0x7fffffffLL)   // the grid
+        (N / 128 + 8) * gemm_m_tiles(M) > 0x7fffffffLL)   // the tile count
         return QG_ERR_SHAPE;
-    const GemmPlan p = gemm_plan(N, K, M);
+    const GemmPlan p = gemm_plan(fmt, N, K, M);
     if ((p.n_tiles + 7) * p.m_tiles * p.splits > 0x7fffffffLL ||
         p.m_tiles * QG_GEMM_BM / 16 * p.steps * QG_GEMM_KSTEP / 32 > 0x7fffffffLL)
         return QG_ERR_SHAPE;
@@ -851,6 +851,7 @@ int qgemm(int fmt, const void *W, int64_t N, int64_t K, const float *x, int64_t 
     a.sc_row = L.sc_row;
     a.n_tiles = (int)p.n_tiles;
     a.m_tiles = (int)p.m_tiles;
+    a.bn = (int)p.bn;
     a.KBp = (int)(p.steps * QG_GEMM_KSTEP / 32);
     a.steps = (int)p.steps;
     a.sps = (int)p.sps;

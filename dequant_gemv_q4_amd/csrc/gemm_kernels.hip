@@ -11,10 +11,12 @@
 //    puts its largest |x| in [2^14, 2^15), the high-nibble positions of Q4_0 times 1/16, and laid
 //    out in 1 KB chunks (16 rows x one 32-k block) whose 64 16-byte pieces are the A operands of
 //    v_mfma_f32_16x16x32_f16 in lane order (mf_elem), zero past K and past M;
-//  - a workgroup (8 waves) owns a 128 x 128 tile of Y; wave w owns all 128 x rows against weight
-//    rows 16 w .. 16 w + 15 (8 x 1 MFMA tiles), so each weight is decoded once per workgroup and
-//    feeds 16 MFMAs per block (the decode is VALU work; eight x tiles per decoded weight tile keep
-//    it under the matrix-core time).  A step covers 128 k (4 blocks);
+//  - a workgroup (8 waves) owns a 128 x 256 tile of Y (Q4_0 when such tiles fill the device, else
+//    128 x 128); wave w owns all 128 x rows against weight rows 32 w .. 32 w + 31 (8 x 2 MFMA
+//    tiles; with 128-row tiles 16 rows, 8 x 1), so
+//    each weight is decoded once per workgroup and feeds 16 MFMAs per block (the decode is VALU
+//    work; eight x tiles per decoded weight tile keep it under the matrix-core time), and each x
+//    operand read from LDS feeds two weight tiles.  A step covers 128 k (4 blocks);
 //  - x chunks, weight chunks (16 rows x 64 bytes for Q4_0, x 128 bytes for Q8_0) and the block
 //    scales go from global memory straight into LDS (global_load_lds: no registers, no LDS store
 //    instructions), three stages deep: the loads of step s + 2 are issued while step s computes,
@@ -40,21 +42,25 @@
 namespace qg {
 
 constexpr int GM_THREADS = 512;                   // 8 waves
-constexpr int GM_BM = 128, GM_BN = 128;           // rows of x, rows of W per workgroup
+constexpr int GM_BM = 128;                        // rows of x per workgroup
 constexpr int GM_BPS = 4;                         // 32-k blocks per step
 constexpr int GM_STAGES = 3;
-static_assert(GM_BM == QG_GEMM_BM && GM_BN == QG_GEMM_BN && GM_BPS * 32 == QG_GEMM_KSTEP,
-              "the host plans with these tiles");
+static_assert(GM_BM == QG_GEMM_BM && GM_BPS * 32 == QG_GEMM_KSTEP, "the host plans with these tiles");
 
 // LDS stage of one step: x chunks [row group 0..7][block 0..3] (1 KB each), then weight chunks
-// [row group 0..7][half] (1 KB each: 16 rows x 4 chunks of 16 B), then the scales [row][block],
-// one dword each (a 2-byte copy to LDS fills its lane's dword, zero-extended).
-template <int FMT>
+// [row group][half] (1 KB each: 16 rows x 4 chunks of 16 B), then the scales [row][block], one
+// dword each (a 2-byte copy to LDS fills its lane's dword, zero-extended).  A wave owns WPW
+// 16-row weight groups: two for Q4_0 when the 128 x 256 tiles alone fill the device (each x
+// operand read from LDS then feeds twice the products), else one (more, smaller tiles; Q8_0
+// always, its weight chunks being twice as many).
+template <int FMT, int WPW_>
 struct GemmStage {
     static constexpr int WH = FMT == FQ8_0 ? 2 : 1;            // weight wave-loads per row group
+    static constexpr int WPW = WPW_;                           // weight row groups per wave
+    static constexpr int BN = 8 * 16 * WPW;                    // weight rows per workgroup
     static constexpr int XB = GM_BM / 16 * GM_BPS * 1024;
-    static constexpr int WB = GM_BN / 16 * WH * 1024;
-    static constexpr int SB = GM_BN * GM_BPS * 4;
+    static constexpr int WB = BN / 16 * WH * 1024;
+    static constexpr int SB = BN * GM_BPS * 4;
     static constexpr int BYTES = XB + WB + SB;
     static constexpr int XPW = GM_BM / 16 * GM_BPS / 8;         // x wave-loads per wave
 };
@@ -169,10 +175,11 @@ __global__ __launch_bounds__(256) void k_xprep(const float *x, int64_t M, int64_
     }
 }
 
-template <int FMT>
+template <int FMT, int WPW>
 __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
 {
-    using G = GemmStage<FMT>;
+    using G = GemmStage<FMT, WPW>;
+    static_assert(FMT == FQ4_0 || WPW == 1, "Q8_0 stages one weight group per wave");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[GM_STAGES * G::BYTES];
     __shared__ __attribute__((aligned(16))) float s_rs[3][GM_BM];   // row factors of 3 tiles
 
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
     auto tile_of = [&](int k8) {
         Tile t;
         const int rest = k8 / ntx;
-        t.n0 = (int64_t)(n_base + k8 % ntx) * GM_BN;
+        t.n0 = (int64_t)(n_base + k8 % ntx) * G::BN;
         t.m0 = (int64_t)(rest % a.m_tiles) * GM_BM;
         t.split = rest / a.m_tiles;
         t.s0 = t.split * a.sps;
@@ -209,10 +216,10 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
     const int C = (int)(a.qs_row / 16), KB = (int)(a.K / 32);
 
     // loads of step s of tile t into ring slot `ring`.  x: chunk c = XPW wave + u of the stage is
-    // row group c / 4, block c % 4.  Weights: row group `wave`, lane (ir, lc) -> row 16 wave + ir,
-    // chunk 4 h + lc of the step (rows past N read row N - 1, chunks past the row its last chunk).
-    // Scales: lane l -> row 16 wave + l / 4, block l % 4 of the step (dword 4 row + block of the
-    // scale area).  With a tile's first step, waves 0 and 1 also load its 128 row factors.
+    // row group c / 4, block c % 4.  Weights: row groups g = WPW wave + wt, lane (ir, lc) -> row
+    // 16 g + ir, chunk 4 h + lc of the step (rows past N read row N - 1, chunks past the row its
+    // last chunk).  Scales: lane l -> row 16 g + l / 4, block l % 4 of the step (dword 4 row +
+    // block of the scale area).  With a tile's first step, waves 0 and 1 also load its 128 row factors.
     auto issue = [&](const Tile &t, int s_rel, int ring, int rs_slot) {
         const int s = t.s0 + s_rel;
         uint8_t *st = lds + ring * G::BYTES;
@@ -224,31 +231,37 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
                 xsrc + ((int64_t)(c / GM_BPS) * a.KBp + (int64_t)s * GM_BPS + c % GM_BPS) * 512;
             gm_dma16(src, st + c * 1024);
         }
-        const int64_t wr = t.n0 + 16 * wave + ir < a.N ? t.n0 + 16 * wave + ir : a.N - 1;
-        const uint8_t *wsrc = a.qs + wr * a.qs_row;
-#pragma unroll
-        for (int h = 0; h < G::WH; ++h) {
-            const int ch0 = (s * G::WH + h) * 4 + lc;
-            const int ch = ch0 < C ? ch0 : C - 1;
-            gm_dma16(wsrc + 16 * (int64_t)ch, st + G::XB + (wave * G::WH + h) * 1024);
-        }
-        const int64_t sr =
-            t.n0 + 16 * wave + (lane >> 2) < a.N ? t.n0 + 16 * wave + (lane >> 2) : a.N - 1;
         const int b0 = s * GM_BPS + (lane & 3);
         const int blk = b0 < KB ? b0 : KB - 1;
-        gm_dma2(a.sc + sr * a.sc_row + 2 * (int64_t)blk, st + G::XB + G::WB + wave * 256);
+#pragma unroll
+        for (int wt = 0; wt < G::WPW; ++wt) {
+            const int g = G::WPW * wave + wt;                  // weight row group
+            const int64_t wr = t.n0 + 16 * g + ir < a.N ? t.n0 + 16 * g + ir : a.N - 1;
+            const uint8_t *wsrc = a.qs + wr * a.qs_row;
+#pragma unroll
+            for (int h = 0; h < G::WH; ++h) {
+                const int ch0 = (s * G::WH + h) * 4 + lc;
+                const int ch = ch0 < C ? ch0 : C - 1;
+                gm_dma16(wsrc + 16 * (int64_t)ch, st + G::XB + (g * G::WH + h) * 1024);
+            }
+            const int64_t sr =
+                t.n0 + 16 * g + (lane >> 2) < a.N ? t.n0 + 16 * g + (lane >> 2) : a.N - 1;
+            gm_dma2(a.sc + sr * a.sc_row + 2 * (int64_t)blk, st + G::XB + G::WB + g * 256);
+        }
         if (s_rel == 0 && wave < 2)
             gm_dma4(a.rs + t.m0 + 64 * wave + lane, &s_rs[rs_slot][64 * wave]);
     };
 
-    float acc[8][4];        // Q8_0: per-block scaled sums (VALU)
-    mf4 macc[8];            // Q4_0: sums kept in the MFMA accumulators
+    float acc[8][G::WPW][4];    // Q8_0: per-block scaled sums (VALU)
+    mf4 macc[8][G::WPW];        // Q4_0: sums kept in the MFMA accumulators
     auto zero_acc = [&]() {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            acc[i][0] = acc[i][1] = acc[i][2] = acc[i][3] = 0.f;
-            macc[i] = mf4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int wt = 0; wt < G::WPW; ++wt) {
+                acc[i][wt][0] = acc[i][wt][1] = acc[i][wt][2] = acc[i][wt][3] = 0.f;
+                macc[i][wt] = mf4{0.f, 0.f, 0.f, 0.f};
+            }
     };
     zero_acc();
 
@@ -256,19 +269,26 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
     auto compute = [&](const Tile &t, int s_rel, int ring) {
         const int s = t.s0 + s_rel;
         const uint8_t *st = lds + ring * G::BYTES;
-        // this wave's weights (row group `wave`, loaded by this wave); after the transpose q[h][b']
-        // is dword lc of chunk 4 h + b' of row ir
-        uint32_t q[G::WH][4];
+        // this wave's weights (row groups WPW wave + wt, loaded by this wave); after the transpose
+        // q[wt][h][b'] is dword lc of chunk 4 h + b' of row ir
+        uint32_t q[G::WPW][G::WH][4];
+        uint4 dsc[G::WPW];
 #pragma unroll
-        for (int h = 0; h < G::WH; ++h) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(st + G::XB + (wave * G::WH + h) * 1024 +
-                                                             16 * lane);
-            q[h][0] = v.x; q[h][1] = v.y; q[h][2] = v.z; q[h][3] = v.w;
+        for (int wt = 0; wt < G::WPW; ++wt) {
+            const int g = G::WPW * wave + wt;
+#pragma unroll
+            for (int h = 0; h < G::WH; ++h) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(st + G::XB + (g * G::WH + h) * 1024 +
+                                                                 16 * lane);
+                q[wt][h][0] = v.x; q[wt][h][1] = v.y; q[wt][h][2] = v.z; q[wt][h][3] = v.w;
+            }
+            dsc[wt] = *reinterpret_cast<const uint4 *>(st + G::XB + G::WB + (16 * g + ir) * 16);
         }
-        const uint4 dsc = *reinterpret_cast<const uint4 *>(st + G::XB + G::WB + (16 * wave + ir) * 16);
 #pragma unroll
-        for (int h = 0; h < G::WH; ++h)
-            mf_xpose(q[h]);
+        for (int wt = 0; wt < G::WPW; ++wt)
+#pragma unroll
+            for (int h = 0; h < G::WH; ++h)
+                mf_xpose(q[wt][h]);
 #pragma unroll
         for (int b = 0; b < GM_BPS; ++b) {
             const int blk = GM_BPS * s + b;
@@ -276,72 +296,80 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
 #pragma unroll
             for (int bt = 0; bt < 8; ++bt)
                 A[bt] = *reinterpret_cast<const mh8 *>(st + (bt * GM_BPS + b) * 1024 + 16 * lane);
-            const uint32_t dw = b == 0 ? dsc.x : b == 1 ? dsc.y : b == 2 ? dsc.z : dsc.w;
-            if constexpr (FMT == FQ4_0) {
-                // exact scaled weights: d = d_hi + d_lo with d_hi the top 8 significant bits of
-                // the f16 scale, d_lo the rest (3 bits); |q - 8| <= 8 needs at most 3 more bits,
-                // so d_hi (q - 8) and d_lo (q - 8) are exact f16 values (the high-nibble halves,
-                // held x16, too).  Two MFMAs per block accumulate them straight into the
-                // accumulators: first the d_hi products of all 8 tiles, then the d_lo ones.
-                const mh8 B = mf_bop<FMT>(q[0][b], 0u, kc);
-                const uint16_t db = blk < KB ? (uint16_t)(dw & 0xFFFFu) : (uint16_t)0;
-                const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)(db & 0xFFF8u));
-                const _Float16 dl = __builtin_bit_cast(_Float16, db) - dh;
-                const mh8 Bh = B * dh, Bl = B * dl;
 #pragma unroll
-                for (int bt = 0; bt < 8; ++bt)
-                    macc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt], Bh, macc[bt], 0, 0, 0);
+            for (int wt = 0; wt < G::WPW; ++wt) {
+                const uint32_t dw = b == 0 ? dsc[wt].x : b == 1 ? dsc[wt].y : b == 2 ? dsc[wt].z : dsc[wt].w;
+                if constexpr (FMT == FQ4_0) {
+                    // exact scaled weights: d = d_hi + d_lo with d_hi the top 8 significant bits
+                    // of the f16 scale, d_lo the rest (3 bits); |q - 8| <= 8 needs at most 3 more
+                    // bits, so d_hi (q - 8) and d_lo (q - 8) are exact f16 values (the high-nibble
+                    // halves, held x16, too).  Two MFMAs per block accumulate them straight into
+                    // the accumulators: first the d_hi products of all 8 tiles, then the d_lo ones.
+                    const mh8 B = mf_bop<FMT>(q[wt][0][b], 0u, kc);
+                    const uint16_t db = blk < KB ? (uint16_t)(dw & 0xFFFFu) : (uint16_t)0;
+                    const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)(db & 0xFFF8u));
+                    const _Float16 dl = __builtin_bit_cast(_Float16, db) - dh;
+                    const mh8 Bh = B * dh, Bl = B * dl;
 #pragma unroll
-                for (int bt = 0; bt < 8; ++bt)
-                    macc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt], Bl, macc[bt], 0, 0, 0);
-            } else {
-                // block b = chunks 2 b, 2 b + 1 of the step
-                const int h = b >> 1, p = 2 * (b & 1);
-                const mh8 B = mf_bop<FMT>(q[h][p], q[h][p + 1], kc);
-                const uint16_t db = (uint16_t)(dw & 0xFFFFu);
-                const float d = blk < KB ? (float)__builtin_bit_cast(_Float16, db) : 0.f;
-                const mf4 zero = {0.f, 0.f, 0.f, 0.f};
+                    for (int bt = 0; bt < 8; ++bt)
+                        macc[bt][wt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt], Bh, macc[bt][wt], 0, 0, 0);
 #pragma unroll
-                for (int bt = 0; bt < 8; bt += 4) {
-                    mf4 D[4];
+                    for (int bt = 0; bt < 8; ++bt)
+                        macc[bt][wt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt], Bl, macc[bt][wt], 0, 0, 0);
+                } else {
+                    // block b = chunks 2 b, 2 b + 1 of the step
+                    const int h = b >> 1, p = 2 * (b & 1);
+                    const mh8 B = mf_bop<FMT>(q[wt][h][p], q[wt][h][p + 1], kc);
+                    const uint16_t db = (uint16_t)(dw & 0xFFFFu);
+                    const float d = blk < KB ? (float)__builtin_bit_cast(_Float16, db) : 0.f;
+                    const mf4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        D[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt + i], B, zero, 0, 0, 0);
+                    for (int bt = 0; bt < 8; bt += 4) {
+                        mf4 D[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[bt + i][0] = fmaf(d, D[i][0], acc[bt + i][0]);
-                        acc[bt + i][1] = fmaf(d, D[i][1], acc[bt + i][1]);
-                        acc[bt + i][2] = fmaf(d, D[i][2], acc[bt + i][2]);
-                        acc[bt + i][3] = fmaf(d, D[i][3], acc[bt + i][3]);
+                        for (int i = 0; i < 4; ++i)
+                            D[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt + i], B, zero, 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            acc[bt + i][wt][0] = fmaf(d, D[i][0], acc[bt + i][wt][0]);
+                            acc[bt + i][wt][1] = fmaf(d, D[i][1], acc[bt + i][wt][1]);
+                            acc[bt + i][wt][2] = fmaf(d, D[i][2], acc[bt + i][wt][2]);
+                            acc[bt + i][wt][3] = fmaf(d, D[i][3], acc[bt + i][wt][3]);
+                        }
                     }
                 }
             }
         }
     };
 
-    // lane (ir, lc) holds D[4 lc + v][ir]: x row 16 bt + 4 lc + v, weight row 16 wave + ir
+    // lane (ir, lc) holds D[4 lc + v][ir] of tile (bt, wt): x row 16 bt + 4 lc + v, weight row
+    // 16 (WPW wave + wt) + ir
     auto epilogue = [&](const Tile &t, int rs_slot) {
         const bool fold = a.splits > 1;
         float *out = fold ? a.part + (int64_t)t.split * a.M * a.N : a.y;
-        const int64_t n = t.n0 + 16 * wave + ir;
 #pragma unroll
         for (int bt = 0; bt < 8; ++bt)
 #pragma unroll
             for (int vv = 0; vv < 4; ++vv) {
                 const int rl = 16 * bt + 4 * lc + vv;
                 const int64_t r = t.m0 + rl;
-                if (r >= a.M || n >= a.N)
+                if (r >= a.M)
                     continue;
                 const float f = fold ? 1.0f : s_rs[rs_slot][rl];
-                const float v = FMT == FQ4_0 ? macc[bt][vv] : acc[bt][vv];
-                out[r * a.N + n] = v * f;
+#pragma unroll
+                for (int wt = 0; wt < G::WPW; ++wt) {
+                    const int64_t n = t.n0 + 16 * (G::WPW * wave + wt) + ir;
+                    const float v = FMT == FQ4_0 ? macc[bt][wt][vv] : acc[bt][wt][vv];
+                    if (n < a.N)
+                        out[r * a.N + n] = v * f;
+                }
             }
     };
 
     // One stream of (tile, step) pairs per workgroup; the loads run two steps ahead of the
     // compute, across tile boundaries (the next tile's first loads overlap this tile's last steps
     // and its stores).  Ring slot of stream position p: p % 3.
-    constexpr int LPS = G::XPW + G::WH + 1;   // loads per thread per step (+1 at a tile's start)
+    constexpr int LPS = G::XPW + G::WPW * (G::WH + 1);   // loads per thread per step (+1 at a tile's start)
     int ik8 = slot, is = 0, itn = 0, pi = 0;  // issue cursor: tile, step, tile ordinal, position
     Tile ti = tile_of(ik8);
     auto issue_next = [&]() {
@@ -418,10 +446,12 @@ int launch_gemm(int fmt, const GemmArgs &a, const float *x, void *stream)
     // XCD, each walking its XCD's tiles
     const int per_xcd = ((a.n_tiles + 7) / 8) * a.m_tiles * a.splits;
     const int grid = 8 * (per_xcd < 32 ? per_xcd : 32);
-    if (fmt == FQ4_0)
-        hipLaunchKernelGGL(k_gemm<FQ4_0>, dim3(grid), dim3(GM_THREADS), 0, s, a);
+    if (fmt == FQ4_0 && a.bn == 256)
+        hipLaunchKernelGGL((k_gemm<FQ4_0, 2>), dim3(grid), dim3(GM_THREADS), 0, s, a);
+    else if (fmt == FQ4_0)
+        hipLaunchKernelGGL((k_gemm<FQ4_0, 1>), dim3(grid), dim3(GM_THREADS), 0, s, a);
     else
-        hipLaunchKernelGGL(k_gemm<FQ8_0>, dim3(grid), dim3(GM_THREADS), 0, s, a);
+        hipLaunchKernelGGL((k_gemm<FQ8_0, 1>), dim3(grid), dim3(GM_THREADS), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1)
         return (int)e;

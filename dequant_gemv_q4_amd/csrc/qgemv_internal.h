@@ -194,9 +194,9 @@ struct MoeArgs {
     int pool_max;               // most row groups one workgroup's range may hold
 };
 
-// Tile of the wide row-batch GEMM: rows of x and rows of W per workgroup, k per step.
+// Tile of the wide row-batch GEMM: rows of x per workgroup, k per step; rows of W per workgroup
+// are 128 or (Q4_0, when the tiles fill the device) 256.
 #define QG_GEMM_BM 128
-#define QG_GEMM_BN 128
 #define QG_GEMM_KSTEP 128
 // Arguments of the wide row-batch GEMM (gemm_kernels.hip).
 struct GemmArgs {
@@ -207,7 +207,8 @@ struct GemmArgs {
     float *y;                   // [M][N]
     int64_t N, K, M;
     int64_t qs_row, sc_row;
-    int n_tiles, m_tiles;       // tiles of W (QG_GEMM_BN rows) and of x (QG_GEMM_BM rows)
+    int n_tiles, m_tiles;       // tiles of W (bn rows) and of x (QG_GEMM_BM rows)
+    int bn;                     // rows of W per tile: 128 or 256
     int KBp;                    // 32-k blocks of a padded x row: steps * QG_GEMM_KSTEP / 32
     int steps, sps, splits;     // K steps, steps per split, splits (ceil(steps / sps))
 };

@@ -46,9 +46,11 @@ def test_qgemm_parity(fmt, M, N, K):
     assert_within(y, yr, tol_gemv(A, yr), f"qgemm fmt={fmt} M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("fmt,M,N,K", [(q.Q4_0, 2048, 4096, 2048), (q.Q8_0, 2048, 2048, 1536)])
+@pytest.mark.parametrize("fmt,M,N,K", [(q.Q4_0, 2048, 4096, 2048), (q.Q8_0, 2048, 2048, 1536),
+                                       (q.Q4_0, 1950, 4000, 1056)])
 def test_qgemm_large_sampled(fmt, M, N, K):
-    """Full-size launch; the oracle checks 64 sampled x rows against 256 sampled W rows."""
+    """Full-size launch; the oracle checks 64 sampled x rows against 256 sampled W rows.  The
+    Q4_0 cases take the 256-row weight tiles (the second one ragged in M, N and K)."""
     say(f"qgemm large fmt={fmt} M={M} N={N} K={K}")
     g = wl.rng(3100 + fmt, M)
     W = wl.matrix(fmt, g, N, K)
