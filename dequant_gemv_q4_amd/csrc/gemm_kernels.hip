@@ -13,10 +13,10 @@
 //    v_mfma_f32_16x16x32_f16 in lane order (mf_elem), zero past K and past M;
 //  - a workgroup (8 waves) owns a 128 x 256 tile of Y (Q4_0 when such tiles fill the device, else
 //    128 x 128); wave w owns all 128 x rows against weight rows 32 w .. 32 w + 31 (8 x 2 MFMA
-//    tiles; with 128-row tiles 16 rows, 8 x 1), so
-//    each weight is decoded once per workgroup and feeds 16 MFMAs per block (the decode is VALU
-//    work; eight x tiles per decoded weight tile keep it under the matrix-core time), and each x
-//    operand read from LDS feeds two weight tiles.  A step covers 128 k (4 blocks);
+//    tiles; with 128-row tiles 16 rows, 8 x 1), so each weight is decoded once per workgroup and
+//    feeds 16 MFMAs per block (the decode is VALU work; eight x tiles per decoded weight tile keep
+//    it under the matrix-core time), and each x operand read from LDS feeds one or two weight
+//    tiles.  A step covers 128 k (4 blocks);
 //  - x chunks, weight chunks (16 rows x 64 bytes for Q4_0, x 128 bytes for Q8_0) and the block
 //    scales go from global memory straight into LDS (global_load_lds: no registers, no LDS store
 //    instructions), three stages deep: the loads of step s + 2 are issued while step s computes,
@@ -75,23 +75,24 @@ __device__ __forceinline__ void gm_wait()
 
 // Global -> LDS copies (global_load_lds): lane l's 16 bytes land at LDS address M0 + 16 l, M0
 // being the wave's destination; a 4-byte copy lands at M0 + 4 l and a 2-byte copy writes lane
-// l's value zero-extended to the dword at M0 + 4 l.  Written as asm so that the compiler does not track them: it
-// would otherwise wait for every copy in flight before any LDS read; the kernel waits for each
-// stage with vmcnt itself.  One wait state between the M0 write and the copy.
+// l's value zero-extended to the dword at M0 + 4 l.  Written as asm so that the compiler does not
+// track them for its waits: it would otherwise wait for every copy in flight before any LDS read;
+// the kernel waits for each stage with vmcnt itself.  The memory clobber tells the compiler that
+// LDS changes here.  One wait state between the M0 write and the copy.
 __device__ __forceinline__ void gm_dma16(const void *src, const void *lds_dst)
 {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0));
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
 }
 __device__ __forceinline__ void gm_dma4(const void *src, const void *lds_dst)
 {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(src), "{m0}"(m0));
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(src), "{m0}"(m0) : "memory");
 }
 __device__ __forceinline__ void gm_dma2(const void *src, const void *lds_dst)
 {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-    asm volatile("s_nop 0\n\tglobal_load_lds_ushort %0, off" : : "v"(src), "{m0}"(m0));
+    asm volatile("s_nop 0\n\tglobal_load_lds_ushort %0, off" : : "v"(src), "{m0}"(m0) : "memory");
 }
 
 // workgroup barrier that the compiler may not move memory accesses across (the LDS reads of a
