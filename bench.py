@@ -322,10 +322,10 @@ def make_gemm(warm, M=512, N=8192, K=2048, fmt=None):
                  flops=2 * M * N * K)
 
 
-def make_read(warm, nbytes=75497472, shape=(256, 1024)):
+def make_read(warm, nbytes=75497472, shape=(256, 1024), chunked=False):
     """The attainable read rate: the plain 16-byte-load read kernel (libqgbw.so) over the same
     number of bytes as the gate's weights, rotated over >= 1 GiB like the GEMV, at one launch
-    shape."""
+    shape, in grid-stride order or one contiguous chunk per workgroup."""
     import torch
     from dequant_gemv_q4_amd import bwref
 
@@ -336,13 +336,14 @@ def make_read(warm, nbytes=75497472, shape=(256, 1024)):
     out = torch.empty(grid * threads // 64, dtype=torch.int32, device="cuda")
 
     def step(i):
-        bwref.read(sets[i % R], nbytes, out, grid, threads)
+        bwref.read(sets[i % R], nbytes, out, grid, threads, chunked)
 
-    name = f"read_{nbytes}B_{grid}x{threads}"
-    cfg = {"workload": name, "bytes": nbytes, "grid": grid, "threads": threads,
+    order = "chunked" if chunked else "grid_stride"
+    name = f"read_{nbytes}B_{grid}x{threads}_{order}"
+    cfg = {"workload": name, "bytes": nbytes, "grid": grid, "threads": threads, "order": order,
            "launches_per_step": 1, "weight_copies": R, "cold": not warm}
-    return Bench(name, nbytes, nbytes, f"plain 16-byte read ({grid} x {threads})", step, step,
-                 lambda: 0, cfg)
+    return Bench(name, nbytes, nbytes, f"plain 16-byte read ({grid} x {threads}, {order})", step,
+                 step, lambda: 0, cfg)
 
 
 def make_copy(warm):
@@ -623,13 +624,17 @@ def main():
         w = run_extra("gemv warm", lambda: make_gemv(True, 1), es, ew, torch)
         w["label"] = "cache-assisted: one weight copy reused, served in part by the 256 MB MALL"
         extras["gemv_nb1_warm"] = w
-        # attainable: the plain read kernel over the gate's bytes at a few launch shapes (best kept)
+        # attainable: the plain read kernel over the gate's bytes at a few launch shapes and
+        # both orders (best kept)
         best = None
-        for shape in ((256, 1024), (512, 1024), (1024, 512), (2048, 256)):
-            r = run_extra(f"read {shape}", lambda: make_read(False, shape=shape), es, ew, torch)
-            if best is None or r["value"] > best["value"]:
-                best = r
-        best["label"] = "plain 16-byte non-temporal read of the same bytes, best launch shape"
+        for chunked in (False, True):
+            for shape in ((256, 1024), (512, 1024), (1024, 512), (2048, 256)):
+                r = run_extra(f"read {shape}{' chunked' if chunked else ''}",
+                              lambda: make_read(False, shape=shape, chunked=chunked), es, ew, torch)
+                if best is None or r["value"] > best["value"]:
+                    best = r
+        best["label"] = ("plain 16-byte non-temporal read of the same bytes, best launch shape "
+                         "and order")
         extras["read_attainable"] = best
         out["attainable_read_gbps"] = best["value"]
         out["pct_of_attainable"] = round(100 * out["value"] / best["value"], 2)
