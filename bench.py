@@ -621,6 +621,9 @@ def main():
         for M in (64, 512, 2048):
             extras[f"gemm_q4_0_m{M}"] = run_extra(f"gemm M={M}", lambda M=M: make_gemm(False, M),
                                                   min(es, 50), 5, torch)
+        extras["gemm_q1_0_m2048"] = run_extra("gemm q1_0 M=2048",
+                                              lambda: make_gemm(False, 2048, fmt=q.Q1_0),
+                                              min(es, 50), 5, torch)
         w = run_extra("gemv warm", lambda: make_gemv(True, 1), es, ew, torch)
         w["label"] = "cache-assisted: one weight copy reused, served in part by the 256 MB MALL"
         extras["gemv_nb1_warm"] = w

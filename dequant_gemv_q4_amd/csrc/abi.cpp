@@ -800,7 +800,8 @@ static GemmPlan gemm_plan(int fmt, int64_t N, int64_t K, int64_t M)
 int64_t qgemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M)
 {
     Layout L;
-    if ((fmt != QG_Q4_0 && fmt != QG_Q8_0) || M < 1 || M > QG_GEMM_MAX_M || !layout(fmt, N, K, &L))
+    if ((fmt != QG_Q4_0 && fmt != QG_Q8_0 && fmt != QG_Q1_0) || M < 1 || M > QG_GEMM_MAX_M ||
+        !layout(fmt, N, K, &L))
         return -1;
     const GemmPlan p = gemm_plan(fmt, N, K, M);
     return p.xh_bytes + p.rs_bytes + p.part_bytes;
@@ -811,7 +812,7 @@ int qgemm(int fmt, const void *W, int64_t N, int64_t K, const float *x, int64_t 
 {
     if (!fmt_valid(fmt))
         return QG_ERR_FORMAT;
-    if (fmt != QG_Q4_0 && fmt != QG_Q8_0)
+    if (fmt != QG_Q4_0 && fmt != QG_Q8_0 && fmt != QG_Q1_0)
         return QG_ERR_FORMAT;
     if (!W || !x || !y)
         return QG_ERR_NULL;

@@ -1,5 +1,5 @@
 // gemm_kernels.hip -- wide row-batch dequant GEMM (prefill chunks of many rows) on the gfx950
-// matrix cores: Y[M][N] = X[M][K] W[N][K]^T with W block-quantized (Q4_0, Q8_0).
+// matrix cores: Y[M][N] = X[M][K] W[N][K]^T with W block-quantized (Q4_0, Q8_0, Q1_0).
 //
 // "Module gpu" (cherenkov qwen4_exp docs), module prefill: a prompt chunk of up to a few thousand
 // tokens goes through a layer at once so that each weight is streamed once for the whole chunk;
@@ -29,7 +29,9 @@
 //    splits exactly into d_hi (8 significant bits) + d_lo, so d_hi (q - 8) and d_lo (q - 8) are
 //    exact f16 operands and two MFMAs per block accumulate the scaled product straight into the
 //    MFMA accumulators; Q8_0 (8-bit q): one MFMA per block gives D = A B and acc += d D on the
-//    VALU.  Either way the weights stay exact; only x is rounded, by at most 2^-11 of itself;
+//    VALU; Q1_0 (sign bits, one f16 d per 128 weights, "Crate inferencelayer" docs, gemm_q1_src):
+//    the weights are +-d, exact f16, one MFMA per block.  Either way the weights stay exact; only
+//    x is rounded, by at most 2^-11 of itself;
 //  - the grid walks the tiles XCD by XCD (workgroup i runs on XCD i % 8): each XCD owns a range of
 //    weight tiles and walks them row-tile-major, so the workgroups resident on an XCD share a few x
 //    row tiles and the XCD's weight tiles in its L2;
@@ -53,14 +55,16 @@ static_assert(GM_BM == QG_GEMM_BM && GM_BPS * 32 == QG_GEMM_KSTEP, "the host pla
 // 16-row weight groups: two for Q4_0 when the 128 x 256 tiles alone fill the device (each x
 // operand read from LDS then feeds twice the products), else one (more, smaller tiles; Q8_0
 // always, its weight chunks being twice as many).
+// Q1_0: a step is one 128-weight block, 16 bytes of sign bits per row ([row][4 dwords], one
+// dword wave-load per 16 rows) and one scale per row (lane r of the wave's 256-byte area).
 template <int FMT, int WPW_>
 struct GemmStage {
     static constexpr int WH = FMT == FQ8_0 ? 2 : 1;            // weight wave-loads per row group
     static constexpr int WPW = WPW_;                           // weight row groups per wave
     static constexpr int BN = 8 * 16 * WPW;                    // weight rows per workgroup
     static constexpr int XB = GM_BM / 16 * GM_BPS * 1024;
-    static constexpr int WB = BN / 16 * WH * 1024;
-    static constexpr int SB = BN * GM_BPS * 4;
+    static constexpr int WB = FMT == FQ1_0 ? BN * 16 : BN / 16 * WH * 1024;
+    static constexpr int SB = FMT == FQ1_0 ? BN / 16 * 256 : BN * GM_BPS * 4;
     static constexpr int BYTES = XB + WB + SB;
     static constexpr int XPW = GM_BM / 16 * GM_BPS / 8;         // x wave-loads per wave
 };
@@ -180,7 +184,7 @@ template <int FMT, int WPW>
 __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
 {
     using G = GemmStage<FMT, WPW>;
-    static_assert(FMT == FQ4_0 || WPW == 1, "Q8_0 stages one weight group per wave");
+    static_assert(FMT == FQ4_0 || WPW == 1, "Q8_0 and Q1_0 stage one weight group per wave");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[GM_STAGES * G::BYTES];
     __shared__ __attribute__((aligned(16))) float s_rs[3][GM_BM];   // row factors of 3 tiles
 
@@ -232,6 +236,20 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
                 xsrc + ((int64_t)(c / GM_BPS) * a.KBp + (int64_t)s * GM_BPS + c % GM_BPS) * 512;
             gm_dma16(src, st + c * 1024);
         }
+        if constexpr (FMT == FQ1_0) {
+            // sign words: lane l -> row 16 wave + l / 4, dword l % 4 of the step's block; scale:
+            // lane l -> row 16 wave + l % 16 (lanes 16.. repeat those rows)
+            const int64_t wr = t.n0 + 16 * wave + (lane >> 2) < a.N ? t.n0 + 16 * wave + (lane >> 2)
+                                                                    : a.N - 1;
+            gm_dma4(a.qs + wr * a.qs_row + 16 * (int64_t)s + 4 * (lane & 3),
+                    st + G::XB + wave * 256);
+            const int64_t sr = t.n0 + 16 * wave + (lane & 15) < a.N ? t.n0 + 16 * wave + (lane & 15)
+                                                                   : a.N - 1;
+            gm_dma2(a.sc + sr * a.sc_row + 2 * (int64_t)s, st + G::XB + G::WB + wave * 256);
+            if (s_rel == 0 && wave < 2)
+                gm_dma4(a.rs + t.m0 + 64 * wave + lane, &s_rs[rs_slot][64 * wave]);
+            return;
+        }
         const int b0 = s * GM_BPS + (lane & 3);
         const int blk = b0 < KB ? b0 : KB - 1;
 #pragma unroll
@@ -270,6 +288,32 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
     auto compute = [&](const Tile &t, int s_rel, int ring) {
         const int s = t.s0 + s_rel;
         const uint8_t *st = lds + ring * G::BYTES;
+        if constexpr (FMT == FQ1_0) {
+            // row ir's four sign words and its scale; lane column lc of block b takes the pairs
+            // (element 4 lc + p, element 4 lc + p + 16), p = 0..3, as +-d: the sign bits moved to
+            // bits 15 and 31 (a set bit is +d), then xor-ed into the f16 pair (d, d)
+            const uint4 qv = *reinterpret_cast<const uint4 *>(st + G::XB + (16 * wave + ir) * 16);
+            const uint32_t db = *reinterpret_cast<const uint32_t *>(st + G::XB + G::WB + wave * 256 +
+                                                                   4 * ir) & 0xFFFFu;
+            const uint32_t dp = db | (db << 16);
+#pragma unroll
+            for (int b = 0; b < GM_BPS; ++b) {
+                const uint32_t w = ~(b == 0 ? qv.x : b == 1 ? qv.y : b == 2 ? qv.z : qv.w);
+                uint4 bw;
+                bw.x = (((w >> (4 * lc + 0)) << 15) & 0x80008000u) ^ dp;
+                bw.y = (((w >> (4 * lc + 1)) << 15) & 0x80008000u) ^ dp;
+                bw.z = (((w >> (4 * lc + 2)) << 15) & 0x80008000u) ^ dp;
+                bw.w = (((w >> (4 * lc + 3)) << 15) & 0x80008000u) ^ dp;
+                const mh8 B = __builtin_bit_cast(mh8, bw);
+#pragma unroll
+                for (int bt = 0; bt < 8; ++bt) {
+                    const mh8 A = *reinterpret_cast<const mh8 *>(st + (bt * GM_BPS + b) * 1024 + 16 * lane);
+                    macc[bt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, macc[bt][0], 0, 0, 0);
+                }
+            }
+            (void)s;
+            return;
+        }
         // this wave's weights (row groups WPW wave + wt, loaded by this wave); after the transpose
         // q[wt][h][b'] is dword lc of chunk 4 h + b' of row ir
         uint32_t q[G::WPW][G::WH][4];
@@ -360,7 +404,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
 #pragma unroll
                 for (int wt = 0; wt < G::WPW; ++wt) {
                     const int64_t n = t.n0 + 16 * (G::WPW * wave + wt) + ir;
-                    const float v = FMT == FQ4_0 ? macc[bt][wt][vv] : acc[bt][wt][vv];
+                    const float v = FMT == FQ8_0 ? acc[bt][wt][vv] : macc[bt][wt][vv];
                     if (n < a.N)
                         out[r * a.N + n] = v * f;
                 }
@@ -437,6 +481,9 @@ int launch_gemm(int fmt, const GemmArgs &a, const float *x, void *stream)
     if (fmt == FQ4_0)
         hipLaunchKernelGGL(k_xprep<FQ4_0>, dim3(groups), dim3(256), 0, s, x, a.M, a.K, a.KBp,
                            a.xh, a.rs);
+    else if (fmt == FQ1_0)
+        hipLaunchKernelGGL(k_xprep<FQ1_0>, dim3(groups), dim3(256), 0, s, x, a.M, a.K, a.KBp,
+                           a.xh, a.rs);
     else
         hipLaunchKernelGGL(k_xprep<FQ8_0>, dim3(groups), dim3(256), 0, s, x, a.M, a.K, a.KBp,
                            a.xh, a.rs);
@@ -451,6 +498,8 @@ int launch_gemm(int fmt, const GemmArgs &a, const float *x, void *stream)
         hipLaunchKernelGGL((k_gemm<FQ4_0, 2>), dim3(grid), dim3(GM_THREADS), 0, s, a);
     else if (fmt == FQ4_0)
         hipLaunchKernelGGL((k_gemm<FQ4_0, 1>), dim3(grid), dim3(GM_THREADS), 0, s, a);
+    else if (fmt == FQ1_0)
+        hipLaunchKernelGGL((k_gemm<FQ1_0, 1>), dim3(grid), dim3(GM_THREADS), 0, s, a);
     else
         hipLaunchKernelGGL((k_gemm<FQ8_0, 1>), dim3(grid), dim3(GM_THREADS), 0, s, a);
     e = hipGetLastError();

@@ -244,8 +244,12 @@ __device__ __forceinline__ void mf_xpose(uint32_t (&v)[4])
 template <int FMT>
 __device__ __forceinline__ int mf_elem(int j, int h, bool &hi)
 {
-    static_assert(FMT != FAQ4 && FMT != FQ1_0 && FMT != FQ6_K, "no inverse layout here");
-    if constexpr (FMT != FQ4_0) {
+    static_assert(FMT != FAQ4 && FMT != FQ6_K, "no inverse layout here");
+    if constexpr (FMT == FQ1_0) {
+        // pair t = h / 2 of lane column j: elements 4j + t (low half) and 4j + t + 16 (high)
+        hi = false;
+        return 4 * j + (h >> 1) + 16 * (h & 1);
+    } else if constexpr (FMT != FQ4_0) {
         // halves: [b0, b2, b1, b3] of half 0, then of half 1
         const int second = h >> 2, t4 = h & 3;
         const int t = t4 == 0 ? 0 : t4 == 1 ? 2 : t4 == 2 ? 1 : 3;

@@ -36,8 +36,8 @@
  *    The field orders and bit orders of IQ4_NL, IQ4_XS, Q1_0 and AQ4 are this library's reading
  *    of pages that name the formats without printing their layout.  The IQ4 formats' codebook
  *    is an input (qgemv_pack_codebook), stored inside the packed matrix.
- *    Routed experts (qgemv_moe) take Q4_0, Q8_0 and Q4_K; the row-batch GEMM (qgemm) Q4_0 and
- *    Q8_0.
+ *    Routed experts (qgemv_moe) take Q4_0, Q8_0 and Q4_K; the row-batch GEMM (qgemm) Q4_0, Q8_0
+ *    and Q1_0.
  *  - W arguments of the compute entry points are in the PACKED device layout written by
  *    qgemv_pack (same bytes per weight as GGUF, split into planes so every hot load is an
  *    aligned 16-byte load).  Rows are in output order; K is the reduction length.  A W buffer
@@ -212,12 +212,15 @@ int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t 
 
 /* Wide row batch (prefill chunks): y[m][n] = sum_k W[n][k] x[m][k] for M rows of x at once, so
  * every weight streams once for the whole chunk ("Module gpu", module prefill; "Crate
- * inferencelayer", gemm_q1_src / gemm_q4_src: tiles sharing one weight stream, one 32-weight
- * block per inner step).  Formats Q4_0 and Q8_0 (others: QG_ERR_FORMAT).  x f32 [M][K], y f32
- * [M][N], 4-B aligned; 1 <= M <= QG_GEMM_MAX_M.  ws: at least qgemm_workspace_bytes(fmt, N, K, M)
- * bytes, 256-B aligned, written before it is read (x converted to f16 once per call); two
- * launches on `stream`.  The same arithmetic as the row-batch GEMV: exact weights, x rounded to
- * f16 after a power-of-two scaling of each row, f32 accumulation. */
+ * inferencelayer", gemm_q4_src / gemm_q8_0n_src / gemm_q1_src: tiles sharing one weight stream,
+ * one 32-weight block per inner step; gemm_q4_splitk_src / gemm_q4_splitk_reduce_src: K split
+ * over workgroups when the tiles do not fill the device).  Formats Q4_0, Q8_0 and Q1_0 (others:
+ * QG_ERR_FORMAT).  x f32 [M][K], y f32 [M][N], 4-B aligned; 1 <= M <= QG_GEMM_MAX_M.  ws: at
+ * least qgemm_workspace_bytes(fmt, N, K, M) bytes, 256-B aligned, written before it is read (x
+ * converted to f16 once per call, split-K partial tiles); two launches on `stream` (three when
+ * K is split: the partial tiles are then added in a fixed order).  The same arithmetic as the
+ * row-batch GEMV: exact weights, x rounded to f16 after a power-of-two scaling of each row, f32
+ * accumulation. */
 #define QG_GEMM_MAX_M (1 << 20)
 int64_t qgemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M);
 int qgemm(int fmt, const void *W, int64_t N, int64_t K, const float *x, int64_t M, float *y,

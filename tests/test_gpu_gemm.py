@@ -1,5 +1,5 @@
 """The wide row-batch GEMM (prefill chunks, M > 16 rows of x; "Module gpu", module prefill) on the
-GPU against the f64 oracle: Q4_0 and Q8_0, M in {17, 64, 512, 2048} and ragged sizes (partial
+GPU against the f64 oracle: Q4_0, Q8_0 and Q1_0, M in {17, 64, 512, 2048} and ragged sizes (partial
 128-row tiles of x and W, K not a multiple of the 128-k step, K split over workgroups with a
 shorter last split), every output compared up to M = 512 and sampled rows and columns beyond;
 integer inputs bit for bit."""
@@ -35,7 +35,9 @@ def _gemm(fmt, Wp, N, K, x):
                                        (q.Q4_0, 200, 130, 96), (q.Q8_0, 131, 77, 32),
                                        (q.Q4_0, 1, 64, 4096), (q.Q4_0, 129, 257, 8192),
                                        (q.Q4_0, 40, 200, 608), (q.Q8_0, 33, 150, 608),
-                                       (q.Q4_0, 100, 3000, 1024)])
+                                       (q.Q4_0, 100, 3000, 1024), (q.Q1_0, 17, 300, 2048),
+                                       (q.Q1_0, 512, 517, 1024), (q.Q1_0, 200, 130, 128),
+                                       (q.Q1_0, 131, 1000, 640)])
 def test_qgemm_parity(fmt, M, N, K):
     say(f"qgemm fmt={fmt} M={M} N={N} K={K}")
     g = wl.rng(3000 + fmt, M + N + K)
@@ -47,7 +49,7 @@ def test_qgemm_parity(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [(q.Q4_0, 2048, 4096, 2048), (q.Q8_0, 2048, 2048, 1536),
-                                       (q.Q4_0, 1950, 4000, 1056)])
+                                       (q.Q4_0, 1950, 4000, 1056), (q.Q1_0, 2048, 4096, 2048)])
 def test_qgemm_large_sampled(fmt, M, N, K):
     """Full-size launch; the oracle checks 64 sampled x rows against 256 sampled W rows.  The
     Q4_0 cases take the 256-row weight tiles (the second one ragged in M, N and K)."""
@@ -62,7 +64,7 @@ def test_qgemm_large_sampled(fmt, M, N, K):
     assert_within(y[np.ix_(rows, cols)], yr, tol_gemv(A, yr), f"qgemm large fmt={fmt}")
 
 
-@pytest.mark.parametrize("fmt", [q.Q4_0, q.Q8_0])
+@pytest.mark.parametrize("fmt", [q.Q4_0, q.Q8_0, q.Q1_0])
 def test_qgemm_integer_inputs_bitwise(fmt):
     say(f"qgemm integer fmt={fmt}")
     M, N, K = 150, 140, 512
