@@ -11,13 +11,14 @@
 //    puts its largest |x| in [2^14, 2^15), the high-nibble positions of Q4_0 times 1/16, and laid
 //    out in 1 KB chunks (16 rows x one 32-k block) whose 64 16-byte pieces are the A operands of
 //    v_mfma_f32_16x16x32_f16 in lane order (mf_elem), zero past K and past M;
-//  - a workgroup (8 waves) owns a 128 x 256 tile of Y (Q4_0 when such tiles fill the device, else
-//    128 x 128); wave w owns all 128 x rows against weight rows 32 w .. 32 w + 31 (8 x 2 MFMA
-//    tiles; with 128-row tiles 16 rows, 8 x 1), so each weight is decoded once per workgroup and
-//    feeds 16 MFMAs per block (the decode is VALU work; eight x tiles per decoded weight tile keep
-//    it under the matrix-core time), and each x operand read from LDS feeds one or two weight
-//    tiles.  A step covers 128 k (4 blocks);
-//  - x chunks, weight chunks (16 rows x 64 bytes for Q4_0, x 128 bytes for Q8_0) and the block
+//  - a workgroup (8 waves) owns a 128 x 256 tile of Y (Q4_0 and Q1_0 when such tiles fill the
+//    device, else 128 x 128); wave w owns all 128 x rows against weight rows 32 w .. 32 w + 31
+//    (8 x 2 MFMA tiles; with 128-row tiles 16 rows, 8 x 1), so each weight is decoded once per
+//    workgroup and feeds 8 (Q1_0) or 16 MFMAs per block (the decode is VALU work; eight x tiles
+//    per decoded weight tile keep it under the matrix-core time), and each x operand read from LDS
+//    feeds one or two weight tiles.  A step covers 128 k (4 blocks);
+//  - x chunks, weight chunks (16 rows x 64 bytes for Q4_0, x 128 bytes for Q8_0, x 16 bytes for
+//    Q1_0) and the block
 //    scales go from global memory straight into LDS (global_load_lds: no registers, no LDS store
 //    instructions), three stages deep: the loads of step s + 2 are issued while step s computes,
 //    so each load has two steps of matrix work to arrive in.  One barrier per step;
@@ -184,7 +185,7 @@ template <int FMT, int WPW>
 __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
 {
     using G = GemmStage<FMT, WPW>;
-    static_assert(FMT == FQ4_0 || WPW == 1, "Q8_0 and Q1_0 stage one weight group per wave");
+    static_assert(FMT != FQ8_0 || WPW == 1, "Q8_0 stages one weight group per wave");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[GM_STAGES * G::BYTES];
     __shared__ __attribute__((aligned(16))) float s_rs[3][GM_BM];   // row factors of 3 tiles
 
@@ -237,15 +238,19 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
             gm_dma16(src, st + c * 1024);
         }
         if constexpr (FMT == FQ1_0) {
-            // sign words: lane l -> row 16 wave + l / 4, dword l % 4 of the step's block; scale:
-            // lane l -> row 16 wave + l % 16 (lanes 16.. repeat those rows)
-            const int64_t wr = t.n0 + 16 * wave + (lane >> 2) < a.N ? t.n0 + 16 * wave + (lane >> 2)
-                                                                    : a.N - 1;
-            gm_dma4(a.qs + wr * a.qs_row + 16 * (int64_t)s + 4 * (lane & 3),
-                    st + G::XB + wave * 256);
-            const int64_t sr = t.n0 + 16 * wave + (lane & 15) < a.N ? t.n0 + 16 * wave + (lane & 15)
-                                                                   : a.N - 1;
-            gm_dma2(a.sc + sr * a.sc_row + 2 * (int64_t)s, st + G::XB + G::WB + wave * 256);
+            // row group g = WPW wave + wt: sign words, lane l -> row 16 g + l / 4, dword l % 4 of
+            // the step's block; scale, lane l -> row 16 g + l % 16 (lanes 16.. repeat those rows)
+#pragma unroll
+            for (int wt = 0; wt < G::WPW; ++wt) {
+                const int g = G::WPW * wave + wt;
+                const int64_t wr =
+                    t.n0 + 16 * g + (lane >> 2) < a.N ? t.n0 + 16 * g + (lane >> 2) : a.N - 1;
+                gm_dma4(a.qs + wr * a.qs_row + 16 * (int64_t)s + 4 * (lane & 3),
+                        st + G::XB + g * 256);
+                const int64_t sr =
+                    t.n0 + 16 * g + (lane & 15) < a.N ? t.n0 + 16 * g + (lane & 15) : a.N - 1;
+                gm_dma2(a.sc + sr * a.sc_row + 2 * (int64_t)s, st + G::XB + G::WB + g * 256);
+            }
             if (s_rel == 0 && wave < 2)
                 gm_dma4(a.rs + t.m0 + 64 * wave + lane, &s_rs[rs_slot][64 * wave]);
             return;
@@ -289,26 +294,39 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
         const int s = t.s0 + s_rel;
         const uint8_t *st = lds + ring * G::BYTES;
         if constexpr (FMT == FQ1_0) {
-            // row ir's four sign words and its scale; lane column lc of block b takes the pairs
-            // (element 4 lc + p, element 4 lc + p + 16), p = 0..3, as +-d: the sign bits moved to
-            // bits 15 and 31 (a set bit is +d), then xor-ed into the f16 pair (d, d)
-            const uint4 qv = *reinterpret_cast<const uint4 *>(st + G::XB + (16 * wave + ir) * 16);
-            const uint32_t db = *reinterpret_cast<const uint32_t *>(st + G::XB + G::WB + wave * 256 +
-                                                                   4 * ir) & 0xFFFFu;
-            const uint32_t dp = db | (db << 16);
+            // row ir of each of the wave's row groups: its four sign words and its scale; lane
+            // column lc of block b takes the pairs (element 4 lc + p, element 4 lc + p + 16),
+            // p = 0..3, as +-d: the sign bits moved to bits 15 and 31 (a set bit is +d), then
+            // xor-ed into the f16 pair (d, d)
+            uint4 qv[G::WPW];
+            uint32_t dp[G::WPW];
+#pragma unroll
+            for (int wt = 0; wt < G::WPW; ++wt) {
+                const int g = G::WPW * wave + wt;
+                qv[wt] = *reinterpret_cast<const uint4 *>(st + G::XB + (16 * g + ir) * 16);
+                const uint32_t db = *reinterpret_cast<const uint32_t *>(st + G::XB + G::WB +
+                                                                       g * 256 + 4 * ir) & 0xFFFFu;
+                dp[wt] = db | (db << 16);
+            }
 #pragma unroll
             for (int b = 0; b < GM_BPS; ++b) {
-                const uint32_t w = ~(b == 0 ? qv.x : b == 1 ? qv.y : b == 2 ? qv.z : qv.w);
-                uint4 bw;
-                bw.x = (((w >> (4 * lc + 0)) << 15) & 0x80008000u) ^ dp;
-                bw.y = (((w >> (4 * lc + 1)) << 15) & 0x80008000u) ^ dp;
-                bw.z = (((w >> (4 * lc + 2)) << 15) & 0x80008000u) ^ dp;
-                bw.w = (((w >> (4 * lc + 3)) << 15) & 0x80008000u) ^ dp;
-                const mh8 B = __builtin_bit_cast(mh8, bw);
+                mh8 A[8];
 #pragma unroll
-                for (int bt = 0; bt < 8; ++bt) {
-                    const mh8 A = *reinterpret_cast<const mh8 *>(st + (bt * GM_BPS + b) * 1024 + 16 * lane);
-                    macc[bt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, macc[bt][0], 0, 0, 0);
+                for (int bt = 0; bt < 8; ++bt)
+                    A[bt] = *reinterpret_cast<const mh8 *>(st + (bt * GM_BPS + b) * 1024 + 16 * lane);
+#pragma unroll
+                for (int wt = 0; wt < G::WPW; ++wt) {
+                    const uint4 q4 = qv[wt];
+                    const uint32_t w = ~(b == 0 ? q4.x : b == 1 ? q4.y : b == 2 ? q4.z : q4.w);
+                    uint4 bw;
+                    bw.x = (((w >> (4 * lc + 0)) << 15) & 0x80008000u) ^ dp[wt];
+                    bw.y = (((w >> (4 * lc + 1)) << 15) & 0x80008000u) ^ dp[wt];
+                    bw.z = (((w >> (4 * lc + 2)) << 15) & 0x80008000u) ^ dp[wt];
+                    bw.w = (((w >> (4 * lc + 3)) << 15) & 0x80008000u) ^ dp[wt];
+                    const mh8 B = __builtin_bit_cast(mh8, bw);
+#pragma unroll
+                    for (int bt = 0; bt < 8; ++bt)
+                        macc[bt][wt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt], B, macc[bt][wt], 0, 0, 0);
                 }
             }
             (void)s;
@@ -498,6 +516,8 @@ int launch_gemm(int fmt, const GemmArgs &a, const float *x, void *stream)
         hipLaunchKernelGGL((k_gemm<FQ4_0, 2>), dim3(grid), dim3(GM_THREADS), 0, s, a);
     else if (fmt == FQ4_0)
         hipLaunchKernelGGL((k_gemm<FQ4_0, 1>), dim3(grid), dim3(GM_THREADS), 0, s, a);
+    else if (fmt == FQ1_0 && a.bn == 256)
+        hipLaunchKernelGGL((k_gemm<FQ1_0, 2>), dim3(grid), dim3(GM_THREADS), 0, s, a);
     else if (fmt == FQ1_0)
         hipLaunchKernelGGL((k_gemm<FQ1_0, 1>), dim3(grid), dim3(GM_THREADS), 0, s, a);
     else

@@ -49,10 +49,11 @@ def test_qgemm_parity(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [(q.Q4_0, 2048, 4096, 2048), (q.Q8_0, 2048, 2048, 1536),
-                                       (q.Q4_0, 1950, 4000, 1056), (q.Q1_0, 2048, 4096, 2048)])
+                                       (q.Q4_0, 1950, 4000, 1056), (q.Q1_0, 2048, 4096, 2048),
+                                       (q.Q1_0, 1950, 4000, 1152)])
 def test_qgemm_large_sampled(fmt, M, N, K):
     """Full-size launch; the oracle checks 64 sampled x rows against 256 sampled W rows.  The
-    Q4_0 cases take the 256-row weight tiles (the second one ragged in M, N and K)."""
+    Q4_0 and Q1_0 cases take the 256-row weight tiles (the second of each ragged in M and N)."""
     say(f"qgemm large fmt={fmt} M={M} N={N} K={K}")
     g = wl.rng(3100 + fmt, M)
     W = wl.matrix(fmt, g, N, K)
