@@ -26,13 +26,13 @@
 //    load stream runs across tile boundaries, so the next tile's first loads overlap the current
 //    tile's last steps and its stores, and there is no per-wave launch ramp between tiles;
 //  - a wave reads the weight chunks it loaded itself from LDS, transposes them across the lane
-//    rows (mf_xpose) and decodes exact f16 weights (mf_bop).  Q4_0: the block scale
-//    splits exactly into d_hi (8 significant bits) + d_lo, so d_hi (q - 8) and d_lo (q - 8) are
-//    exact f16 operands and two MFMAs per block accumulate the scaled product straight into the
-//    MFMA accumulators; Q8_0 (8-bit q): one MFMA per block gives D = A B and acc += d D on the
-//    VALU; Q1_0 (sign bits, one f16 d per 128 weights, "Crate inferencelayer" docs, gemm_q1_src):
-//    the weights are +-d, exact f16, one MFMA per block.  Either way the weights stay exact; only
-//    x is rounded, by at most 2^-11 of itself;
+//    rows (mf_xpose) and decodes exact f16 weights (mf_bop).  Q4_0 (q - 8) and Q8_0 (q): one
+//    MFMA per block gives D = A B and acc += d D on the VALU (those FMAs run beside the other
+//    wave's products; splitting d into two exact f16 halves for two scaled products per block
+//    keeps the sums in the accumulators but doubles the matrix work, 130 vs 108 us at
+//    2048 x 8192 x 2048); Q1_0 (sign bits, one f16 d per 128 weights, "Crate inferencelayer"
+//    docs, gemm_q1_src): the weights are +-d, exact f16, one MFMA per block accumulating in
+//    place.  Either way the weights stay exact; only x is rounded, by at most 2^-11 of itself;
 //  - the grid walks the tiles XCD by XCD (workgroup i runs on XCD i % 8): each XCD owns a range of
 //    weight tiles and walks them row-tile-major, so the workgroups resident on an XCD share a few x
 //    row tiles and the XCD's weight tiles in its L2;
@@ -276,8 +276,8 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
             gm_dma4(a.rs + t.m0 + 64 * wave + lane, &s_rs[rs_slot][64 * wave]);
     };
 
-    float acc[8][G::WPW][4];    // Q8_0: per-block scaled sums (VALU)
-    mf4 macc[8][G::WPW];        // Q4_0: sums kept in the MFMA accumulators
+    float acc[8][G::WPW][4];    // Q4_0, Q8_0: per-block scaled sums (VALU)
+    mf4 macc[8][G::WPW];        // Q1_0: sums kept in the MFMA accumulators
     auto zero_acc = [&]() {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -362,43 +362,28 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
 #pragma unroll
             for (int wt = 0; wt < G::WPW; ++wt) {
                 const uint32_t dw = b == 0 ? dsc[wt].x : b == 1 ? dsc[wt].y : b == 2 ? dsc[wt].z : dsc[wt].w;
-                if constexpr (FMT == FQ4_0) {
-                    // exact scaled weights: d = d_hi + d_lo with d_hi the top 8 significant bits
-                    // of the f16 scale, d_lo the rest (3 bits); |q - 8| <= 8 needs at most 3 more
-                    // bits, so d_hi (q - 8) and d_lo (q - 8) are exact f16 values (the high-nibble
-                    // halves, held x16, too).  Two MFMAs per block accumulate them straight into
-                    // the accumulators: first the d_hi products of all 8 tiles, then the d_lo ones.
-                    const mh8 B = mf_bop<FMT>(q[wt][0][b], 0u, kc);
-                    const uint16_t db = blk < KB ? (uint16_t)(dw & 0xFFFFu) : (uint16_t)0;
-                    const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)(db & 0xFFF8u));
-                    const _Float16 dl = __builtin_bit_cast(_Float16, db) - dh;
-                    const mh8 Bh = B * dh, Bl = B * dl;
+                // exact weights (Q4_0: q - 8, the high-nibble halves x16; Q8_0: q, block b being
+                // chunks 2 b, 2 b + 1 of the step) in one product per block, D = A B with the
+                // f32 sums of exact products, then acc += d D on the VALU, where it overlaps the
+                // other wave's products
+                const int h = FMT == FQ4_0 ? 0 : b >> 1, p = 2 * (b & 1);
+                const mh8 B = FMT == FQ4_0 ? mf_bop<FMT>(q[wt][0][b], 0u, kc)
+                                           : mf_bop<FMT>(q[wt][h][p], q[wt][h][p + 1], kc);
+                const uint16_t db = (uint16_t)(dw & 0xFFFFu);
+                const float d = blk < KB ? (float)__builtin_bit_cast(_Float16, db) : 0.f;
+                const mf4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int bt = 0; bt < 8; ++bt)
-                        macc[bt][wt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt], Bh, macc[bt][wt], 0, 0, 0);
+                for (int bt = 0; bt < 8; bt += 4) {
+                    mf4 D[4];
 #pragma unroll
-                    for (int bt = 0; bt < 8; ++bt)
-                        macc[bt][wt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt], Bl, macc[bt][wt], 0, 0, 0);
-                } else {
-                    // block b = chunks 2 b, 2 b + 1 of the step
-                    const int h = b >> 1, p = 2 * (b & 1);
-                    const mh8 B = mf_bop<FMT>(q[wt][h][p], q[wt][h][p + 1], kc);
-                    const uint16_t db = (uint16_t)(dw & 0xFFFFu);
-                    const float d = blk < KB ? (float)__builtin_bit_cast(_Float16, db) : 0.f;
-                    const mf4 zero = {0.f, 0.f, 0.f, 0.f};
+                    for (int i = 0; i < 4; ++i)
+                        D[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt + i], B, zero, 0, 0, 0);
 #pragma unroll
-                    for (int bt = 0; bt < 8; bt += 4) {
-                        mf4 D[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            D[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt + i], B, zero, 0, 0, 0);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            acc[bt + i][wt][0] = fmaf(d, D[i][0], acc[bt + i][wt][0]);
-                            acc[bt + i][wt][1] = fmaf(d, D[i][1], acc[bt + i][wt][1]);
-                            acc[bt + i][wt][2] = fmaf(d, D[i][2], acc[bt + i][wt][2]);
-                            acc[bt + i][wt][3] = fmaf(d, D[i][3], acc[bt + i][wt][3]);
-                        }
+                    for (int i = 0; i < 4; ++i) {
+                        acc[bt + i][wt][0] = fmaf(d, D[i][0], acc[bt + i][wt][0]);
+                        acc[bt + i][wt][1] = fmaf(d, D[i][1], acc[bt + i][wt][1]);
+                        acc[bt + i][wt][2] = fmaf(d, D[i][2], acc[bt + i][wt][2]);
+                        acc[bt + i][wt][3] = fmaf(d, D[i][3], acc[bt + i][wt][3]);
                     }
                 }
             }
@@ -422,7 +407,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
 #pragma unroll
                 for (int wt = 0; wt < G::WPW; ++wt) {
                     const int64_t n = t.n0 + 16 * (G::WPW * wave + wt) + ir;
-                    const float v = FMT == FQ8_0 ? acc[bt][wt][vv] : macc[bt][wt][vv];
+                    const float v = FMT == FQ1_0 ? macc[bt][wt][vv] : acc[bt][wt][vv];
                     if (n < a.N)
                         out[r * a.N + n] = v * f;
                 }
