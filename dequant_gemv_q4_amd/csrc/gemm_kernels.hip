@@ -111,11 +111,13 @@ __device__ __forceinline__ void gm_barrier()
 
 // x [M][K] f32 -> xh chunks [Mp / 16][KBp][64 lanes][8 halves] in the A-operand order of each
 // 32-k block, and rs[r] = the factor undoing row r's scale; rows past M and columns past K are
-// zero (rs 0 past M).  One wave per row: it finds the row's largest |x|, then writes the row's
-// pieces (lane l = (ir, j) of a chunk holds elements 4j..4j+3 and 16+4j..16+4j+3 of row ir in
-// both formats: mf_elem(j, h) = mf_elem(0, h) + 4 j).  The second pass re-reads the row from the
-// cache.
-template <int FMT>
+// zero (rs 0 past M).  One wave per row: piece q of the row (block q / 4, j = q % 4; chunk lane
+// 16 j + r % 16) holds elements 4j..4j+3 and 16+4j..16+4j+3 of its block in both formats
+// (mf_elem(j, h) = mf_elem(0, h) + 4 j).  With PPL > 0 each lane keeps its PPL pieces
+// q = lane + 64 i in registers, so the row is read once: the wave's largest |x| (the power-of-two
+// scale) comes from the held values; PPL = 0 (rows of more than 512 pieces) finds the largest
+// |x| in a first pass and re-reads the row, from the cache, in the second.
+template <int FMT, int PPL>
 __global__ __launch_bounds__(256) void k_xprep(const float *x, int64_t M, int64_t K, int KBp,
                                                _Float16 *xh, float *rs)
 {
@@ -124,36 +126,12 @@ __global__ __launch_bounds__(256) void k_xprep(const float *x, int64_t M, int64_
     const bool live = r < M;
     const bool vec = ((uintptr_t)x & 15) == 0;          // K % 32 == 0: every row is aligned too
     const float *xr = x + (live ? r : 0) * K;
-    float mx = 0.f;
-    if (live) {
-        if (vec) {
-#pragma unroll 8
-            for (int64_t e = 4 * lane; e < K; e += 256) {
-                const float4 v = *reinterpret_cast<const float4 *>(xr + e);
-                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-            }
-        } else {
-#pragma unroll 8
-            for (int64_t e = lane; e < K; e += 64)
-                mx = fmaxf(mx, fabsf(xr[e]));
-        }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        mx = fmaxf(mx, __shfl_xor(mx, off));
-    int e2 = 0;
-    frexpf(mx, &e2);                                   // max |x| = f 2^e2, f in [0.5, 1)
-    const int sk = 15 - e2 < 127 ? 15 - e2 : 127;      // 2^sk stays a finite f32
-    const float sc = live ? ldexpf(1.0f, sk) : 0.f;
-    if (lane == 0)
-        rs[r] = live ? ldexpf(1.0f, -sk) : 0.f;
-    // piece q of the row: block q / 4, j = q % 4 -> chunk lane 16 j + (r % 16)
     const int KB = (int)(K / 32);
-    _Float16 *dst = xh + (r / 16) * (int64_t)KBp * 512 + (int64_t)(r % 16) * 8;
-#pragma unroll 4
-    for (int q = lane; q < 4 * KBp; q += 64) {
+    auto load_piece = [&](int q, float (&lo)[4], float (&hi4)[4]) {
         const int blk = q >> 2, j = q & 3;
-        float lo[4] = {0.f, 0.f, 0.f, 0.f}, hi4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            lo[i] = hi4[i] = 0.f;
         if (live && blk < KB) {
             const float *xb = xr + (int64_t)blk * 32 + 4 * j;
             if (vec) {
@@ -169,6 +147,9 @@ __global__ __launch_bounds__(256) void k_xprep(const float *x, int64_t M, int64_
                 }
             }
         }
+    };
+    _Float16 *dst = xh + (r / 16) * (int64_t)KBp * 512 + (int64_t)(r % 16) * 8;
+    auto store_piece = [&](int q, const float (&lo)[4], const float (&hi4)[4], float sc) {
         mh8 v;
 #pragma unroll
         for (int h = 0; h < 8; ++h) {
@@ -177,7 +158,57 @@ __global__ __launch_bounds__(256) void k_xprep(const float *x, int64_t M, int64_
             const float xv = e >= 16 ? hi4[e - 16] : lo[e];
             v[h] = (_Float16)(xv * sc * (hi ? 0.0625f : 1.0f));
         }
-        *reinterpret_cast<mh8 *>(dst + ((int64_t)blk * 64 + 16 * j) * 8) = v;
+        *reinterpret_cast<mh8 *>(dst + ((int64_t)(q >> 2) * 64 + 16 * (q & 3)) * 8) = v;
+    };
+    auto scale_of = [&](float mx) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            mx = fmaxf(mx, __shfl_xor(mx, off));
+        int e2 = 0;
+        frexpf(mx, &e2);                                   // max |x| = f 2^e2, f in [0.5, 1)
+        const int sk = 15 - e2 < 127 ? 15 - e2 : 127;      // 2^sk stays a finite f32
+        if (lane == 0)
+            rs[r] = live ? ldexpf(1.0f, -sk) : 0.f;
+        return live ? ldexpf(1.0f, sk) : 0.f;
+    };
+    const int NP = 4 * KBp;                                // pieces of the padded row
+    if constexpr (PPL > 0) {
+        float lo[PPL][4], hi4[PPL][4];
+        float mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < PPL; ++i) {
+            load_piece(lane + 64 * i, lo[i], hi4[i]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                mx = fmaxf(mx, fmaxf(fabsf(lo[i][e]), fabsf(hi4[i][e])));
+        }
+        const float sc = scale_of(mx);
+#pragma unroll
+        for (int i = 0; i < PPL; ++i)
+            if (lane + 64 * i < NP)
+                store_piece(lane + 64 * i, lo[i], hi4[i], sc);
+    } else {
+        float mx = 0.f;
+        if (live) {
+            if (vec) {
+#pragma unroll 8
+                for (int64_t e = 4 * lane; e < K; e += 256) {
+                    const float4 v = *reinterpret_cast<const float4 *>(xr + e);
+                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+                }
+            } else {
+#pragma unroll 8
+                for (int64_t e = lane; e < K; e += 64)
+                    mx = fmaxf(mx, fabsf(xr[e]));
+            }
+        }
+        const float sc = scale_of(mx);
+#pragma unroll 4
+        for (int q = lane; q < NP; q += 64) {
+            float lo[4], hi4[4];
+            load_piece(q, lo, hi4);
+            store_piece(q, lo, hi4, sc);
+        }
     }
 }
 
@@ -226,7 +257,33 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
     // 16 g + ir, chunk 4 h + lc of the step (rows past N read row N - 1, chunks past the row its
     // last chunk).  Scales: lane l -> row 16 g + l / 4, block l % 4 of the step (dword 4 row +
     // block of the scale area).  With a tile's first step, waves 0 and 1 also load its 128 row factors.
-    auto issue = [&](const Tile &t, int s_rel, int ring, int rs_slot) {
+    // This lane's weight and scale row pointers of a tile (rows past N read row N - 1), formed
+    // once per tile by the issue cursor.  Weights: row group g = WPW wave + wt, lane (ir, lc) ->
+    // row 16 g + ir (Q1_0: row 16 g + l / 4, dword l % 4 of a block); scales: lane l -> row
+    // 16 g + l / 4 (Q1_0: row 16 g + l % 16, lanes 16.. repeating those rows).
+    struct RowPtrs {
+        const uint8_t *w[G::WPW];
+        const uint8_t *sc[G::WPW];
+    };
+    auto row_ptrs = [&](const Tile &t) {
+        RowPtrs rp;
+#pragma unroll
+        for (int wt = 0; wt < G::WPW; ++wt) {
+            const int64_t r0 = t.n0 + 16 * (G::WPW * wave + wt);
+            const int64_t wi = r0 + (FMT == FQ1_0 ? lane >> 2 : ir);
+            const int64_t si = r0 + (FMT == FQ1_0 ? lane & 15 : lane >> 2);
+            rp.w[wt] = a.qs + (wi < a.N ? wi : a.N - 1) * a.qs_row + (FMT == FQ1_0 ? 4 * (lane & 3) : 0);
+            rp.sc[wt] = a.sc + (si < a.N ? si : a.N - 1) * a.sc_row;
+        }
+        return rp;
+    };
+
+    // loads of step s of tile t into ring slot `ring`.  x: chunk c = XPW wave + u of the stage is
+    // row group c / 4, block c % 4.  Weights: lane (ir, lc) of row group g loads chunk 4 h + lc of
+    // the step (chunks past the row its last chunk); Q1_0: the block's sign dword.  Scales: block
+    // l % 4 of the step (dword 4 row + block of the scale area); Q1_0: the block's scale.  With a
+    // tile's first step, waves 0 and 1 also load its 128 row factors.
+    auto issue = [&](const Tile &t, const RowPtrs &rp, int s_rel, int ring, int rs_slot) {
         const int s = t.s0 + s_rel;
         uint8_t *st = lds + ring * G::BYTES;
         const _Float16 *xsrc = a.xh + (t.m0 / 16) * (int64_t)a.KBp * 512 + (int64_t)lane * 8;
@@ -238,39 +295,26 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
             gm_dma16(src, st + c * 1024);
         }
         if constexpr (FMT == FQ1_0) {
-            // row group g = WPW wave + wt: sign words, lane l -> row 16 g + l / 4, dword l % 4 of
-            // the step's block; scale, lane l -> row 16 g + l % 16 (lanes 16.. repeat those rows)
 #pragma unroll
             for (int wt = 0; wt < G::WPW; ++wt) {
                 const int g = G::WPW * wave + wt;
-                const int64_t wr =
-                    t.n0 + 16 * g + (lane >> 2) < a.N ? t.n0 + 16 * g + (lane >> 2) : a.N - 1;
-                gm_dma4(a.qs + wr * a.qs_row + 16 * (int64_t)s + 4 * (lane & 3),
-                        st + G::XB + g * 256);
-                const int64_t sr =
-                    t.n0 + 16 * g + (lane & 15) < a.N ? t.n0 + 16 * g + (lane & 15) : a.N - 1;
-                gm_dma2(a.sc + sr * a.sc_row + 2 * (int64_t)s, st + G::XB + G::WB + g * 256);
+                gm_dma4(rp.w[wt] + 16 * (uint32_t)s, st + G::XB + g * 256);
+                gm_dma2(rp.sc[wt] + 2 * (uint32_t)s, st + G::XB + G::WB + g * 256);
             }
-            if (s_rel == 0 && wave < 2)
-                gm_dma4(a.rs + t.m0 + 64 * wave + lane, &s_rs[rs_slot][64 * wave]);
-            return;
-        }
-        const int b0 = s * GM_BPS + (lane & 3);
-        const int blk = b0 < KB ? b0 : KB - 1;
+        } else {
+            const int b0 = s * GM_BPS + (lane & 3);
+            const int blk = b0 < KB ? b0 : KB - 1;
 #pragma unroll
-        for (int wt = 0; wt < G::WPW; ++wt) {
-            const int g = G::WPW * wave + wt;                  // weight row group
-            const int64_t wr = t.n0 + 16 * g + ir < a.N ? t.n0 + 16 * g + ir : a.N - 1;
-            const uint8_t *wsrc = a.qs + wr * a.qs_row;
+            for (int wt = 0; wt < G::WPW; ++wt) {
+                const int g = G::WPW * wave + wt;                  // weight row group
 #pragma unroll
-            for (int h = 0; h < G::WH; ++h) {
-                const int ch0 = (s * G::WH + h) * 4 + lc;
-                const int ch = ch0 < C ? ch0 : C - 1;
-                gm_dma16(wsrc + 16 * (int64_t)ch, st + G::XB + (g * G::WH + h) * 1024);
+                for (int h = 0; h < G::WH; ++h) {
+                    const int ch0 = (s * G::WH + h) * 4 + lc;
+                    const int ch = ch0 < C ? ch0 : C - 1;
+                    gm_dma16(rp.w[wt] + 16 * (uint32_t)ch, st + G::XB + (g * G::WH + h) * 1024);
+                }
+                gm_dma2(rp.sc[wt] + 2 * (uint32_t)blk, st + G::XB + G::WB + g * 256);
             }
-            const int64_t sr =
-                t.n0 + 16 * g + (lane >> 2) < a.N ? t.n0 + 16 * g + (lane >> 2) : a.N - 1;
-            gm_dma2(a.sc + sr * a.sc_row + 2 * (int64_t)blk, st + G::XB + G::WB + g * 256);
         }
         if (s_rel == 0 && wave < 2)
             gm_dma4(a.rs + t.m0 + 64 * wave + lane, &s_rs[rs_slot][64 * wave]);
@@ -420,17 +464,20 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
     constexpr int LPS = G::XPW + G::WPW * (G::WH + 1);   // loads per thread per step (+1 at a tile's start)
     int ik8 = slot, is = 0, itn = 0, pi = 0;  // issue cursor: tile, step, tile ordinal, position
     Tile ti = tile_of(ik8);
+    RowPtrs rpi = row_ptrs(ti);
     auto issue_next = [&]() {
         if (ik8 >= ntiles)
             return;
-        issue(ti, is, pi % GM_STAGES, itn % 3);
+        issue(ti, rpi, is, pi % GM_STAGES, itn % 3);
         ++pi;
         if (++is == ti.S) {
             is = 0;
             ++itn;
             ik8 += nslots;
-            if (ik8 < ntiles)
+            if (ik8 < ntiles) {
                 ti = tile_of(ik8);
+                rpi = row_ptrs(ti);
+            }
         }
     };
     issue_next();
@@ -479,17 +526,21 @@ __global__ __launch_bounds__(256) void k_gemm_fold(const float *part, const floa
 int launch_gemm(int fmt, const GemmArgs &a, const float *x, void *stream)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // x preparation: one wave per row of the padded x
+    // x preparation: one wave per row of the padded x, its pieces held in registers when there
+    // are at most 512
     const unsigned groups = (unsigned)((int64_t)a.m_tiles * GM_BM / 4);
-    if (fmt == FQ4_0)
-        hipLaunchKernelGGL(k_xprep<FQ4_0>, dim3(groups), dim3(256), 0, s, x, a.M, a.K, a.KBp,
-                           a.xh, a.rs);
-    else if (fmt == FQ1_0)
-        hipLaunchKernelGGL(k_xprep<FQ1_0>, dim3(groups), dim3(256), 0, s, x, a.M, a.K, a.KBp,
-                           a.xh, a.rs);
-    else
-        hipLaunchKernelGGL(k_xprep<FQ8_0>, dim3(groups), dim3(256), 0, s, x, a.M, a.K, a.KBp,
-                           a.xh, a.rs);
+    const int np = 4 * a.KBp;
+    const int ppl = np <= 64 ? 1 : np <= 128 ? 2 : np <= 256 ? 4 : np <= 512 ? 8 : 0;
+    using XP = void (*)(const float *, int64_t, int64_t, int, _Float16 *, float *);
+    XP xp = nullptr;
+    switch (ppl) {
+    case 1: xp = fmt == FQ4_0 ? k_xprep<FQ4_0, 1> : fmt == FQ1_0 ? k_xprep<FQ1_0, 1> : k_xprep<FQ8_0, 1>; break;
+    case 2: xp = fmt == FQ4_0 ? k_xprep<FQ4_0, 2> : fmt == FQ1_0 ? k_xprep<FQ1_0, 2> : k_xprep<FQ8_0, 2>; break;
+    case 4: xp = fmt == FQ4_0 ? k_xprep<FQ4_0, 4> : fmt == FQ1_0 ? k_xprep<FQ1_0, 4> : k_xprep<FQ8_0, 4>; break;
+    case 8: xp = fmt == FQ4_0 ? k_xprep<FQ4_0, 8> : fmt == FQ1_0 ? k_xprep<FQ1_0, 8> : k_xprep<FQ8_0, 8>; break;
+    default: xp = fmt == FQ4_0 ? k_xprep<FQ4_0, 0> : fmt == FQ1_0 ? k_xprep<FQ1_0, 0> : k_xprep<FQ8_0, 0>; break;
+    }
+    hipLaunchKernelGGL(xp, dim3(groups), dim3(256), 0, s, x, a.M, a.K, a.KBp, a.xh, a.rs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return (int)e;

@@ -79,6 +79,27 @@ def test_qgemm_integer_inputs_bitwise(fmt):
     assert np.array_equal(y.astype(np.float64), yr)
 
 
+@pytest.mark.parametrize("K", [1024, 8192])
+def test_qgemm_x_only_4_byte_aligned(K):
+    """x starting 4 bytes past a 16-byte boundary (the boundary accepts 4-byte alignment): the x
+    preparation takes scalar loads, with the row held in registers (K = 1024) and re-read
+    (K = 8192)."""
+    say(f"qgemm x+4 bytes K={K}")
+    M, N = 70, 300
+    g = wl.rng(3400, K)
+    W = wl.q4_0_matrix(g, N, K)
+    x = wl.normal_f32(g, (M, K))
+    big = torch.empty(M * K + 4, dtype=torch.float32, device="cuda")
+    big[1:1 + M * K].copy_(dev(x).reshape(-1))
+    xv = big[1:1 + M * K].view(M, K)
+    assert xv.data_ptr() % 16 == 4
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(q.qgemm_workspace_bytes(q.Q4_0, N, K, M), dtype=torch.uint8, device="cuda")
+    q.qgemm(q.Q4_0, gpu_matrix(q.Q4_0, W, N, K), N, K, xv, M, y, ws)
+    yr, A = oracle.gemv(q.Q4_0, W, N, K, x)
+    assert_within(host(y), yr, tol_gemv(A, yr), f"qgemm x+4 K={K}")
+
+
 def test_qgemm_rows_match_row_batch_gemv():
     """The first 16 rows of a wide call against qgemv on the same 16 rows (both bounded by the
     oracle; here the two GPU paths are held to each other's bound)."""
