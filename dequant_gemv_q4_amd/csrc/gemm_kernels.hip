@@ -11,17 +11,17 @@
 //    puts its largest |x| in [2^14, 2^15), the high-nibble positions of Q4_0 times 1/16, and laid
 //    out in 1 KB chunks (16 rows x one 32-k block) whose 64 16-byte pieces are the A operands of
 //    v_mfma_f32_16x16x32_f16 in lane order (mf_elem), zero past K and past M;
-//  - a workgroup (8 waves) owns a 128 x 256 tile of Y (Q4_0 and Q1_0 when such tiles fill the
-//    device, else 128 x 128); wave w owns all 128 x rows against weight rows 32 w .. 32 w + 31
-//    (8 x 2 MFMA tiles; with 128-row tiles 16 rows, 8 x 1), so each weight is decoded once per
-//    workgroup and feeds 8 (Q1_0) or 16 MFMAs per block (the decode is VALU work; eight x tiles
-//    per decoded weight tile keep it under the matrix-core time), and each x operand read from LDS
-//    feeds one or two weight tiles.  A step covers 128 k (4 blocks);
+//  - a workgroup (8 waves) owns a 128 x 16 WPW tile of Y, the widest that still fills the device
+//    (Q4_0: 512, 256 or 128 weight rows; Q1_0: 256 or 128; Q8_0: 128); wave w owns all 128 x
+//    rows against its WPW groups of 16 weight rows (8 x WPW MFMA tiles), so each weight is decoded
+//    once per workgroup and feeds 8 MFMAs per block (the decode is VALU work; eight x tiles per
+//    decoded weight tile keep it under the matrix-core time), and each x operand read from LDS
+//    feeds WPW weight tiles.  A step covers 128 k (4 blocks);
 //  - x chunks, weight chunks (16 rows x 64 bytes for Q4_0, x 128 bytes for Q8_0, x 16 bytes for
 //    Q1_0) and the block
 //    scales go from global memory straight into LDS (global_load_lds: no registers, no LDS store
-//    instructions), three stages deep: the loads of step s + 2 are issued while step s computes,
-//    so each load has two steps of matrix work to arrive in.  One barrier per step;
+//    instructions), three stages deep (two for Q4_0's 512-row tiles, whose stage is 72 KB): the
+//    loads of step s + 2 (s + 1) are issued while step s computes.  One barrier per step;
 //  - the kernel is persistent (one workgroup per compute unit, each walking a list of tiles): the
 //    load stream runs across tile boundaries, so the next tile's first loads overlap the current
 //    tile's last steps and its stores, and there is no per-wave launch ramp between tiles;
@@ -53,9 +53,9 @@ static_assert(GM_BM == QG_GEMM_BM && GM_BPS * 32 == QG_GEMM_KSTEP, "the host pla
 // LDS stage of one step: x chunks [row group 0..7][block 0..3] (1 KB each), then weight chunks
 // [row group][half] (1 KB each: 16 rows x 4 chunks of 16 B), then the scales [row][block], one
 // dword each (a 2-byte copy to LDS fills its lane's dword, zero-extended).  A wave owns WPW
-// 16-row weight groups: two for Q4_0 when the 128 x 256 tiles alone fill the device (each x
-// operand read from LDS then feeds twice the products), else one (more, smaller tiles; Q8_0
-// always, its weight chunks being twice as many).
+// 16-row weight groups: the most (Q4_0 up to four, Q1_0 two) whose tiles alone still fill the
+// device, since each x operand read from LDS then feeds WPW products, else one (more, smaller
+// tiles; Q8_0 always, its weight chunks being twice as many).
 // Q1_0: a step is one 128-weight block, 16 bytes of sign bits per row ([row][4 dwords], one
 // dword wave-load per 16 rows) and one scale per row (lane r of the wave's 256-byte area).
 template <int FMT, int WPW_>
@@ -68,6 +68,8 @@ struct GemmStage {
     static constexpr int SB = FMT == FQ1_0 ? BN / 16 * 256 : BN * GM_BPS * 4;
     static constexpr int BYTES = XB + WB + SB;
     static constexpr int XPW = GM_BM / 16 * GM_BPS / 8;         // x wave-loads per wave
+    // ring depth: three stages where they fit in the 160 KB of LDS (beside the row factors), else two
+    static constexpr int STG = 3 * BYTES + 3 * GM_BM * 4 <= 160 * 1024 ? GM_STAGES : 2;
 };
 
 // s_waitcnt with vmcnt(N), lgkmcnt(0), expcnt left alone (gfx9 encoding).
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
 {
     using G = GemmStage<FMT, WPW>;
     static_assert(FMT != FQ8_0 || WPW == 1, "Q8_0 stages one weight group per wave");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[GM_STAGES * G::BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[G::STG * G::BYTES];
     __shared__ __attribute__((aligned(16))) float s_rs[3][GM_BM];   // row factors of 3 tiles
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -458,9 +460,9 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
             }
     };
 
-    // One stream of (tile, step) pairs per workgroup; the loads run two steps ahead of the
+    // One stream of (tile, step) pairs per workgroup; the loads run STG - 1 steps ahead of the
     // compute, across tile boundaries (the next tile's first loads overlap this tile's last steps
-    // and its stores).  Ring slot of stream position p: p % 3.
+    // and its stores).  Ring slot of stream position p: p % STG.
     constexpr int LPS = G::XPW + G::WPW * (G::WH + 1);   // loads per thread per step (+1 at a tile's start)
     int ik8 = slot, is = 0, itn = 0, pi = 0;  // issue cursor: tile, step, tile ordinal, position
     Tile ti = tile_of(ik8);
@@ -468,7 +470,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
     auto issue_next = [&]() {
         if (ik8 >= ntiles)
             return;
-        issue(ti, rpi, is, pi % GM_STAGES, itn % 3);
+        issue(ti, rpi, is, pi % G::STG, itn % 3);
         ++pi;
         if (++is == ti.S) {
             is = 0;
@@ -480,22 +482,23 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
             }
         }
     };
-    issue_next();
-    issue_next();
+#pragma unroll
+    for (int p = 0; p < G::STG - 1; ++p)
+        issue_next();
     int ck8 = slot, cs = 0, ctn = 0, pc = 0;  // compute cursor
     Tile tc = tile_of(ck8);
     while (true) {
-        // this thread's loads of position pc have landed (those of pc + 1 may still be in
-        // flight; the stores of a finished tile are waited for too), and after the barrier
-        // everyone's have; every wave is also done reading position pc - 1, whose ring slot the
-        // loads of pc + 2 overwrite
-        if (pi - pc >= 2)
-            gm_wait<LPS>();
+        // this thread's loads of position pc have landed (those of pc + 1 .. pc + STG - 2 may
+        // still be in flight; the stores of a finished tile are waited for too), and after the
+        // barrier everyone's have; every wave is also done reading position pc - 1, whose ring
+        // slot the loads of pc + STG - 1 overwrite
+        if (pi - pc >= G::STG - 1)
+            gm_wait<LPS * (G::STG - 2)>();
         else
             gm_wait<0>();
         gm_barrier();
         issue_next();
-        compute(tc, cs, pc % GM_STAGES);
+        compute(tc, cs, pc % G::STG);
         ++pc;
         if (++cs == tc.S) {
             epilogue(tc, ctn % 3);
@@ -550,6 +553,8 @@ int launch_gemm(int fmt, const GemmArgs &a, const float *x, void *stream)
     const int grid = 8 * (per_xcd < 32 ? per_xcd : 32);
     if (fmt == FQ4_0 && a.bn == 256)
         hipLaunchKernelGGL((k_gemm<FQ4_0, 2>), dim3(grid), dim3(GM_THREADS), 0, s, a);
+    else if (fmt == FQ4_0 && a.bn == 512)
+        hipLaunchKernelGGL((k_gemm<FQ4_0, 4>), dim3(grid), dim3(GM_THREADS), 0, s, a);
     else if (fmt == FQ4_0)
         hipLaunchKernelGGL((k_gemm<FQ4_0, 1>), dim3(grid), dim3(GM_THREADS), 0, s, a);
     else if (fmt == FQ1_0 && a.bn == 256)
