@@ -769,9 +769,9 @@ int qgemv_qk_norm_rope(float *qkv, int nb, int n_q_heads, int n_kv_heads, int he
 static int64_t gemm_m_tiles(int64_t M) { return (M + QG_GEMM_BM - 1) / QG_GEMM_BM; }
 // Tiles, K steps and K splits of a qgemm call, from the shape alone (so the workspace size is
 // too).  Q4_0 takes 512-row weight tiles when those alone give the 256 compute units a tile each,
-// else, like Q1_0, 256-row tiles when those do, else 128-row ones (Q8_0 always); when the output
-// tiles are still fewer than the compute units the K steps are dealt out to several workgroups per
-// tile, at least two steps each.
+// else (every format) 256-row tiles when those do, else 128-row ones; when the output tiles are
+// still fewer than the compute units the K steps are dealt out to several workgroups per tile, at
+// least two steps each.
 struct GemmPlan {
     int64_t m_tiles, n_tiles, bn, steps, sps, splits;
     int64_t xh_bytes, rs_bytes, part_bytes;
@@ -780,7 +780,7 @@ static GemmPlan gemm_plan(int fmt, int64_t N, int64_t K, int64_t M)
 {
     GemmPlan p;
     p.m_tiles = gemm_m_tiles(M);
-    p.bn = fmt != QG_Q8_0 && p.m_tiles * ((N + 255) / 256) >= 256 ? 256 : 128;
+    p.bn = p.m_tiles * ((N + 255) / 256) >= 256 ? 256 : 128;
     if (fmt == QG_Q4_0 && p.m_tiles * ((N + 511) / 512) >= 256)
         p.bn = 512;
     p.n_tiles = (N + p.bn - 1) / p.bn;

@@ -12,7 +12,7 @@
 //    out in 1 KB chunks (16 rows x one 32-k block) whose 64 16-byte pieces are the A operands of
 //    v_mfma_f32_16x16x32_f16 in lane order (mf_elem), zero past K and past M;
 //  - a workgroup (8 waves) owns a 128 x 16 WPW tile of Y, the widest that still fills the device
-//    (Q4_0: 512, 256 or 128 weight rows; Q1_0: 256 or 128; Q8_0: 128); wave w owns all 128 x
+//    (Q4_0: 512, 256 or 128 weight rows; Q1_0 and Q8_0: 256 or 128); wave w owns all 128 x
 //    rows against its WPW groups of 16 weight rows (8 x WPW MFMA tiles), so each weight is decoded
 //    once per workgroup and feeds 8 MFMAs per block (the decode is VALU work; eight x tiles per
 //    decoded weight tile keep it under the matrix-core time), and each x operand read from LDS
@@ -20,8 +20,9 @@
 //  - x chunks, weight chunks (16 rows x 64 bytes for Q4_0, x 128 bytes for Q8_0, x 16 bytes for
 //    Q1_0) and the block
 //    scales go from global memory straight into LDS (global_load_lds: no registers, no LDS store
-//    instructions), three stages deep (two for Q4_0's 512-row tiles, whose stage is 72 KB): the
-//    loads of step s + 2 (s + 1) are issued while step s computes.  One barrier per step;
+//    instructions), three stages deep (two where three do not fit in LDS: Q4_0's 512-row tiles,
+//    Q8_0's 256-row ones): the loads of step s + 2 (s + 1) are issued while step s computes.
+//    One barrier per step;
 //  - the kernel is persistent (one workgroup per compute unit, each walking a list of tiles): the
 //    load stream runs across tile boundaries, so the next tile's first loads overlap the current
 //    tile's last steps and its stores, and there is no per-wave launch ramp between tiles;
@@ -53,9 +54,9 @@ static_assert(GM_BM == QG_GEMM_BM && GM_BPS * 32 == QG_GEMM_KSTEP, "the host pla
 // LDS stage of one step: x chunks [row group 0..7][block 0..3] (1 KB each), then weight chunks
 // [row group][half] (1 KB each: 16 rows x 4 chunks of 16 B), then the scales [row][block], one
 // dword each (a 2-byte copy to LDS fills its lane's dword, zero-extended).  A wave owns WPW
-// 16-row weight groups: the most (Q4_0 up to four, Q1_0 two) whose tiles alone still fill the
-// device, since each x operand read from LDS then feeds WPW products, else one (more, smaller
-// tiles; Q8_0 always, its weight chunks being twice as many).
+// 16-row weight groups: the most (Q4_0 up to four, Q1_0 and Q8_0 two) whose tiles alone still
+// fill the device, since each x operand read from LDS then feeds WPW products, else one (more,
+// smaller tiles).
 // Q1_0: a step is one 128-weight block, 16 bytes of sign bits per row ([row][4 dwords], one
 // dword wave-load per 16 rows) and one scale per row (lane r of the wave's 256-byte area).
 template <int FMT, int WPW_>
@@ -218,7 +219,6 @@ template <int FMT, int WPW>
 __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
 {
     using G = GemmStage<FMT, WPW>;
-    static_assert(FMT != FQ8_0 || WPW == 1, "Q8_0 stages one weight group per wave");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[G::STG * G::BYTES];
     __shared__ __attribute__((aligned(16))) float s_rs[3][GM_BM];   // row factors of 3 tiles
 
@@ -561,6 +561,8 @@ int launch_gemm(int fmt, const GemmArgs &a, const float *x, void *stream)
         hipLaunchKernelGGL((k_gemm<FQ1_0, 2>), dim3(grid), dim3(GM_THREADS), 0, s, a);
     else if (fmt == FQ1_0)
         hipLaunchKernelGGL((k_gemm<FQ1_0, 1>), dim3(grid), dim3(GM_THREADS), 0, s, a);
+    else if (a.bn == 256)
+        hipLaunchKernelGGL((k_gemm<FQ8_0, 2>), dim3(grid), dim3(GM_THREADS), 0, s, a);
     else
         hipLaunchKernelGGL((k_gemm<FQ8_0, 1>), dim3(grid), dim3(GM_THREADS), 0, s, a);
     e = hipGetLastError();

@@ -51,11 +51,13 @@ def test_qgemm_parity(fmt, M, N, K):
 @pytest.mark.parametrize("fmt,M,N,K", [(q.Q4_0, 2048, 4096, 2048), (q.Q8_0, 2048, 2048, 1536),
                                        (q.Q4_0, 1950, 4000, 1056), (q.Q1_0, 2048, 4096, 2048),
                                        (q.Q1_0, 1950, 4000, 1152), (q.Q4_0, 2048, 8192, 2048),
-                                       (q.Q4_0, 1990, 7900, 1056)])
+                                       (q.Q4_0, 1990, 7900, 1056), (q.Q8_0, 2048, 4096, 1536),
+                                       (q.Q8_0, 1990, 4000, 1056)])
 def test_qgemm_large_sampled(fmt, M, N, K):
     """Full-size launch; the oracle checks 64 sampled x rows against 256 sampled W rows.  The
-    Q4_0 and Q1_0 cases at N ~ 4000 take the 256-row weight tiles, the Q4_0 ones at N ~ 8000 the
-    512-row tiles with the two-stage ring (the second of each pair ragged in M, N and K)."""
+    Q4_0, Q1_0 and Q8_0 cases at N ~ 4000 take the 256-row weight tiles (Q8_0 with the two-stage
+    ring), the Q4_0 ones at N ~ 8000 the 512-row tiles with the two-stage ring (the second of each
+    pair ragged in M, N and K)."""
     say(f"qgemm large fmt={fmt} M={M} N={N} K={K}")
     g = wl.rng(3100 + fmt, M)
     W = wl.matrix(fmt, g, N, K)
