@@ -766,23 +766,32 @@ int qgemv_qk_norm_rope(float *qkv, int nb, int n_q_heads, int n_kv_heads, int he
                                              rope_sin, stream));
 }
 
-static int64_t gemm_m_tiles(int64_t M) { return (M + QG_GEMM_BM - 1) / QG_GEMM_BM; }
 // Tiles, K steps and K splits of a qgemm call, from the shape alone (so the workspace size is
-// too).  Q4_0 takes 512-row weight tiles when those alone give the 256 compute units a tile each,
-// else (every format) 256-row tiles when those do, else 128-row ones; when the output tiles are
-// still fewer than the compute units the K steps are dealt out to several workgroups per tile, at
-// least two steps each.
+// too).  Weight tiles: the widest that alone give the 256 compute units a tile each (Q4_0 up to
+// 512 rows, the others, and any format against 64-row x tiles, 256), else 128 rows.  x tiles of
+// 128 rows, or of 64 for M <= 64 (half the operand copies and products of a 128-row tile that
+// would be half zero rows); when the output tiles are still fewer than the compute units the K
+// steps are dealt out to several workgroups per tile, at least two steps each.
 struct GemmPlan {
-    int64_t m_tiles, n_tiles, bn, steps, sps, splits;
+    int64_t m_tiles, n_tiles, bm, bn, steps, sps, splits;
     int64_t xh_bytes, rs_bytes, part_bytes;
 };
+
+static int64_t gemm_bn(int fmt, int64_t m_tiles, int64_t N)
+{
+    if (fmt == QG_Q4_0 && m_tiles * ((N + 511) / 512) >= 256)
+        return 512;
+    return m_tiles * ((N + 255) / 256) >= 256 ? 256 : 128;
+}
+
 static GemmPlan gemm_plan(int fmt, int64_t N, int64_t K, int64_t M)
 {
     GemmPlan p;
-    p.m_tiles = gemm_m_tiles(M);
-    p.bn = p.m_tiles * ((N + 255) / 256) >= 256 ? 256 : 128;
-    if (fmt == QG_Q4_0 && p.m_tiles * ((N + 511) / 512) >= 256)
-        p.bn = 512;
+    p.bm = M <= 64 ? 64 : QG_GEMM_BM;
+    p.m_tiles = (M + p.bm - 1) / p.bm;
+    p.bn = gemm_bn(fmt, p.m_tiles, N);
+    if (p.bm == 64 && p.bn > 256)
+        p.bn = 256;
     p.n_tiles = (N + p.bn - 1) / p.bn;
     p.steps = (K + QG_GEMM_KSTEP - 1) / QG_GEMM_KSTEP;
     const int64_t tiles = p.m_tiles * p.n_tiles;
@@ -793,7 +802,7 @@ static GemmPlan gemm_plan(int fmt, int64_t N, int64_t K, int64_t M)
         p.sps = sps < 2 ? 2 : sps;
     }
     p.splits = (p.steps + p.sps - 1) / p.sps;
-    const int64_t Mp = p.m_tiles * QG_GEMM_BM;
+    const int64_t Mp = p.m_tiles * p.bm;
     p.xh_bytes = round256(Mp * p.steps * QG_GEMM_KSTEP * 2);
     p.rs_bytes = round256(Mp * 4);
     p.part_bytes = p.splits > 1 ? round256(p.splits * M * N * 4) : 0;
@@ -822,11 +831,11 @@ int qgemm(int fmt, const void *W, int64_t N, int64_t K, const float *x, int64_t 
     Layout L;
     if (M < 1 || M > QG_GEMM_MAX_M || N < 1 || N > 0x7fffffffLL || !layout(fmt, N, K, &L) ||
         N * L.qs_row >= QG_BUF_MAX || N * L.sc_row >= QG_BUF_MAX ||
-        (N / 128 + 8) * gemm_m_tiles(M) > 0x7fffffffLL)   // the tile count
+        (N / 128 + 8) * ((M + 63) / 64) > 0x7fffffffLL)   // the tile count
         return QG_ERR_SHAPE;
     const GemmPlan p = gemm_plan(fmt, N, K, M);
     if ((p.n_tiles + 7) * p.m_tiles * p.splits > 0x7fffffffLL ||
-        p.m_tiles * QG_GEMM_BM / 16 * p.steps * QG_GEMM_KSTEP / 32 > 0x7fffffffLL)
+        p.m_tiles * p.bm / 16 * p.steps * QG_GEMM_KSTEP / 32 > 0x7fffffffLL)
         return QG_ERR_SHAPE;
     if (!ws)
         return QG_ERR_WORKSPACE;
@@ -856,6 +865,7 @@ int qgemm(int fmt, const void *W, int64_t N, int64_t K, const float *x, int64_t 
     a.n_tiles = (int)p.n_tiles;
     a.m_tiles = (int)p.m_tiles;
     a.bn = (int)p.bn;
+    a.bm = (int)p.bm;
     a.KBp = (int)(p.steps * QG_GEMM_KSTEP / 32);
     a.steps = (int)p.steps;
     a.sps = (int)p.sps;

@@ -46,7 +46,7 @@
 namespace qg {
 
 constexpr int GM_THREADS = 512;                   // 8 waves
-constexpr int GM_BM = 128;                        // rows of x per workgroup
+constexpr int GM_BM = 128;                        // rows of x per workgroup (the larger tile)
 constexpr int GM_BPS = 4;                         // 32-k blocks per step
 constexpr int GM_STAGES = 3;
 static_assert(GM_BM == QG_GEMM_BM && GM_BPS * 32 == QG_GEMM_KSTEP, "the host plans with these tiles");
@@ -59,18 +59,20 @@ static_assert(GM_BM == QG_GEMM_BM && GM_BPS * 32 == QG_GEMM_KSTEP, "the host pla
 // smaller tiles).
 // Q1_0: a step is one 128-weight block, 16 bytes of sign bits per row ([row][4 dwords], one
 // dword wave-load per 16 rows) and one scale per row (lane r of the wave's 256-byte area).
-template <int FMT, int WPW_>
+template <int FMT, int WPW_, int BM_ = GM_BM>
 struct GemmStage {
+    static constexpr int BM = BM_;                             // x rows per tile (64 or 128)
+    static constexpr int NBT = BM / 16;                        // MFMA tiles along M
     static constexpr int WH = FMT == FQ8_0 ? 2 : 1;            // weight wave-loads per row group
     static constexpr int WPW = WPW_;                           // weight row groups per wave
     static constexpr int BN = 8 * 16 * WPW;                    // weight rows per workgroup
-    static constexpr int XB = GM_BM / 16 * GM_BPS * 1024;
+    static constexpr int XB = NBT * GM_BPS * 1024;
     static constexpr int WB = FMT == FQ1_0 ? BN * 16 : BN / 16 * WH * 1024;
     static constexpr int SB = FMT == FQ1_0 ? BN / 16 * 256 : BN * GM_BPS * 4;
     static constexpr int BYTES = XB + WB + SB;
-    static constexpr int XPW = GM_BM / 16 * GM_BPS / 8;         // x wave-loads per wave
+    static constexpr int XPW = NBT * GM_BPS / 8;               // x wave-loads per wave
     // ring depth: three stages where they fit in the 160 KB of LDS (beside the row factors), else two
-    static constexpr int STG = 3 * BYTES + 3 * GM_BM * 4 <= 160 * 1024 ? GM_STAGES : 2;
+    static constexpr int STG = 3 * BYTES + 3 * BM * 4 <= 160 * 1024 ? GM_STAGES : 2;
 };
 
 // s_waitcnt with vmcnt(N), lgkmcnt(0), expcnt left alone (gfx9 encoding).
@@ -215,12 +217,13 @@ __global__ __launch_bounds__(256) void k_xprep(const float *x, int64_t M, int64_
     }
 }
 
-template <int FMT, int WPW>
+template <int FMT, int WPW, int BM>
 __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
 {
-    using G = GemmStage<FMT, WPW>;
+    using G = GemmStage<FMT, WPW, BM>;
+    constexpr int NBT = G::NBT;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[G::STG * G::BYTES];
-    __shared__ __attribute__((aligned(16))) float s_rs[3][GM_BM];   // row factors of 3 tiles
+    __shared__ __attribute__((aligned(16))) float s_rs[3][BM];   // row factors of 3 tiles
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
         Tile t;
         const int rest = k8 / ntx;
         t.n0 = (int64_t)(n_base + k8 % ntx) * G::BN;
-        t.m0 = (int64_t)(rest % a.m_tiles) * GM_BM;
+        t.m0 = (int64_t)(rest % a.m_tiles) * BM;
         t.split = rest / a.m_tiles;
         t.s0 = t.split * a.sps;
         t.S = a.steps - t.s0 < a.sps ? a.steps - t.s0 : a.sps;   // >= 1 (host plan)
@@ -318,15 +321,15 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
                 gm_dma2(rp.sc[wt] + 2 * (uint32_t)blk, st + G::XB + G::WB + g * 256);
             }
         }
-        if (s_rel == 0 && wave < 2)
+        if (s_rel == 0 && wave < BM / 64)
             gm_dma4(a.rs + t.m0 + 64 * wave + lane, &s_rs[rs_slot][64 * wave]);
     };
 
-    float acc[8][G::WPW][4];    // Q4_0, Q8_0: per-block scaled sums (VALU)
-    mf4 macc[8][G::WPW];        // Q1_0: sums kept in the MFMA accumulators
+    float acc[NBT][G::WPW][4];  // Q4_0, Q8_0: per-block scaled sums (VALU)
+    mf4 macc[NBT][G::WPW];      // Q1_0: sums kept in the MFMA accumulators
     auto zero_acc = [&]() {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < NBT; ++i)
 #pragma unroll
             for (int wt = 0; wt < G::WPW; ++wt) {
                 acc[i][wt][0] = acc[i][wt][1] = acc[i][wt][2] = acc[i][wt][3] = 0.f;
@@ -356,9 +359,9 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
             }
 #pragma unroll
             for (int b = 0; b < GM_BPS; ++b) {
-                mh8 A[8];
+                mh8 A[NBT];
 #pragma unroll
-                for (int bt = 0; bt < 8; ++bt)
+                for (int bt = 0; bt < NBT; ++bt)
                     A[bt] = *reinterpret_cast<const mh8 *>(st + (bt * GM_BPS + b) * 1024 + 16 * lane);
 #pragma unroll
                 for (int wt = 0; wt < G::WPW; ++wt) {
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
                     bw.w = (((w >> (4 * lc + 3)) << 15) & 0x80008000u) ^ dp[wt];
                     const mh8 B = __builtin_bit_cast(mh8, bw);
 #pragma unroll
-                    for (int bt = 0; bt < 8; ++bt)
+                    for (int bt = 0; bt < NBT; ++bt)
                         macc[bt][wt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bt], B, macc[bt][wt], 0, 0, 0);
                 }
             }
@@ -401,9 +404,9 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
 #pragma unroll
         for (int b = 0; b < GM_BPS; ++b) {
             const int blk = GM_BPS * s + b;
-            mh8 A[8];
+            mh8 A[NBT];
 #pragma unroll
-            for (int bt = 0; bt < 8; ++bt)
+            for (int bt = 0; bt < NBT; ++bt)
                 A[bt] = *reinterpret_cast<const mh8 *>(st + (bt * GM_BPS + b) * 1024 + 16 * lane);
 #pragma unroll
             for (int wt = 0; wt < G::WPW; ++wt) {
@@ -419,7 +422,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
                 const float d = blk < KB ? (float)__builtin_bit_cast(_Float16, db) : 0.f;
                 const mf4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int bt = 0; bt < 8; bt += 4) {
+                for (int bt = 0; bt < NBT; bt += 4) {
                     mf4 D[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -442,7 +445,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
         const bool fold = a.splits > 1;
         float *out = fold ? a.part + (int64_t)t.split * a.M * a.N : a.y;
 #pragma unroll
-        for (int bt = 0; bt < 8; ++bt)
+        for (int bt = 0; bt < NBT; ++bt)
 #pragma unroll
             for (int vv = 0; vv < 4; ++vv) {
                 const int rl = 16 * bt + 4 * lc + vv;
@@ -531,7 +534,7 @@ int launch_gemm(int fmt, const GemmArgs &a, const float *x, void *stream)
     hipStream_t s = static_cast<hipStream_t>(stream);
     // x preparation: one wave per row of the padded x, its pieces held in registers when there
     // are at most 512
-    const unsigned groups = (unsigned)((int64_t)a.m_tiles * GM_BM / 4);
+    const unsigned groups = (unsigned)((int64_t)a.m_tiles * a.bm / 4);
     const int np = 4 * a.KBp;
     const int ppl = np <= 64 ? 1 : np <= 128 ? 2 : np <= 256 ? 4 : np <= 512 ? 8 : 0;
     using XP = void (*)(const float *, int64_t, int64_t, int, _Float16 *, float *);
@@ -551,20 +554,24 @@ int launch_gemm(int fmt, const GemmArgs &a, const float *x, void *stream)
     // XCD, each walking its XCD's tiles
     const int per_xcd = ((a.n_tiles + 7) / 8) * a.m_tiles * a.splits;
     const int grid = 8 * (per_xcd < 32 ? per_xcd : 32);
-    if (fmt == FQ4_0 && a.bn == 256)
-        hipLaunchKernelGGL((k_gemm<FQ4_0, 2>), dim3(grid), dim3(GM_THREADS), 0, s, a);
-    else if (fmt == FQ4_0 && a.bn == 512)
-        hipLaunchKernelGGL((k_gemm<FQ4_0, 4>), dim3(grid), dim3(GM_THREADS), 0, s, a);
-    else if (fmt == FQ4_0)
-        hipLaunchKernelGGL((k_gemm<FQ4_0, 1>), dim3(grid), dim3(GM_THREADS), 0, s, a);
-    else if (fmt == FQ1_0 && a.bn == 256)
-        hipLaunchKernelGGL((k_gemm<FQ1_0, 2>), dim3(grid), dim3(GM_THREADS), 0, s, a);
-    else if (fmt == FQ1_0)
-        hipLaunchKernelGGL((k_gemm<FQ1_0, 1>), dim3(grid), dim3(GM_THREADS), 0, s, a);
-    else if (a.bn == 256)
-        hipLaunchKernelGGL((k_gemm<FQ8_0, 2>), dim3(grid), dim3(GM_THREADS), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_gemm<FQ8_0, 1>), dim3(grid), dim3(GM_THREADS), 0, s, a);
+    void (*kern)(GemmArgs) = nullptr;
+    if (a.bm == 64) {
+        if (fmt == FQ4_0)
+            kern = a.bn == 256 ? k_gemm<FQ4_0, 2, 64> : k_gemm<FQ4_0, 1, 64>;
+        else if (fmt == FQ1_0)
+            kern = a.bn == 256 ? k_gemm<FQ1_0, 2, 64> : k_gemm<FQ1_0, 1, 64>;
+        else
+            kern = a.bn == 256 ? k_gemm<FQ8_0, 2, 64> : k_gemm<FQ8_0, 1, 64>;
+    } else {
+        if (fmt == FQ4_0)
+            kern = a.bn == 512 ? k_gemm<FQ4_0, 4, 128>
+                 : a.bn == 256 ? k_gemm<FQ4_0, 2, 128> : k_gemm<FQ4_0, 1, 128>;
+        else if (fmt == FQ1_0)
+            kern = a.bn == 256 ? k_gemm<FQ1_0, 2, 128> : k_gemm<FQ1_0, 1, 128>;
+        else
+            kern = a.bn == 256 ? k_gemm<FQ8_0, 2, 128> : k_gemm<FQ8_0, 1, 128>;
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(GM_THREADS), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1)
         return (int)e;

@@ -196,19 +196,20 @@ struct MoeArgs {
 
 // Tile of the wide row-batch GEMM: rows of x per workgroup, k per step; rows of W per workgroup
 // are 128 or (Q4_0, when the tiles fill the device) 256.
-#define QG_GEMM_BM 128
+#define QG_GEMM_BM 128   // rows of x per tile: 128, or 64 when M <= 64
 #define QG_GEMM_KSTEP 128
 // Arguments of the wide row-batch GEMM (gemm_kernels.hip).
 struct GemmArgs {
-    const uint8_t *qs, *sc;     // packed W (Q4_0 / Q8_0)
-    _Float16 *xh;               // workspace: x as f16 in operand chunks, [m_tiles * BM / 16][KBp][512]
-    float *rs;                  // workspace: factor undoing each x row's scale, [m_tiles * BM]
+    const uint8_t *qs, *sc;     // packed W (Q4_0 / Q8_0 / Q1_0)
+    _Float16 *xh;               // workspace: x as f16 in operand chunks, [m_tiles * bm / 16][KBp][512]
+    float *rs;                  // workspace: factor undoing each x row's scale, [m_tiles * bm]
     float *part;                // workspace: partial tiles of the K splits, [splits][M][N] (splits > 1)
     float *y;                   // [M][N]
     int64_t N, K, M;
     int64_t qs_row, sc_row;
-    int n_tiles, m_tiles;       // tiles of W (bn rows) and of x (QG_GEMM_BM rows)
-    int bn;                     // rows of W per tile: 128 or 256
+    int n_tiles, m_tiles;       // tiles of W (bn rows) and of x (bm rows)
+    int bn;                     // rows of W per tile: 128, 256 or 512 (Q4_0)
+    int bm;                     // rows of x per tile: 128 or 64
     int KBp;                    // 32-k blocks of a padded x row: steps * QG_GEMM_KSTEP / 32
     int steps, sps, splits;     // K steps, steps per split, splits (ceil(steps / sps))
 };

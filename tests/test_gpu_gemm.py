@@ -52,7 +52,8 @@ def test_qgemm_parity(fmt, M, N, K):
                                        (q.Q4_0, 1950, 4000, 1056), (q.Q1_0, 2048, 4096, 2048),
                                        (q.Q1_0, 1950, 4000, 1152), (q.Q4_0, 2048, 8192, 2048),
                                        (q.Q4_0, 1990, 7900, 1056), (q.Q8_0, 2048, 4096, 1536),
-                                       (q.Q8_0, 1990, 4000, 1056)])
+                                       (q.Q8_0, 1990, 4000, 1056), (q.Q4_0, 512, 8192, 2048),
+                                       (q.Q8_0, 500, 8000, 1056), (q.Q1_0, 450, 8100, 640)])
 def test_qgemm_large_sampled(fmt, M, N, K):
     """Full-size launch; the oracle checks 64 sampled x rows against 256 sampled W rows.  The
     Q4_0, Q1_0 and Q8_0 cases at N ~ 4000 take the 256-row weight tiles (Q8_0 with the two-stage
@@ -81,6 +82,22 @@ def test_qgemm_integer_inputs_bitwise(fmt):
     y = _gemm(fmt, gpu_matrix(fmt, W, N, K), N, K, x)
     yr, _ = oracle.gemv(fmt, W, N, K, x)
     assert np.array_equal(y.astype(np.float64), yr)
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [(q.Q4_0, 40, 66000, 256), (q.Q8_0, 33, 66000, 256),
+                                       (q.Q1_0, 64, 65600, 384)])
+def test_qgemm_few_rows_tall_matrix(fmt, M, N, K):
+    """M <= 64 takes 64-row x tiles; against more than 65280 weight rows the 256-row weight tiles
+    alone fill the device (every other small-M case takes 128-row ones with split K).  The oracle
+    checks every x row against 256 sampled W rows."""
+    say(f"qgemm tall fmt={fmt} M={M} N={N} K={K}")
+    g = wl.rng(3500 + fmt, M)
+    W = wl.matrix(fmt, g, N, K)
+    x = wl.normal_f32(g, (M, K))
+    y = _gemm(fmt, gpu_matrix(fmt, W, N, K), N, K, x)
+    cols = np.sort(g.choice(N, 256, replace=False))
+    yr, A = oracle.gemv(fmt, W, N, K, x, rows=cols)
+    assert_within(y[:, cols], yr, tol_gemv(A, yr), f"qgemm tall fmt={fmt}")
 
 
 @pytest.mark.parametrize("K", [1024, 8192])
