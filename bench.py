@@ -528,6 +528,10 @@ def main():
     ap.add_argument("--nb", type=int, default=None)
     ap.add_argument("--rows", type=int, default=65536, help="gemv workload: output rows")
     ap.add_argument("--hidden", type=int, default=2048, help="gemv workload: reduction length")
+    ap.add_argument("--format", default="q4_0",
+                    choices=["q4_0", "q5_0", "q8_0", "q4_k", "q5_k", "q6_k", "iq4_nl", "iq4_xs",
+                             "q1_0", "aq4"],
+                    help="gemv / gemm workloads: block format of W (gemm: q4_0, q8_0, q1_0)")
     ap.add_argument("--warm", action="store_true", help="reuse one weight copy (cache-assisted)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
@@ -551,16 +555,18 @@ def main():
     torch.cuda.set_device(0)
 
     wl_name = args.workload
+    import workloads as wlm
+    fmt = {v: k for k, v in wlm.FMT_NAME.items()}[args.format]
     if wl_name == "decode_mlp":
         b = make_decode_mlp(args.warm)
     elif wl_name == "lm_head":
         b = make_lm_head(args.warm, args.nb or 1)
     elif wl_name == "gemv":
-        b = make_gemv(args.warm, args.nb or 1, args.rows, args.hidden)
+        b = make_gemv(args.warm, args.nb or 1, args.rows, args.hidden, fmt=fmt)
     elif wl_name == "qkv":
         b = make_qkv(args.warm, args.nb or 16)
     elif wl_name == "gemm":
-        b = make_gemm(args.warm, args.nb or 512)
+        b = make_gemm(args.warm, args.nb or 512, fmt=fmt)
     elif wl_name == "read":
         b = make_read(args.warm)
         args.no_cpu = True
@@ -600,7 +606,8 @@ def main():
         out["tflops"] = s["tflops"]
 
     cpu_b = Bench(b.name, 0, 0, "", None, None, b.cpu, {})   # the oracle needs host arrays only
-    if not args.no_extras and wl_name == "gemv" and not args.warm and args.nb in (None, 1):
+    if (not args.no_extras and wl_name == "gemv" and not args.warm and args.nb in (None, 1) and
+            args.format == "q4_0"):
         del b
         torch.cuda.empty_cache()
         es, ew = args.extra_steps, min(args.warmup, 20)

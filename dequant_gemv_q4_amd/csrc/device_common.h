@@ -212,20 +212,26 @@ __device__ __forceinline__ ChunkScale chunk_scale(const uint4 &s, int q /* chunk
         cs.a2 = d * (float)(int8_t)((s.y >> (8 * u)) & 0xffu);
         cs.b = cs.b2 = 0.f;
     } else if constexpr (fmt_min(FMT)) {
+        // sub-blocks 2c, 2c + 1 of the 12 scale bytes (s.y: bytes 0-3, s.z: 4-7, s.w: 8-11):
+        // sub-block j < 4 keeps its scale in the low 6 bits of byte j and its min in byte j + 4;
+        // j >= 4 keeps 4 low bits of each in byte j + 4 (scale low nibble, min high nibble) and
+        // the 2 high bits in the top bits of bytes j - 4 and j.  Both cases as one set of bit-field
+        // extracts whose source word and widths depend on c (the lanes of a wave hold different
+        // chunks of their super-blocks, so a branch on c would run both sides)
         const float d = h2f(s.x & 0xffffu), dmin = h2f(s.x >> 16);
         const int c = q >> 1;
-        const int jA = 2 * c, jB = 2 * c + 1;
-        uint32_t scA, mA, scB, mB;
-        if (c < 2) {
-            scA = (s.y >> (8 * jA)) & 63u;  mA = (s.z >> (8 * jA)) & 63u;
-            scB = (s.y >> (8 * jB)) & 63u;  mB = (s.z >> (8 * jB)) & 63u;
-        } else {
-            const int kA = jA - 4, kB = jB - 4;
-            scA = ((s.w >> (8 * kA)) & 15u) | (((s.y >> (8 * kA + 6)) & 3u) << 4);
-            mA = ((s.w >> (8 * kA + 4)) & 15u) | (((s.z >> (8 * kA + 6)) & 3u) << 4);
-            scB = ((s.w >> (8 * kB)) & 15u) | (((s.y >> (8 * kB + 6)) & 3u) << 4);
-            mB = ((s.w >> (8 * kB + 4)) & 15u) | (((s.z >> (8 * kB + 6)) & 3u) << 4);
-        }
+        const bool up = c >= 2;
+        const uint32_t sA = 16u * (uint32_t)(c & 1), sB = sA + 8u;
+        const uint32_t lsc = up ? s.w : s.y, lm = up ? s.w : s.z;
+        const uint32_t wl = up ? 4u : 6u, om = up ? 4u : 0u, hm = up ? 3u : 0u;
+        const uint32_t scA = __builtin_amdgcn_ubfe(lsc, sA, wl) |
+                             ((__builtin_amdgcn_ubfe(s.y, sA + 6u, 2u) & hm) << 4);
+        const uint32_t mA = __builtin_amdgcn_ubfe(lm, sA + om, wl) |
+                            ((__builtin_amdgcn_ubfe(s.z, sA + 6u, 2u) & hm) << 4);
+        const uint32_t scB = __builtin_amdgcn_ubfe(lsc, sB, wl) |
+                             ((__builtin_amdgcn_ubfe(s.y, sB + 6u, 2u) & hm) << 4);
+        const uint32_t mB = __builtin_amdgcn_ubfe(lm, sB + om, wl) |
+                            ((__builtin_amdgcn_ubfe(s.z, sB + 6u, 2u) & hm) << 4);
         cs.a = d * (float)scA;
         cs.b = dmin * (float)mA;
         cs.a2 = d * (float)scB;
