@@ -11,18 +11,18 @@
 //    puts its largest |x| in [2^14, 2^15), the high-nibble positions of Q4_0 times 1/16, and laid
 //    out in 1 KB chunks (16 rows x one 32-k block) whose 64 16-byte pieces are the A operands of
 //    v_mfma_f32_16x16x32_f16 in lane order (mf_elem), zero past K and past M;
-//  - a workgroup (8 waves) owns a 128 x 16 WPW tile of Y, the widest that still fills the device
-//    (Q4_0: 512, 256 or 128 weight rows; Q1_0 and Q8_0: 256 or 128); wave w owns all 128 x
-//    rows against its WPW groups of 16 weight rows (8 x WPW MFMA tiles), so each weight is decoded
-//    once per workgroup and feeds 8 MFMAs per block (the decode is VALU work; eight x tiles per
-//    decoded weight tile keep it under the matrix-core time), and each x operand read from LDS
-//    feeds WPW weight tiles.  A step covers 128 k (4 blocks);
-//  - x chunks, weight chunks (16 rows x 64 bytes for Q4_0, x 128 bytes for Q8_0, x 16 bytes for
-//    Q1_0) and the block
-//    scales go from global memory straight into LDS (global_load_lds: no registers, no LDS store
-//    instructions), three stages deep (two where three do not fit in LDS: Q4_0's 512-row tiles,
-//    Q8_0's 256-row ones): the loads of step s + 2 (s + 1) are issued while step s computes.
-//    One barrier per step;
+//  - a workgroup (8 waves) owns a BM x 128 WPW tile of Y: BM = 128 x rows (64 when M <= 64, a
+//    128-row tile being then half zero rows) against the widest weight tile that still fills the
+//    device (Q4_0: 512, 256 or 128 weight rows; Q1_0 and Q8_0: 256 or 128); wave w owns all BM x
+//    rows against its WPW groups of 16 weight rows (BM / 16 x WPW MFMA tiles), so each weight is
+//    decoded once per workgroup and feeds BM / 16 MFMAs per block (the decode is VALU work; eight
+//    x tiles per decoded weight tile keep it under the matrix-core time), and each x operand read
+//    from LDS feeds WPW weight tiles.  A step covers 128 k (4 blocks);
+//  - x chunks, weight chunks (16 rows x 64 bytes for Q4_0, 128 for Q8_0, 16 for Q1_0) and the
+//    block scales go from global memory straight into LDS (global_load_lds: no registers, no LDS
+//    store instructions), three stages deep (two where three do not fit in LDS: Q4_0's 512-row
+//    tiles, Q8_0's 256-row ones): the loads of step s + 2 (s + 1) are issued while step s
+//    computes.  One barrier per step;
 //  - the kernel is persistent (one workgroup per compute unit, each walking a list of tiles): the
 //    load stream runs across tile boundaries, so the next tile's first loads overlap the current
 //    tile's last steps and its stores, and there is no per-wave launch ramp between tiles;
@@ -46,12 +46,12 @@
 namespace qg {
 
 constexpr int GM_THREADS = 512;                   // 8 waves
-constexpr int GM_BM = 128;                        // rows of x per workgroup (the larger tile)
+constexpr int GM_BM = 128;                        // rows of x per tile (the larger of 128, 64)
 constexpr int GM_BPS = 4;                         // 32-k blocks per step
 constexpr int GM_STAGES = 3;
 static_assert(GM_BM == QG_GEMM_BM && GM_BPS * 32 == QG_GEMM_KSTEP, "the host plans with these tiles");
 
-// LDS stage of one step: x chunks [row group 0..7][block 0..3] (1 KB each), then weight chunks
+// LDS stage of one step: x chunks [row group 0..BM/16-1][block 0..3] (1 KB each), then weight chunks
 // [row group][half] (1 KB each: 16 rows x 4 chunks of 16 B), then the scales [row][block], one
 // dword each (a 2-byte copy to LDS fills its lane's dword, zero-extended).  A wave owns WPW
 // 16-row weight groups: the most (Q4_0 up to four, Q1_0 and Q8_0 two) whose tiles alone still
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
     // row group c / 4, block c % 4.  Weights: lane (ir, lc) of row group g loads chunk 4 h + lc of
     // the step (chunks past the row its last chunk); Q1_0: the block's sign dword.  Scales: block
     // l % 4 of the step (dword 4 row + block of the scale area); Q1_0: the block's scale.  With a
-    // tile's first step, waves 0 and 1 also load its 128 row factors.
+    // tile's first step, the first BM / 64 waves also load its BM row factors.
     auto issue = [&](const Tile &t, const RowPtrs &rp, int s_rel, int ring, int rs_slot) {
         const int s = t.s0 + s_rel;
         uint8_t *st = lds + ring * G::BYTES;
