@@ -257,11 +257,6 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
 
     const int C = (int)(a.qs_row / 16), KB = (int)(a.K / 32);
 
-    // loads of step s of tile t into ring slot `ring`.  x: chunk c = XPW wave + u of the stage is
-    // row group c / 4, block c % 4.  Weights: row groups g = WPW wave + wt, lane (ir, lc) -> row
-    // 16 g + ir, chunk 4 h + lc of the step (rows past N read row N - 1, chunks past the row its
-    // last chunk).  Scales: lane l -> row 16 g + l / 4, block l % 4 of the step (dword 4 row +
-    // block of the scale area).  With a tile's first step, waves 0 and 1 also load its 128 row factors.
     // This lane's weight and scale row pointers of a tile (rows past N read row N - 1), formed
     // once per tile by the issue cursor.  Weights: row group g = WPW wave + wt, lane (ir, lc) ->
     // row 16 g + ir (Q1_0: row 16 g + l / 4, dword l % 4 of a block); scales: lane l -> row
