@@ -1,8 +1,9 @@
 """The wide row-batch GEMM (prefill chunks, M > 16 rows of x; "Module gpu", module prefill) on the
-GPU against the f64 oracle: Q4_0, Q8_0 and Q1_0, M in {17, 64, 512, 2048} and ragged sizes (partial
-128-row tiles of x and W, K not a multiple of the 128-k step, K split over workgroups with a
-shorter last split), every output compared up to M = 512 and sampled rows and columns beyond;
-integer inputs bit for bit."""
+GPU against the f64 oracle: Q4_0, Q8_0 and Q1_0, M from 1 to 2048 and ragged sizes (partial x and
+W tiles, 64-row x tiles for M <= 64 and 128-row ones above, every weight-tile width, K not a
+multiple of the 128-k step, K split over workgroups with a shorter last split), every output
+compared up to M = 512 and sampled rows and columns beyond; integer inputs bit for bit; x only
+4-byte aligned."""
 import numpy as np
 import pytest
 
@@ -37,7 +38,8 @@ def _gemm(fmt, Wp, N, K, x):
                                        (q.Q4_0, 40, 200, 608), (q.Q8_0, 33, 150, 608),
                                        (q.Q4_0, 100, 3000, 1024), (q.Q1_0, 17, 300, 2048),
                                        (q.Q1_0, 512, 517, 1024), (q.Q1_0, 200, 130, 128),
-                                       (q.Q1_0, 131, 1000, 640)])
+                                       (q.Q1_0, 131, 1000, 640), (q.Q4_0, 65, 300, 256),
+                                       (q.Q1_0, 64, 1000, 128), (q.Q8_0, 1, 16, 32)])
 def test_qgemm_parity(fmt, M, N, K):
     say(f"qgemm fmt={fmt} M={M} N={N} K={K}")
     g = wl.rng(3000 + fmt, M + N + K)
