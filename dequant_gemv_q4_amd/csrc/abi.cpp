@@ -317,9 +317,23 @@ struct GemvPlan {
     Plan p;
 };
 
-// Choose the kernel: the matrix-core kernel from QG_MFMA_MIN_NB batch rows when it takes the
-// shape, else the streaming kernel when the shape allows it (a whole wave per row), else the
-// tiled kernel (any nb, any K).  false: no kernel takes the shape.
+// Batch rows from which the matrix-core kernel takes a call.  Three rows already do where the
+// vector path's dot chains per decoded weight (one per row) outweigh the matrix path's fixed
+// costs: Q4_0 and Q4_K matrices of at least 2^24 weights, outside the gated product (65536 x
+// 2048 Q4_0 nb 4: 26.4 -> 21.3 us, with argmax 30.5 -> 23.6 us, nb 3: 22.7 -> 20.9 us; Q4_K nb
+// 4: 30.7 -> 26.8 us, nb 3: 28.1 -> 27.3 us; 8192 x 2048 Q4_0 nb 4: 10.9 -> 8.4 us, nb 3: 8.6
+// -> 8.3 us).  Q8_0 (twice the bytes per weight, a cheaper decode), the gated product and small
+// matrices stay on the vector path below QG_MFMA_MIN_NB rows, and two rows everywhere.
+static int mfma_min_nb(int fmt, int epi, int64_t N, int64_t K)
+{
+    if ((fmt == FQ4_0 || fmt == FQ4_K) && epi != E_GUS && N * K >= ((int64_t)1 << 24))
+        return QG_MFMA_MIN_NB < 3 ? QG_MFMA_MIN_NB : 3;
+    return QG_MFMA_MIN_NB;
+}
+
+// Choose the kernel: the matrix-core kernel from mfma_min_nb batch rows when it takes the shape,
+// else the streaming kernel when the shape allows it (a whole wave per row), else the tiled
+// kernel (any nb, any K).  false: no kernel takes the shape.
 static bool plan_call(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb, GemvPlan *g)
 {
     Layout L;
@@ -328,7 +342,7 @@ static bool plan_call(int fmt, int epi, bool nrm, int64_t N, int64_t K, int nb, 
     // the streaming and matrix kernels address each plane with 32-bit buffer offsets
     const bool small = N * L.qs_row < QG_BUF_MAX && N * L.sc_row < QG_BUF_MAX &&
                        N * L.hb_row < QG_BUF_MAX && N * L.d_row < QG_BUF_MAX;
-    if (small && nb >= QG_MFMA_MIN_NB && plan_mfma(fmt, epi, nrm, N, K, nb, &g->mp) &&
+    if (small && nb >= mfma_min_nb(fmt, epi, N, K) && plan_mfma(fmt, epi, nrm, N, K, nb, &g->mp) &&
         g->mp.grid <= QG_ARGMAX_MAX_GRID) {
         g->kind = 0;
         return true;

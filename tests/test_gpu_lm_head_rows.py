@@ -1,4 +1,5 @@
-"""The matrix-core GEMV (nb 5-16) on lm_head-sized matrices: 65521..65536 rows, K <= 2048, where
+"""The matrix-core GEMV (nb 5-16, and nb 3-4 for Q4_0 / Q4_K matrices of at least 2^24 weights)
+on lm_head-sized matrices: 65521..65536 rows (and 8192, the smallest that takes nb 3-4), K <= 2048, where
 each workgroup owns one group of 16 whole-row tiles (one wave per tile, every K step of its rows).
 Every format, every epilogue, K that is not a multiple of a scale round, a ragged last tile;
 sampled rows against the f64 oracle ("Crate inferencelayer" docs: the lm_head GEMV of the decode
@@ -47,7 +48,9 @@ def _packed(fmt, W, N, K):
     (q.Q8_0, 65536, 2048, 16), (q.Q8_0, 65536, 1600, 7), (q.Q4_K, 65536, 2048, 16),
     (q.Q5_0, 65536, 2048, 8), (q.Q5_K, 65536, 1536, 16), (q.Q6_K, 65536, 2048, 6),
     (q.IQ4_NL, 65536, 2048, 16), (q.IQ4_XS, 65536, 2048, 12), (q.Q1_0, 65536, 2048, 16),
-    (q.AQ4, 65533, 2048, 10)])
+    (q.AQ4, 65533, 2048, 10), (q.Q4_0, 65536, 2048, 4), (q.Q4_K, 65536, 2048, 4),
+    (q.Q4_0, 8192, 2048, 4), (q.Q8_0, 65536, 2048, 4), (q.Q4_0, 65536, 2048, 3),
+    (q.Q4_K, 8192, 2048, 3), (q.Q4_0, 8191, 2048, 3)])
 def test_lm_head_rows_parity(fmt, N, K, nb):
     say(f"lm_head rows fmt={fmt} N={N} K={K} nb={nb}")
     g = wl.rng(7000 + fmt, N + K + nb)
@@ -64,11 +67,12 @@ def test_lm_head_rows_parity(fmt, N, K, nb):
     assert_within(y1[:, rows], yr, tol_gemv(A, yr), f"lm_head rows fmt={fmt} N={N} K={K} nb={nb}")
 
 
-@pytest.mark.parametrize("fmt", [q.Q4_0, q.Q6_K])
-def test_lm_head_rows_epilogues(fmt):
-    """Norm prologue, residual add (in place), gated product and argmax at 65536 rows."""
-    N, K, nb = 65536, 2048, 8
-    say(f"lm_head rows epilogues fmt={fmt}")
+@pytest.mark.parametrize("fmt,nb", [(q.Q4_0, 8), (q.Q6_K, 8), (q.Q4_0, 4), (q.Q4_K, 3)])
+def test_lm_head_rows_epilogues(fmt, nb):
+    """Norm prologue, residual add (in place), gated product and argmax at 65536 rows (at nb 3-4
+    every one but the gated product on the matrix cores)."""
+    N, K = 65536, 2048
+    say(f"lm_head rows epilogues fmt={fmt} nb={nb}")
     g = wl.rng(7100 + fmt, 1)
     W = _matrix(fmt, g, N, K)
     Wu = _matrix(fmt, g, N, K)
