@@ -619,6 +619,8 @@ def main():
         extras["qkv_attn_nb1"] = run_extra("qkv + bias + qk norm + rope",
                                            lambda: make_qkv_attn(False, 1), es, ew, torch)
         extras["lm_head_nb1"] = run_extra("lm_head", lambda: make_lm_head(False, 1), es, ew, torch)
+        extras["lm_head_nb4"] = run_extra("lm_head nb=4", lambda: make_lm_head(False, 4), es, ew,
+                                          torch)
         import dequant_gemv_q4_amd as qq
         for f, nm in ((qq.Q8_0, "q8_0"), (qq.Q4_K, "q4_k"), (qq.Q5_0, "q5_0"), (qq.Q5_K, "q5_k"),
                       (qq.Q6_K, "q6_k"), (qq.IQ4_NL, "iq4_nl"), (qq.IQ4_XS, "iq4_xs"),
