@@ -317,18 +317,28 @@ struct GemvPlan {
     Plan p;
 };
 
-// Batch rows from which the matrix-core kernel takes a call.  Three rows already do where the
-// vector path's dot chains per decoded weight (one per row) outweigh the matrix path's fixed
-// costs: Q4_0 and Q4_K matrices of at least 2^24 weights, outside the gated product (65536 x
-// 2048 Q4_0 nb 4: 26.4 -> 21.3 us, with argmax 30.5 -> 23.6 us, nb 3: 22.7 -> 20.9 us; Q4_K nb
-// 4: 30.7 -> 26.8 us, nb 3: 28.1 -> 27.3 us; 8192 x 2048 Q4_0 nb 4: 10.9 -> 8.4 us, nb 3: 8.6
-// -> 8.3 us).  Q8_0 (twice the bytes per weight, a cheaper decode), the gated product and small
-// matrices stay on the vector path below QG_MFMA_MIN_NB rows, and two rows everywhere.
+// Batch rows from which the matrix-core kernel takes a call.  Fewer than QG_MFMA_MIN_NB already
+// do on matrices of at least 2^24 weights outside the gated product, for the formats whose
+// vector path spends the most per decoded weight on its one dot chain per batch row (same-box
+// timings, 65536 x 2048, vector -> matrix cores): three rows for Q4_0 (nb 4: 26.4 -> 21.3 us,
+// argmax 30.5 -> 23.6; nb 3: 22.7 -> 20.9), Q4_K (nb 4: 30.7 -> 26.8; 3: 28.1 -> 27.3), Q5_0 (4:
+// 29.2 -> 26.6; 3: 27.1 -> 25.9), IQ4_NL (4: 30.8 -> 23.3; 3: 27.5 -> 23.2), IQ4_XS (4: 29.6 ->
+// 24.0; 3: 27.1 -> 23.2) and Q1_0 (4: 23.4 -> 18.3; 3: 19.7 -> 18.3); four rows for Q5_K (4: 34.4
+// -> 31.7; 3: 31.6 -> 32.2).  Q8_0 (twice the bytes per weight, 4: 31.9 -> 33.8), Q6_K (4: 30.5 ->
+// 30.8), the affine format (4: 28.3 -> 29.5), the gated product (the Q4_0 MLP, 4: even; 3: 19.6 ->
+// 20.8), smaller matrices (the 2048 x 1536 Q8_0 QKV, 4: 6.7 -> 7.2) and two rows (19.9 -> 21.3)
+// keep the vector path.
 static int mfma_min_nb(int fmt, int epi, int64_t N, int64_t K)
 {
-    if ((fmt == FQ4_0 || fmt == FQ4_K) && epi != E_GUS && N * K >= ((int64_t)1 << 24))
-        return QG_MFMA_MIN_NB < 3 ? QG_MFMA_MIN_NB : 3;
-    return QG_MFMA_MIN_NB;
+    int m = QG_MFMA_MIN_NB;
+    if (epi != E_GUS && N * K >= ((int64_t)1 << 24)) {
+        if (fmt == FQ4_0 || fmt == FQ4_K || fmt == FQ5_0 || fmt == FIQ4_NL || fmt == FIQ4_XS ||
+            fmt == FQ1_0)
+            m = 3;
+        else if (fmt == FQ5_K)
+            m = 4;
+    }
+    return m < QG_MFMA_MIN_NB ? m : QG_MFMA_MIN_NB;
 }
 
 // Choose the kernel: the matrix-core kernel from mfma_min_nb batch rows when it takes the shape,

@@ -1,5 +1,6 @@
-"""The matrix-core GEMV (nb 5-16, and nb 3-4 for Q4_0 / Q4_K matrices of at least 2^24 weights)
-on lm_head-sized matrices: 65521..65536 rows (and 8192, the smallest that takes nb 3-4), K <= 2048, where
+"""The matrix-core GEMV (nb 5-16; from nb 3 or 4 for most formats on matrices of at least 2^24
+weights) on lm_head-sized matrices: 65521..65536 rows (and 8192, the smallest that takes nb 3-4;
+Q8_0, Q6_K and the affine format at nb 4 and Q5_K at nb 3 as vector-path contrasts), K <= 2048, where
 each workgroup owns one group of 16 whole-row tiles (one wave per tile, every K step of its rows).
 Every format, every epilogue, K that is not a multiple of a scale round, a ragged last tile;
 sampled rows against the f64 oracle ("Crate inferencelayer" docs: the lm_head GEMV of the decode
@@ -50,7 +51,10 @@ def _packed(fmt, W, N, K):
     (q.IQ4_NL, 65536, 2048, 16), (q.IQ4_XS, 65536, 2048, 12), (q.Q1_0, 65536, 2048, 16),
     (q.AQ4, 65533, 2048, 10), (q.Q4_0, 65536, 2048, 4), (q.Q4_K, 65536, 2048, 4),
     (q.Q4_0, 8192, 2048, 4), (q.Q8_0, 65536, 2048, 4), (q.Q4_0, 65536, 2048, 3),
-    (q.Q4_K, 8192, 2048, 3), (q.Q4_0, 8191, 2048, 3)])
+    (q.Q4_K, 8192, 2048, 3), (q.Q4_0, 8191, 2048, 3), (q.IQ4_NL, 8192, 2048, 4),
+    (q.IQ4_XS, 8192, 2048, 3), (q.Q1_0, 65536, 2048, 3), (q.Q5_0, 8192, 2048, 3),
+    (q.Q5_K, 65536, 2048, 4), (q.Q5_K, 65536, 2048, 3), (q.Q6_K, 65536, 2048, 4),
+    (q.AQ4, 8192, 2048, 4)])
 def test_lm_head_rows_parity(fmt, N, K, nb):
     say(f"lm_head rows fmt={fmt} N={N} K={K} nb={nb}")
     g = wl.rng(7000 + fmt, N + K + nb)
