@@ -218,9 +218,11 @@ int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t 
  * QG_ERR_FORMAT).  x f32 [M][K], y f32 [M][N], 4-B aligned; 1 <= M <= QG_GEMM_MAX_M.  ws: at
  * least qgemm_workspace_bytes(fmt, N, K, M) bytes, 256-B aligned, written before it is read (x
  * converted to f16 once per call, split-K partial tiles); two launches on `stream` (three when
- * K is split: the partial tiles are then added in a fixed order).  The same arithmetic as the
- * row-batch GEMV: exact weights, x rounded to f16 after a power-of-two scaling of each row, f32
- * accumulation. */
+ * K is split: the partial tiles are then added in a fixed order).  Up to QG_MAX_NB rows with x
+ * 16-B aligned the call runs the row-batch GEMV of qgemv instead (one launch, faster there; the
+ * workspace is then not touched).  Either way: exact weights, x rounded to f16 after a
+ * power-of-two scaling (of each row; of each 32-weight chunk on the GEMV's vector path, nb <= 4),
+ * f32 accumulation. */
 #define QG_GEMM_MAX_M (1 << 20)
 int64_t qgemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M);
 int qgemm(int fmt, const void *W, int64_t N, int64_t K, const float *x, int64_t M, float *y,

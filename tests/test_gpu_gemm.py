@@ -102,14 +102,15 @@ def test_qgemm_few_rows_tall_matrix(fmt, M, N, K):
     assert_within(y[:, cols], yr, tol_gemv(A, yr), f"qgemm tall fmt={fmt}")
 
 
-@pytest.mark.parametrize("K", [1024, 8192])
-def test_qgemm_x_only_4_byte_aligned(K):
+@pytest.mark.parametrize("M,K", [(70, 1024), (70, 8192), (5, 1024)])
+def test_qgemm_x_only_4_byte_aligned(M, K):
     """x starting 4 bytes past a 16-byte boundary (the boundary accepts 4-byte alignment): the x
     preparation takes scalar loads, with the row held in registers (K = 1024) and re-read
-    (K = 8192)."""
-    say(f"qgemm x+4 bytes K={K}")
-    M, N = 70, 300
-    g = wl.rng(3400, K)
+    (K = 8192); with M <= 16 such an x keeps the call on the GEMM kernels (an aligned one goes to
+    the row-batch GEMV)."""
+    say(f"qgemm x+4 bytes M={M} K={K}")
+    N = 300
+    g = wl.rng(3400 + M, K)
     W = wl.q4_0_matrix(g, N, K)
     x = wl.normal_f32(g, (M, K))
     big = torch.empty(M * K + 4, dtype=torch.float32, device="cuda")
@@ -120,7 +121,7 @@ def test_qgemm_x_only_4_byte_aligned(K):
     ws = torch.empty(q.qgemm_workspace_bytes(q.Q4_0, N, K, M), dtype=torch.uint8, device="cuda")
     q.qgemm(q.Q4_0, gpu_matrix(q.Q4_0, W, N, K), N, K, xv, M, y, ws)
     yr, A = oracle.gemv(q.Q4_0, W, N, K, x)
-    assert_within(host(y), yr, tol_gemv(A, yr), f"qgemm x+4 K={K}")
+    assert_within(host(y), yr, tol_gemv(A, yr), f"qgemm x+4 M={M} K={K}")
 
 
 def test_qgemm_rows_match_row_batch_gemv():
