@@ -875,12 +875,13 @@ int qgemm(int fmt, const void *W, int64_t N, int64_t K, const float *x, int64_t 
     // Up to QG_MAX_NB rows the row-batch GEMV kernels do the same product faster (one launch,
     // no x preparation or fold pass; 8192 x 2048 Q4_0, GEMM -> GEMV: 16 rows 15.4 -> 8.4 us, 4
     // rows 14.8 -> 8.3, 1 row 14.5 -> 5.5), where their own requirements hold (x 16-byte
-    // aligned); the workspace is then not touched.
+    // aligned) and the GEMV takes the shape on the matrix cores or the streaming kernel (not the
+    // K-tiled fallback); the workspace is then not touched.
     if (M <= QG_MAX_NB) {
         Layout Lg;
         GemvPlan g;
         if (check_common(fmt, W, N, K, x, (int)M, y, &Lg) == QG_OK &&
-            cached_plan(fmt, E_STORE, false, N, K, (int)M, &g))
+            cached_plan(fmt, E_STORE, false, N, K, (int)M, &g) && g.kind != 2)
             return run_gemv(fmt, E_STORE, false, gemv_args(Lg, W, N, K, x, (int)M, y), stream);
     }
     GemmArgs a;

@@ -219,8 +219,8 @@ int qgemv_moe(int fmt, const void *W_experts, int64_t n_exp, int64_t N, int64_t 
  * least qgemm_workspace_bytes(fmt, N, K, M) bytes, 256-B aligned, written before it is read (x
  * converted to f16 once per call, split-K partial tiles); two launches on `stream` (three when
  * K is split: the partial tiles are then added in a fixed order).  Up to QG_MAX_NB rows with x
- * 16-B aligned the call runs the row-batch GEMV of qgemv instead (one launch, faster there; the
- * workspace is then not touched).  Either way: exact weights, x rounded to f16 after a
+ * 16-B aligned, where qgemv runs on its matrix-core or streaming kernel, the call runs that
+ * row-batch GEMV instead (one launch, faster there; the workspace is then not touched).  Either way: exact weights, x rounded to f16 after a
  * power-of-two scaling (of each row; of each 32-weight chunk on the GEMV's vector path, nb <= 4),
  * f32 accumulation. */
 #define QG_GEMM_MAX_M (1 << 20)

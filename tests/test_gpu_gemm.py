@@ -39,7 +39,8 @@ def _gemm(fmt, Wp, N, K, x):
                                        (q.Q4_0, 100, 3000, 1024), (q.Q1_0, 17, 300, 2048),
                                        (q.Q1_0, 512, 517, 1024), (q.Q1_0, 200, 130, 128),
                                        (q.Q1_0, 131, 1000, 640), (q.Q4_0, 65, 300, 256),
-                                       (q.Q1_0, 64, 1000, 128), (q.Q8_0, 1, 16, 32)])
+                                       (q.Q1_0, 64, 1000, 128), (q.Q8_0, 1, 16, 32),
+                                       (q.Q4_0, 12, 500, 8192)])
 def test_qgemm_parity(fmt, M, N, K):
     say(f"qgemm fmt={fmt} M={M} N={N} K={K}")
     g = wl.rng(3000 + fmt, M + N + K)
