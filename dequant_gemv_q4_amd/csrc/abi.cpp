@@ -419,6 +419,30 @@ static int run_gemv(int fmt, int epi, bool nrm, GemvArgs a, void *stream)
     GemvPlan g;
     if (!cached_plan(fmt, epi, nrm, a.N, a.K, a.nb, &g))
         return QG_ERR_SHAPE;
+    // 5..16 rows that only the K-tiled kernel takes (K > 4096, or the norm prologue with
+    // K > 2048, or K not whole 128-weight steps) run as batches of at most 4 rows on the vector
+    // path where it takes the shape: every output row depends on its own x row alone (2048 x
+    // 8192 Q4_0 + residual: 8 rows 44.7 -> ~20 us, 16 rows 106 -> ~40 us).  The argmax batches
+    // reuse the workspace one after the other on the stream.
+    if (g.kind == 2 && a.nb > 4) {
+        GemvPlan g4;
+        if (cached_plan(fmt, epi, nrm, a.N, a.K, 4, &g4) && g4.kind == 1) {
+            for (int r0 = 0; r0 < a.nb; r0 += 4) {
+                GemvArgs c = a;
+                c.nb = a.nb - r0 < 4 ? a.nb - r0 : 4;
+                c.x = a.x + (int64_t)r0 * a.K;
+                c.y = a.y + (int64_t)r0 * a.N;
+                if (a.res)
+                    c.res = a.res + (int64_t)r0 * a.res_rstride;
+                if (a.idx)
+                    c.idx = a.idx + r0;
+                const int st = run_gemv(fmt, epi, nrm, c, stream);
+                if (st != QG_OK)
+                    return st;
+            }
+            return QG_OK;
+        }
+    }
     if (g.kind == 0) {
         const MfmaPlan &mp = g.mp;
         grid = mp.grid;

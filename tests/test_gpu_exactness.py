@@ -10,8 +10,10 @@ workloads do not reach.
   batch size (vector and matrix-core paths).
 * Q4_0 against its exact Q8_0 upcast ("Crate inferencelayer" docs, q4_0_to_q8_0n: d8 = d4,
   q8 = nib - 8): on integer inputs both formats give the same bits.
-* Shapes served by the K-tiled kernel: rows longer than 256 chunks at nb <= 4, K > 4096 at nb >= 5,
-  and the norm prologue with K > 2048 at nb >= 5; and Q8_0 bytes of -128.
+* Shapes the matrix-core kernel does not take at nb >= 5 (K > 4096, the norm prologue with
+  K > 2048): batches of at most 4 rows on the vector path where its rows fit (<= 256 chunks), else
+  the K-tiled kernel, which also serves rows longer than 256 chunks at nb <= 4; and Q8_0 bytes of
+  -128.
 """
 import numpy as np
 import pytest
@@ -149,7 +151,8 @@ def test_q4_0_equals_its_q8_0_upcast(nb):
 
 
 TILED_CASES = [(q.Q4_0, 70, 16384, 1), (q.Q4_0, 33, 65536, 2), (q.Q8_0, 50, 8192, 2),
-               (q.Q8_0, 40, 8192, 3), (q.Q4_0, 40, 8192, 8), (q.Q8_0, 31, 6144, 12)]
+               (q.Q8_0, 40, 8192, 3), (q.Q4_0, 40, 8192, 8), (q.Q8_0, 31, 6144, 12),
+               (q.Q4_0, 40, 16384, 8), (q.Q4_0, 37, 8192, 13)]
 
 
 @pytest.mark.parametrize("fmt,N,K,nb", TILED_CASES)
@@ -163,7 +166,8 @@ def test_k_tiled_shapes(fmt, N, K, nb):
     assert_within(y, yr, tol_gemv(A, yr), f"tiled fmt={fmt} N={N} K={K} nb={nb}")
 
 
-@pytest.mark.parametrize("fmt,N,K,nb", [(q.Q4_0, 60, 4096, 6), (q.Q8_0, 45, 4096, 8)])
+@pytest.mark.parametrize("fmt,N,K,nb", [(q.Q4_0, 60, 4096, 6), (q.Q8_0, 45, 4096, 8),
+                                       (q.Q4_0, 50, 16384, 6)])
 def test_k_tiled_norm_and_gated(fmt, N, K, nb):
     say(f"tiled nrm/gus fmt={fmt} N={N} K={K} nb={nb}")
     g = wl.rng(1100 + fmt, N + nb)
@@ -194,3 +198,40 @@ def test_q8_0_minus_128_bytes(N, K, nb):
     y = _gemv(q.Q8_0, W, N, K, x)
     yr, A = oracle.gemv(q.Q8_0, W, N, K, x)
     assert_within(y, yr, tol_gemv(A, yr), f"q8 -128 N={N} K={K} nb={nb}")
+
+
+@pytest.mark.parametrize("nb", [5, 7, 16])
+def test_batched_vector_path_epilogues(nb):
+    """5..16 rows of K = 8192 run as batches of at most 4 rows on the vector path: the residual
+    (in place), norm + bias and argmax epilogues of each batch take their own rows (and the argmax
+    its own index slots)."""
+    fmt, N, K = q.Q4_0, 300, 8192
+    say(f"batched vector path nb={nb}")
+    g = wl.rng(1200, nb)
+    W = wl.matrix(fmt, g, N, K)
+    x = wl.normal_f32(g, (nb, K))
+    Wd = gpu_matrix(fmt, W, N, K)
+
+    res = wl.normal_f32(g, (nb, N))
+    yres = dev(res.copy())
+    q.qgemv_res(fmt, Wd, N, K, dev(x), yres, nb, yres)            # in place
+    yr, A = oracle.qgemv_res(fmt, W, N, K, x, res)
+    assert_within(host(yres), yr, tol_gemv(A, yr), "res")
+
+    gamma = wl.gamma_f32(g, K)
+    bias = wl.normal_f32(g, (N,))
+    yb = torch.empty((nb, N), dtype=torch.float32, device="cuda")
+    q.qgemv_nrm_bias(fmt, Wd, N, K, dev(x), dev(gamma), 1e-5, dev(bias), nb, yb)
+    yr, A = oracle.qgemv_nrm_bias(fmt, W, N, K, x, gamma, 1e-5, bias)
+    assert_within(host(yb), yr, tol_gemv(A, yr), "nrm bias")
+
+    logits = torch.empty((nb, N), dtype=torch.float32, device="cuda")
+    idx = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+    ws = D.workspace(q.OP_ARGMAX, fmt, N, K, nb)
+    q.qgemv_argmax(fmt, Wd, N, K, dev(x), nb, logits, idx, ws)
+    lg, ig = host(logits), host(idx)
+    for r in range(nb):
+        i = int(ig[r])
+        assert 0 <= i < N and lg[r, i] == lg[r].max() and int(np.argmax(lg[r])) == i, r
+    yr, A = oracle.gemv(fmt, W, N, K, x)
+    assert_within(lg, yr, tol_gemv(A, yr), "argmax logits")
