@@ -488,10 +488,10 @@ const char *qgemv_status_str(int status)
     switch (status) {
     case QG_OK: return "ok";
     case QG_ERR_NULL: return "a required pointer is NULL";
-    case QG_ERR_FORMAT: return "unknown or unsupported format (Q4_0=2, Q5_0=6, Q8_0=8, Q4_K=12, Q5_K=13, Q6_K=14; experts: Q4_0, Q8_0, Q4_K)";
-    case QG_ERR_SHAPE: return "bad shape (N, K, nb, topk or n_exp out of range, or K not a multiple of the block)";
-    case QG_ERR_ALIGN: return "misaligned pointer (W needs 256 B, x and gamma 16 B, other arrays 4 B)";
-    case QG_ERR_WORKSPACE: return "workspace missing or smaller than qgemv_workspace_bytes()";
+    case QG_ERR_FORMAT: return "unknown or unsupported format (Q4_0=2, Q5_0=6, Q8_0=8, Q4_K=12, Q5_K=13, Q6_K=14, IQ4_NL=20, IQ4_XS=23, Q1_0=40, affine Q4=41; experts: Q4_0, Q8_0, Q4_K; qgemm: Q4_0, Q8_0, Q1_0)";
+    case QG_ERR_SHAPE: return "bad shape (N, K, nb, M, topk or n_exp out of range, or K not a multiple of the block)";
+    case QG_ERR_ALIGN: return "misaligned pointer (W and workspaces need 256 B, x and gamma 16 B (qgemm x: 4 B), other arrays 4 B)";
+    case QG_ERR_WORKSPACE: return "workspace missing or smaller than qgemv_workspace_bytes() / qgemm_workspace_bytes()";
     case QG_ERR_LAUNCH: return "HIP launch failed";
     case QG_ERR_ALIAS: return "an output overlaps an input";
     default: return "unknown status";

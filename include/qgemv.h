@@ -54,8 +54,10 @@
  *    that is 0).  It is scratch that every call writes before it reads (argmax: one partial key
  *    per workgroup; experts: partial outputs), except the sticky bad-id flag of qgemv_moe, so a
  *    qgemv_moe workspace must be zero-filled once after allocation.  Calls that share one
- *    workspace must be ordered on one stream.  An operation with a workspace runs as two
- *    launches on `stream` (the main kernel, then a small fold / combine kernel).
+ *    workspace must be ordered on one stream.  The argmax and expert operations follow their
+ *    main kernel with a small fold / combine kernel on `stream`.  A call of 5..16 rows that the
+ *    matrix-core kernel does not take (K > 4096, or K > 2048 with the norm prologue) runs as
+ *    batches of at most 4 rows, each its own launch (pair), one after the other on `stream`.
  *  - Errors: every argument is validated on the host before anything is launched; a failed
  *    check returns its status and launches nothing.  QG_ERR_LAUNCH reports a HIP error from the
  *    launch itself.  qgemv_status_str gives a static description.
