@@ -601,6 +601,7 @@ def main():
         "roofline": s["roofline"],
         "cpu_baseline": None,
         "pages_context": PAGES_CONTEXT,
+        "host_loadavg": list(os.getloadavg()),
     }
     if "tflops" in s:
         out["tflops"] = s["tflops"]
@@ -621,6 +622,11 @@ def main():
         extras["lm_head_nb1"] = run_extra("lm_head", lambda: make_lm_head(False, 1), es, ew, torch)
         extras["lm_head_nb4"] = run_extra("lm_head nb=4", lambda: make_lm_head(False, 4), es, ew,
                                           torch)
+        # the gate's GEMV over shorter matrices (K = 2048): where the launch ramp takes over
+        for n in (2048, 8192, 16384, 32768):
+            extras[f"gemv_q4_0_n{n}"] = run_extra(f"gemv N={n}",
+                                                  lambda n=n: make_gemv(False, 1, n, 2048),
+                                                  es, ew, torch)
         import dequant_gemv_q4_amd as qq
         for f, nm in ((qq.Q8_0, "q8_0"), (qq.Q4_K, "q4_k"), (qq.Q5_0, "q5_0"), (qq.Q5_K, "q5_k"),
                       (qq.Q6_K, "q6_k"), (qq.IQ4_NL, "iq4_nl"), (qq.IQ4_XS, "iq4_xs"),
