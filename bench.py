@@ -541,8 +541,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the kernels shard by output rows; see the design notes)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (every entry "
+              "point would shard by output rows, one GPU's share being the single-GPU kernel "
+              "at N / G rows)", file=sys.stderr)
         sys.exit(2)
 
     import torch
