@@ -41,6 +41,7 @@ def _noalloc_raw(fmt, Wp, N, K, xd, nb, logits, idx):
     (q.Q4_0, (65536, 2048, 4), (5000, 1024, 1)),     # many partial keys, then few
     (q.Q8_0, (20000, 1536, 16), (777, 512, 3)),     # row-batch kernel, then vector kernel
     (q.Q4_K, (9000, 2048, 2), (300, 256, 1)),
+    (q.Q4_0, (3000, 8192, 7), (500, 8192, 6)),      # long rows: batches of at most 4 rows
 ])
 def test_noalloc_matches_workspace_argmax(fmt, big, small):
     for i, (N, K, nb) in enumerate((big, small)):
