@@ -96,6 +96,10 @@ __global__ __launch_bounds__(MF_THREADS) void k_mfma(GemvArgs a)
         const int fc = f < K4 ? f : K4 - 1;
         xv[i] = reinterpret_cast<const float4 *>(a.x)[(int64_t)(xrow ? bx : 0) * K4 + fc];
     }
+    // the weight pointers' kernel-argument line is fetched now, beside x's, not after x arrives
+    asm volatile("" ::"s"(a.qs0), "s"(a.sc0));
+    if constexpr (MATS == 2)
+        asm volatile("" ::"s"(a.qs1), "s"(a.sc1));
     // gamma (norm): K4 <= 512 float4s, one per thread, staged in the (not yet used) result area
     float4 gone = make_float4(0.f, 0.f, 0.f, 0.f);
     if constexpr (NRM)

@@ -868,8 +868,7 @@ void k_stream(GemvArgs a)
     const int tgl = a.tg_log2, TG = 1 << tgl;    // groups per tile (1..8, set by the host)
     const int64_t T = (a.N + R - 1) / R;
     const int n_tiles = (int)((T + TG - 1) >> tgl);
-    const int pool = (int)blockIdx.x < n_tiles
-                         ? ((n_tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1) << tgl : 0;
+    const int pool = (int)(((uint32_t)(n_tiles - (int)blockIdx.x) + gridDim.x - 1u) / gridDim.x) << tgl;
     auto gmap = [&](int c) -> int64_t {
         return ((int64_t)((c >> tgl) * (int)gridDim.x + (int)blockIdx.x) << tgl) + (c & (TG - 1));
     };
