@@ -228,6 +228,8 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm(GemmArgs a)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ir = lane & 15, lc = lane >> 4;
+    // the pointers' kernel-argument line is fetched with the tile counts', not after them
+    asm volatile("" ::"s"(a.qs), "s"(a.xh));
 
     // tiles of this workgroup (workgroup id i runs on XCD i % 8): XCD x owns weight tiles
     // [x NTX, (x + 1) NTX) and numbers its tiles k8 row-tile-major, then split by split; its
